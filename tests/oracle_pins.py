@@ -1,0 +1,212 @@
+"""Pins for the oracle: checks against what the pages and the mathematics fix.
+
+Each pin takes an oracle-like module ``o`` and raises AssertionError on a mismatch. The
+same pins run against the real oracle (test_oracle_pins.py) and against copies of it with
+a planted mistake (test_oracle_mutants.py), which every pin set must catch.
+
+Nothing here retypes the oracle's formulas: expected values are hand-derived closed
+forms, invariants of the quantiser, or exact sums.
+
+Pages cited: "Beating FP16 with 4-bit Weights: A Portable W4A16 GEMM in Triton",
+section "The design" (grouping, K-packing, dequant (w - zero) * scale, fp32 accumulate).
+"""
+import math
+
+import numpy as np
+
+import synth
+
+
+def _exact_group_weight(K, N, centres, log2_spacing):
+    """W[k, n] = ((k + n) mod 16 - c_g) * 2**e_g for K-group g = k // 128.
+
+    Each aligned block of 16 rows in a column visits every residue 0..15 once, so every
+    group's min is -c_g * d_g and its max (15 - c_g) * d_g: the scale is exactly d_g
+    (a power of two), the zero is exactly c_g and the codes are (k + n) mod 16.
+    """
+    k = np.arange(K)[:, None]
+    n = np.arange(N)[None, :]
+    g = k // 128
+    c = np.asarray(centres, dtype=np.float64)[g]
+    d = np.exp2(np.asarray(log2_spacing, dtype=np.float64))[g]
+    return (((k + n) % 16 - c) * d).astype(np.float32)
+
+
+def pin_hand_words(o):
+    """Packed words worked out by hand: nibble j of word i is K index 8i + j at shift 4j."""
+    codes = np.zeros((8, 5), dtype=np.uint8)
+    codes[:, 0] = np.arange(8)          # 0,1,...,7   -> 0x76543210
+    codes[:, 1] = 15                    # all ones    -> 0xFFFFFFFF == int32 -1
+    codes[7, 2] = 8                     # only top    -> 0x80000000 == int32 min
+    codes[0, 3] = 1                     # only bottom -> 0x00000001
+    codes[3, 4] = 0xA                   # nibble 3    -> 0x0000A000
+    words = o.pack(codes)
+    assert words.dtype == np.int32 and words.shape == (1, 5)
+    expect = np.array([[0x76543210, -1, -2**31, 1, 0xA000]], dtype=np.int64)
+    assert np.array_equal(words.astype(np.int64), expect), words
+    assert np.array_equal(o.unpack(words), codes)
+
+
+def pin_roundtrip(o):
+    """pack and unpack are inverse bijections (codes <-> words), bit for bit."""
+    for K, N, seed in [(8, 1, 0), (64, 24, 1), (256, 13, 2)]:
+        c = synth.uniform_codes(K, N, seed)
+        assert np.array_equal(o.unpack(o.pack(c)), c)
+    rng = np.random.default_rng(7)
+    words = rng.integers(-2**31, 2**31, size=(9, 11), dtype=np.int64).astype(np.int32)
+    assert np.array_equal(o.pack(o.unpack(words)), words)
+
+
+def pin_exact_group(o):
+    """K=128, N=8 exact case: scale 2**-6, zero 8, codes (k+n) mod 16, zero error."""
+    W = _exact_group_weight(128, 8, [8], [-6])
+    codes, s, z = o.quantize(W)
+    assert s.dtype == np.float16 and z.dtype == np.float16
+    assert s.shape == (1, 8) and z.shape == (1, 8)
+    assert np.all(s == np.float16(2.0 ** -6)) and np.all(z == 8)
+    k = np.arange(128)[:, None]
+    n = np.arange(8)[None, :]
+    assert np.array_equal(codes, ((k + n) % 16).astype(np.uint8))
+    assert np.array_equal(o.dequant(codes, s, z), W)
+    qw, s2, z2 = o.quantize_pack(W)
+    # column 0: rows 0..7 hold codes 0..7, rows 8..15 codes 8..15; column 4 is shifted by 4
+    u = qw.view(np.uint32)
+    assert u.shape == (16, 8)
+    assert u[0, 0] == 0x76543210 and u[1, 0] == 0xFEDCBA98
+    assert u[0, 4] == 0xBA987654 and u[1, 4] == 0x3210FEDC
+
+
+def pin_exact_products(o):
+    """Hand-summed products on the K=128, N=8 case (every value exact in fp16)."""
+    W = _exact_group_weight(128, 8, [8], [-6])
+    qw, s, z = o.quantize_pack(W)
+    ones = np.ones((1, 128), dtype=np.float16)
+    # sum over 8 blocks of sum_{r=0}^{15} (r - 8) / 64 = 8 * (-8) / 64 = -1 for every column
+    assert np.array_equal(o.matmul(ones, qw, s, z), -np.ones((1, 8)))
+    alt = ((-1.0) ** np.arange(128))[None, :].astype(np.float16)
+    # (-1)^k (r - 8) summed over a block = (-1)^n * (-8); over 8 blocks / 64 -> -(-1)^n
+    assert np.array_equal(o.matmul(alt, qw, s, z), -((-1.0) ** np.arange(8))[None, :])
+    for k0 in (0, 5, 77, 127):
+        e = np.zeros((1, 128), dtype=np.float16)
+        e[0, k0] = 1
+        expect = (((k0 + np.arange(8)) % 16) - 8) / 64.0
+        assert np.array_equal(o.matmul(e, qw, s, z)[0], expect)
+
+
+def pin_multigroup(o):
+    """Three K-groups with different spacing and centre; zeros 8, 3, 12; y(ones) = -19."""
+    centres, log2d = [8, 3, 12], [-6, -5, -4]
+    W = _exact_group_weight(384, 5, centres, log2d)
+    codes, s, z = o.quantize(W)
+    assert s.shape == (3, 5) and z.shape == (3, 5)
+    for g in range(3):
+        assert np.all(s[g] == np.float16(2.0 ** log2d[g])) and np.all(z[g] == centres[g])
+    assert np.array_equal(o.dequant(codes, s, z), W)
+    qw = o.pack(codes)
+    ones = np.ones((1, 384), dtype=np.float16)
+    # per group 8 * sum_r (r - c) * d = 8 * (120 - 16 c) * d: -1 + 18 - 36 = -19
+    assert np.array_equal(o.matmul(ones, qw, s, z), np.full((1, 5), -19.0))
+    for k0 in (3, 130, 300, 383):
+        e = np.zeros((2, 384), dtype=np.float16)
+        e[1, k0] = 1
+        g = k0 // 128
+        expect = (((k0 + np.arange(5)) % 16) - centres[g]) * 2.0 ** log2d[g]
+        y = o.matmul(e, qw, s, z)
+        assert np.array_equal(y[1], expect) and np.array_equal(y[0], np.zeros(5))
+
+
+def _bound_checks(o, W):
+    codes, s16, z16 = o.quantize(W)
+    K, N = W.shape
+    G = K // 128
+    s = s16.astype(np.float64)
+    zz = z16.astype(np.float64)
+    deq = o.dequant(codes, s16, z16).astype(np.float64)
+    Wd = W.astype(np.float64)
+    Wg = Wd.reshape(G, 128, N)
+    cg = codes.reshape(G, 128, N)
+    mn, mx = Wg.min(axis=1), Wg.max(axis=1)
+    # fp16 scale is the nearest fp16 to (max - min)/15: within half an fp16 ulp (2**-11 rel.)
+    target = (mx - mn) / 15.0
+    assert np.all(np.abs(s - target) <= target * 2.0 ** -11 * (1 + 2.0 ** -10))
+    # the zero point puts the group minimum at code 0 (round(mn/s) = -round(-mn/s))
+    argmin = Wg.argmin(axis=1)
+    assert np.all(np.take_along_axis(cg, argmin[:, None, :], axis=1) == 0)
+    assert np.all(np.abs(zz * s + mn) <= 0.5 * s * (1 + 2.0 ** -20))
+    # the group maximum lands on code 14 or 15
+    argmax = Wg.argmax(axis=1)
+    top = np.take_along_axis(cg, argmax[:, None, :], axis=1)
+    assert np.all((top == 14) | (top == 15))
+    # error bound: |W - deq| <= s/2 (plus the fp32 rounding of w/s) unless clamped at 15
+    err = np.abs(Wd - deq).reshape(G, 128, N)
+    slack = np.abs(Wg) * 2.0 ** -22
+    half = 0.5 * s[:, None, :] + slack
+    clamped = (cg == 15) & (Wg > deq.reshape(G, 128, N) + half)
+    assert np.all(err[~clamped] <= np.broadcast_to(half, err.shape)[~clamped])
+    # clamped codes only ever occur at the top and stay within s*(1/2 + 15*2**-11)
+    wide = 0.5 * s[:, None, :] + 15 * 2.0 ** -11 * s[:, None, :] + slack
+    assert np.all(err[clamped] <= np.broadcast_to(wide, err.shape)[clamped])
+    # dequant of every code is the exact value (q - z) * s (no rounding in fp32)
+    assert np.array_equal(deq.reshape(G, 128, N),
+                          (cg.astype(np.float64) - zz[:, None, :]) * s[:, None, :])
+    return int(clamped.sum())
+
+
+def pin_bounds_random(o):
+    """Min-code invariant, max code 14/15, fp16-nearest scale and the error bound on
+    random weights: the N(0, 0.02) workload draw and one-signed / wide groups."""
+    _bound_checks(o, synth.weight(512, 96, wid=0))
+    _bound_checks(o, synth.weight_custom(256, 64, seed=1, std=0.02, mean=1.0))
+    _bound_checks(o, synth.weight_custom(256, 64, seed=2, std=3.0, mean=-2.0))
+
+
+def pin_fsum(o):
+    """Oracle y within K * 2**-53 * sum|terms| of math.fsum over the exact products."""
+    M, K, N = 3, 256, 7
+    W = synth.weight(K, N, wid=0)
+    x = synth.activations(M, K, wid=0)
+    qw, s, z = o.quantize_pack(W)
+    y = o.matmul(x, qw, s, z)
+    assert y.dtype == np.float64 and y.shape == (M, N)
+    codes = o.unpack(qw)
+    deq = o.dequant(codes, s, z)
+    for m in range(M):
+        for n in range(N):
+            terms = [float(x[m, k]) * float(deq[k, n]) for k in range(K)]
+            exact = math.fsum(terms)
+            bound = K * 2.0 ** -53 * sum(abs(t) for t in terms)
+            assert abs(y[m, n] - exact) <= bound, (m, n, y[m, n], exact)
+
+
+def pin_dequant_fp16_rounding(o):
+    """fp16 dequant rounds the exact product half-to-even.
+
+    scale = 1 + 3*2**-10 (an fp16 value), q - z = 3: the exact product 3 + 9*2**-10 lies
+    halfway between the fp16 neighbours 3 + 4*2**-9 and 3 + 5*2**-9; the even one is
+    3 + 4*2**-9 = 3.0078125.
+    """
+    codes = np.full((128, 1), 11, dtype=np.uint8)
+    s = np.array([[1 + 3 * 2.0 ** -10]], dtype=np.float16)
+    z = np.array([[8]], dtype=np.float16)
+    d16 = o.dequant_fp16(codes, s, z)
+    assert d16.dtype == np.float16
+    assert np.all(d16 == np.float16(3.0078125))
+    assert np.all(o.dequant(codes, s, z) == np.float32(3 + 9 * 2.0 ** -10))
+
+
+def pin_scale_rounding(o):
+    """A group whose (max - min)/15 is not an fp16 value stores the nearest fp16 scale.
+
+    Values 0 .. 15 * 1.001 spread evenly: (max-min)/15 = 1.001, nearest fp16 is
+    1 + 1*2**-10 = 1.0009765625 (1.001 lies 0.24 ulp above it).
+    """
+    W = np.zeros((128, 1), dtype=np.float32)
+    W[:16, 0] = np.arange(16, dtype=np.float32) * np.float32(1.001)
+    codes, s, z = o.quantize(W)
+    assert s[0, 0] == np.float16(1.0009765625) and z[0, 0] == 0
+    assert codes[15, 0] == 15 and codes[16:, 0].max() == 0
+
+
+ALL_PINS = [pin_hand_words, pin_roundtrip, pin_exact_group, pin_exact_products,
+            pin_multigroup, pin_bounds_random, pin_fsum, pin_dequant_fp16_rounding,
+            pin_scale_rounding]

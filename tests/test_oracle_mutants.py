@@ -1,0 +1,105 @@
+"""Plant plausible mistakes in copies of the oracle and check that the pins catch each.
+
+Every mutant is the oracle's own source with one edit, executed into a fresh module on
+the CPU. A mutant that passes every pin would mean the pins cannot tell that mistake
+from the method, so the test fails.
+"""
+import os
+import types
+
+import pytest
+
+import oracle_pins
+
+SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "oracle", "w4a16_oracle.py")
+
+MUTANTS = [
+    # packing / unpacking
+    ("nibble order reversed in pack",
+     "codes[j::NIBBLES_PER_WORD, :].astype(np.uint32) << np.uint32(4 * j)",
+     "codes[j::NIBBLES_PER_WORD, :].astype(np.uint32) << np.uint32(4 * (7 - j))"),
+    ("nibble order reversed in both pack and unpack",
+     "np.uint32(4 * j)", "np.uint32(4 * (7 - j))"),
+    ("K split into 8 planes instead of 8 consecutive rows (pack and unpack)",
+     [("words |= codes[j::NIBBLES_PER_WORD, :]", "words |= codes[j * (K // 8):(j + 1) * (K // 8), :]"),
+      ("codes[j::NIBBLES_PER_WORD, :] = (words", "codes[j * P:(j + 1) * P, :] = (words")], None),
+    ("unpack mask 0x7",
+     "& np.uint32(0xF)", "& np.uint32(0x7)"),
+    # quantiser
+    ("floor instead of round for codes",
+     "q = np.rint(Wg / s[:, None, :]) + z[:, None, :]",
+     "q = np.floor(Wg / s[:, None, :]) + z[:, None, :]"),
+    ("zero point with the wrong sign",
+     "z = np.rint(-mn / s)", "z = np.rint(mn / s)"),
+    ("scale over 16 levels",
+     "s32 = rng / np.float32(QMAX)", "s32 = rng / np.float32(16)"),
+    ("codes computed with the unrounded fp32 scale",
+     "q = np.rint(Wg / s[:, None, :]) + z[:, None, :]",
+     "q = np.rint(Wg / s32[:, None, :]) + z[:, None, :]"),
+    ("zero computed with the unrounded fp32 scale",
+     "z = np.rint(-mn / s)", "z = np.rint(-mn / s32)"),
+    ("no upper clamp",
+     "q = np.clip(q, 0, QMAX)", "q = np.clip(q, 0, 16)"),
+    ("groups interleaved along K (k mod G) instead of contiguous",
+     "Wg = W.reshape(G, group_size, N)",
+     "Wg = W.reshape(group_size, G, N).transpose(1, 0, 2)"),
+    ("range from max only",
+     "rng = mx - mn", "rng = mx - np.float32(0)"),
+    # dequant
+    ("dequant adds the zero",
+     "(codes.astype(np.float32) - z) * s", "(codes.astype(np.float32) + z) * s"),
+    ("dequant forgets to scale the zero",
+     "(codes.astype(np.float32) - z) * s", "codes.astype(np.float32) * s - z"),
+    ("dequant drops the zero",
+     "(codes.astype(np.float32) - z) * s", "codes.astype(np.float32) * s"),
+    ("group broadcast tiled instead of repeated",
+     "s = np.repeat(np.asarray(scales).astype(np.float32), group_size, axis=0)",
+     "s = np.tile(np.asarray(scales).astype(np.float32), (group_size, 1))"),
+    ("fp16 dequant rounds half away from zero",
+     "return dequant(codes, scales, zeros, group_size).astype(np.float16)",
+     "d = dequant(codes, scales, zeros, group_size).astype(np.float64); "
+     "return (np.sign(d) * np.floor(np.abs(d) * 2.0 ** 9 + 0.5) / 2.0 ** 9).astype(np.float16)"),
+    # matmul
+    ("matmul accumulates in fp32",
+     "w = dequant(codes, scales, zeros, group_size).astype(np.float64)\n    return x.astype(np.float64) @ w",
+     "w = dequant(codes, scales, zeros, group_size)\n    return (x.astype(np.float32) @ w).astype(np.float64)"),
+    ("matmul drops the last K row",
+     "return x.astype(np.float64) @ w", "return x.astype(np.float64)[:, :-1] @ w[:-1]"),
+    ("matmul rounds weights to fp16 first",
+     "w = dequant(codes, scales, zeros, group_size).astype(np.float64)",
+     "w = dequant(codes, scales, zeros, group_size).astype(np.float16).astype(np.float64)"),
+]
+
+
+def _edits(old, new):
+    return old if new is None else [(old, new)]
+
+
+def _load_mutant(old, new):
+    src = open(SRC_PATH).read()
+    for a, b in _edits(old, new):
+        assert src.count(a) >= 1, f"mutation anchor not found: {a!r}"
+        src = src.replace(a, b)
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src, "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def test_mutation_anchors_present():
+    src = open(SRC_PATH).read()
+    for name, old, new in MUTANTS:
+        for a, _ in _edits(old, new):
+            assert src.count(a) >= 1, name
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new):
+    mod = _load_mutant(old, new)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mod)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the mutant: {name}"
