@@ -1,0 +1,165 @@
+/*
+ * w4a16.h - C ABI of the MI355X (gfx950) W4A16 weight-only GEMM/GEMV library.
+ *
+ *   y[M, N] = x[M, K] . dequant(Wq)[K, N],   dequant(q) = (q - zero) * scale
+ *
+ * The operation is the one described on "Beating FP16 with 4-bit Weights: A Portable
+ * W4A16 GEMM in Triton", section "The design": fp16 activations, 4-bit weights with one
+ * scale and one zero-point per group of 128 rows of the contraction dimension, eight
+ * 4-bit values packed into one int32 along that dimension (packed row i, nibble j holds
+ * K index 8*i + j), dequantised inside the product, fp32 accumulation.  The GemLite README
+ * ("Packing") states the same (W_q - zeros) * scales convention.
+ *
+ * Layouts (all row-major, contiguous, no padding):
+ *   W        fp32  [K, N]        host; input x output (y = x . W)
+ *   qweight  int32 [K/8, N]      nibble j of word [i, n] (bits 4j..4j+3) is code q[8i+j, n]
+ *   scales   fp16  [K/g, N]      one per (K-group, column), g = group_size
+ *   zeros    fp16  [K/g, N]      integer-valued fp16 zero points, |zero| <= 1024
+ *   x        fp16  [M, K]
+ *   y        fp16  [M, N]        fully overwritten (never accumulated into)
+ * fp16 values cross the ABI as their 16-bit patterns (uint16_t / void*).
+ *
+ * Ownership: every buffer is the caller's. The library never frees or keeps a pointer to
+ * a caller buffer after a call returns. It owns one split-K workspace (fp32 partial sums
+ * and arrival counters) per (device, stream) pair, allocated on first use and grown when a
+ * larger one is needed; two calls on one stream are ordered by the stream, so they never
+ * share it concurrently.
+ *
+ * Errors: every entry point returns W4A16_OK (0) or a negative W4A16_ERR_* code and never
+ * throws. Arguments are validated before any HIP call is made; a call rejected by
+ * validation changes no output. w4a16_strerror() names a code; w4a16_last_error_detail() gives the message of
+ * the last failure on the calling thread.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A16_OK                 0
+#define W4A16_ERR_INVALID_ARG   -1  /* null pointer, non-positive size, bad enum value   */
+#define W4A16_ERR_UNSUPPORTED   -2  /* valid but not built: group size, K or N multiple  */
+#define W4A16_ERR_ALIGNMENT     -3  /* a device pointer is not 16-byte aligned           */
+#define W4A16_ERR_NONFINITE     -4  /* NaN/Inf in W, or a scale that overflows fp16      */
+#define W4A16_ERR_HIP           -5  /* a HIP runtime call or kernel launch failed        */
+
+/* Kernel selection for w4a16_matmul_ex / w4a16_plan. */
+#define W4A16_KERNEL_AUTO     0   /* shape-based dispatcher (what w4a16_matmul uses)        */
+#define W4A16_KERNEL_SKINNY   1   /* decode: weight stream, split-K, M <= 64 per row block  */
+#define W4A16_KERNEL_PREFILL  2   /* prefill: LDS-staged fp16 dequant tiles feeding MFMA    */
+
+/*
+ * Execution plan of one w4a16_matmul call (what the dispatcher chose, or what a caller
+ * forces through w4a16_matmul_ex). Fields a caller sets to 0 are chosen by the library.
+ *   kernel     W4A16_KERNEL_*.
+ *   kc         SKINNY: K-steps of 32 rows that one wavefront streams (>= 1).
+ *   splits     SKINNY: work-groups along K per 64-column strip (derived from kc; output).
+ *   row_tiles  SKINNY: 16-row MFMA tiles per work-group (1..4; derived from M; output).
+ *   tile       PREFILL: tile configuration id (0 = default).
+ */
+typedef struct w4a16_plan {
+    int32_t kernel;
+    int32_t kc;
+    int32_t splits;
+    int32_t row_tiles;
+    int32_t tile;
+    int32_t reserved[3];
+} w4a16_plan_t;
+
+/*
+ * w4a16_pack - quantise and pack a weight matrix on the host (CPU only, synchronous).
+ *
+ * Follows "The design" (one scale and zero per 128-row K-group per column, eight codes per
+ * int32 along K) with the asymmetric min/max quantiser, per (group, column):
+ *   scale = fp16_rne((max - min) / 15)          (1.0 if that rounds to 0)
+ *   zero  = rne(-min / scale)                   (stored as fp16; not clamped)
+ *   q     = clamp(rne(w / scale) + zero, 0, 15) (rne = round half to even)
+ * every step an IEEE fp32 operation (true division, no fused multiply-add).
+ * Deterministic and independent of the number of threads used.
+ *
+ *   W          host fp32 [K, N]
+ *   K, N       K >= group_size, K % group_size == 0; N >= 1
+ *   group_size must be 128
+ *   qweight    host int32 [K/8, N]     (written)
+ *   scales     host fp16 bits [K/g, N] (written)
+ *   zeros      host fp16 bits [K/g, N] (written)
+ * Errors: INVALID_ARG (null, K or N <= 0), UNSUPPORTED (group size, K % g, |zero| > 1024),
+ * NONFINITE (NaN/Inf in W, scale overflow). Argument errors and NaN/Inf in W are found
+ * before anything is written; after a scale overflow or an out-of-domain zero point
+ * (found while packing) the contents of qweight / scales / zeros are unspecified.
+ */
+int w4a16_pack(const float* W, int64_t K, int64_t N, int64_t group_size,
+               int32_t* qweight, uint16_t* scales, uint16_t* zeros);
+
+/*
+ * w4a16_unpack - host inverse of the packing: codes[8i + j, n] = (qweight[i, n] >> 4j) & 15.
+ *   qweight host int32 [K/8, N]; codes host uint8 [K, N] (written). K % 8 == 0.
+ * Errors: INVALID_ARG.
+ */
+int w4a16_unpack(const int32_t* qweight, int64_t K, int64_t N, uint8_t* codes);
+
+/*
+ * w4a16_matmul - y = x . dequant(qweight, scales, zeros) on the GPU ("The design": the
+ * weights cross HBM packed and are dequantised in registers inside the product; fp32
+ * accumulation; y rounded to fp16 once at the end).
+ *
+ *   x, qweight, scales, zeros, y   device pointers (layouts above), 16-byte aligned
+ *   M >= 1, N >= 4 with N % 4 == 0, K >= 128 with K % group_size == 0
+ *   group_size must be 128
+ *   stream     hipStream_t as void* (NULL = the null stream)
+ * Asynchronous: returns once the kernel is enqueued on `stream`. y is fully overwritten.
+ * The result is deterministic: the same call gives the same bits (split-K partial sums are
+ * combined in a fixed order; no floating-point atomics).
+ * Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT (no HIP call made), HIP (launch failure or
+ * workspace allocation failure).
+ */
+int w4a16_matmul(const void* x, const int32_t* qweight, const void* scales,
+                 const void* zeros, void* y, int64_t M, int64_t N, int64_t K,
+                 int64_t group_size, void* stream);
+
+/*
+ * w4a16_matmul_ex - w4a16_matmul with the plan forced by the caller (tuning and tests).
+ * plan->kernel == W4A16_KERNEL_AUTO behaves as w4a16_matmul. Fields left 0 are filled by
+ * the dispatcher. Errors as w4a16_matmul, plus INVALID_ARG for an unusable plan.
+ */
+int w4a16_matmul_ex(const void* x, const int32_t* qweight, const void* scales,
+                    const void* zeros, void* y, int64_t M, int64_t N, int64_t K,
+                    int64_t group_size, void* stream, const w4a16_plan_t* plan);
+
+/*
+ * w4a16_plan - the plan w4a16_matmul would use for (M, N, K, group_size), or the completed
+ * version of a forced plan when `plan->kernel` is non-zero on entry. Host only; no HIP call.
+ * Errors: INVALID_ARG, UNSUPPORTED.
+ */
+int w4a16_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, w4a16_plan_t* plan);
+
+/*
+ * w4a16_dequant - the GPU's unpack/dequant, exposed for bit-exact checks.
+ *   codes  device uint8 [K, N] or NULL: codes[8i + j, n] = nibble j of qweight[i, n]
+ *   w      device fp16 [K, N] or NULL: fp16_rne((q - zero) * scale), i.e. one rounding of
+ *          the exact product (the fp16 weight the prefill kernel stages in LDS)
+ *   qweight, scales, zeros as for w4a16_matmul; N % 4 == 0, K % group_size == 0,
+ *   group_size == 128; at least one of codes / w non-NULL.
+ * Asynchronous on `stream`. Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT, HIP.
+ */
+int w4a16_dequant(const int32_t* qweight, const void* scales, const void* zeros,
+                  uint8_t* codes, void* w, int64_t N, int64_t K, int64_t group_size,
+                  void* stream);
+
+/* w4a16_strerror - static description of an error code (never NULL). */
+const char* w4a16_strerror(int code);
+
+/* w4a16_last_error_detail - message of the last failing call on this thread ("" if none). */
+const char* w4a16_last_error_detail(void);
+
+/* w4a16_version - library version as major*10000 + minor*100 + patch. */
+int w4a16_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

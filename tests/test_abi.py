@@ -1,0 +1,134 @@
+"""The C-ABI library loads, exports every function include/w4a16.h declares, and rejects
+bad arguments before making any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import weight_only_bit_gemv_amd as lib
+from weight_only_bit_gemv_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(w4a16_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ["w4a16_pack", "w4a16_matmul", "w4a16_matmul_ex", "w4a16_plan",
+                     "w4a16_dequant", "w4a16_unpack", "w4a16_strerror"]:
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    so = ctypes.CDLL(B.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(so, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (w4a16_\w+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_binding_covers_every_symbol():
+    assert set(declared_functions()) == set(B._SIGS)
+
+
+def test_strerror_and_version():
+    for code in [0, -1, -2, -3, -4, -5]:
+        assert lib.strerror(code) and lib.strerror(code) != "unknown error code"
+    assert lib.strerror(-99) == "unknown error code"
+    assert lib.w4a16_version() >= 100
+
+
+# Fake, 16-byte aligned, never-dereferenced addresses: validation rejects every call below
+# before any HIP call, so no device is needed.
+A = 0x100000
+P = [ctypes.c_void_p(A + 0x1000 * i) for i in range(5)]
+
+
+def _mm(M, N, K, g=128, ptrs=None):
+    p = ptrs or P
+    return B.load().w4a16_matmul(p[0], p[1], p[2], p[3], p[4], M, N, K, g, None)
+
+
+@pytest.mark.parametrize("M,N,K,g,code", [
+    (0, 64, 128, 128, lib.W4A16_ERR_INVALID_ARG),
+    (1, 0, 128, 128, lib.W4A16_ERR_INVALID_ARG),
+    (1, 64, 0, 128, lib.W4A16_ERR_INVALID_ARG),
+    (-3, 64, 128, 128, lib.W4A16_ERR_INVALID_ARG),
+    (1, 64, 128, 64, lib.W4A16_ERR_UNSUPPORTED),
+    (1, 64, 200, 128, lib.W4A16_ERR_UNSUPPORTED),
+    (1, 66, 128, 128, lib.W4A16_ERR_UNSUPPORTED),
+    (1, 1 << 20, 1 << 16, 128, lib.W4A16_ERR_UNSUPPORTED),
+])
+def test_matmul_rejects_bad_shapes(M, N, K, g, code):
+    assert _mm(M, N, K, g) == code
+    assert B.load().w4a16_last_error_detail().decode()
+
+
+def test_matmul_rejects_null_and_misaligned():
+    for i in range(5):
+        ptrs = list(P)
+        ptrs[i] = None
+        assert _mm(1, 64, 128, ptrs=ptrs) == lib.W4A16_ERR_INVALID_ARG
+        ptrs = list(P)
+        ptrs[i] = ctypes.c_void_p(A + 8)
+        assert _mm(1, 64, 128, ptrs=ptrs) == lib.W4A16_ERR_ALIGNMENT
+
+
+def test_matmul_ex_rejects_bad_plans():
+    so = B.load()
+    for kw in [dict(kernel=7), dict(kernel=1, kc=3), dict(kernel=1, kc=6), dict(kernel=1, kc=-4),
+               dict(kernel=1, row_tiles=5)]:
+        pl = B.w4a16_plan_t(**kw)
+        rc = so.w4a16_matmul_ex(P[0], P[1], P[2], P[3], P[4], 1, 64, 128, 128, None,
+                                ctypes.byref(pl))
+        assert rc == lib.W4A16_ERR_INVALID_ARG, kw
+    assert so.w4a16_matmul_ex(P[0], P[1], P[2], P[3], P[4], 1, 64, 128, 128, None,
+                              None) == lib.W4A16_ERR_INVALID_ARG
+
+
+def test_dequant_rejects_bad_arguments():
+    so = B.load()
+    assert so.w4a16_dequant(P[0], P[1], P[2], None, None, 64, 128, 128, None) == lib.W4A16_ERR_INVALID_ARG
+    assert so.w4a16_dequant(None, P[1], P[2], P[3], None, 64, 128, 128, None) == lib.W4A16_ERR_INVALID_ARG
+    assert so.w4a16_dequant(P[0], P[1], P[2], P[3], None, 62, 128, 128, None) == lib.W4A16_ERR_UNSUPPORTED
+    assert so.w4a16_dequant(ctypes.c_void_p(A + 4), P[1], P[2], P[3], None, 64, 128, 128,
+                            None) == lib.W4A16_ERR_ALIGNMENT
+
+
+# ---- dispatcher (host only) ----
+
+PLAN_SHAPES = [(m, k, n) for m in (1, 2, 4, 8, 16, 17, 33, 64, 65, 128, 2048)
+               for (k, n) in [(4096, 4096), (4096, 14336), (14336, 4096), (2048, 1408),
+                              (768, 2048), (4096, 128256), (128, 4), (384, 100)]]
+
+
+@pytest.mark.parametrize("M,K,N", PLAN_SHAPES)
+def test_auto_plan_is_valid_and_covers_k(M, K, N):
+    pl = lib.w4a16_plan(M, N, K)
+    assert pl["kernel"] in (lib.W4A16_KERNEL_SKINNY, lib.W4A16_KERNEL_PREFILL)
+    if pl["kernel"] == lib.W4A16_KERNEL_SKINNY:
+        kc, splits = pl["kc"], pl["splits"]
+        assert kc in (1, 2) or kc % 4 == 0
+        KS = K // 32
+        chunks = -(-KS // kc)
+        assert splits == -(-chunks // 4)
+        assert splits * 4 * kc >= KS                 # every K-step is covered
+        assert (splits - 1) * 4 * kc < KS            # no work-group is entirely empty
+        assert 1 <= pl["row_tiles"] <= 4
+        assert pl["row_tiles"] * 16 >= min(M, 64)
+
+
+@pytest.mark.parametrize("kc", [1, 2, 4, 8, 12, 16, 64])
+def test_forced_kc_plan(kc):
+    pl = lib.w4a16_plan(3, 4096, 4096, kernel=lib.W4A16_KERNEL_SKINNY, kc=kc)
+    assert pl["kc"] == kc and pl["splits"] == -(-(-(-128 // kc)) // 4)

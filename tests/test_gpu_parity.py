@@ -1,0 +1,263 @@
+"""GPU parity: libw4a16.so against the oracle on the same seeded inputs (needs an MI355X).
+
+Inputs come from synth.py and are quantised and packed by the oracle; nothing the GPU
+computes feeds an expected value. Bars:
+  * codes and fp16 dequantised weights: bit-exact (fp16_rne of the oracle's exact value);
+  * y: |y_gpu - y_ref| <= 1e-2 + 5e-3 * |y_ref| per element (y_ref in fp64);
+  * repeated calls: bitwise identical.
+Full-size shapes whose oracle would be slow are checked on sampled columns (all rows),
+with the kernel launched at its full size.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+ATOL, RTOL = 1e-2, 5e-3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    import weight_only_bit_gemv_amd as L
+    return L
+
+
+_QCACHE = {}
+
+
+def quantised(K, N, wid, layer=0):
+    key = (K, N, wid, layer)
+    if key not in _QCACHE:
+        _QCACHE.clear() if len(_QCACHE) > 6 else None
+        W = synth.weight(K, N, wid=wid, layer=layer)
+        _QCACHE[key] = oracle.quantize_pack(W)
+    return _QCACHE[key]
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def check_y(y_gpu, y_ref, what=""):
+    y = y_gpu.detach().cpu().numpy().astype(np.float64)
+    assert y.shape == y_ref.shape
+    assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+    err = np.abs(y - y_ref)
+    bound = ATOL + RTOL * np.abs(y_ref)
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert np.all(err <= bound), (f"{what}: max err {err.max():.3e} at {worst}, "
+                                  f"y={y[worst]:.6f} ref={y_ref[worst]:.6f}")
+    return float(err.max())
+
+
+def run(lib, x, qw, s, z, plan=None, y=None, stream=None):
+    out = lib.w4a16_matmul(dev(x) if isinstance(x, np.ndarray) else x,
+                           dev(qw) if isinstance(qw, np.ndarray) else qw,
+                           dev(s) if isinstance(s, np.ndarray) else s,
+                           dev(z) if isinstance(z, np.ndarray) else z,
+                           y=y, plan=plan, stream=stream)
+    torch.cuda.synchronize()
+    return out
+
+
+# ---------------------------------------------------------------------------------------
+# dequant hook: bit-exact codes and fp16 weights
+
+_DQ = {}
+
+
+def _dequant_inputs():
+    if _DQ:
+        return _DQ
+    cases = _DQ
+    cases.update({
+        "4096x4096 N(0,0.02)": quantised(4096, 4096, 0),
+        "768x2048 N(0,0.02)": quantised(768, 2048, 2),
+        "one-signed N(1,0.02)": oracle.quantize_pack(synth.weight_custom(256, 64, 1, 0.02, 1.0)),
+        "wide N(-3,5)": oracle.quantize_pack(synth.weight_custom(256, 64, 2, 5.0, -3.0)),
+        "subnormal scales": oracle.quantize_pack(synth.weight_custom(256, 64, 3, 3e-7, 0.0)),
+    })
+    codes = synth.uniform_codes(384, 100, seed=9)
+    s = np.full((3, 100), 1 + 3 * 2.0 ** -10, dtype=np.float16)   # fp16 product ties
+    z = np.full((3, 100), 8, dtype=np.float16)
+    z[1] = -1000
+    z[2] = 1000
+    cases["uniform codes, tie scale, extreme zeros"] = (oracle.pack(codes), s, z)
+    return cases
+
+
+DEQUANT_CASES = ["4096x4096 N(0,0.02)", "768x2048 N(0,0.02)", "one-signed N(1,0.02)",
+                 "wide N(-3,5)", "subnormal scales", "uniform codes, tie scale, extreme zeros"]
+
+
+@pytest.mark.parametrize("name", DEQUANT_CASES)
+def test_dequant_bit_exact(lib, name):
+    qw, s, z = _dequant_inputs()[name]
+    print(f"\n[dequant] {name} K={qw.shape[0] * 8} N={qw.shape[1]}", flush=True)
+    c, w = lib.w4a16_dequant(dev(qw), dev(s), dev(z))
+    torch.cuda.synchronize()
+    codes_ref = oracle.unpack(qw)
+    w_ref = oracle.dequant_fp16(codes_ref, s, z)
+    assert np.array_equal(c.cpu().numpy(), codes_ref)
+    got = w.cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), w_ref.view(np.uint16)), \
+        f"{np.count_nonzero(got.view(np.uint16) != w_ref.view(np.uint16))} fp16 weights differ"
+
+
+# ---------------------------------------------------------------------------------------
+# matmul against the oracle on every decode / MoE workload shape (full outputs)
+
+DECODE = [("gemv_4096", m, k, n) for (m, k, n) in synth.WORKLOADS["gemv_4096"]["shapes"]] + \
+         [("decode_sweep", m, k, n) for (m, k, n) in synth.WORKLOADS["decode_sweep"]["shapes"]] + \
+         [("moe_expert", m, k, n) for (m, k, n) in synth.WORKLOADS["moe_expert"]["shapes"]]
+
+
+@pytest.mark.parametrize("wl,M,K,N", DECODE, ids=[f"{w}-M{m}-K{k}-N{n}" for w, m, k, n in DECODE])
+def test_matmul_decode_shapes(lib, wl, M, K, N):
+    wid = synth.WORKLOADS[wl]["wid"]
+    print(f"\n[matmul] {wl} M={M} K={K} N={N} plan={lib.w4a16_plan(M, N, K)}", flush=True)
+    qw, s, z = quantised(K, N, wid)
+    x = synth.activations(M, K, wid=wid)
+    y = run(lib, x, qw, s, z)
+    check_y(y, oracle.matmul(x, qw, s, z), f"{wl} M={M} K={K} N={N}")
+
+
+# ---------------------------------------------------------------------------------------
+# prefill-sized and 7B-chain shapes: full-size launches, sampled columns
+
+def _sample_cols(N, count=160, seed=0):
+    rng = np.random.default_rng((5, N, seed))
+    cols = rng.choice(N, size=min(count, N), replace=False)
+    return np.unique(np.concatenate([cols, [0, 1, N - 2, N - 1]]))
+
+
+PREFILL = synth.WORKLOADS["prefill"]["shapes"]
+
+
+@pytest.mark.parametrize("M,K,N", PREFILL, ids=[f"M{m}-K{k}-N{n}" for m, k, n in PREFILL])
+def test_matmul_prefill_shapes_sampled(lib, M, K, N):
+    wid = synth.WORKLOADS["prefill"]["wid"]
+    print(f"\n[matmul] prefill M={M} K={K} N={N} plan={lib.w4a16_plan(M, N, K)}", flush=True)
+    qw, s, z = quantised(K, N, wid)
+    x = synth.activations(M, K, wid=wid)
+    y = run(lib, x, qw, s, z)
+    cols = _sample_cols(N)
+    y_ref = oracle.matmul(x, qw[:, cols], s[:, cols], z[:, cols])
+    check_y(y[:, torch.from_numpy(cols).to(DEV)], y_ref, f"prefill M={M} K={K} N={N}")
+
+
+def test_chain_layer_in_one_stream(lib):
+    """One transformer layer of the 7B-shaped decode chain, back to back on one stream."""
+    wid = synth.WORKLOADS["decode_chain_7b"]["wid"]
+    outs = []
+    for name, K, N in synth.CHAIN_7B_LAYER:
+        qw, s, z = quantised(K, N, wid, layer=0)
+        x = synth.activations(1, K, wid=wid)
+        print(f"\n[chain] {name} K={K} N={N}", flush=True)
+        outs.append((name, x, (qw, s, z),
+                     lib.w4a16_matmul(dev(x), dev(qw), dev(s), dev(z))))
+    torch.cuda.synchronize()
+    for name, x, (qw, s, z), y in outs:
+        check_y(y, oracle.matmul(x, qw, s, z), f"chain {name}")
+
+
+def test_chain_lm_head_sampled(lib):
+    wid = synth.WORKLOADS["decode_chain_7b"]["wid"]
+    _, K, N = synth.CHAIN_7B_LM_HEAD
+    print(f"\n[chain] lm_head K={K} N={N} plan={lib.w4a16_plan(1, N, K)}", flush=True)
+    W = synth.weight(K, N, wid=wid, layer=0)
+    qw, s, z = oracle.quantize_pack(W)
+    del W
+    x = synth.activations(1, K, wid=wid)
+    y = run(lib, x, qw, s, z)
+    cols = _sample_cols(N, 512)
+    y_ref = oracle.matmul(x, qw[:, cols], s[:, cols], z[:, cols])
+    check_y(y[:, torch.from_numpy(cols).to(DEV)], y_ref, "lm_head")
+
+
+# ---------------------------------------------------------------------------------------
+# ragged edges, every plan, determinism, streams, overwrite
+
+RAGGED = [(1, 128, 4), (3, 128, 100), (17, 384, 1412), (33, 256, 68), (65, 512, 260),
+          (100, 1408, 196), (5, 768, 2052), (16, 128, 64), (64, 256, 8)]
+
+
+@pytest.mark.parametrize("M,K,N", RAGGED, ids=[f"M{m}-K{k}-N{n}" for m, k, n in RAGGED])
+def test_matmul_ragged(lib, M, K, N):
+    print(f"\n[ragged] M={M} K={K} N={N} plan={lib.w4a16_plan(M, N, K)}", flush=True)
+    W = synth.weight_custom(K, N, seed=M, std=0.02)
+    qw, s, z = oracle.quantize_pack(W)
+    x = synth.activations(M, K, wid=7)
+    check_y(run(lib, x, qw, s, z), oracle.matmul(x, qw, s, z), f"ragged M={M} K={K} N={N}")
+
+
+PLANS = [dict(kernel=1, kc=kc, row_tiles=rt) for kc in (1, 2, 4, 8, 16, 32) for rt in (1, 2, 3, 4)]
+
+
+@pytest.mark.parametrize("plan", PLANS, ids=[f"kc{p['kc']}-rt{p['row_tiles']}" for p in PLANS])
+def test_matmul_every_skinny_plan(lib, plan):
+    M, K, N = 37, 1024, 320
+    print(f"\n[plan] {plan} M={M} K={K} N={N}", flush=True)
+    W = synth.weight_custom(K, N, seed=11, std=0.02)
+    qw, s, z = oracle.quantize_pack(W)
+    x = synth.activations(M, K, wid=8)
+    check_y(run(lib, x, qw, s, z, plan=plan), oracle.matmul(x, qw, s, z), f"plan {plan}")
+
+
+def test_deterministic_split_k(lib):
+    M, K, N = 1, 4096, 4096
+    qw, s, z = quantised(K, N, 0)
+    x = synth.activations(M, K, wid=0)
+    assert lib.w4a16_plan(M, N, K)["splits"] > 1
+    args = [dev(x), dev(qw), dev(s), dev(z)]
+    a = lib.w4a16_matmul(*args).clone()
+    for _ in range(5):
+        b = lib.w4a16_matmul(*args)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_nondefault_stream_and_full_overwrite(lib):
+    M, K, N = 4, 2048, 1408
+    qw, s, z = quantised(K, N, 2)
+    x = synth.activations(M, K, wid=2)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        args = [dev(x), dev(qw), dev(s), dev(z)]
+        y = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+        lib.w4a16_matmul(*args, y=y, stream=st)
+    st.synchronize()
+    check_y(y, oracle.matmul(x, qw, s, z), "stream")
+
+
+def test_alternating_shapes_reuse_counters(lib):
+    """Split-K arrival counters must be back at zero after every call."""
+    cases = [(1, 4096, 4096, 0), (4, 2048, 1408, 2), (16, 768, 2048, 2), (2, 4096, 4096, 0)]
+    data = []
+    for M, K, N, wid in cases:
+        qw, s, z = quantised(K, N, wid)
+        x = synth.activations(M, K, wid=wid)
+        data.append((x, qw, s, z, [dev(x), dev(qw), dev(s), dev(z)]))
+    for rep in range(3):
+        for (x, qw, s, z, args) in data:
+            y = lib.w4a16_matmul(*args)
+            torch.cuda.synchronize()
+            check_y(y, oracle.matmul(x, qw, s, z), f"alternating rep {rep}")
+
+
+def test_exact_closed_form_on_gpu(lib):
+    """K=128 exact case (W = ((k+n) mod 16 - 8) / 64): y(ones) = -1 for every column."""
+    k = np.arange(128)[:, None]
+    n = np.arange(64)[None, :]
+    W = (((k + n) % 16 - 8) / 64.0).astype(np.float32)
+    qw, s, z = oracle.quantize_pack(W)
+    x = np.ones((1, 128), dtype=np.float16)
+    y = run(lib, x, qw, s, z).cpu().numpy()
+    assert np.all(y == np.float16(-1.0))

@@ -1,0 +1,15 @@
+"""MI355X (gfx950) W4A16 weight-only GEMM/GEMV: y = x . dequant(Wq).
+
+The compute lives in libw4a16.so (hand-written HIP kernels behind a C ABI, include/w4a16.h);
+this package only marshals arguments to it. Importing the package loads the library and
+raises if it cannot, so there is no silent fallback path.
+"""
+from ._binding import (  # noqa: F401
+    GROUP_SIZE, LIB_PATH, W4A16Error, w4a16_pack, w4a16_unpack, w4a16_plan, w4a16_matmul,
+    w4a16_matmul_ex, w4a16_dequant, w4a16_version, strerror, load,
+    W4A16_OK, W4A16_ERR_INVALID_ARG, W4A16_ERR_UNSUPPORTED, W4A16_ERR_ALIGNMENT,
+    W4A16_ERR_NONFINITE, W4A16_ERR_HIP, W4A16_KERNEL_AUTO, W4A16_KERNEL_SKINNY,
+    W4A16_KERNEL_PREFILL,
+)
+
+load()

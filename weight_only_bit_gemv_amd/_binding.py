@@ -1,0 +1,203 @@
+"""ctypes binding of libw4a16.so: argument marshalling only.
+
+Every entry point has the name of its C function (include/w4a16.h). Device buffers are
+torch tensors on a HIP device (torch provides memory and streams, nothing else); host
+buffers are NumPy arrays. All arithmetic happens in the library.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libw4a16.so")
+
+W4A16_OK = 0
+W4A16_ERR_INVALID_ARG = -1
+W4A16_ERR_UNSUPPORTED = -2
+W4A16_ERR_ALIGNMENT = -3
+W4A16_ERR_NONFINITE = -4
+W4A16_ERR_HIP = -5
+
+W4A16_KERNEL_AUTO = 0
+W4A16_KERNEL_SKINNY = 1
+W4A16_KERNEL_PREFILL = 2
+
+GROUP_SIZE = 128
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, code, func, detail):
+        self.code = code
+        super().__init__(f"{func} failed: {code} ({strerror(code)}): {detail}")
+
+
+class w4a16_plan_t(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("kc", ctypes.c_int32), ("splits", ctypes.c_int32),
+                ("row_tiles", ctypes.c_int32), ("tile", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 3)]
+
+    def as_dict(self):
+        return {"kernel": self.kernel, "kc": self.kc, "splits": self.splits,
+                "row_tiles": self.row_tiles, "tile": self.tile}
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SIGS = {
+    "w4a16_pack": ([_P, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "w4a16_unpack": ([_P, _I64, _I64, _P], ctypes.c_int),
+    "w4a16_matmul": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
+    "w4a16_matmul_ex": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P,
+                         ctypes.POINTER(w4a16_plan_t)], ctypes.c_int),
+    "w4a16_plan": ([_I64, _I64, _I64, _I64, ctypes.POINTER(w4a16_plan_t)], ctypes.c_int),
+    "w4a16_dequant": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "w4a16_strerror": ([ctypes.c_int], ctypes.c_char_p),
+    "w4a16_last_error_detail": ([], ctypes.c_char_p),
+    "w4a16_version": ([], ctypes.c_int),
+}
+
+
+def load(build_if_missing=True):
+    """Load libw4a16.so (building it in-tree first if it is absent). Raises if it cannot."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        if not build_if_missing:
+            raise ImportError(f"{LIB_PATH} is not built")
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (args, res) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def strerror(code):
+    return load().w4a16_strerror(code).decode()
+
+
+def _check(rc, func):
+    if rc != W4A16_OK:
+        raise W4A16Error(rc, func, load().w4a16_last_error_detail().decode())
+
+
+def _stream_ptr(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_ptr(t, name, dtype):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a torch tensor on a HIP device")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+# ---- host entry points ------------------------------------------------------------------
+
+def w4a16_pack(W, group_size=GROUP_SIZE):
+    """W fp32 [K, N] (NumPy) -> (qweight int32 [K/8, N], scales fp16, zeros fp16)."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    if W.ndim != 2:
+        raise ValueError("W must be 2-D")
+    K, N = W.shape
+    G = K // group_size if group_size > 0 else 0
+    qweight = np.empty((K // 8, N), dtype=np.int32)
+    scales = np.empty((max(G, 0), N), dtype=np.float16)
+    zeros = np.empty((max(G, 0), N), dtype=np.float16)
+    rc = load().w4a16_pack(W.ctypes.data, K, N, group_size, qweight.ctypes.data,
+                           scales.ctypes.data, zeros.ctypes.data)
+    _check(rc, "w4a16_pack")
+    return qweight, scales, zeros
+
+
+def w4a16_unpack(qweight):
+    """qweight int32 [K/8, N] (NumPy) -> codes uint8 [K, N]."""
+    qweight = np.ascontiguousarray(qweight, dtype=np.int32)
+    P, N = qweight.shape
+    codes = np.empty((P * 8, N), dtype=np.uint8)
+    _check(load().w4a16_unpack(qweight.ctypes.data, P * 8, N, codes.ctypes.data), "w4a16_unpack")
+    return codes
+
+
+def w4a16_plan(M, N, K, group_size=GROUP_SIZE, kernel=0, kc=0, row_tiles=0, tile=0):
+    pl = w4a16_plan_t(kernel=kernel, kc=kc, splits=0, row_tiles=row_tiles, tile=tile)
+    _check(load().w4a16_plan(M, N, K, group_size, ctypes.byref(pl)), "w4a16_plan")
+    return pl.as_dict()
+
+
+# ---- device entry points ------------------------------------------------------------------
+
+def w4a16_matmul(x, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, stream=None, plan=None):
+    """y[M, N] = x[M, K] . dequant(qweight, scales, zeros); torch tensors on one device.
+
+    x fp16 [M, K]; qweight int32 [K/8, N]; scales, zeros fp16 [K/g, N]; y fp16 [M, N]
+    (allocated when None). Enqueued on `stream` (default: torch's current stream).
+    `plan` (dict with kernel/kc/row_tiles/tile) forces the execution plan.
+    """
+    import torch
+    if x.dim() != 2 or qweight.dim() != 2:
+        raise ValueError("x and qweight must be 2-D")
+    M, K = x.shape
+    N = qweight.shape[1]
+    if qweight.shape[0] * 8 != K:
+        raise ValueError(f"qweight rows {qweight.shape[0]} do not match K={K}")
+    if scales.shape != (K // group_size, N) or zeros.shape != (K // group_size, N):
+        raise ValueError("scales/zeros must be [K/group_size, N]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    elif y.shape != (M, N):
+        raise ValueError("y must be [M, N]")
+    args = [_dev_ptr(x, "x", torch.float16), _dev_ptr(qweight, "qweight", torch.int32),
+            _dev_ptr(scales, "scales", torch.float16), _dev_ptr(zeros, "zeros", torch.float16),
+            _dev_ptr(y, "y", torch.float16), M, N, K, group_size, _stream_ptr(stream, x.device)]
+    if plan is None:
+        rc = load().w4a16_matmul(*args)
+        _check(rc, "w4a16_matmul")
+    else:
+        pl = w4a16_plan_t(kernel=plan.get("kernel", 0), kc=plan.get("kc", 0), splits=0,
+                          row_tiles=plan.get("row_tiles", 0), tile=plan.get("tile", 0))
+        rc = load().w4a16_matmul_ex(*args, ctypes.byref(pl))
+        _check(rc, "w4a16_matmul_ex")
+    return y
+
+
+def w4a16_matmul_ex(x, qweight, scales, zeros, y=None, plan=None, group_size=GROUP_SIZE,
+                    stream=None):
+    """w4a16_matmul with a forced plan (dict: kernel, kc, row_tiles, tile)."""
+    return w4a16_matmul(x, qweight, scales, zeros, y=y, group_size=group_size, stream=stream,
+                        plan=plan if plan is not None else {})
+
+
+def w4a16_dequant(qweight, scales, zeros, codes=True, weights=True, group_size=GROUP_SIZE,
+                  stream=None):
+    """The GPU's unpack/dequant: returns (codes uint8 [K, N] or None, w fp16 [K, N] or None)."""
+    import torch
+    K = qweight.shape[0] * 8
+    N = qweight.shape[1]
+    c = torch.empty((K, N), dtype=torch.uint8, device=qweight.device) if codes else None
+    w = torch.empty((K, N), dtype=torch.float16, device=qweight.device) if weights else None
+    rc = load().w4a16_dequant(_dev_ptr(qweight, "qweight", torch.int32),
+                              _dev_ptr(scales, "scales", torch.float16),
+                              _dev_ptr(zeros, "zeros", torch.float16),
+                              ctypes.c_void_p(c.data_ptr()) if c is not None else None,
+                              ctypes.c_void_p(w.data_ptr()) if w is not None else None,
+                              N, K, group_size, _stream_ptr(stream, qweight.device))
+    _check(rc, "w4a16_dequant")
+    return c, w
+
+
+def w4a16_version():
+    return load().w4a16_version()

@@ -1,0 +1,78 @@
+"""Build libw4a16.so in-tree: HIP kernels for gfx950 with hipcc, host code with g++.
+
+    python -m weight_only_bit_gemv_amd.build        (or __graft_entry__.build())
+
+Output: weight_only_bit_gemv_amd/lib/libw4a16.so. Objects go to weight_only_bit_gemv_amd/_build/.
+"""
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIBDIR = os.path.join(PKG, "lib")
+LIB = os.path.join(LIBDIR, "libw4a16.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+ARCH = "gfx950"
+
+HIP_SOURCES = ["w4a16_skinny.hip", "w4a16_dequant.hip"]
+# The packer must round every fp32 step on its own: no contraction, no fast-math.
+PACK_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math"]
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # keep packed-fp32 VALU instructions out of the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs (no accvgpr copies around the fp32 epilogue)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
+]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # hipcc's host pass warns that it does not know the packed-fp32 feature; drop that line
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose=False):
+    hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
+    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(LIBDIR, exist_ok=True)
+    inc = ["-I", INCLUDE, "-I", CSRC]
+    jobs = []
+    objs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        jobs.append([hipcc] + HIPCC_FLAGS + inc + ["-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    obj = os.path.join(BUILD, "w4a16_pack.o")
+    jobs.append(["g++", "-std=c++17", "-fPIC"] + PACK_FLAGS + inc +
+                ["-c", os.path.join(CSRC, "w4a16_pack.cpp"), "-o", obj])
+    objs.append(obj)
+    obj = os.path.join(BUILD, "w4a16_api.o")
+    jobs.append(["g++", "-std=c++17", "-fPIC", "-O2", "-D__HIP_PLATFORM_AMD__",
+                 "-I", os.path.join(ROCM, "include")] + inc +
+                ["-c", os.path.join(CSRC, "w4a16_api.cpp"), "-o", obj])
+    objs.append(obj)
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        outs = list(ex.map(_run, jobs))
+    if verbose:
+        for o in outs:
+            if o.strip():
+                print(o)
+    tmp = LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs +
+         ["-lpthread"])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,270 @@
+// C ABI of the W4A16 library: argument validation, the shape-based dispatcher, and the
+// library-owned split-K workspace. Declarations and contracts are in include/w4a16.h.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "w4a16_internal.h"
+
+namespace {
+
+thread_local std::string g_detail;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_detail = buf;
+    return code;
+}
+
+int ok() {
+    g_detail.clear();
+    return W4A16_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shape checks shared by the GPU entry points.
+int check_gpu_shape(int64_t M, int64_t N, int64_t K, int64_t group_size) {
+    if (M < 1 || N < 1 || K < 1) return fail(W4A16_ERR_INVALID_ARG, "M, N, K must be >= 1 (got %lld, %lld, %lld)",
+                                            (long long)M, (long long)N, (long long)K);
+    if (group_size != w4a16::kGroup)
+        return fail(W4A16_ERR_UNSUPPORTED, "group_size %lld not supported (128 only)", (long long)group_size);
+    if (K % group_size != 0)
+        return fail(W4A16_ERR_UNSUPPORTED, "K=%lld is not a multiple of group_size", (long long)K);
+    if (N % 4 != 0) return fail(W4A16_ERR_UNSUPPORTED, "N=%lld is not a multiple of 4", (long long)N);
+    const int64_t lim = INT32_MAX;
+    if ((K / 8) * N > lim || M * K > lim || M * N > lim)
+        return fail(W4A16_ERR_UNSUPPORTED, "problem too large for 32-bit indexing");
+    return W4A16_OK;
+}
+
+// ---- dispatcher --------------------------------------------------------------------------
+
+// K-steps per wavefront for the skinny kernel: aim at ~kTargetWaves wavefronts in the grid,
+// whole 128-row groups per wavefront once a wavefront streams more than one group, and no
+// more than a quarter of K per wavefront so that all 4 wavefronts of a work-group stream.
+constexpr int64_t kTargetWaves = 2048;
+
+int64_t auto_kc(int64_t KS, int64_t n_strips, int64_t row_blocks) {
+    const int64_t work = KS * n_strips * row_blocks;
+    int64_t kc = std::max<int64_t>(1, ceil_div(work, kTargetWaves));
+    if (kc == 3) kc = 4;
+    if (kc > 4) kc = ceil_div(kc, 4) * 4;
+    // at most a quarter of K per wavefront, rounded down to a valid segment multiple
+    const int64_t quarter = std::max<int64_t>(1, KS / w4a16::kSkinnyWaves);
+    if (kc > quarter) kc = quarter >= 4 ? quarter / 4 * 4 : (quarter >= 2 ? 2 : 1);
+    return kc;
+}
+
+int complete_plan(int64_t M, int64_t N, int64_t K, w4a16_plan_t* pl) {
+    if (pl->kernel == W4A16_KERNEL_AUTO) pl->kernel = W4A16_KERNEL_SKINNY;
+    if (pl->kernel == W4A16_KERNEL_PREFILL)
+        return fail(W4A16_ERR_UNSUPPORTED, "prefill kernel not available in this build");
+    if (pl->kernel != W4A16_KERNEL_SKINNY)
+        return fail(W4A16_ERR_INVALID_ARG, "unknown kernel id %d", pl->kernel);
+    if (pl->row_tiles == 0) pl->row_tiles = (int32_t)std::min<int64_t>(4, ceil_div(M, 16));
+    if (pl->row_tiles < 1 || pl->row_tiles > 4)
+        return fail(W4A16_ERR_INVALID_ARG, "row_tiles must be 1..4 (got %d)", pl->row_tiles);
+    const int64_t KS = K / w4a16::kKStep;
+    const int64_t n_strips = ceil_div(N, w4a16::kStripN);
+    const int64_t row_blocks = ceil_div(M, 16 * (int64_t)pl->row_tiles);
+    if (pl->kc == 0) pl->kc = (int32_t)auto_kc(KS, n_strips, row_blocks);
+    if (pl->kc < 1 || pl->kc == 3 || (pl->kc > 4 && pl->kc % 4 != 0))
+        return fail(W4A16_ERR_INVALID_ARG, "kc must be 1, 2 or a multiple of 4 (got %d)", pl->kc);
+    const int64_t chunks = ceil_div(KS, pl->kc);
+    const int64_t splits = ceil_div(chunks, w4a16::kSkinnyWaves);
+    if (pl->splits != 0 && pl->splits != splits)
+        return fail(W4A16_ERR_INVALID_ARG, "splits=%d does not match kc=%d (needs %lld)", pl->splits,
+                    pl->kc, (long long)splits);
+    pl->splits = (int32_t)splits;
+    if (n_strips * splits > INT32_MAX || row_blocks > 65535)
+        return fail(W4A16_ERR_UNSUPPORTED, "grid too large");
+    return W4A16_OK;
+}
+
+// ---- workspace ---------------------------------------------------------------------------
+
+struct Workspace {
+    float* partials = nullptr;
+    uint64_t partial_bytes = 0;
+    uint32_t* counters = nullptr;
+    uint64_t n_counters = 0;
+};
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, void*>, Workspace> g_ws;
+
+int get_workspace(void* stream, uint64_t bytes, uint64_t n_counters, Workspace* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(W4A16_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    Workspace& w = g_ws[{dev, stream}];
+    if (w.partial_bytes < bytes || w.n_counters < n_counters) {
+        hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        if (w.partials || w.counters) {
+            // Earlier launches on this stream may still read the old buffers.
+            e = hipStreamSynchronize(s);
+            if (e != hipSuccess) return fail(W4A16_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+            (void)hipFree(w.partials);
+            (void)hipFree(w.counters);
+            w = Workspace{};
+        }
+        const uint64_t nb = std::max<uint64_t>(bytes, 1u << 20);
+        const uint64_t nc = std::max<uint64_t>(n_counters, 4096);
+        e = hipMalloc(reinterpret_cast<void**>(&w.partials), nb);
+        if (e != hipSuccess) { w = Workspace{}; return fail(W4A16_ERR_HIP, "hipMalloc workspace: %s", hipGetErrorString(e)); }
+        e = hipMalloc(reinterpret_cast<void**>(&w.counters), nc * sizeof(uint32_t));
+        if (e != hipSuccess) {
+            (void)hipFree(w.partials);
+            w = Workspace{};
+            return fail(W4A16_ERR_HIP, "hipMalloc counters: %s", hipGetErrorString(e));
+        }
+        e = hipMemsetAsync(w.counters, 0, nc * sizeof(uint32_t), s);
+        if (e != hipSuccess) return fail(W4A16_ERR_HIP, "hipMemsetAsync: %s", hipGetErrorString(e));
+        w.partial_bytes = nb;
+        w.n_counters = nc;
+    }
+    *out = w;
+    return W4A16_OK;
+}
+
+int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const void* zeros,
+                void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, void* stream,
+                const w4a16_plan_t* forced) {
+    if (!x || !qweight || !scales || !zeros || !y)
+        return fail(W4A16_ERR_INVALID_ARG, "null pointer argument");
+    int rc = check_gpu_shape(M, N, K, group_size);
+    if (rc) return rc;
+    if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros) || !aligned16(y))
+        return fail(W4A16_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+    w4a16_plan_t pl = forced ? *forced : w4a16_plan_t{};
+    rc = complete_plan(M, N, K, &pl);
+    if (rc) return rc;
+
+    w4a16::SkinnyParams p{};
+    p.x = static_cast<const uint16_t*>(x);
+    p.qweight = reinterpret_cast<const uint32_t*>(qweight);
+    p.scales = static_cast<const uint16_t*>(scales);
+    p.zeros = static_cast<const uint16_t*>(zeros);
+    p.y = static_cast<uint16_t*>(y);
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.kc = pl.kc;
+    p.splits = pl.splits;
+    p.n_strips = (int)ceil_div(N, w4a16::kStripN);
+    p.row_tiles = pl.row_tiles;
+    p.row_blocks = (int)ceil_div(M, 16 * (int64_t)pl.row_tiles);
+    uint64_t ws_bytes = 0, n_counters = 0;
+    w4a16::skinny_workspace(p, &ws_bytes, &n_counters);
+    if (ws_bytes) {
+        Workspace w;
+        rc = get_workspace(stream, ws_bytes, n_counters, &w);
+        if (rc) return rc;
+        p.ws = w.partials;
+        p.counters = w.counters;
+    }
+    const int e = w4a16::launch_skinny(p, stream);
+    if (e != (int)hipSuccess)
+        return fail(W4A16_ERR_HIP, "skinny kernel launch: %s", hipGetErrorString((hipError_t)e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_pack(const float* W, int64_t K, int64_t N, int64_t group_size, int32_t* qweight,
+               uint16_t* scales, uint16_t* zeros) {
+    if (!W || !qweight || !scales || !zeros) return fail(W4A16_ERR_INVALID_ARG, "null pointer argument");
+    if (K < 1 || N < 1) return fail(W4A16_ERR_INVALID_ARG, "K and N must be >= 1");
+    if (group_size != w4a16::kGroup)
+        return fail(W4A16_ERR_UNSUPPORTED, "group_size %lld not supported (128 only)", (long long)group_size);
+    if (K % group_size != 0)
+        return fail(W4A16_ERR_UNSUPPORTED, "K=%lld is not a multiple of group_size", (long long)K);
+    const int rc = w4a16::pack_host(W, K, N, group_size, qweight, scales, zeros);
+    if (rc == W4A16_ERR_NONFINITE) return fail(rc, "non-finite weight or fp16 scale overflow");
+    if (rc == W4A16_ERR_UNSUPPORTED) return fail(rc, "zero point outside |zero| <= 1024");
+    if (rc) return fail(rc, "pack failed");
+    return ok();
+}
+
+int w4a16_unpack(const int32_t* qweight, int64_t K, int64_t N, uint8_t* codes) {
+    if (!qweight || !codes) return fail(W4A16_ERR_INVALID_ARG, "null pointer argument");
+    if (K < 8 || N < 1 || K % 8 != 0) return fail(W4A16_ERR_INVALID_ARG, "K must be a positive multiple of 8, N >= 1");
+    w4a16::unpack_host(qweight, K, N, codes);
+    return ok();
+}
+
+int w4a16_matmul(const void* x, const int32_t* qweight, const void* scales, const void* zeros,
+                 void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, void* stream) {
+    return matmul_impl(x, qweight, scales, zeros, y, M, N, K, group_size, stream, nullptr);
+}
+
+int w4a16_matmul_ex(const void* x, const int32_t* qweight, const void* scales, const void* zeros,
+                    void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, void* stream,
+                    const w4a16_plan_t* plan) {
+    if (!plan) return fail(W4A16_ERR_INVALID_ARG, "null plan");
+    return matmul_impl(x, qweight, scales, zeros, y, M, N, K, group_size, stream, plan);
+}
+
+int w4a16_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, w4a16_plan_t* plan) {
+    if (!plan) return fail(W4A16_ERR_INVALID_ARG, "null plan");
+    int rc = check_gpu_shape(M, N, K, group_size);
+    if (rc) return rc;
+    w4a16_plan_t pl = *plan;
+    rc = complete_plan(M, N, K, &pl);
+    if (rc) return rc;
+    *plan = pl;
+    return ok();
+}
+
+int w4a16_dequant(const int32_t* qweight, const void* scales, const void* zeros, uint8_t* codes,
+                  void* w, int64_t N, int64_t K, int64_t group_size, void* stream) {
+    if (!qweight || !scales || !zeros) return fail(W4A16_ERR_INVALID_ARG, "null pointer argument");
+    if (!codes && !w) return fail(W4A16_ERR_INVALID_ARG, "codes and w are both NULL");
+    int rc = check_gpu_shape(1, N, K, group_size);
+    if (rc) return rc;
+    if (!aligned16(qweight) || !aligned16(scales) || !aligned16(zeros) || (w && !aligned16(w)))
+        return fail(W4A16_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+    const int e = w4a16::launch_dequant(reinterpret_cast<const uint32_t*>(qweight),
+                                        static_cast<const uint16_t*>(scales),
+                                        static_cast<const uint16_t*>(zeros), codes,
+                                        static_cast<uint16_t*>(w), (int)N, (int)K, stream);
+    if (e != (int)hipSuccess)
+        return fail(W4A16_ERR_HIP, "dequant kernel launch: %s", hipGetErrorString((hipError_t)e));
+    return ok();
+}
+
+const char* w4a16_strerror(int code) {
+    switch (code) {
+        case W4A16_OK: return "success";
+        case W4A16_ERR_INVALID_ARG: return "invalid argument";
+        case W4A16_ERR_UNSUPPORTED: return "unsupported shape or parameter";
+        case W4A16_ERR_ALIGNMENT: return "device pointer not 16-byte aligned";
+        case W4A16_ERR_NONFINITE: return "non-finite value";
+        case W4A16_ERR_HIP: return "HIP runtime error";
+        default: return "unknown error code";
+    }
+}
+
+const char* w4a16_last_error_detail(void) { return g_detail.c_str(); }
+
+int w4a16_version(void) { return 100; }
+
+}  // extern "C"

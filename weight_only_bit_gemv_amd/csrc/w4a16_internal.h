@@ -1,0 +1,52 @@
+// Internal declarations shared by the C ABI layer, the host packer and the kernel launchers.
+#pragma once
+
+#include <cstdint>
+
+#include "w4a16.h"
+
+namespace w4a16 {
+
+// ---- host packer (w4a16_pack.cpp) ----
+uint16_t f32_to_f16_rne(float f);
+float f16_to_f32(uint16_t h);
+int pack_host(const float* W, int64_t K, int64_t N, int64_t g,
+              int32_t* qweight, uint16_t* scales, uint16_t* zeros);
+void unpack_host(const int32_t* qweight, int64_t K, int64_t N, uint8_t* codes);
+
+// ---- decode / skinny kernel (w4a16_skinny.hip) ----
+constexpr int kSkinnyWaves = 4;      // wavefronts per work-group, each on its own K range
+constexpr int kStripN = 64;          // output columns per work-group (16 lanes x 4 columns)
+constexpr int kKStep = 32;           // K rows per MFMA step (4 packed rows)
+constexpr int kGroup = 128;          // K rows per scale/zero group
+
+struct SkinnyParams {
+    const uint16_t* x;        // fp16 [M, K]
+    const uint32_t* qweight;  // int32 [K/8, N]
+    const uint16_t* scales;   // fp16 [K/g, N]
+    const uint16_t* zeros;    // fp16 [K/g, N]
+    uint16_t* y;              // fp16 [M, N]
+    float* ws;                // fp32 partials [row_blocks][n_strips][splits][16*row_tiles][64]
+    uint32_t* counters;       // arrival counters [row_blocks][n_strips], zero between calls
+    int M, N, K;
+    int kc;                   // K-steps per wavefront
+    int splits;               // work-groups along K per strip
+    int n_strips;             // ceil(N / 64)
+    int row_tiles;            // 16-row tiles per work-group (1..4)
+    int row_blocks;           // ceil(M / (16 * row_tiles))
+};
+
+// Workspace a skinny launch needs (bytes of partials, number of counters).
+inline void skinny_workspace(const SkinnyParams& p, uint64_t* ws_bytes, uint64_t* n_counters) {
+    if (p.splits <= 1) { *ws_bytes = 0; *n_counters = 0; return; }
+    *ws_bytes = (uint64_t)p.row_blocks * p.n_strips * p.splits * 16ull * p.row_tiles * kStripN * 4ull;
+    *n_counters = (uint64_t)p.row_blocks * p.n_strips;
+}
+
+int launch_skinny(const SkinnyParams& p, void* stream);   // returns a hipError_t value
+
+// ---- dequant hook (w4a16_dequant.hip) ----
+int launch_dequant(const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                   uint8_t* codes, uint16_t* w, int N, int K, void* stream);
+
+}  // namespace w4a16
