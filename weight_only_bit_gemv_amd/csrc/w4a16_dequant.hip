@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint4* __restrict__ 
             const half8_t d = dequant_frag(words[t], zero_offsets(zc[t]), sc[t], uc);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                w[(size_t)(i * 8 + frag_k(e)) * N + n + t] = __builtin_bit_cast(uint16_t, d[e]);
+                w[(size_t)(i * 8 + frag_k(e)) * N + n + t] = f16_bits(d[e]);
         }
     }
 }

@@ -37,6 +37,9 @@ struct ZeroOffsets {
 
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 __device__ __forceinline__ uint32_t as_u32(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
+// Bits of one fp16 value. Takes the value as a scalar: __builtin_bit_cast applied directly to
+// a vector-element lvalue (v[e]) reads element 0 whatever e is, so never write that form.
+__device__ __forceinline__ uint16_t f16_bits(_Float16 h) { return __builtin_bit_cast(uint16_t, h); }
 
 __device__ __forceinline__ ZeroOffsets zero_offsets(_Float16 z) {
     ZeroOffsets o;
