@@ -55,10 +55,13 @@ extern "C" {
  * Execution plan of one w4a16_matmul call (what the dispatcher chose, or what a caller
  * forces through w4a16_matmul_ex). Fields a caller sets to 0 are chosen by the library.
  *   kernel     W4A16_KERNEL_*.
- *   kc         SKINNY: K-steps of 32 rows that one wavefront streams (>= 1).
- *   splits     SKINNY: work-groups along K per 64-column strip (derived from kc; output).
- *   row_tiles  SKINNY: 16-row MFMA tiles per work-group (1..4; derived from M; output).
+ *   kc         SKINNY: K-steps of 32 rows that one wavefront streams: 1, 2 or a multiple
+ *              of 4.
+ *   splits     SKINNY: work-groups along K per 64-column strip (output: derived from kc
+ *              and waves; a caller may leave it 0 or give the matching value).
+ *   row_tiles  SKINNY: 16-row MFMA tiles per work-group (1..4; default ceil(M/16) <= 4).
  *   tile       PREFILL: tile configuration id (0 = default).
+ *   waves      SKINNY: wavefronts per work-group, 4, 8 or 16, with (waves-1)*row_tiles <= 15.
  */
 typedef struct w4a16_plan {
     int32_t kernel;
@@ -66,7 +69,8 @@ typedef struct w4a16_plan {
     int32_t splits;
     int32_t row_tiles;
     int32_t tile;
-    int32_t reserved[3];
+    int32_t waves;
+    int32_t reserved[2];
 } w4a16_plan_t;
 
 /*

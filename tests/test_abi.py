@@ -87,7 +87,8 @@ def test_matmul_rejects_null_and_misaligned():
 def test_matmul_ex_rejects_bad_plans():
     so = B.load()
     for kw in [dict(kernel=7), dict(kernel=1, kc=3), dict(kernel=1, kc=6), dict(kernel=1, kc=-4),
-               dict(kernel=1, row_tiles=5)]:
+               dict(kernel=1, row_tiles=5), dict(kernel=1, waves=6), dict(kernel=1, waves=16, row_tiles=2),
+               dict(kernel=1, kc=4, waves=4, splits=3)]:
         pl = B.w4a16_plan_t(**kw)
         rc = so.w4a16_matmul_ex(P[0], P[1], P[2], P[3], P[4], 1, 64, 128, 128, None,
                                 ctypes.byref(pl))
@@ -117,18 +118,21 @@ def test_auto_plan_is_valid_and_covers_k(M, K, N):
     pl = lib.w4a16_plan(M, N, K)
     assert pl["kernel"] in (lib.W4A16_KERNEL_SKINNY, lib.W4A16_KERNEL_PREFILL)
     if pl["kernel"] == lib.W4A16_KERNEL_SKINNY:
-        kc, splits = pl["kc"], pl["splits"]
+        kc, splits, W = pl["kc"], pl["splits"], pl["waves"]
         assert kc in (1, 2) or kc % 4 == 0
+        assert W in (4, 8, 16) and (W - 1) * pl["row_tiles"] <= 15
         KS = K // 32
         chunks = -(-KS // kc)
-        assert splits == -(-chunks // 4)
-        assert splits * 4 * kc >= KS                 # every K-step is covered
-        assert (splits - 1) * 4 * kc < KS            # no work-group is entirely empty
+        assert splits == -(-chunks // W)
+        assert splits * W * kc >= KS                 # every K-step is covered
+        assert (splits - 1) * W * kc < KS            # no work-group is entirely empty
         assert 1 <= pl["row_tiles"] <= 4
         assert pl["row_tiles"] * 16 >= min(M, 64)
 
 
+@pytest.mark.parametrize("waves", [4, 8, 16])
 @pytest.mark.parametrize("kc", [1, 2, 4, 8, 12, 16, 64])
-def test_forced_kc_plan(kc):
-    pl = lib.w4a16_plan(3, 4096, 4096, kernel=lib.W4A16_KERNEL_SKINNY, kc=kc)
-    assert pl["kc"] == kc and pl["splits"] == -(-(-(-128 // kc)) // 4)
+def test_forced_kc_plan(kc, waves):
+    pl = lib.w4a16_plan(3, 4096, 4096, kernel=lib.W4A16_KERNEL_SKINNY, kc=kc, waves=waves)
+    assert pl["kc"] == kc and pl["waves"] == waves
+    assert pl["splits"] == -(-(-(-128 // kc)) // waves)

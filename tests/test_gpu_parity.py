@@ -198,10 +198,12 @@ def test_matmul_ragged(lib, M, K, N):
     check_y(run(lib, x, qw, s, z), oracle.matmul(x, qw, s, z), f"ragged M={M} K={K} N={N}")
 
 
-PLANS = [dict(kernel=1, kc=kc, row_tiles=rt) for kc in (1, 2, 4, 8, 16, 32) for rt in (1, 2, 3, 4)]
+PLANS = [dict(kernel=1, kc=kc, row_tiles=rt, waves=w) for kc in (1, 2, 4, 8, 16, 32)
+         for rt in (1, 2, 3, 4) for w in (4, 8, 16) if (w - 1) * rt <= 15]
 
 
-@pytest.mark.parametrize("plan", PLANS, ids=[f"kc{p['kc']}-rt{p['row_tiles']}" for p in PLANS])
+@pytest.mark.parametrize("plan", PLANS,
+                         ids=[f"kc{p['kc']}-rt{p['row_tiles']}-w{p['waves']}" for p in PLANS])
 def test_matmul_every_skinny_plan(lib, plan):
     M, K, N = 37, 1024, 320
     print(f"\n[plan] {plan} M={M} K={K} N={N}", flush=True)

@@ -35,11 +35,11 @@ class W4A16Error(RuntimeError):
 class w4a16_plan_t(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("kc", ctypes.c_int32), ("splits", ctypes.c_int32),
                 ("row_tiles", ctypes.c_int32), ("tile", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 3)]
+                ("waves", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
 
     def as_dict(self):
         return {"kernel": self.kernel, "kc": self.kc, "splits": self.splits,
-                "row_tiles": self.row_tiles, "tile": self.tile}
+                "row_tiles": self.row_tiles, "tile": self.tile, "waves": self.waves}
 
 
 _lib = None
@@ -132,8 +132,15 @@ def w4a16_unpack(qweight):
     return codes
 
 
-def w4a16_plan(M, N, K, group_size=GROUP_SIZE, kernel=0, kc=0, row_tiles=0, tile=0):
-    pl = w4a16_plan_t(kernel=kernel, kc=kc, splits=0, row_tiles=row_tiles, tile=tile)
+def _make_plan(d):
+    return w4a16_plan_t(kernel=d.get("kernel", 0), kc=d.get("kc", 0), splits=d.get("splits", 0),
+                        row_tiles=d.get("row_tiles", 0), tile=d.get("tile", 0),
+                        waves=d.get("waves", 0))
+
+
+def w4a16_plan(M, N, K, group_size=GROUP_SIZE, **plan):
+    """The completed plan for (M, N, K): the dispatcher's, or a forced one filled in."""
+    pl = _make_plan(plan)
     _check(load().w4a16_plan(M, N, K, group_size, ctypes.byref(pl)), "w4a16_plan")
     return pl.as_dict()
 
@@ -145,7 +152,7 @@ def w4a16_matmul(x, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, strea
 
     x fp16 [M, K]; qweight int32 [K/8, N]; scales, zeros fp16 [K/g, N]; y fp16 [M, N]
     (allocated when None). Enqueued on `stream` (default: torch's current stream).
-    `plan` (dict with kernel/kc/row_tiles/tile) forces the execution plan.
+    `plan` (dict with kernel/kc/row_tiles/waves/tile) forces the execution plan.
     """
     import torch
     if x.dim() != 2 or qweight.dim() != 2:
@@ -167,8 +174,7 @@ def w4a16_matmul(x, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, strea
         rc = load().w4a16_matmul(*args)
         _check(rc, "w4a16_matmul")
     else:
-        pl = w4a16_plan_t(kernel=plan.get("kernel", 0), kc=plan.get("kc", 0), splits=0,
-                          row_tiles=plan.get("row_tiles", 0), tile=plan.get("tile", 0))
+        pl = _make_plan(plan)
         rc = load().w4a16_matmul_ex(*args, ctypes.byref(pl))
         _check(rc, "w4a16_matmul_ex")
     return y
@@ -176,7 +182,7 @@ def w4a16_matmul(x, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, strea
 
 def w4a16_matmul_ex(x, qweight, scales, zeros, y=None, plan=None, group_size=GROUP_SIZE,
                     stream=None):
-    """w4a16_matmul with a forced plan (dict: kernel, kc, row_tiles, tile)."""
+    """w4a16_matmul with a forced plan (dict: kernel, kc, row_tiles, waves, tile)."""
     return w4a16_matmul(x, qweight, scales, zeros, y=y, group_size=group_size, stream=stream,
                         plan=plan if plan is not None else {})
 

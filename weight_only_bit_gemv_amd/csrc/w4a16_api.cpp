@@ -54,20 +54,28 @@ int check_gpu_shape(int64_t M, int64_t N, int64_t K, int64_t group_size) {
 
 // ---- dispatcher --------------------------------------------------------------------------
 
-// K-steps per wavefront for the skinny kernel: aim at ~kTargetWaves wavefronts in the grid,
-// whole 128-row groups per wavefront once a wavefront streams more than one group, and no
-// more than a quarter of K per wavefront so that all 4 wavefronts of a work-group stream.
+// Skinny-kernel plan. The wavefronts of one work-group split its K range and are summed in
+// LDS; work-groups along K (splits) are summed through the workspace. Heuristic, from a
+// sweep of block size x K-steps per wavefront on MI355X: about kTargetWaves wavefronts in
+// the grid (enough loads in flight to cover memory latency on 256 CUs), at least two
+// 4-step segments per wavefront so that its software pipeline has something to overlap,
+// 8-wavefront work-groups for M <= 8 and 4 above (larger M holds more registers), and
+// never more than an equal share of K per wavefront.
 constexpr int64_t kTargetWaves = 2048;
 
-int64_t auto_kc(int64_t KS, int64_t n_strips, int64_t row_blocks) {
-    const int64_t work = KS * n_strips * row_blocks;
-    int64_t kc = std::max<int64_t>(1, ceil_div(work, kTargetWaves));
-    if (kc == 3) kc = 4;
-    if (kc > 4) kc = ceil_div(kc, 4) * 4;
-    // at most a quarter of K per wavefront, rounded down to a valid segment multiple
-    const int64_t quarter = std::max<int64_t>(1, KS / w4a16::kSkinnyWaves);
-    if (kc > quarter) kc = quarter >= 4 ? quarter / 4 * 4 : (quarter >= 2 ? 2 : 1);
-    return kc;
+int64_t valid_kc(int64_t kc) {
+    if (kc <= 1) return 1;
+    if (kc <= 3) return 2;
+    return kc / 4 * 4;
+}
+
+int64_t auto_kc(int64_t KS, int64_t n_strips, int64_t row_blocks, int64_t waves) {
+    const int64_t work = KS * n_strips * row_blocks;             // wavefront K-steps in total
+    int64_t kc = std::max<int64_t>(8, ceil_div(work, kTargetWaves));
+    kc = ceil_div(kc, 4) * 4;
+    // at most an equal share of K per wavefront of one work-group
+    const int64_t share = std::max<int64_t>(1, KS / waves);
+    return std::min(kc, valid_kc(share));
 }
 
 int complete_plan(int64_t M, int64_t N, int64_t K, w4a16_plan_t* pl) {
@@ -79,17 +87,21 @@ int complete_plan(int64_t M, int64_t N, int64_t K, w4a16_plan_t* pl) {
     if (pl->row_tiles == 0) pl->row_tiles = (int32_t)std::min<int64_t>(4, ceil_div(M, 16));
     if (pl->row_tiles < 1 || pl->row_tiles > 4)
         return fail(W4A16_ERR_INVALID_ARG, "row_tiles must be 1..4 (got %d)", pl->row_tiles);
+    if (pl->waves == 0) pl->waves = (pl->row_tiles == 1 && M <= 8) ? 8 : 4;
+    if (!w4a16::skinny_config_supported(pl->row_tiles, pl->waves))
+        return fail(W4A16_ERR_INVALID_ARG, "waves=%d with row_tiles=%d is not built", pl->waves,
+                    pl->row_tiles);
     const int64_t KS = K / w4a16::kKStep;
     const int64_t n_strips = ceil_div(N, w4a16::kStripN);
     const int64_t row_blocks = ceil_div(M, 16 * (int64_t)pl->row_tiles);
-    if (pl->kc == 0) pl->kc = (int32_t)auto_kc(KS, n_strips, row_blocks);
+    if (pl->kc == 0) pl->kc = (int32_t)auto_kc(KS, n_strips, row_blocks, pl->waves);
     if (pl->kc < 1 || pl->kc == 3 || (pl->kc > 4 && pl->kc % 4 != 0))
         return fail(W4A16_ERR_INVALID_ARG, "kc must be 1, 2 or a multiple of 4 (got %d)", pl->kc);
     const int64_t chunks = ceil_div(KS, pl->kc);
-    const int64_t splits = ceil_div(chunks, w4a16::kSkinnyWaves);
+    const int64_t splits = ceil_div(chunks, pl->waves);
     if (pl->splits != 0 && pl->splits != splits)
-        return fail(W4A16_ERR_INVALID_ARG, "splits=%d does not match kc=%d (needs %lld)", pl->splits,
-                    pl->kc, (long long)splits);
+        return fail(W4A16_ERR_INVALID_ARG, "splits=%d does not match kc=%d, waves=%d (needs %lld)",
+                    pl->splits, pl->kc, pl->waves, (long long)splits);
     pl->splits = (int32_t)splits;
     if (n_strips * splits > INT32_MAX || row_blocks > 65535)
         return fail(W4A16_ERR_UNSUPPORTED, "grid too large");
@@ -170,6 +182,7 @@ int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const
     p.n_strips = (int)ceil_div(N, w4a16::kStripN);
     p.row_tiles = pl.row_tiles;
     p.row_blocks = (int)ceil_div(M, 16 * (int64_t)pl.row_tiles);
+    p.waves = pl.waves;
     uint64_t ws_bytes = 0, n_counters = 0;
     w4a16::skinny_workspace(p, &ws_bytes, &n_counters);
     if (ws_bytes) {

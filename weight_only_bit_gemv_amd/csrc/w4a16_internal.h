@@ -15,7 +15,6 @@ int pack_host(const float* W, int64_t K, int64_t N, int64_t g,
 void unpack_host(const int32_t* qweight, int64_t K, int64_t N, uint8_t* codes);
 
 // ---- decode / skinny kernel (w4a16_skinny.hip) ----
-constexpr int kSkinnyWaves = 4;      // wavefronts per work-group, each on its own K range
 constexpr int kStripN = 64;          // output columns per work-group (16 lanes x 4 columns)
 constexpr int kKStep = 32;           // K rows per MFMA step (4 packed rows)
 constexpr int kGroup = 128;          // K rows per scale/zero group
@@ -34,6 +33,7 @@ struct SkinnyParams {
     int n_strips;             // ceil(N / 64)
     int row_tiles;            // 16-row tiles per work-group (1..4)
     int row_blocks;           // ceil(M / (16 * row_tiles))
+    int waves;                // wavefronts per work-group (4, 8 or 16), each on its own K range
 };
 
 // Workspace a skinny launch needs (bytes of partials, number of counters).
@@ -44,6 +44,7 @@ inline void skinny_workspace(const SkinnyParams& p, uint64_t* ws_bytes, uint64_t
 }
 
 int launch_skinny(const SkinnyParams& p, void* stream);   // returns a hipError_t value
+bool skinny_config_supported(int row_tiles, int waves);
 
 // ---- dequant hook (w4a16_dequant.hip) ----
 int launch_dequant(const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
