@@ -49,7 +49,8 @@ extern "C" {
 /* Kernel selection for w4a16_matmul_ex / w4a16_plan. */
 #define W4A16_KERNEL_AUTO     0   /* shape-based dispatcher (what w4a16_matmul uses)        */
 #define W4A16_KERNEL_SKINNY   1   /* decode: weight stream, split-K, M <= 64 per row block  */
-#define W4A16_KERNEL_PREFILL  2   /* prefill: LDS-staged fp16 dequant tiles feeding MFMA    */
+#define W4A16_KERNEL_PREFILL  2   /* prefill: LDS-staged fp16 dequant tiles feeding MFMA;   */
+                                  /* 128 x 128 output tiles, no plan fields besides kernel */
 
 /*
  * Execution plan of one w4a16_matmul call (what the dispatcher chose, or what a caller

@@ -88,7 +88,8 @@ def test_matmul_ex_rejects_bad_plans():
     so = B.load()
     for kw in [dict(kernel=7), dict(kernel=1, kc=3), dict(kernel=1, kc=6), dict(kernel=1, kc=-4),
                dict(kernel=1, row_tiles=5), dict(kernel=1, waves=6), dict(kernel=1, waves=16, row_tiles=2),
-               dict(kernel=1, kc=4, waves=4, splits=3)]:
+               dict(kernel=1, kc=4, waves=4, splits=3), dict(kernel=2, tile=3), dict(kernel=2, kc=4),
+               dict(kernel=2, waves=8)]:
         pl = B.w4a16_plan_t(**kw)
         rc = so.w4a16_matmul_ex(P[0], P[1], P[2], P[3], P[4], 1, 64, 128, 128, None,
                                 ctypes.byref(pl))
@@ -117,6 +118,7 @@ PLAN_SHAPES = [(m, k, n) for m in (1, 2, 4, 8, 16, 17, 33, 64, 65, 128, 2048)
 def test_auto_plan_is_valid_and_covers_k(M, K, N):
     pl = lib.w4a16_plan(M, N, K)
     assert pl["kernel"] in (lib.W4A16_KERNEL_SKINNY, lib.W4A16_KERNEL_PREFILL)
+    assert pl["kernel"] == (lib.W4A16_KERNEL_PREFILL if M >= 65 else lib.W4A16_KERNEL_SKINNY)
     if pl["kernel"] == lib.W4A16_KERNEL_SKINNY:
         kc, splits, W = pl["kc"], pl["splits"], pl["waves"]
         assert kc in (1, 2) or kc % 4 == 0

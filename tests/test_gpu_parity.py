@@ -213,6 +213,33 @@ def test_matmul_every_skinny_plan(lib, plan):
     check_y(run(lib, x, qw, s, z, plan=plan), oracle.matmul(x, qw, s, z), f"plan {plan}")
 
 
+PREFILL_FORCED = [(1, 128, 4), (3, 256, 100), (130, 384, 1412), (257, 1408, 260), (64, 768, 2052),
+                  (128, 4096, 256), (200, 128, 132), (129, 2048, 1408)]
+
+
+@pytest.mark.parametrize("M,K,N", PREFILL_FORCED, ids=[f"M{m}-K{k}-N{n}" for m, k, n in PREFILL_FORCED])
+def test_matmul_prefill_kernel_forced(lib, M, K, N):
+    print(f"\n[prefill forced] M={M} K={K} N={N}", flush=True)
+    W = synth.weight_custom(K, N, seed=100 + M, std=0.02)
+    qw, s, z = oracle.quantize_pack(W)
+    x = synth.activations(M, K, wid=9)
+    check_y(run(lib, x, qw, s, z, plan=dict(kernel=lib.W4A16_KERNEL_PREFILL)),
+            oracle.matmul(x, qw, s, z), f"prefill forced M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("M,K,N", [(32, 8192, 8192), (128, 8192, 8192)])
+def test_skinny_kernel_on_prefill_shapes(lib, M, K, N):
+    """Both kernels must hold the bar where the dispatcher could pick either."""
+    wid = synth.WORKLOADS["prefill"]["wid"]
+    qw, s, z = quantised(K, N, wid)
+    x = synth.activations(M, K, wid=wid)
+    cols = _sample_cols(N)
+    y_ref = oracle.matmul(x, qw[:, cols], s[:, cols], z[:, cols])
+    for plan in (dict(kernel=lib.W4A16_KERNEL_SKINNY), dict(kernel=lib.W4A16_KERNEL_PREFILL)):
+        y = run(lib, x, qw, s, z, plan=plan)
+        check_y(y[:, torch.from_numpy(cols).to(DEV)], y_ref, f"{plan} M={M}")
+
+
 def test_deterministic_split_k(lib):
     M, K, N = 1, 4096, 4096
     qw, s, z = quantised(K, N, 0)
@@ -254,12 +281,13 @@ def test_alternating_shapes_reuse_counters(lib):
             check_y(y, oracle.matmul(x, qw, s, z), f"alternating rep {rep}")
 
 
-def test_exact_closed_form_on_gpu(lib):
+@pytest.mark.parametrize("kernel", [1, 2])
+def test_exact_closed_form_on_gpu(lib, kernel):
     """K=128 exact case (W = ((k+n) mod 16 - 8) / 64): y(ones) = -1 for every column."""
     k = np.arange(128)[:, None]
     n = np.arange(64)[None, :]
     W = (((k + n) % 16 - 8) / 64.0).astype(np.float32)
     qw, s, z = oracle.quantize_pack(W)
-    x = np.ones((1, 128), dtype=np.float16)
-    y = run(lib, x, qw, s, z).cpu().numpy()
+    x = np.ones((3, 128), dtype=np.float16)
+    y = run(lib, x, qw, s, z, plan=dict(kernel=kernel)).cpu().numpy()
     assert np.all(y == np.float16(-1.0))

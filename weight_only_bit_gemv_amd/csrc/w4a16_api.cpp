@@ -78,10 +78,19 @@ int64_t auto_kc(int64_t KS, int64_t n_strips, int64_t row_blocks, int64_t waves)
     return std::min(kc, valid_kc(share));
 }
 
+// Rows of M from which the LDS-tiled prefill kernel replaces the weight-streaming kernel.
+constexpr int64_t kPrefillMinM = 65;
+
 int complete_plan(int64_t M, int64_t N, int64_t K, w4a16_plan_t* pl) {
-    if (pl->kernel == W4A16_KERNEL_AUTO) pl->kernel = W4A16_KERNEL_SKINNY;
-    if (pl->kernel == W4A16_KERNEL_PREFILL)
-        return fail(W4A16_ERR_UNSUPPORTED, "prefill kernel not available in this build");
+    if (pl->kernel == W4A16_KERNEL_AUTO)
+        pl->kernel = M >= kPrefillMinM ? W4A16_KERNEL_PREFILL : W4A16_KERNEL_SKINNY;
+    if (pl->kernel == W4A16_KERNEL_PREFILL) {
+        if (pl->tile != 0) return fail(W4A16_ERR_INVALID_ARG, "prefill tile %d is not built", pl->tile);
+        if (pl->kc || pl->row_tiles || pl->waves || pl->splits)
+            return fail(W4A16_ERR_INVALID_ARG, "kc/row_tiles/waves/splits apply to the skinny kernel only");
+        if (ceil_div(M, w4a16::kPrefillBM) > 65535) return fail(W4A16_ERR_UNSUPPORTED, "grid too large");
+        return W4A16_OK;
+    }
     if (pl->kernel != W4A16_KERNEL_SKINNY)
         return fail(W4A16_ERR_INVALID_ARG, "unknown kernel id %d", pl->kernel);
     if (pl->row_tiles == 0) pl->row_tiles = (int32_t)std::min<int64_t>(4, ceil_div(M, 16));
@@ -167,6 +176,22 @@ int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const
     w4a16_plan_t pl = forced ? *forced : w4a16_plan_t{};
     rc = complete_plan(M, N, K, &pl);
     if (rc) return rc;
+
+    if (pl.kernel == W4A16_KERNEL_PREFILL) {
+        w4a16::PrefillParams q{};
+        q.x = static_cast<const uint16_t*>(x);
+        q.qweight = reinterpret_cast<const uint32_t*>(qweight);
+        q.scales = static_cast<const uint16_t*>(scales);
+        q.zeros = static_cast<const uint16_t*>(zeros);
+        q.y = static_cast<uint16_t*>(y);
+        q.M = (int)M;
+        q.N = (int)N;
+        q.K = (int)K;
+        const int e = w4a16::launch_prefill(q, stream);
+        if (e != (int)hipSuccess)
+            return fail(W4A16_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString((hipError_t)e));
+        return ok();
+    }
 
     w4a16::SkinnyParams p{};
     p.x = static_cast<const uint16_t*>(x);

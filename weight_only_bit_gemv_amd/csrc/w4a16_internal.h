@@ -46,6 +46,22 @@ inline void skinny_workspace(const SkinnyParams& p, uint64_t* ws_bytes, uint64_t
 int launch_skinny(const SkinnyParams& p, void* stream);   // returns a hipError_t value
 bool skinny_config_supported(int row_tiles, int waves);
 
+// ---- prefill kernel (w4a16_prefill.hip) ----
+constexpr int kPrefillBM = 128;      // rows of M per work-group
+constexpr int kPrefillBN = 128;      // columns per work-group
+constexpr int kPrefillBK = 64;       // K rows per LDS step
+
+struct PrefillParams {
+    const uint16_t* x;        // fp16 [M, K]
+    const uint32_t* qweight;  // int32 [K/8, N]
+    const uint16_t* scales;   // fp16 [K/g, N]
+    const uint16_t* zeros;    // fp16 [K/g, N]
+    uint16_t* y;              // fp16 [M, N]
+    int M, N, K;
+};
+
+int launch_prefill(const PrefillParams& p, void* stream);  // returns a hipError_t value
+
 // ---- dequant hook (w4a16_dequant.hip) ----
 int launch_dequant(const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                    uint8_t* codes, uint16_t* w, int N, int K, void* stream);
