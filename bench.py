@@ -1,21 +1,32 @@
-"""Benchmark of the W4A16 decode hot path on one MI355X.
+"""Benchmark of the W4A16 hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step = the decode batch sweep: y = x . dequant(Wq) for M in {1,2,4,8,16} on each of
-(K, N) = (4096, 14336), (14336, 4096), (4096, 4096), group 128 (15 launches). Inputs are
-seeded synthetic data (synth.py) resident in HBM before timing; the packed weights rotate
-over enough distinct device copies (>= 1 GiB per shape family) that no launch finds its
-weights in the 256 MB Infinity Cache. The K timed steps are replayed from one HIP graph on
-one stream and bracketed by HIP events on that stream.
+Default workload `decode_sweep` (the JSON line the headline metric is quoted on): one step
+= y = x . dequant(Wq) for M in {1,2,4,8,16} on each of (K, N) = (4096, 14336),
+(14336, 4096), (4096, 4096), group 128 (15 launches). Inputs are seeded synthetic data
+(synth.py) resident in HBM before timing; the packed weights rotate over enough distinct
+device copies (>= 1 GiB per shape family) that no launch finds its weights in the 256 MB
+Infinity Cache. The K timed steps are replayed from one HIP graph on one stream and
+bracketed by HIP events on that stream; every replay is checked bit for bit against an
+eager run.
 
-Printed: one JSON line. `value` is the weight-stream rate over the whole timed region:
-algorithmic bytes (int4 weights + fp16 scales/zeros + fp16 x + fp16 y) / time, in GB/s.
-`roofline` relates the decode kernel's average launch to the 8 TB/s HBM peak;
-`cpu_baseline` times the oracle (NumPy, fp64) on the host cores on one sweep.
+Other workloads (same JSON keys, config.workload names them):
+  gemv_4096     one M=1, 4096 x 4096 GEMV
+  moe_expert    M in {1,4,16} on (2048,1408), (1408,2048), (2048,768), (768,2048)
+  chain_7b      batch-1 decode weight stream of a 32-layer 7B-shaped model + lm_head:
+                225 GEMVs per token in one graph (one layer's weights packed once and
+                copied into 32 distinct device buffers); also reports tokens/s
+  prefill       M-crossover against torch fp16 matmul (hipBLASLt) for M = 1..2048 on
+                (8192,8192), (8192,28672), (28672,8192) and the decode shapes
 
-Extra modes (profiling support):
-  --pmc-pass               run a fixed copy calibration + a few sweep steps, eagerly, for
+Printed: one JSON line. `value` is the algorithmic byte rate over the timed region
+(int4 weights + fp16 scales/zeros + fp16 x + fp16 y) / time, in GB/s. `roofline` relates
+the dominant kernel's average launch to the 8 TB/s HBM peak (MFMA peak for prefill);
+`cpu_baseline` times the oracle (NumPy, fp64) on the host cores on one decode sweep.
+
+Profiling support:
+  --pmc-pass               a fixed copy calibration + a few eager sweep steps, for
                            rocprofv3 --pmc; prints no JSON
   --summarize-pmc DIR...   read rocprofv3 counter CSVs of --pmc-pass runs and write the
                            per-launch HBM traffic summary to profiles/
@@ -36,10 +47,10 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak (8 TB/s)
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA peak
 GROUP = 128
 SWEEP_KN = [(4096, 14336), (14336, 4096), (4096, 4096)]
 SWEEP_M = [1, 2, 4, 8, 16]
-WID = synth.WORKLOADS["decode_sweep"]["wid"]
 ROTATE_BYTES = 1 << 30         # >= 4x the 256 MB Infinity Cache per shape family
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_skinny_decode_sweep.json")
 KERNEL_SOURCES = ["weight_only_bit_gemv_amd/csrc/w4a16_skinny.hip",
@@ -47,6 +58,7 @@ KERNEL_SOURCES = ["weight_only_bit_gemv_amd/csrc/w4a16_skinny.hip",
                   "weight_only_bit_gemv_amd/csrc/w4a16_internal.h",
                   "weight_only_bit_gemv_amd/csrc/w4a16_api.cpp"]
 COPY_CAL_BYTES = 256 << 20     # calibration copy for the PMC byte counters
+METRIC = "W4A16 weight-stream HBM GB/s (% of peak) and us/call at M=1..16"
 
 
 def alg_bytes(M, K, N):
@@ -68,62 +80,78 @@ def log(msg):
 
 # ---------------------------------------------------------------------------------------
 
-class Sweep:
-    """Device-resident inputs of the decode sweep with rotating weight copies."""
+class Runner:
+    """Device-resident inputs for a list of GEMM launches.
 
-    def __init__(self, torch, lib, dev, stream):
+    families: key -> (K, N, wid, layer); every family gets its own packed weights, copied
+    until its copies total `rotate_bytes` (1 copy when rotate_bytes is 0).
+    items: list of (M, K, N, family key), launched in order by step().
+    """
+
+    def __init__(self, torch, lib, dev, stream, families, items, rotate_bytes, replicate=None):
         self.torch, self.lib, self.dev, self.stream = torch, lib, dev, stream
-        self.weights = {}       # (K, N) -> list of (qw, s, z) device copies
-        self.host = {}          # (K, N) -> host (qw, s, z)
-        for (K, N) in SWEEP_KN:
+        self.weights, self.host = {}, {}
+        packed = {}
+        for key, (K, N, wid, layer) in families.items():
+            src = (replicate or {}).get(key)
+            if src is not None and src in self.weights:     # same values, distinct memory
+                self.weights[key] = [[t.clone() for t in self.weights[src][0]]]
+                self.host[key] = self.host[src]
+                continue
             t0 = time.time()
-            W = synth.weight(K, N, wid=WID)
-            qw, s, z = lib.w4a16_pack(W)
-            del W
-            self.host[(K, N)] = (qw, s, z)
+            if (K, N, wid, layer) not in packed:
+                W = synth.weight(K, N, wid=wid, layer=layer)
+                packed[(K, N, wid, layer)] = lib.w4a16_pack(W)
+                del W
+            qw, s, z = packed[(K, N, wid, layer)]
+            self.host[key] = (qw, s, z)
             one = [torch.from_numpy(a).to(dev) for a in (qw, s, z)]
             per = sum(t.numel() * t.element_size() for t in one)
-            copies = max(2, -(-ROTATE_BYTES // per))
-            self.weights[(K, N)] = [one] + [[t.clone() for t in one] for _ in range(copies - 1)]
-            log(f"[bench] weights K={K} N={N}: {copies} copies x {per / 1e6:.1f} MB "
-                f"({time.time() - t0:.1f}s)")
-        self.shapes = [(M, K, N) for (K, N) in SWEEP_KN for M in SWEEP_M]
-        self.x = {(M, K): torch.from_numpy(synth.activations(M, K, wid=WID)).to(dev)
-                  for (M, K, N) in self.shapes}
-        self.y = {(M, K, N): torch.empty((M, N), dtype=torch.float16, device=dev)
-                  for (M, K, N) in self.shapes}
-        self.cursor = {kn: 0 for kn in SWEEP_KN}
-        self.step_bytes = sum(alg_bytes(M, K, N) for (M, K, N) in self.shapes)
-        so = lib.load()
-        self.fn = so.w4a16_matmul
+            copies = max(1, -(-rotate_bytes // per)) if rotate_bytes else 1
+            self.weights[key] = [one] + [[t.clone() for t in one] for _ in range(copies - 1)]
+            log(f"[bench] weights {key} K={K} N={N}: {copies} x {per / 1e6:.1f} MB ({time.time() - t0:.1f}s)")
+        self.items = items
+        wids = {key: fam[2] for key, fam in families.items()}
+        self.x = {}
+        for (M, K, N, key) in items:
+            if (M, K, wids[key]) not in self.x:
+                self.x[(M, K, wids[key])] = torch.from_numpy(synth.activations(M, K, wid=wids[key])).to(dev)
+        self.xk = [self.x[(M, K, wids[key])] for (M, K, N, key) in items]
+        self.y = [torch.empty((M, N), dtype=torch.float16, device=dev) for (M, K, N, key) in items]
+        self.cursor = {key: 0 for key in families}
+        self.step_bytes = sum(alg_bytes(M, K, N) for (M, K, N, key) in items)
+        self.fn = lib.load().w4a16_matmul
         self.sptr = stream.cuda_stream
 
-    def launch(self, M, K, N):
-        kn = (K, N)
-        i = self.cursor[kn]
-        self.cursor[kn] = (i + 1) % len(self.weights[kn])
-        qw, s, z = self.weights[kn][i]
-        rc = self.fn(self.x[(M, K)].data_ptr(), qw.data_ptr(), s.data_ptr(), z.data_ptr(),
-                     self.y[(M, K, N)].data_ptr(), M, N, K, GROUP, self.sptr)
+    def launch(self, i):
+        M, K, N, key = self.items[i]
+        c = self.cursor[key]
+        self.cursor[key] = (c + 1) % len(self.weights[key])
+        qw, s, z = self.weights[key][c]
+        rc = self.fn(self.xk[i].data_ptr(), qw.data_ptr(), s.data_ptr(), z.data_ptr(),
+                     self.y[i].data_ptr(), M, N, K, GROUP, self.sptr)
         if rc != 0:
             raise RuntimeError(f"w4a16_matmul failed ({rc}) for M={M} K={K} N={N}")
 
     def step(self):
-        for (M, K, N) in self.shapes:
-            self.launch(M, K, N)
+        for i in range(len(self.items)):
+            self.launch(i)
+
+
+def events(torch, stream):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
 def time_graph(torch, stream, body, reps, warm=2):
     """Capture `body` once into a HIP graph on `stream`; replay `reps` times between HIP
-    events recorded on the same stream. Returns seconds per replay."""
+    events recorded on the same stream. Returns (seconds per replay, graph)."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         body()
     for _ in range(warm):
         g.replay()
     stream.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    e0, e1 = events(torch, stream)
     with torch.cuda.stream(stream):
         e0.record(stream)
         for _ in range(reps):
@@ -131,6 +159,63 @@ def time_graph(torch, stream, body, reps, warm=2):
         e1.record(stream)
     e1.synchronize()
     return e0.elapsed_time(e1) / 1e3 / reps, g
+
+
+def timed_steps(torch, runner, steps, warmup):
+    """Warm up eagerly (allocates this stream's split-K workspace), capture `steps` steps in
+    one graph, check replays against the eager outputs, time one replay. Returns seconds."""
+    stream = runner.stream
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, warmup)):
+            runner.step()
+    stream.synchronize()
+    ref = [y.clone() for y in runner.y]
+
+    def body():
+        for _ in range(steps):
+            runner.step()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        body()
+    for _ in range(max(0, warmup)):
+        g.replay()
+    stream.synchronize()
+    _check_same(torch, runner, ref, "graph warm-up replay")
+    torch.cuda.synchronize()
+    e0, e1 = events(torch, stream)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    e1.synchronize()
+    torch.cuda.synchronize()
+    _check_same(torch, runner, ref, "timed replay")
+    del g
+    return e0.elapsed_time(e1) / 1e3
+
+
+def _check_same(torch, runner, ref, what):
+    for i, (y, r) in enumerate(zip(runner.y, ref)):
+        if not torch.equal(y, r):
+            raise RuntimeError(f"{what} differs from the eager result for item {runner.items[i][:3]}")
+
+
+def per_item_times(torch, lib, runner, reps_per_copy=1):
+    """Per-shape time: a graph of one launch per rotation copy of that shape's weights."""
+    out = []
+    seen = set()
+    for i, (M, K, N, key) in enumerate(runner.items):
+        if (M, K, N, key) in seen:
+            continue
+        seen.add((M, K, N, key))
+        reps = len(runner.weights[key]) * reps_per_copy
+        sec, _ = time_graph(torch, runner.stream, lambda: [runner.launch(i) for _ in range(reps)], 5)
+        t = sec / reps
+        b = alg_bytes(M, K, N)
+        out.append({"M": M, "K": K, "N": N, "us": round(t * 1e6, 3),
+                    "GBps": round(b / t / 1e9, 1), "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
+                    "TFLOPs": round(2 * M * K * N / t / 1e12, 3), "plan": lib.w4a16_plan(M, N, K)})
+    return out
 
 
 def copy_bandwidth(torch, dev, stream):
@@ -141,8 +226,7 @@ def copy_bandwidth(torch, dev, stream):
     with torch.cuda.stream(stream):
         for _ in range(3):
             b.copy_(a)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+        e0, e1 = events(torch, stream)
         e0.record(stream)
         for _ in range(10):
             b.copy_(a)
@@ -151,42 +235,35 @@ def copy_bandwidth(torch, dev, stream):
     return 2 * n * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9
 
 
-def dense_baseline(torch, lib, sw, dev, stream):
-    """torch fp16 matmul (hipBLASLt/rocBLAS) on the same shapes with fp16 weights that are
-    the GPU's dequantised values, rotated the same way. Returns per-shape seconds.
+def dense_time(torch, x, ws, y, stream, reps):
+    """Seconds per torch fp16 matmul (hipBLASLt/rocBLAS), rotating over the weights `ws`.
 
     Timed eagerly, never inside a HIP graph: a library GEMM may reset its own split-K flags
-    with a memset, which does not replay correctly from a captured graph. The GPU stays
-    ahead of the host for these sizes, so back-to-back eager calls measure the kernels."""
-    out = {}
-    for (K, N) in SWEEP_KN:
-        qw, s, z = sw.weights[(K, N)][0]
-        _, w16 = lib.w4a16_dequant(qw, s, z, codes=False)
-        per = w16.numel() * 2
-        copies = max(2, -(-ROTATE_BYTES // per))
-        ws = [w16] + [w16.clone() for _ in range(copies - 1)]
-        for M in SWEEP_M:
-            x = sw.x[(M, K)]
-            y = torch.empty((M, N), dtype=torch.float16, device=dev)
-            reps = 4 * len(ws)
-            with torch.cuda.stream(stream):
-                for i in range(len(ws)):                       # warm-up (library initialisation)
-                    torch.matmul(x, ws[i], out=y)
-                stream.synchronize()
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                for i in range(reps):
-                    torch.matmul(x, ws[i % len(ws)], out=y)
-                e1.record(stream)
-            e1.synchronize()
-            out[(M, K, N)] = e0.elapsed_time(e1) / 1e3 / reps
-        del ws
-    return out
+    with a memset, which does not replay correctly from a captured graph. For these sizes
+    the GPU stays ahead of the host, so back-to-back eager calls measure the kernels."""
+    with torch.cuda.stream(stream):
+        for i in range(len(ws)):                              # warm-up (library initialisation)
+            torch.matmul(x, ws[i], out=y)
+        stream.synchronize()
+        e0, e1 = events(torch, stream)
+        e0.record(stream)
+        for i in range(reps):
+            torch.matmul(x, ws[i % len(ws)], out=y)
+        e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / reps
 
 
-def cpu_baseline(sw):
-    """The oracle as it stands (unpack + exact dequant + fp64 BLAS matmul) on one sweep."""
+def dense_weights(torch, lib, runner, key):
+    """fp16 weights [K, N] equal to the GPU's dequantised values, rotated like the int4 ones."""
+    qw, s, z = runner.weights[key][0]
+    _, w16 = lib.w4a16_dequant(qw, s, z, codes=False)
+    copies = max(2, -(-ROTATE_BYTES // (w16.numel() * 2)))
+    return [w16] + [w16.clone() for _ in range(copies - 1)]
+
+
+def cpu_baseline(runner, wid):
+    """The oracle as it stands (unpack + exact dequant + fp64 BLAS matmul) on one step."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -195,22 +272,21 @@ def cpu_baseline(sw):
         blas_threads = None
     total_bytes = 0
     t0 = time.perf_counter()
-    for (M, K, N) in sw.shapes:
-        qw, s, z = sw.host[(K, N)]
-        x = synth.activations(M, K, wid=WID)
+    for (M, K, N, key) in runner.items:
+        qw, s, z = runner.host[key]
+        x = synth.activations(M, K, wid=wid)
         oracle.matmul(x, qw, s, z)
         total_bytes += alg_bytes(M, K, N)
     dt = time.perf_counter() - t0
-    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s",
-            "cores": blas_threads,
+    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": blas_threads,
             "kind": "oracle",
-            "sample": (f"one pass over the 15 decode-sweep GEMMs (same shapes and data), "
-                       f"{dt:.1f} s; NumPy elementwise unpack/dequant on 1 thread, fp64 BLAS "
-                       f"matmul on {blas_threads} threads of "
+            "sample": (f"one pass over the {len(runner.items)} GEMMs of one step (same shapes "
+                       f"and data), {dt:.1f} s; NumPy elementwise unpack/dequant on 1 thread, "
+                       f"fp64 BLAS matmul on {blas_threads} threads of "
                        f"{len(os.sched_getaffinity(0))} available")}
 
 
-def load_traffic(launches_per_step):
+def load_traffic():
     """Measured HBM bytes per launch from the committed PMC summary, if it was taken on the
     current kernel source (else None)."""
     try:
@@ -222,122 +298,166 @@ def load_traffic(launches_per_step):
     return d.get("traffic_bytes_per_launch")
 
 
-# ---------------------------------------------------------------------------------------
+# ---- workloads ----------------------------------------------------------------------------
 
-def run_bench(args):
+def workload_items(name):
+    """(families, items, description, replicate) of a decode-type workload."""
+    if name == "decode_sweep":
+        wid = synth.WORKLOADS[name]["wid"]
+        fam = {(K, N): (K, N, wid, 0) for (K, N) in SWEEP_KN}
+        items = [(M, K, N, (K, N)) for (K, N) in SWEEP_KN for M in SWEEP_M]
+        desc = ("decode_sweep: M in {1,2,4,8,16} x (K,N) in {(4096,14336),(14336,4096),"
+                "(4096,4096)}, int4 weights packed 8/int32 along K, fp16 scale+zero per 128-row group")
+        return fam, items, desc, None
+    if name == "gemv_4096":
+        fam = {(4096, 4096): (4096, 4096, 0, 0)}
+        return fam, [(1, 4096, 4096, (4096, 4096))], "gemv_4096: M=1, K=N=4096, group 128", None
+    if name == "moe_expert":
+        wid = synth.WORKLOADS[name]["wid"]
+        kns = [(2048, 1408), (1408, 2048), (2048, 768), (768, 2048)]
+        fam = {(K, N): (K, N, wid, 0) for (K, N) in kns}
+        items = [(M, K, N, (K, N)) for (K, N) in kns for M in (1, 4, 16)]
+        return fam, items, "moe_expert: M in {1,4,16} x (2048,1408),(1408,2048),(2048,768),(768,2048)", None
+    if name == "chain_7b":
+        wid = synth.WORKLOADS["decode_chain_7b"]["wid"]
+        fam, items, replicate = {}, [], {}
+        for layer in range(synth.CHAIN_7B_LAYERS):
+            for p, (pname, K, N) in enumerate(synth.CHAIN_7B_LAYER):
+                key = (layer, pname)
+                # one layer's seven matrices are drawn (distinct seeds per projection);
+                # the other 31 layers are device copies of them (distinct memory)
+                fam[key] = (K, N, wid, p)
+                if layer > 0:
+                    replicate[key] = (0, pname)
+                items.append((1, K, N, key))
+        _, K, N = synth.CHAIN_7B_LM_HEAD
+        fam[("lm_head",)] = (K, N, wid, 100)
+        items.append((1, K, N, ("lm_head",)))
+        desc = ("chain_7b: batch-1 decode of a 32-layer 7B-shaped model, per layer q,k,v,o "
+                "4096x4096, gate,up 4096x14336, down 14336x4096, plus lm_head 4096x128256; "
+                "225 GEMVs per token")
+        return fam, items, desc, replicate
+    raise SystemExit(f"unknown workload {name}")
+
+
+def run_decode(args):
     import torch
     import weight_only_bit_gemv_amd as lib
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.Stream(device=dev)
-    sw = Sweep(torch, lib, dev, stream)
-    launches = len(sw.shapes)
-
-    # eager warm-up on the bench stream (allocates the split-K workspace for this stream)
-    with torch.cuda.stream(stream):
-        for _ in range(max(1, args.warmup)):
-            sw.step()
-    stream.synchronize()
-    eager_ref = {k: v.clone() for k, v in sw.y.items()}
-
-    # timed region: K steps replayed from one graph
-    steps = args.steps
-
-    def body():
-        for _ in range(steps):
-            sw.step()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        body()
-    for _ in range(max(0, args.warmup)):
-        g.replay()
-    stream.synchronize()
-    for k, v in sw.y.items():        # every replay must reproduce the eager results
-        if not torch.equal(v, eager_ref[k]):
-            raise RuntimeError(f"graph replay differs from eager result for {k}")
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
-    e1.synchronize()
-    torch.cuda.synchronize()
-    elapsed = e0.elapsed_time(e1) / 1e3
-    total_bytes = sw.step_bytes * steps
-    value = total_bytes / elapsed / 1e9
+    fam, items, desc, replicate = workload_items(args.workload)
+    rotate = 0 if args.workload == "chain_7b" else ROTATE_BYTES
+    runner = Runner(torch, lib, dev, stream, fam, items, rotate, replicate)
+    launches = len(items)
+    steps = args.steps if args.workload != "chain_7b" else max(1, args.steps // 10)
+    elapsed = timed_steps(torch, runner, steps, args.warmup)
+    value = runner.step_bytes * steps / elapsed / 1e9
     avg_launch_s = elapsed / (steps * launches)
-    for k, v in sw.y.items():
-        if not torch.equal(v, eager_ref[k]):
-            raise RuntimeError(f"timed replay differs from eager result for {k}")
 
-    # eager (no graph) rate for reference: includes host launch cost
-    with torch.cuda.stream(stream):
+    with torch.cuda.stream(stream):                 # eager rate, for reference
+        e0, e1 = events(torch, stream)
         e0.record(stream)
         for _ in range(steps):
-            sw.step()
+            runner.step()
         e1.record(stream)
     e1.synchronize()
     eager_elapsed = e0.elapsed_time(e1) / 1e3
 
-    # per-shape timing (graph of one launch per rotation copy)
-    per_shape = []
-    for (M, K, N) in sw.shapes:
-        reps = len(sw.weights[(K, N)])
-        sec, _ = time_graph(torch, stream, lambda: [sw.launch(M, K, N) for _ in range(reps)], 5)
-        t = sec / reps
-        b = alg_bytes(M, K, N)
-        per_shape.append({"M": M, "K": K, "N": N, "us": round(t * 1e6, 3),
-                          "GBps": round(b / t / 1e9, 1),
-                          "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
-                          "TFLOPs": round(2 * M * K * N / t / 1e12, 3),
-                          "plan": lib.w4a16_plan(M, N, K)})
-    del g
-
-    copy_gbs = copy_bandwidth(torch, dev, stream)
-    dense = {} if args.no_dense else dense_baseline(torch, lib, sw, dev, stream)
-    for r in per_shape:
-        d = dense.get((r["M"], r["K"], r["N"]))
-        if d:
+    per = per_item_times(torch, lib, runner) if args.workload != "chain_7b" else []
+    if not args.no_dense and args.workload != "chain_7b":
+        dw = {}
+        for r in per:
+            key = next(k for (M, K, N, k) in items if (K, N) == (r["K"], r["N"]))
+            if key not in dw:
+                dw[key] = dense_weights(torch, lib, runner, key)
+            x = runner.x[(r["M"], r["K"], fam[key][2])]
+            y = torch.empty((r["M"], r["N"]), dtype=torch.float16, device=dev)
+            d = dense_time(torch, x, dw[key], y, stream, 4 * len(dw[key]))
             r["dense_fp16_us"] = round(d * 1e6, 3)
             r["speedup_vs_dense_fp16"] = round(d / (r["us"] / 1e6), 3)
-
-    traffic = load_traffic(launches)
-    achieved = sw.step_bytes / launches / avg_launch_s / 1e9
+        del dw
+    copy_gbs = copy_bandwidth(torch, dev, stream)
+    achieved = runner.step_bytes / launches / avg_launch_s / 1e9
     result = {
-        "metric": "W4A16 weight-stream HBM GB/s (% of peak) and us/call at M=1..16",
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(elapsed / steps * 1e3, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16",
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(elapsed / steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": "decode_sweep: M in {1,2,4,8,16} x (K,N) in {(4096,14336),"
-                               "(14336,4096),(4096,4096)}, int4 weights packed 8/int32 along K, "
-                               "fp16 scale+zero per 128-row group",
-                   "launches_per_step": launches,
-                   "bytes_per_step": sw.step_bytes,
+        "config": {"workload": desc, "launches_per_step": launches, "bytes_per_step": runner.step_bytes,
                    "timing": "HIP graph of all steps, events on the launch stream",
-                   "weight_copies_rotated": {f"{k}x{n}": len(v) for (k, n), v in sw.weights.items()}},
+                   "weight_copies_rotated": {str(k): len(v) for k, v in runner.weights.items()
+                                             if args.workload != "chain_7b"}},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
+                     "traffic": load_traffic() if args.workload == "decode_sweep" else None,
                      "kernel": "skinny_kernel (decode split-K MFMA)",
                      "avg_launch_us": round(avg_launch_s * 1e6, 3)},
         "measured_copy_GBps": round(copy_gbs, 1),
         "frac_of_measured_copy": round(value / copy_gbs, 4),
         "eager_ms_per_step": round(eager_elapsed / steps * 1e3, 4),
-        "per_shape": per_shape,
+        "per_shape": per,
     }
-    if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(sw)
+    if args.workload == "chain_7b":
+        result["tokens_per_s"] = round(steps / elapsed, 2)
+        result["us_per_token"] = round(elapsed / steps * 1e6, 2)
+        result["ceiling_tokens_per_s_at_8TBps"] = round(HBM_PEAK_GBS * 1e9 / runner.step_bytes, 1)
+        result["ceiling_tokens_per_s_at_measured_copy"] = round(copy_gbs * 1e9 / runner.step_bytes, 1)
+    if not args.no_cpu and args.workload == "decode_sweep":
+        result["cpu_baseline"] = cpu_baseline(runner, synth.WORKLOADS["decode_sweep"]["wid"])
+    print(json.dumps(result), flush=True)
+
+
+def run_prefill(args):
+    """M-crossover of the W4A16 path (dispatcher's choice) against torch fp16 matmul."""
+    import torch
+    import weight_only_bit_gemv_amd as lib
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    wid = synth.WORKLOADS["prefill"]["wid"]
+    kns = [(8192, 8192), (8192, 28672), (28672, 8192)] + SWEEP_KN
+    ms = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048]
+    rows, best_gbs = [], None
+    for (K, N) in kns:
+        fam = {(K, N): (K, N, wid, 0)}
+        items = [(M, K, N, (K, N)) for M in ms]
+        runner = Runner(torch, lib, dev, stream, fam, items, ROTATE_BYTES // 2)
+        with torch.cuda.stream(stream):
+            runner.step()
+        stream.synchronize()
+        ws = dense_weights(torch, lib, runner, (K, N))
+        cross = None
+        for i, M in enumerate(ms):
+            log(f"[prefill] K={K} N={N} M={M}")
+            reps = len(runner.weights[(K, N)])
+            sec, _ = time_graph(torch, stream, lambda: [runner.launch(i) for _ in range(reps)], 2, warm=1)
+            t = sec / reps
+            y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            d = dense_time(torch, runner.xk[i], ws, y, stream, 2 * len(ws))
+            fl = 2 * M * K * N
+            rows.append({"M": M, "K": K, "N": N, "w4a16_us": round(t * 1e6, 2),
+                         "w4a16_TFLOPs": round(fl / t / 1e12, 2), "w4a16_GBps": round(alg_bytes(M, K, N) / t / 1e9, 1),
+                         "dense_fp16_us": round(d * 1e6, 2), "dense_TFLOPs": round(fl / d / 1e12, 2),
+                         "speedup_vs_dense": round(d / t, 3), "plan": lib.w4a16_plan(M, N, K)})
+            if cross is None and d < t:
+                cross = M
+        rows.append({"K": K, "N": N, "crossover_M_dense_faster_from": cross})
+        del ws, runner
+        torch.cuda.empty_cache()
+    big = [r for r in rows if "w4a16_TFLOPs" in r and r["M"] >= 512]
+    best = max(big, key=lambda r: r["w4a16_TFLOPs"])
+    result = {"metric": "W4A16 prefill TFLOP/s and M-crossover against dense fp16",
+              "value": best["w4a16_TFLOPs"], "unit": "TFLOP/s", "n_gpus": 1, "steps": 1,
+              "warmup": 1, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+              "config": {"workload": "prefill crossover: M in 1..2048 on (8192,8192),(8192,28672),"
+                                     "(28672,8192) and the decode-sweep shapes"},
+              "roofline": {"bound": "mfma", "achieved": best["w4a16_TFLOPs"],
+                           "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(best["w4a16_TFLOPs"] / MFMA_F16_PEAK_TFLOPS, 4),
+                           "traffic": None, "kernel": "prefill_kernel", "shape": [best["M"], best["K"], best["N"]]},
+              "rows": rows}
     print(json.dumps(result), flush=True)
 
 
@@ -354,10 +474,11 @@ def run_pmc_pass(args):
             b.copy_(a)
     stream.synchronize()
     log("[pmc] calibration copies done")
-    sw = Sweep(torch, lib, dev, stream)
+    fam, items, _, replicate = workload_items("decode_sweep")
+    runner = Runner(torch, lib, dev, stream, fam, items, ROTATE_BYTES, replicate)
     with torch.cuda.stream(stream):
         for _ in range(args.steps):
-            sw.step()
+            runner.step()
     stream.synchronize()
     log(f"[pmc] {args.steps} sweep steps done")
 
@@ -407,6 +528,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_sweep",
+                    choices=["decode_sweep", "gemv_4096", "moe_expert", "chain_7b", "prefill"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense fp16 baseline")
     ap.add_argument("--pmc-pass", action="store_true")
@@ -421,8 +544,10 @@ def main():
         return 2
     if args.pmc_pass:
         run_pmc_pass(args)
-        return 0
-    run_bench(args)
+    elif args.workload == "prefill":
+        run_prefill(args)
+    else:
+        run_decode(args)
     return 0
 
 

@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -138,3 +139,14 @@ def test_forced_kc_plan(kc, waves):
     pl = lib.w4a16_plan(3, 4096, 4096, kernel=lib.W4A16_KERNEL_SKINNY, kc=kc, waves=waves)
     assert pl["kc"] == kc and pl["waves"] == waves
     assert pl["splits"] == -(-(-(-128 // kc)) // waves)
+
+
+def test_one_hip_runtime_per_process():
+    """Importing the package (before or after torch) leaves exactly one libamdhip64 mapped:
+    the library must call the runtime that owns torch's device memory and streams."""
+    code = ("import weight_only_bit_gemv_amd as L, torch; "
+            "import sys; r = L.hip_runtimes_loaded(); print(r); sys.exit(0 if len(r) == 1 else 1)")
+    for src in (code, "import torch; " + code):
+        r = subprocess.run([sys.executable, "-c", src], cwd=ROOT, capture_output=True, text=True,
+                           timeout=300)
+        assert r.returncode == 0, f"{src}\n{r.stdout}\n{r.stderr}"

@@ -5,7 +5,7 @@ this package only marshals arguments to it. Importing the package loads the libr
 raises if it cannot, so there is no silent fallback path.
 """
 from ._binding import (  # noqa: F401
-    GROUP_SIZE, LIB_PATH, W4A16Error, w4a16_pack, w4a16_unpack, w4a16_plan, w4a16_matmul,
+    GROUP_SIZE, LIB_PATH, W4A16Error, hip_runtimes_loaded, w4a16_pack, w4a16_unpack, w4a16_plan, w4a16_matmul,
     w4a16_matmul_ex, w4a16_dequant, w4a16_version, strerror, load,
     W4A16_OK, W4A16_ERR_INVALID_ARG, W4A16_ERR_UNSUPPORTED, W4A16_ERR_ALIGNMENT,
     W4A16_ERR_NONFINITE, W4A16_ERR_HIP, W4A16_KERNEL_AUTO, W4A16_KERNEL_SKINNY,

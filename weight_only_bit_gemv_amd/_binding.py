@@ -59,6 +59,34 @@ _SIGS = {
 }
 
 
+def _bind_hip_runtime():
+    """Make the library use the HIP runtime that torch already uses.
+
+    torch ships its own libamdhip64 with the same soname (libamdhip64.so.7) as the ROCm
+    one libw4a16.so is linked against. Loaded after torch, the library binds to torch's
+    copy, so device pointers and stream handles from torch belong to the runtime the
+    library calls. Loaded first, it would pull in a second HIP and HSA runtime, whose
+    streams are not torch's and which may not see the device at all.
+    """
+    try:
+        import torch  # noqa: F401
+    except ImportError:          # no torch in the process: the ROCm runtime is the only one
+        pass
+
+
+def hip_runtimes_loaded():
+    """Paths of the libamdhip64 files mapped into this process (Linux)."""
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(line.split()[-1])
+    except OSError:
+        pass
+    return sorted(paths)
+
+
 def load(build_if_missing=True):
     """Load libw4a16.so (building it in-tree first if it is absent). Raises if it cannot."""
     global _lib
@@ -69,6 +97,7 @@ def load(build_if_missing=True):
             raise ImportError(f"{LIB_PATH} is not built")
         from . import build as _build
         _build.build()
+    _bind_hip_runtime()
     lib = ctypes.CDLL(LIB_PATH)
     for name, (args, res) in _SIGS.items():
         fn = getattr(lib, name)
