@@ -54,6 +54,10 @@ SWEEP_M = [1, 2, 4, 8, 16]
 ROTATE_BYTES = 1 << 30         # >= 4x the 256 MB Infinity Cache per shape family
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_skinny_decode_sweep.json")
 KERNEL_SOURCES = ["weight_only_bit_gemv_amd/csrc/w4a16_skinny.hip",
+                  "weight_only_bit_gemv_amd/csrc/w4a16_skinny.hpp",
+                  "weight_only_bit_gemv_amd/csrc/w4a16_skinny_lw1.hip",
+                  "weight_only_bit_gemv_amd/csrc/w4a16_skinny_lw2.hip",
+                  "weight_only_bit_gemv_amd/csrc/w4a16_skinny_lw4.hip",
                   "weight_only_bit_gemv_amd/csrc/w4a16_device.hpp",
                   "weight_only_bit_gemv_amd/csrc/w4a16_internal.h",
                   "weight_only_bit_gemv_amd/csrc/w4a16_api.cpp"]
@@ -142,23 +146,44 @@ def events(torch, stream):
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def time_graph(torch, stream, body, reps, warm=2):
-    """Capture `body` once into a HIP graph on `stream`; replay `reps` times between HIP
-    events recorded on the same stream. Returns (seconds per replay, graph)."""
+CLOCK_WARM_S = 0.3             # sustained load before a timed region (the GPU clock ramps up)
+
+
+def keep_busy(stream, g, seconds):
+    """Replay graph `g` until `seconds` of wall time have passed: the GPU raises its clock
+    under sustained load, and a timed region that starts cold measures the ramp."""
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        g.replay()
+        n += 1
+        if n % 8 == 0:
+            stream.synchronize()
+    stream.synchronize()
+    return n
+
+
+def time_graph(torch, stream, body, reps, warm=2, busy_s=0.05, trials=3):
+    """Capture `body` once into a HIP graph on `stream`; after `warm` replays and `busy_s`
+    seconds of sustained replays, time `trials` runs of `reps` replays between HIP events
+    recorded on the same stream. Returns (median seconds per replay, graph)."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         body()
     for _ in range(warm):
         g.replay()
-    stream.synchronize()
-    e0, e1 = events(torch, stream)
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-    e1.synchronize()
-    return e0.elapsed_time(e1) / 1e3 / reps, g
+    keep_busy(stream, g, busy_s)
+    ts = []
+    for _ in range(trials):
+        e0, e1 = events(torch, stream)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) / 1e3 / reps)
+    return float(np.median(ts)), g
 
 
 def timed_steps(torch, runner, steps, warmup):
@@ -181,6 +206,7 @@ def timed_steps(torch, runner, steps, warmup):
         g.replay()
     stream.synchronize()
     _check_same(torch, runner, ref, "graph warm-up replay")
+    keep_busy(stream, g, CLOCK_WARM_S)
     torch.cuda.synchronize()
     e0, e1 = events(torch, stream)
     with torch.cuda.stream(stream):
@@ -244,6 +270,13 @@ def dense_time(torch, x, ws, y, stream, reps):
     with torch.cuda.stream(stream):
         for i in range(len(ws)):                              # warm-up (library initialisation)
             torch.matmul(x, ws[i], out=y)
+        stream.synchronize()
+        t0, i = time.perf_counter(), 0
+        while time.perf_counter() - t0 < 0.05:                # sustained load: clock ramp-up
+            torch.matmul(x, ws[i % len(ws)], out=y)
+            i += 1
+            if i % 16 == 0:
+                stream.synchronize()
         stream.synchronize()
         e0, e1 = events(torch, stream)
         e0.record(stream)
@@ -392,7 +425,7 @@ def run_decode(args):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic() if args.workload == "decode_sweep" else None,
-                     "kernel": "skinny_kernel (decode split-K MFMA)",
+                     "kernel": "skinny_kernel (decode weight stream, MFMA, split-K when K is deep)",
                      "avg_launch_us": round(avg_launch_s * 1e6, 3)},
         "measured_copy_GBps": round(copy_gbs, 1),
         "frac_of_measured_copy": round(value / copy_gbs, 4),

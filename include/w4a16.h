@@ -57,12 +57,18 @@ extern "C" {
  * forces through w4a16_matmul_ex). Fields a caller sets to 0 are chosen by the library.
  *   kernel     W4A16_KERNEL_*.
  *   kc         SKINNY: K-steps of 32 rows that one wavefront streams: 1, 2 or a multiple
- *              of 4.
- *   splits     SKINNY: work-groups along K per 64-column strip (output: derived from kc
- *              and waves; a caller may leave it 0 or give the matching value).
- *   row_tiles  SKINNY: 16-row MFMA tiles per work-group (1..4; default ceil(M/16) <= 4).
+ *              of 4 (a multiple of seg).
+ *   splits     SKINNY: work-groups along K per column strip (output: derived from kc and
+ *              waves; a caller may leave it 0 or give the matching value).
+ *   row_tiles  SKINNY: 16-row MFMA tiles per work-group (1..4; default ceil(M/16) <= 4;
+ *              at most 2 when cols < 64).
  *   tile       PREFILL: tile configuration id (0 = default).
- *   waves      SKINNY: wavefronts per work-group, 4, 8 or 16, with (waves-1)*row_tiles <= 15.
+ *   waves      SKINNY: wavefronts per work-group, 4, 8 or 16 (the cross-wave reduction
+ *              must fit in 64 KiB of LDS: (waves-1) * 16*row_tiles * cols * 4 bytes).
+ *   cols       SKINNY: output columns per work-group strip, 16, 32 or 64 (each lane loads
+ *              cols/16 consecutive packed words of a row: 4, 8 or 16 bytes).
+ *   seg        SKINNY: K-steps one wavefront loads ahead as a unit, 1, 2, 4 or 8 (8 needs
+ *              K % 256 == 0 and kc % 8 == 0); default from kc.
  */
 typedef struct w4a16_plan {
     int32_t kernel;
@@ -71,7 +77,8 @@ typedef struct w4a16_plan {
     int32_t row_tiles;
     int32_t tile;
     int32_t waves;
-    int32_t reserved[2];
+    int32_t cols;
+    int32_t seg;
 } w4a16_plan_t;
 
 /*

@@ -123,14 +123,16 @@ def test_auto_plan_is_valid_and_covers_k(M, K, N):
     if pl["kernel"] == lib.W4A16_KERNEL_SKINNY:
         kc, splits, W = pl["kc"], pl["splits"], pl["waves"]
         assert kc in (1, 2) or kc % 4 == 0
-        assert W in (4, 8, 16) and (W - 1) * pl["row_tiles"] <= 15
+        assert W in (4, 8, 16) and (W - 1) * pl["row_tiles"] * pl["cols"] <= 15 * 64
         KS = K // 32
         chunks = -(-KS // kc)
         assert splits == -(-chunks // W)
         assert splits * W * kc >= KS                 # every K-step is covered
         assert (splits - 1) * W * kc < KS            # no work-group is entirely empty
-        assert 1 <= pl["row_tiles"] <= 4
-        assert pl["row_tiles"] * 16 >= min(M, 64)
+        assert pl["cols"] in (16, 32, 64) and kc % pl["seg"] == 0
+        assert pl["seg"] != 8 or KS % 8 == 0
+        assert 1 <= pl["row_tiles"] <= (4 if pl["cols"] == 64 else 2)
+        assert pl["row_tiles"] * 16 >= min(M, 64 if pl["cols"] == 64 else 32)
 
 
 @pytest.mark.parametrize("waves", [4, 8, 16])

@@ -198,19 +198,58 @@ def test_matmul_ragged(lib, M, K, N):
     check_y(run(lib, x, qw, s, z), oracle.matmul(x, qw, s, z), f"ragged M={M} K={K} N={N}")
 
 
-PLANS = [dict(kernel=1, kc=kc, row_tiles=rt, waves=w) for kc in (1, 2, 4, 8, 16, 32)
-         for rt in (1, 2, 3, 4) for w in (4, 8, 16) if (w - 1) * rt <= 15]
+def _plan_is_built(plan, M, N, K):
+    """Whether the library accepts a forced plan (host-side check, no GPU needed)."""
+    import weight_only_bit_gemv_amd as L
+    try:
+        L.w4a16_plan(M, N, K, **plan)
+        return True
+    except L.W4A16Error:
+        return False
 
 
-@pytest.mark.parametrize("plan", PLANS,
-                         ids=[f"kc{p['kc']}-rt{p['row_tiles']}-w{p['waves']}" for p in PLANS])
+PLAN_MKN = (37, 1024, 320)
+_SEG_KC = {1: (1, 2, 4), 2: (2, 4, 8), 4: (4, 8, 16), 8: (8, 16, 32)}
+PLANS = [p for p in (dict(kernel=1, kc=kc, row_tiles=rt, waves=w, cols=c, seg=sg)
+                     for c in (16, 32, 64) for sg in (1, 2, 4, 8) for kc in _SEG_KC[sg]
+                     for rt in (1, 2, 3, 4) for w in (4, 8, 16))
+         if _plan_is_built(p, PLAN_MKN[0], PLAN_MKN[2], PLAN_MKN[1])]
+_PLAN_CASE = {}
+
+
+def _plan_case():
+    if not _PLAN_CASE:
+        M, K, N = PLAN_MKN
+        W = synth.weight_custom(K, N, seed=11, std=0.02)
+        qw, s, z = oracle.quantize_pack(W)
+        x = synth.activations(M, K, wid=8)
+        _PLAN_CASE.update(x=x, w=(qw, s, z), dev=[dev(x), dev(qw), dev(s), dev(z)],
+                          ref=oracle.matmul(x, qw, s, z))
+    return _PLAN_CASE
+
+
+@pytest.mark.parametrize("plan", PLANS, ids=[f"c{p['cols']}-seg{p['seg']}-kc{p['kc']}-rt{p['row_tiles']}"
+                                              f"-w{p['waves']}" for p in PLANS])
 def test_matmul_every_skinny_plan(lib, plan):
-    M, K, N = 37, 1024, 320
+    """Every built skinny configuration (strip width, segment, K-steps, row tiles, waves)
+    on one ragged shape: M = 37 spans three 16-row tiles, N = 320 is not a multiple of 64."""
+    M, K, N = PLAN_MKN
     print(f"\n[plan] {plan} M={M} K={K} N={N}", flush=True)
-    W = synth.weight_custom(K, N, seed=11, std=0.02)
+    c = _plan_case()
+    check_y(run(lib, *c["dev"], plan=plan), c["ref"], f"plan {plan}")
+
+
+@pytest.mark.parametrize("cols", [16, 32])
+@pytest.mark.parametrize("M,K,N", RAGGED, ids=[f"M{m}-K{k}-N{n}" for m, k, n in RAGGED])
+def test_matmul_ragged_narrow_strips(lib, M, K, N, cols):
+    """16- and 32-column strips (4- and 8-byte weight loads) on the ragged shapes."""
+    plan = dict(kernel=lib.W4A16_KERNEL_SKINNY, cols=cols)
+    print(f"\n[ragged narrow] M={M} K={K} N={N} plan={lib.w4a16_plan(M, N, K, **plan)}", flush=True)
+    W = synth.weight_custom(K, N, seed=M, std=0.02)
     qw, s, z = oracle.quantize_pack(W)
-    x = synth.activations(M, K, wid=8)
-    check_y(run(lib, x, qw, s, z, plan=plan), oracle.matmul(x, qw, s, z), f"plan {plan}")
+    x = synth.activations(M, K, wid=7)
+    check_y(run(lib, x, qw, s, z, plan=plan), oracle.matmul(x, qw, s, z),
+            f"ragged cols={cols} M={M} K={K} N={N}")
 
 
 PREFILL_FORCED = [(1, 128, 4), (3, 256, 100), (130, 384, 1412), (257, 1408, 260), (64, 768, 2052),
@@ -240,17 +279,23 @@ def test_skinny_kernel_on_prefill_shapes(lib, M, K, N):
         check_y(y[:, torch.from_numpy(cols).to(DEV)], y_ref, f"{plan} M={M}")
 
 
-def test_deterministic_split_k(lib):
-    M, K, N = 1, 4096, 4096
+@pytest.mark.parametrize("M,K,N,plan", [
+    (1, 4096, 4096, dict(kernel=1, cols=64, waves=4, kc=8)),
+    (16, 4096, 4096, dict(kernel=1, cols=16, waves=4, kc=4)),
+    (1, 14336, 4096, None),
+])
+def test_deterministic_split_k(lib, M, K, N, plan):
+    """Split-K sums are combined in a fixed order: repeated calls give the same bits."""
     qw, s, z = quantised(K, N, 0)
     x = synth.activations(M, K, wid=0)
-    assert lib.w4a16_plan(M, N, K)["splits"] > 1
+    assert lib.w4a16_plan(M, N, K, **(plan or {}))["splits"] > 1
     args = [dev(x), dev(qw), dev(s), dev(z)]
-    a = lib.w4a16_matmul(*args).clone()
+    a = lib.w4a16_matmul(*args, plan=plan).clone()
     for _ in range(5):
-        b = lib.w4a16_matmul(*args)
+        b = lib.w4a16_matmul(*args, plan=plan)
         torch.cuda.synchronize()
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    check_y(a, oracle.matmul(x, qw, s, z), f"split-K {plan}")
 
 
 def test_nondefault_stream_and_full_overwrite(lib):

@@ -35,11 +35,12 @@ class W4A16Error(RuntimeError):
 class w4a16_plan_t(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("kc", ctypes.c_int32), ("splits", ctypes.c_int32),
                 ("row_tiles", ctypes.c_int32), ("tile", ctypes.c_int32),
-                ("waves", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
+                ("waves", ctypes.c_int32), ("cols", ctypes.c_int32), ("seg", ctypes.c_int32)]
 
     def as_dict(self):
         return {"kernel": self.kernel, "kc": self.kc, "splits": self.splits,
-                "row_tiles": self.row_tiles, "tile": self.tile, "waves": self.waves}
+                "row_tiles": self.row_tiles, "tile": self.tile, "waves": self.waves,
+                "cols": self.cols, "seg": self.seg}
 
 
 _lib = None
@@ -164,7 +165,7 @@ def w4a16_unpack(qweight):
 def _make_plan(d):
     return w4a16_plan_t(kernel=d.get("kernel", 0), kc=d.get("kc", 0), splits=d.get("splits", 0),
                         row_tiles=d.get("row_tiles", 0), tile=d.get("tile", 0),
-                        waves=d.get("waves", 0))
+                        waves=d.get("waves", 0), cols=d.get("cols", 0), seg=d.get("seg", 0))
 
 
 def w4a16_plan(M, N, K, group_size=GROUP_SIZE, **plan):

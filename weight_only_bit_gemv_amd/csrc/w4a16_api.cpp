@@ -54,28 +54,91 @@ int check_gpu_shape(int64_t M, int64_t N, int64_t K, int64_t group_size) {
 
 // ---- dispatcher --------------------------------------------------------------------------
 
-// Skinny-kernel plan. The wavefronts of one work-group split its K range and are summed in
-// LDS; work-groups along K (splits) are summed through the workspace. Heuristic, from a
-// sweep of block size x K-steps per wavefront on MI355X: about kTargetWaves wavefronts in
-// the grid (enough loads in flight to cover memory latency on 256 CUs), at least two
-// 4-step segments per wavefront so that its software pipeline has something to overlap,
-// 8-wavefront work-groups for M <= 8 and 4 above (larger M holds more registers), and
-// never more than an equal share of K per wavefront.
-constexpr int64_t kTargetWaves = 2048;
+// Skinny-kernel plans. Autotuned per shape (the pages tune block sizes and split factors per
+// shape and cache the winner: "Things I got wrong along the way" on the Triton W4A16 page):
+// kTuned holds, for the projection shapes of the decode, MoE-expert and prefill workloads,
+// the plan with the lowest mean relative time over sweeps of cols x waves x kc x seg on
+// two MI355X machines (graph-timed launches after a clock warm-up, weights rotated over
+// 600 MB), per M bucket: an entry covers M up to m_max and above the
+// previous entry's m_max. Other shapes take the rule the table follows for most shapes:
+// 64-column strips for wide or deep matrices, 16 otherwise (32 past M = 32); 4 wavefronts;
+// each wavefront streams 32 K-steps (fewer when K is short, so that one work-group covers
+// K), and longer K is split over work-groups.
+struct TunedPlan {
+    int32_t K, N, m_max;
+    int8_t cols, waves, kc, seg;
+};
 
-int64_t valid_kc(int64_t kc) {
-    if (kc <= 1) return 1;
-    if (kc <= 3) return 2;
-    return kc / 4 * 4;
+const TunedPlan kTuned[] = {
+    //  K       N      m_max cols waves kc seg      mean time relative to the fastest plan
+    {  768,   2048,  1, 16,  4,  8, 4},   // 1.002 x the fastest
+    {  768,   2048,  4, 16,  4,  8, 4},   // 1.003 x the fastest
+    {  768,   2048, 16, 16,  4,  8, 4},   // 1.008 x the fastest
+    { 1408,   2048,  1, 16, 16,  4, 4},   // 1.000 x the fastest
+    { 1408,   2048,  4, 16,  8,  8, 4},   // 1.000 x the fastest
+    { 1408,   2048, 16, 16,  4, 16, 4},   // 1.038 x the fastest
+    { 2048,    768,  1, 16, 16,  8, 4},   // 1.007 x the fastest
+    { 2048,    768,  4, 16,  8,  8, 4},   // 1.000 x the fastest
+    { 2048,    768, 16, 16, 16,  8, 4},   // 1.042 x the fastest
+    { 2048,   1408,  1, 16, 16,  8, 4},   // 1.013 x the fastest
+    { 2048,   1408,  4, 16,  8,  8, 4},   // 1.000 x the fastest
+    { 2048,   1408, 16, 16, 16,  8, 4},   // 1.044 x the fastest
+    { 4096,   4096,  1, 16,  8, 16, 4},   // 1.014 x the fastest
+    { 4096,   4096,  2, 16,  8, 16, 4},   // 1.000 x the fastest
+    { 4096,   4096,  4, 16,  8, 16, 4},   // 1.000 x the fastest
+    { 4096,   4096,  8, 16,  8, 16, 4},   // 1.026 x the fastest
+    { 4096,   4096, 16, 16,  4, 32, 4},   // 1.039 x the fastest
+    { 4096,   4096, 32, 32,  8, 16, 4},   // 1.050 x the fastest
+    { 4096,   4096, 64, 32,  4, 32, 4},   // 1.005 x the fastest
+    { 4096,  14336,  1, 64,  4, 32, 4},   // 1.011 x the fastest
+    { 4096,  14336,  2, 64,  4, 32, 4},   // 1.000 x the fastest
+    { 4096,  14336,  4, 64,  4, 32, 4},   // 1.000 x the fastest
+    { 4096,  14336,  8, 64,  4, 32, 4},   // 1.000 x the fastest
+    { 4096,  14336, 16, 64,  4, 32, 4},   // 1.000 x the fastest
+    { 4096,  14336, 32, 64,  4, 32, 4},   // 1.000 x the fastest
+    { 4096,  14336, 64, 64,  4, 32, 4},   // 1.000 x the fastest
+    { 4096, 128256,  1, 64,  4, 32, 4},   // 1.000 x the fastest
+    { 8192,   8192,  1, 32,  8, 32, 4},   // 1.012 x the fastest
+    { 8192,   8192, 16, 64,  4, 32, 4},   // 1.000 x the fastest
+    { 8192,   8192, 32, 64,  8, 64, 4},   // 1.069 x the fastest
+    { 8192,   8192, 64, 64,  4, 64, 4},   // 1.065 x the fastest
+    { 8192,  28672,  1, 64,  4, 64, 4},   // 1.004 x the fastest
+    { 8192,  28672, 16, 64,  4, 16, 4},   // 1.001 x the fastest
+    { 8192,  28672, 32, 64,  4, 16, 4},   // 1.022 x the fastest
+    { 8192,  28672, 64, 64,  4, 64, 4},   // 1.000 x the fastest
+    {14336,   4096,  1, 64,  4, 32, 4},   // 1.000 x the fastest
+    {14336,   4096,  2, 64,  4, 32, 4},   // 1.000 x the fastest
+    {14336,   4096,  4, 64,  4, 32, 4},   // 1.031 x the fastest
+    {14336,   4096,  8, 64,  4, 32, 4},   // 1.000 x the fastest
+    {14336,   4096, 16, 64,  4, 32, 4},   // 1.033 x the fastest
+    {14336,   4096, 32, 64,  4, 32, 4},   // 1.000 x the fastest
+    {14336,   4096, 64, 64,  4, 32, 4},   // 1.000 x the fastest
+    {28672,   8192,  1, 64,  4, 64, 4},   // 1.025 x the fastest
+    {28672,   8192, 16, 64,  8, 64, 4},   // fastest in the one complete sweep
+    {28672,   8192, 32, 64,  4, 16, 4},   // 1.000 x the fastest
+    {28672,   8192, 64, 64,  4, 64, 4},   // 1.000 x the fastest
+};
+
+const TunedPlan* tuned_plan(int64_t M, int64_t N, int64_t K) {
+    for (const TunedPlan& t : kTuned)
+        if (t.K == K && t.N == N && M <= t.m_max) return &t;
+    return nullptr;
 }
 
-int64_t auto_kc(int64_t KS, int64_t n_strips, int64_t row_blocks, int64_t waves) {
-    const int64_t work = KS * n_strips * row_blocks;             // wavefront K-steps in total
-    int64_t kc = std::max<int64_t>(8, ceil_div(work, kTargetWaves));
-    kc = ceil_div(kc, 4) * 4;
-    // at most an equal share of K per wavefront of one work-group
-    const int64_t share = std::max<int64_t>(1, KS / waves);
-    return std::min(kc, valid_kc(share));
+int64_t roundup4(int64_t v) { return ceil_div(v, 4) * 4; }
+
+void default_skinny_plan(int64_t M, int64_t N, int64_t K, w4a16_plan_t* pl) {
+    const TunedPlan* t = tuned_plan(M, N, K);
+    const int64_t KS = K / w4a16::kKStep;
+    if (pl->cols == 0) pl->cols = t ? t->cols : (N >= 8192 || K >= 8192) ? 64 : (M > 32 ? 32 : 16);
+    if (pl->waves == 0) pl->waves = t ? t->waves : 4;
+    if (pl->kc == 0)
+        pl->kc = t ? t->kc : (int32_t)(KS <= 4 * 32 ? std::max<int64_t>(4, roundup4(ceil_div(KS, pl->waves))) : 32);
+    if (pl->seg == 0) {
+        int32_t seg = t ? t->seg : 4;
+        if (pl->kc % seg != 0 || (seg == 8 && KS % 8 != 0)) seg = pl->kc % 4 == 0 ? 4 : pl->kc;
+        pl->seg = seg;
+    }
 }
 
 // Rows of M from which the LDS-tiled prefill kernel replaces the weight-streaming kernel.
@@ -86,26 +149,32 @@ int complete_plan(int64_t M, int64_t N, int64_t K, w4a16_plan_t* pl) {
         pl->kernel = M >= kPrefillMinM ? W4A16_KERNEL_PREFILL : W4A16_KERNEL_SKINNY;
     if (pl->kernel == W4A16_KERNEL_PREFILL) {
         if (pl->tile != 0) return fail(W4A16_ERR_INVALID_ARG, "prefill tile %d is not built", pl->tile);
-        if (pl->kc || pl->row_tiles || pl->waves || pl->splits)
-            return fail(W4A16_ERR_INVALID_ARG, "kc/row_tiles/waves/splits apply to the skinny kernel only");
+        if (pl->kc || pl->row_tiles || pl->waves || pl->splits || pl->cols || pl->seg)
+            return fail(W4A16_ERR_INVALID_ARG, "kc/row_tiles/waves/splits/cols/seg apply to the skinny kernel only");
         if (ceil_div(M, w4a16::kPrefillBM) > 65535) return fail(W4A16_ERR_UNSUPPORTED, "grid too large");
         return W4A16_OK;
     }
     if (pl->kernel != W4A16_KERNEL_SKINNY)
         return fail(W4A16_ERR_INVALID_ARG, "unknown kernel id %d", pl->kernel);
-    if (pl->row_tiles == 0) pl->row_tiles = (int32_t)std::min<int64_t>(4, ceil_div(M, 16));
+    default_skinny_plan(M, N, K, pl);
+    if (pl->cols != 16 && pl->cols != 32 && pl->cols != 64)
+        return fail(W4A16_ERR_INVALID_ARG, "cols must be 16, 32 or 64 (got %d)", pl->cols);
+    const int lw = pl->cols / 16;
+    if (pl->row_tiles == 0) pl->row_tiles = (int32_t)std::min<int64_t>(lw == 4 ? 4 : 2, ceil_div(M, 16));
     if (pl->row_tiles < 1 || pl->row_tiles > 4)
         return fail(W4A16_ERR_INVALID_ARG, "row_tiles must be 1..4 (got %d)", pl->row_tiles);
-    if (pl->waves == 0) pl->waves = (pl->row_tiles == 1 && M <= 8) ? 8 : 4;
-    if (!w4a16::skinny_config_supported(pl->row_tiles, pl->waves))
-        return fail(W4A16_ERR_INVALID_ARG, "waves=%d with row_tiles=%d is not built", pl->waves,
-                    pl->row_tiles);
     const int64_t KS = K / w4a16::kKStep;
-    const int64_t n_strips = ceil_div(N, w4a16::kStripN);
+    const int64_t n_strips = ceil_div(N, pl->cols);
     const int64_t row_blocks = ceil_div(M, 16 * (int64_t)pl->row_tiles);
-    if (pl->kc == 0) pl->kc = (int32_t)auto_kc(KS, n_strips, row_blocks, pl->waves);
     if (pl->kc < 1 || pl->kc == 3 || (pl->kc > 4 && pl->kc % 4 != 0))
         return fail(W4A16_ERR_INVALID_ARG, "kc must be 1, 2 or a multiple of 4 (got %d)", pl->kc);
+    if (pl->seg == 8 && KS % 8 != 0)
+        return fail(W4A16_ERR_INVALID_ARG, "seg=8 needs K %% 256 == 0 (K=%lld)", (long long)K);
+    if (pl->kc % pl->seg != 0)
+        return fail(W4A16_ERR_INVALID_ARG, "kc=%d is not a multiple of seg=%d", pl->kc, pl->seg);
+    if (!w4a16::skinny_config_supported(pl->row_tiles, pl->waves, lw, pl->seg))
+        return fail(W4A16_ERR_INVALID_ARG, "waves=%d, row_tiles=%d, cols=%d, seg=%d is not built", pl->waves,
+                    pl->row_tiles, pl->cols, pl->seg);
     const int64_t chunks = ceil_div(KS, pl->kc);
     const int64_t splits = ceil_div(chunks, pl->waves);
     if (pl->splits != 0 && pl->splits != splits)
@@ -204,10 +273,12 @@ int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const
     p.K = (int)K;
     p.kc = pl.kc;
     p.splits = pl.splits;
-    p.n_strips = (int)ceil_div(N, w4a16::kStripN);
+    p.n_strips = (int)ceil_div(N, pl.cols);
     p.row_tiles = pl.row_tiles;
     p.row_blocks = (int)ceil_div(M, 16 * (int64_t)pl.row_tiles);
     p.waves = pl.waves;
+    p.lw = pl.cols / 16;
+    p.seg = pl.seg;
     uint64_t ws_bytes = 0, n_counters = 0;
     w4a16::skinny_workspace(p, &ws_bytes, &n_counters);
     if (ws_bytes) {

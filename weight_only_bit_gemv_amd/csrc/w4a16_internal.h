@@ -15,7 +15,6 @@ int pack_host(const float* W, int64_t K, int64_t N, int64_t g,
 void unpack_host(const int32_t* qweight, int64_t K, int64_t N, uint8_t* codes);
 
 // ---- decode / skinny kernel (w4a16_skinny.hip) ----
-constexpr int kStripN = 64;          // output columns per work-group (16 lanes x 4 columns)
 constexpr int kKStep = 32;           // K rows per MFMA step (4 packed rows)
 constexpr int kGroup = 128;          // K rows per scale/zero group
 
@@ -25,26 +24,32 @@ struct SkinnyParams {
     const uint16_t* scales;   // fp16 [K/g, N]
     const uint16_t* zeros;    // fp16 [K/g, N]
     uint16_t* y;              // fp16 [M, N]
-    float* ws;                // fp32 partials [row_blocks][n_strips][splits][16*row_tiles][64]
+    float* ws;                // fp32 partials [row_blocks][n_strips][splits][16*row_tiles][cols]
     uint32_t* counters;       // arrival counters [row_blocks][n_strips], zero between calls
     int M, N, K;
     int kc;                   // K-steps per wavefront
     int splits;               // work-groups along K per strip
-    int n_strips;             // ceil(N / 64)
+    int n_strips;             // ceil(N / cols)
     int row_tiles;            // 16-row tiles per work-group (1..4)
     int row_blocks;           // ceil(M / (16 * row_tiles))
     int waves;                // wavefronts per work-group (4, 8 or 16), each on its own K range
+    int lw;                   // packed words per lane per K-step (1, 2, 4): cols = 16 * lw
+    int seg;                  // K-steps per software-pipeline segment (1, 2, 4, 8)
 };
 
 // Workspace a skinny launch needs (bytes of partials, number of counters).
 inline void skinny_workspace(const SkinnyParams& p, uint64_t* ws_bytes, uint64_t* n_counters) {
     if (p.splits <= 1) { *ws_bytes = 0; *n_counters = 0; return; }
-    *ws_bytes = (uint64_t)p.row_blocks * p.n_strips * p.splits * 16ull * p.row_tiles * kStripN * 4ull;
+    *ws_bytes = (uint64_t)p.row_blocks * p.n_strips * p.splits * 16ull * p.row_tiles * 16ull * p.lw * 4ull;
     *n_counters = (uint64_t)p.row_blocks * p.n_strips;
 }
 
 int launch_skinny(const SkinnyParams& p, void* stream);   // returns a hipError_t value
-bool skinny_config_supported(int row_tiles, int waves);
+bool skinny_config_supported(int row_tiles, int waves, int lw, int seg);
+// per strip width (w4a16_skinny_lw{1,2,4}.hip); hipErrorInvalidValue for a config not built
+int launch_skinny_lw1(const SkinnyParams& p, void* stream);
+int launch_skinny_lw2(const SkinnyParams& p, void* stream);
+int launch_skinny_lw4(const SkinnyParams& p, void* stream);
 
 // ---- prefill kernel (w4a16_prefill.hip) ----
 constexpr int kPrefillBM = 128;      // rows of M per work-group
