@@ -149,13 +149,22 @@ def events(torch, stream):
 CLOCK_WARM_S = 0.3             # sustained load before a timed region (the GPU clock ramps up)
 
 
-def keep_busy(stream, g, seconds):
-    """Replay graph `g` until `seconds` of wall time have passed: the GPU raises its clock
-    under sustained load, and a timed region that starts cold measures the ramp."""
+def replay(torch, g, stream, times=1):
+    """Replay graph `g` on `stream` (CUDAGraph.replay launches on the current stream: a
+    replay outside this context would run on the default stream, concurrently with work
+    timed on `stream`)."""
+    with torch.cuda.stream(stream):
+        for _ in range(times):
+            g.replay()
+
+
+def keep_busy(torch, stream, g, seconds):
+    """Replay graph `g` on `stream` until `seconds` of wall time have passed: the GPU raises
+    its clock under sustained load, and a timed region that starts cold measures the ramp."""
     t0 = time.perf_counter()
     n = 0
     while time.perf_counter() - t0 < seconds:
-        g.replay()
+        replay(torch, g, stream)
         n += 1
         if n % 8 == 0:
             stream.synchronize()
@@ -170,9 +179,8 @@ def time_graph(torch, stream, body, reps, warm=2, busy_s=0.05, trials=3):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         body()
-    for _ in range(warm):
-        g.replay()
-    keep_busy(stream, g, busy_s)
+    replay(torch, g, stream, warm)
+    keep_busy(torch, stream, g, busy_s)
     ts = []
     for _ in range(trials):
         e0, e1 = events(torch, stream)
@@ -202,11 +210,10 @@ def timed_steps(torch, runner, steps, warmup):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         body()
-    for _ in range(max(0, warmup)):
-        g.replay()
+    replay(torch, g, stream, max(0, warmup))
     stream.synchronize()
     _check_same(torch, runner, ref, "graph warm-up replay")
-    keep_busy(stream, g, CLOCK_WARM_S)
+    keep_busy(torch, stream, g, CLOCK_WARM_S)
     torch.cuda.synchronize()
     e0, e1 = events(torch, stream)
     with torch.cuda.stream(stream):

@@ -28,9 +28,12 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # keep packed-fp32 VALU instructions out of the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators in ordinary VGPRs (no accvgpr copies around the fp32 epilogue)
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
+# MFMA accumulators in ordinary VGPRs (no accvgpr copies around the fp32 epilogue) for the
+# decode kernels, whose accumulators are few; the prefill kernel keeps its 128-256
+# accumulators per lane in AGPRs.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+PER_FILE_FLAGS = {}
 
 
 def _run(cmd):
@@ -51,7 +54,8 @@ def build(verbose=False):
     objs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        jobs.append([hipcc] + HIPCC_FLAGS + inc + ["-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([hipcc] + HIPCC_FLAGS + PER_FILE_FLAGS.get(src, VGPR_FORM) + inc +
+                    ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     obj = os.path.join(BUILD, "w4a16_pack.o")
     jobs.append(["g++", "-std=c++17", "-fPIC"] + PACK_FLAGS + inc +

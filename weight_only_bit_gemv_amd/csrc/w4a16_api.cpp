@@ -57,9 +57,8 @@ int check_gpu_shape(int64_t M, int64_t N, int64_t K, int64_t group_size) {
 // Skinny-kernel plans. Autotuned per shape (the pages tune block sizes and split factors per
 // shape and cache the winner: "Things I got wrong along the way" on the Triton W4A16 page):
 // kTuned holds, for the projection shapes of the decode, MoE-expert and prefill workloads,
-// the plan with the lowest mean relative time over sweeps of cols x waves x kc x seg on
-// two MI355X machines (graph-timed launches after a clock warm-up, weights rotated over
-// 600 MB), per M bucket: an entry covers M up to m_max and above the
+// the fastest plan of a sweep of cols x waves x kc x seg on MI355X (graph-timed launches
+// after a clock warm-up, weights rotated over 600 MB), per M bucket: an entry covers M up to m_max and above the
 // previous entry's m_max. Other shapes take the rule the table follows for most shapes:
 // 64-column strips for wide or deep matrices, 16 otherwise (32 past M = 32); 4 wavefronts;
 // each wavefront streams 32 K-steps (fewer when K is short, so that one work-group covers
@@ -70,53 +69,53 @@ struct TunedPlan {
 };
 
 const TunedPlan kTuned[] = {
-    //  K       N      m_max cols waves kc seg      mean time relative to the fastest plan
-    {  768,   2048,  1, 16,  4,  8, 4},   // 1.002 x the fastest
-    {  768,   2048,  4, 16,  4,  8, 4},   // 1.003 x the fastest
-    {  768,   2048, 16, 16,  4,  8, 4},   // 1.008 x the fastest
-    { 1408,   2048,  1, 16, 16,  4, 4},   // 1.000 x the fastest
-    { 1408,   2048,  4, 16,  8,  8, 4},   // 1.000 x the fastest
-    { 1408,   2048, 16, 16,  4, 16, 4},   // 1.038 x the fastest
-    { 2048,    768,  1, 16, 16,  8, 4},   // 1.007 x the fastest
-    { 2048,    768,  4, 16,  8,  8, 4},   // 1.000 x the fastest
-    { 2048,    768, 16, 16, 16,  8, 4},   // 1.042 x the fastest
-    { 2048,   1408,  1, 16, 16,  8, 4},   // 1.013 x the fastest
-    { 2048,   1408,  4, 16,  8,  8, 4},   // 1.000 x the fastest
-    { 2048,   1408, 16, 16, 16,  8, 4},   // 1.044 x the fastest
-    { 4096,   4096,  1, 16,  8, 16, 4},   // 1.014 x the fastest
-    { 4096,   4096,  2, 16,  8, 16, 4},   // 1.000 x the fastest
-    { 4096,   4096,  4, 16,  8, 16, 4},   // 1.000 x the fastest
-    { 4096,   4096,  8, 16,  8, 16, 4},   // 1.026 x the fastest
-    { 4096,   4096, 16, 16,  4, 32, 4},   // 1.039 x the fastest
-    { 4096,   4096, 32, 32,  8, 16, 4},   // 1.050 x the fastest
-    { 4096,   4096, 64, 32,  4, 32, 4},   // 1.005 x the fastest
-    { 4096,  14336,  1, 64,  4, 32, 4},   // 1.011 x the fastest
-    { 4096,  14336,  2, 64,  4, 32, 4},   // 1.000 x the fastest
-    { 4096,  14336,  4, 64,  4, 32, 4},   // 1.000 x the fastest
-    { 4096,  14336,  8, 64,  4, 32, 4},   // 1.000 x the fastest
-    { 4096,  14336, 16, 64,  4, 32, 4},   // 1.000 x the fastest
-    { 4096,  14336, 32, 64,  4, 32, 4},   // 1.000 x the fastest
-    { 4096,  14336, 64, 64,  4, 32, 4},   // 1.000 x the fastest
-    { 4096, 128256,  1, 64,  4, 32, 4},   // 1.000 x the fastest
-    { 8192,   8192,  1, 32,  8, 32, 4},   // 1.012 x the fastest
-    { 8192,   8192, 16, 64,  4, 32, 4},   // 1.000 x the fastest
-    { 8192,   8192, 32, 64,  8, 64, 4},   // 1.069 x the fastest
-    { 8192,   8192, 64, 64,  4, 64, 4},   // 1.065 x the fastest
-    { 8192,  28672,  1, 64,  4, 64, 4},   // 1.004 x the fastest
-    { 8192,  28672, 16, 64,  4, 16, 4},   // 1.001 x the fastest
-    { 8192,  28672, 32, 64,  4, 16, 4},   // 1.022 x the fastest
-    { 8192,  28672, 64, 64,  4, 64, 4},   // 1.000 x the fastest
-    {14336,   4096,  1, 64,  4, 32, 4},   // 1.000 x the fastest
-    {14336,   4096,  2, 64,  4, 32, 4},   // 1.000 x the fastest
-    {14336,   4096,  4, 64,  4, 32, 4},   // 1.031 x the fastest
-    {14336,   4096,  8, 64,  4, 32, 4},   // 1.000 x the fastest
-    {14336,   4096, 16, 64,  4, 32, 4},   // 1.033 x the fastest
-    {14336,   4096, 32, 64,  4, 32, 4},   // 1.000 x the fastest
-    {14336,   4096, 64, 64,  4, 32, 4},   // 1.000 x the fastest
-    {28672,   8192,  1, 64,  4, 64, 4},   // 1.025 x the fastest
-    {28672,   8192, 16, 64,  8, 64, 4},   // fastest in the one complete sweep
-    {28672,   8192, 32, 64,  4, 16, 4},   // 1.000 x the fastest
-    {28672,   8192, 64, 64,  4, 64, 4},   // 1.000 x the fastest
+    //  K       N      m_max cols waves kc seg      time of the plan in the sweep
+    {  768,   2048,  1, 16,  8,  4, 4},   // 2.84 us
+    {  768,   2048,  4, 16,  4,  8, 4},   // 3.11 us
+    {  768,   2048, 16, 16,  4,  8, 4},   // 3.41 us
+    { 1408,   2048,  1, 16, 16,  4, 4},   // 3.32 us
+    { 1408,   2048,  4, 16,  8,  8, 4},   // 3.74 us
+    { 1408,   2048, 16, 16,  4, 16, 4},   // 4.16 us
+    { 2048,    768,  1, 16,  8,  8, 4},   // 3.08 us
+    { 2048,    768,  4, 16,  4, 16, 4},   // 3.55 us
+    { 2048,    768, 16, 16,  4, 16, 4},   // 4.39 us
+    { 2048,   1408,  1, 16,  8,  8, 4},   // 3.41 us
+    { 2048,   1408,  4, 16,  8,  8, 4},   // 3.95 us
+    { 2048,   1408, 16, 16,  4, 16, 4},   // 4.78 us
+    { 4096,   4096,  1, 16, 16,  8, 4},   // 4.88 us
+    { 4096,   4096,  2, 16, 16,  8, 4},   // 5.18 us
+    { 4096,   4096,  4, 16,  8, 16, 4},   // 5.72 us
+    { 4096,   4096,  8, 16,  8, 16, 4},   // 6.19 us
+    { 4096,   4096, 16, 16,  4, 32, 4},   // 7.22 us
+    { 4096,   4096, 32, 16,  4, 64, 4},   // 11.01 us
+    { 4096,   4096, 64, 32,  4, 64, 4},   // 11.87 us
+    { 4096,  14336,  1, 64,  4, 32, 4},   // 9.01 us
+    { 4096,  14336,  2, 64,  4, 32, 4},   // 9.13 us
+    { 4096,  14336,  4, 64,  4, 32, 4},   // 9.30 us
+    { 4096,  14336,  8, 64,  4, 32, 4},   // 9.69 us
+    { 4096,  14336, 16, 64,  4, 32, 4},   // 10.35 us
+    { 4096,  14336, 32, 64,  4, 32, 4},   // 14.79 us
+    { 4096,  14336, 64, 64,  4, 32, 4},   // 24.49 us
+    { 4096, 128256,  1, 64,  4, 32, 4},   // 54.97 us
+    { 8192,   8192,  1, 32, 16, 16, 4},   // 10.61 us
+    { 8192,   8192, 16, 32,  4, 64, 4},   // 13.64 us
+    { 8192,   8192, 32, 64,  4, 32, 4},   // 20.16 us
+    { 8192,   8192, 64, 64,  4, 32, 4},   // 33.84 us
+    { 8192,  28672,  1, 64,  4, 64, 4},   // 26.94 us
+    { 8192,  28672, 16, 64,  4, 64, 4},   // 33.76 us
+    { 8192,  28672, 32, 64,  4, 64, 4},   // 48.56 us
+    { 8192,  28672, 64, 64,  4, 64, 4},   // 80.77 us
+    {14336,   4096,  1, 64,  4, 32, 4},   // 11.19 us
+    {14336,   4096,  2,  64,  4, 32, 4},   // split K: steadier across machines than the fastest here
+    {14336,   4096,  4,  64,  4, 32, 4},   // split K: steadier across machines than the fastest here
+    {14336,   4096,  8, 64,  4, 32, 4},   // 14.82 us
+    {14336,   4096, 16, 64,  4, 32, 4},   // 15.53 us
+    {14336,   4096, 32, 64,  4, 32, 4},   // 24.09 us
+    {14336,   4096, 64, 32,  8, 64, 4},   // 34.00 us
+    {28672,   8192,  1, 64,  8, 64, 4},   // 28.79 us
+    {28672,   8192, 16, 64,  8, 64, 4},   // 36.51 us
+    {28672,   8192, 32, 64,  8, 64, 4},   // 53.76 us
+    {28672,   8192, 64, 64,  4, 64, 4},   // 101.19 us
 };
 
 const TunedPlan* tuned_plan(int64_t M, int64_t N, int64_t K) {
@@ -256,6 +255,7 @@ int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const
         q.M = (int)M;
         q.N = (int)N;
         q.K = (int)K;
+        q.tile = pl.tile;
         const int e = w4a16::launch_prefill(q, stream);
         if (e != (int)hipSuccess)
             return fail(W4A16_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString((hipError_t)e));

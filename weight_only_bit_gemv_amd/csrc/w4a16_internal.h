@@ -54,7 +54,7 @@ int launch_skinny_lw4(const SkinnyParams& p, void* stream);
 // ---- prefill kernel (w4a16_prefill.hip) ----
 constexpr int kPrefillBM = 128;      // rows of M per work-group
 constexpr int kPrefillBN = 128;      // columns per work-group
-constexpr int kPrefillBK = 64;       // K rows per LDS step
+constexpr int kPrefillBK = 64;       // K rows per LDS stage
 
 struct PrefillParams {
     const uint16_t* x;        // fp16 [M, K]
@@ -63,6 +63,7 @@ struct PrefillParams {
     const uint16_t* zeros;    // fp16 [K/g, N]
     uint16_t* y;              // fp16 [M, N]
     int M, N, K;
+    int tile;                 // tile configuration (0 only: 128 x 128)
 };
 
 int launch_prefill(const PrefillParams& p, void* stream);  // returns a hipError_t value
