@@ -27,11 +27,14 @@ the dominant kernel's average launch to the 8 TB/s HBM peak (MFMA peak for prefi
 
 Profiling support:
   --pmc-pass               a fixed copy calibration + a few eager sweep steps, for
-                           rocprofv3 --pmc; prints no JSON
+                           rocprofv3 --pmc; prints no JSON (with --workload prefill:
+                           eager prefill-kernel launches at M=2048, K=8192, N=28672)
   --summarize-pmc DIR...   read rocprofv3 counter CSVs of --pmc-pass runs and write the
                            per-launch HBM traffic summary to profiles/
+  --summarize-prefill-pmc DIR...  the same for the prefill counter runs (MFMA busy, LDS)
 """
 import argparse
+import ctypes
 import glob
 import hashlib
 import json
@@ -53,14 +56,8 @@ SWEEP_KN = [(4096, 14336), (14336, 4096), (4096, 4096)]
 SWEEP_M = [1, 2, 4, 8, 16]
 ROTATE_BYTES = 1 << 30         # >= 4x the 256 MB Infinity Cache per shape family
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_skinny_decode_sweep.json")
-KERNEL_SOURCES = ["weight_only_bit_gemv_amd/csrc/w4a16_skinny.hip",
-                  "weight_only_bit_gemv_amd/csrc/w4a16_skinny.hpp",
-                  "weight_only_bit_gemv_amd/csrc/w4a16_skinny_lw1.hip",
-                  "weight_only_bit_gemv_amd/csrc/w4a16_skinny_lw2.hip",
-                  "weight_only_bit_gemv_amd/csrc/w4a16_skinny_lw4.hip",
-                  "weight_only_bit_gemv_amd/csrc/w4a16_device.hpp",
-                  "weight_only_bit_gemv_amd/csrc/w4a16_internal.h",
-                  "weight_only_bit_gemv_amd/csrc/w4a16_api.cpp"]
+KERNEL_SOURCES = sorted(os.path.relpath(f, ROOT) for f in
+                        glob.glob(os.path.join(ROOT, "weight_only_bit_gemv_amd", "csrc", "*")))
 COPY_CAL_BYTES = 256 << 20     # calibration copy for the PMC byte counters
 METRIC = "W4A16 weight-stream HBM GB/s (% of peak) and us/call at M=1..16"
 
@@ -125,15 +122,25 @@ class Runner:
         self.cursor = {key: 0 for key in families}
         self.step_bytes = sum(alg_bytes(M, K, N) for (M, K, N, key) in items)
         self.fn = lib.load().w4a16_matmul
+        self.fn_ex = lib.load().w4a16_matmul_ex
+        self.plans = {}
         self.sptr = stream.cuda_stream
 
-    def launch(self, i):
+    def launch(self, i, plan=None):
+        """Enqueue item i (the dispatcher's plan, or a forced plan: a dict of plan fields)."""
         M, K, N, key = self.items[i]
         c = self.cursor[key]
         self.cursor[key] = (c + 1) % len(self.weights[key])
         qw, s, z = self.weights[key][c]
-        rc = self.fn(self.xk[i].data_ptr(), qw.data_ptr(), s.data_ptr(), z.data_ptr(),
-                     self.y[i].data_ptr(), M, N, K, GROUP, self.sptr)
+        args = (self.xk[i].data_ptr(), qw.data_ptr(), s.data_ptr(), z.data_ptr(),
+                self.y[i].data_ptr(), M, N, K, GROUP, self.sptr)
+        if plan is None:
+            rc = self.fn(*args)
+        else:
+            key_p = tuple(sorted(plan.items()))
+            if key_p not in self.plans:
+                self.plans[key_p] = self.lib._binding._make_plan(plan)
+            rc = self.fn_ex(*args, ctypes.byref(self.plans[key_p]))
         if rc != 0:
             raise RuntimeError(f"w4a16_matmul failed ({rc}) for M={M} K={K} N={N}")
 
@@ -176,6 +183,9 @@ def time_graph(torch, stream, body, reps, warm=2, busy_s=0.05, trials=3):
     """Capture `body` once into a HIP graph on `stream`; after `warm` replays and `busy_s`
     seconds of sustained replays, time `trials` runs of `reps` replays between HIP events
     recorded on the same stream. Returns (median seconds per replay, graph)."""
+    with torch.cuda.stream(stream):      # eager call first: allocates any split-K workspace
+        body()
+    stream.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         body()
@@ -476,10 +486,16 @@ def run_prefill(args):
             y = torch.empty((M, N), dtype=torch.float16, device=dev)
             d = dense_time(torch, runner.xk[i], ws, y, stream, 2 * len(ws))
             fl = 2 * M * K * N
-            rows.append({"M": M, "K": K, "N": N, "w4a16_us": round(t * 1e6, 2),
-                         "w4a16_TFLOPs": round(fl / t / 1e12, 2), "w4a16_GBps": round(alg_bytes(M, K, N) / t / 1e9, 1),
-                         "dense_fp16_us": round(d * 1e6, 2), "dense_TFLOPs": round(fl / d / 1e12, 2),
-                         "speedup_vs_dense": round(d / t, 3), "plan": lib.w4a16_plan(M, N, K)})
+            row = {"M": M, "K": K, "N": N, "w4a16_us": round(t * 1e6, 2),
+                   "w4a16_TFLOPs": round(fl / t / 1e12, 2), "w4a16_GBps": round(alg_bytes(M, K, N) / t / 1e9, 1),
+                   "dense_fp16_us": round(d * 1e6, 2), "dense_TFLOPs": round(fl / d / 1e12, 2),
+                   "speedup_vs_dense": round(d / t, 3), "plan": lib.w4a16_plan(M, N, K)}
+            if 32 <= M <= 512:           # both kernels, where the dispatcher's threshold lies
+                for name, kern in (("skinny_us", lib.W4A16_KERNEL_SKINNY), ("prefill_us", lib.W4A16_KERNEL_PREFILL)):
+                    sec, _ = time_graph(torch, stream, lambda: [runner.launch(i, dict(kernel=kern)) for _ in range(reps)],
+                                        2, warm=1)
+                    row[name] = round(sec / reps * 1e6, 2)
+            rows.append(row)
             if cross is None and d < t:
                 cross = M
         rows.append({"K": K, "N": N, "crossover_M_dense_faster_from": cross})
@@ -499,6 +515,59 @@ def run_prefill(args):
                            "traffic": None, "kernel": "prefill_kernel", "shape": [best["M"], best["K"], best["N"]]},
               "rows": rows}
     print(json.dumps(result), flush=True)
+
+
+PREFILL_PMC_SHAPE = (2048, 8192, 28672)      # M, K, N of the prefill counter pass
+PREFILL_PMC_FILE = os.path.join(ROOT, "profiles", "prefill_counters_M2048_K8192_N28672.json")
+SIMDS = 1024                                  # 256 compute units x 4 SIMDs
+SCLK_GHZ = 2.4
+
+
+def run_prefill_pmc_pass(args):
+    """Eager launches of the prefill kernel on one large shape, for rocprofv3 --pmc."""
+    import torch
+    import weight_only_bit_gemv_amd as lib
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    M, K, N = PREFILL_PMC_SHAPE
+    wid = synth.WORKLOADS["prefill"]["wid"]
+    runner = Runner(torch, lib, dev, stream, {(K, N): (K, N, wid, 0)}, [(M, K, N, (K, N))], 0)
+    with torch.cuda.stream(stream):
+        for _ in range(args.steps):
+            runner.launch(0, dict(kernel=lib.W4A16_KERNEL_PREFILL))
+    stream.synchronize()
+    log(f"[pmc] {args.steps} prefill launches done")
+
+
+def summarize_prefill_pmc(dirs):
+    """MFMA and LDS counters of the prefill kernel (runs with --kernel-trace and --pmc)."""
+    import csv
+    vals, durs = {}, []
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for row in csv.DictReader(open(path)):
+                if "prefill_kernel" in row["Kernel_Name"]:
+                    vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+        for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+            for row in csv.DictReader(open(path)):
+                if "prefill_kernel" in row["Kernel_Name"]:
+                    durs.append(int(row["End_Timestamp"]) - int(row["Start_Timestamp"]))
+    mean = {k: float(np.mean(v)) for k, v in vals.items()}
+    M, K, N = PREFILL_PMC_SHAPE
+    dur_ns = float(np.median(durs)) if durs else None
+    out = {"kernel_source_sha": kernel_source_hash(), "shape_MKN": [M, K, N],
+           "counters_mean_per_dispatch": mean, "kernel_ns_median": dur_ns,
+           "TFLOPs": round(2 * M * K * N / dur_ns / 1e3, 1) if dur_ns else None}
+    if dur_ns and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+        # busy cycles summed over SIMDs (16 per 16x16x32 f16 MFMA) against every SIMD busy
+        # for the whole kernel at the nominal clock
+        out["mfma_busy_fraction"] = round(mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (dur_ns * SCLK_GHZ * SIMDS), 4)
+    if "SQ_LDS_BANK_CONFLICT" in mean and "SQ_LDS_IDX_ACTIVE" in mean:
+        out["lds_bank_conflict_over_active"] = round(mean["SQ_LDS_BANK_CONFLICT"] / mean["SQ_LDS_IDX_ACTIVE"], 4)
+    with open(PREFILL_PMC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
 
 
 def run_pmc_pass(args):
@@ -574,15 +643,21 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense fp16 baseline")
     ap.add_argument("--pmc-pass", action="store_true")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR")
+    ap.add_argument("--summarize-prefill-pmc", nargs="+", metavar="DIR")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc)
+        return 0
+    if args.summarize_prefill_pmc:
+        summarize_prefill_pmc(args.summarize_prefill_pmc)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the W4A16 path is built and timed on a single "
               "MI355X (no sharding or collectives); run it with --gpus 1.", file=sys.stderr)
         return 2
-    if args.pmc_pass:
+    if args.pmc_pass and args.workload == "prefill":
+        run_prefill_pmc_pass(args)
+    elif args.pmc_pass:
         run_pmc_pass(args)
     elif args.workload == "prefill":
         run_prefill(args)

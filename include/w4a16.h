@@ -125,8 +125,12 @@ int w4a16_unpack(const int32_t* qweight, int64_t K, int64_t N, uint8_t* codes);
  * Asynchronous: returns once the kernel is enqueued on `stream`. y is fully overwritten.
  * The result is deterministic: the same call gives the same bits (split-K partial sums are
  * combined in a fixed order; no floating-point atomics).
- * Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT (no HIP call made), HIP (launch failure or
- * workspace allocation failure).
+ * Graph capture: a plan with splits > 1 uses the library's split-K workspace for `stream`;
+ * if it is not yet large enough it is allocated (hipMalloc) on the call. Under stream
+ * capture that allocation is not possible, and the call returns HIP without enqueueing
+ * anything: make one call of the shape on the stream before capturing.
+ * Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT (no HIP call made), HIP (launch failure,
+ * workspace allocation failure, or a workspace that would have to grow during capture).
  */
 int w4a16_matmul(const void* x, const int32_t* qweight, const void* scales,
                  const void* zeros, void* y, int64_t M, int64_t N, int64_t K,

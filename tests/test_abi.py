@@ -119,7 +119,9 @@ PLAN_SHAPES = [(m, k, n) for m in (1, 2, 4, 8, 16, 17, 33, 64, 65, 128, 2048)
 def test_auto_plan_is_valid_and_covers_k(M, K, N):
     pl = lib.w4a16_plan(M, N, K)
     assert pl["kernel"] in (lib.W4A16_KERNEL_SKINNY, lib.W4A16_KERNEL_PREFILL)
-    assert pl["kernel"] == (lib.W4A16_KERNEL_PREFILL if M >= 65 else lib.W4A16_KERNEL_SKINNY)
+    tiles = -(-M // 128) * -(-N // 128)
+    expect_prefill = M >= 65 and (tiles >= 128 or M > 1024)
+    assert pl["kernel"] == (lib.W4A16_KERNEL_PREFILL if expect_prefill else lib.W4A16_KERNEL_SKINNY)
     if pl["kernel"] == lib.W4A16_KERNEL_SKINNY:
         kc, splits, W = pl["kc"], pl["splits"], pl["waves"]
         assert kc in (1, 2) or kc % 4 == 0
@@ -133,6 +135,7 @@ def test_auto_plan_is_valid_and_covers_k(M, K, N):
         assert pl["seg"] != 8 or KS % 8 == 0
         assert 1 <= pl["row_tiles"] <= (4 if pl["cols"] == 64 else 2)
         assert pl["row_tiles"] * 16 >= min(M, 64 if pl["cols"] == 64 else 32)
+        assert pl["row_tiles"] == min(4 if pl["cols"] == 64 else 2, -(-M // 16))
 
 
 @pytest.mark.parametrize("waves", [4, 8, 16])

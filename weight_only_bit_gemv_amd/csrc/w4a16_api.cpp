@@ -140,12 +140,22 @@ void default_skinny_plan(int64_t M, int64_t N, int64_t K, w4a16_plan_t* pl) {
     }
 }
 
-// Rows of M from which the LDS-tiled prefill kernel replaces the weight-streaming kernel.
+// Kernel choice (measured crossover on MI355X): the weight-streaming kernel up to M = 64;
+// above, the LDS-tiled prefill kernel once its 128 x 128 output tiles number at least
+// kPrefillMinTiles (half a tile per compute unit; with fewer it leaves the chip idle and
+// streaming the weights once per 64 rows is faster), and always beyond M = 1024.
 constexpr int64_t kPrefillMinM = 65;
+constexpr int64_t kPrefillMinTiles = 128;
+constexpr int64_t kSkinnyMaxM = 1024;
+
+int64_t auto_kernel(int64_t M, int64_t N) {
+    if (M < kPrefillMinM) return W4A16_KERNEL_SKINNY;
+    const int64_t tiles = ceil_div(M, w4a16::kPrefillBM) * ceil_div(N, w4a16::kPrefillBN);
+    return (tiles >= kPrefillMinTiles || M > kSkinnyMaxM) ? W4A16_KERNEL_PREFILL : W4A16_KERNEL_SKINNY;
+}
 
 int complete_plan(int64_t M, int64_t N, int64_t K, w4a16_plan_t* pl) {
-    if (pl->kernel == W4A16_KERNEL_AUTO)
-        pl->kernel = M >= kPrefillMinM ? W4A16_KERNEL_PREFILL : W4A16_KERNEL_SKINNY;
+    if (pl->kernel == W4A16_KERNEL_AUTO) pl->kernel = (int32_t)auto_kernel(M, N);
     if (pl->kernel == W4A16_KERNEL_PREFILL) {
         if (pl->tile != 0) return fail(W4A16_ERR_INVALID_ARG, "prefill tile %d is not built", pl->tile);
         if (pl->kc || pl->row_tiles || pl->waves || pl->splits || pl->cols || pl->seg)
@@ -205,6 +215,11 @@ int get_workspace(void* stream, uint64_t bytes, uint64_t n_counters, Workspace* 
     Workspace& w = g_ws[{dev, stream}];
     if (w.partial_bytes < bytes || w.n_counters < n_counters) {
         hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+            return fail(W4A16_ERR_HIP, "split-K workspace of %llu bytes is not allocated for this stream and "
+                        "cannot be allocated during graph capture: make one call of this shape on the "
+                        "stream before capturing", (unsigned long long)bytes);
         if (w.partials || w.counters) {
             // Earlier launches on this stream may still read the old buffers.
             e = hipStreamSynchronize(s);
