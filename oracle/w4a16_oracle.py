@@ -10,7 +10,12 @@ Sources (the pages this follows):
        group of 128 rows (GPTQ/AWQ style); eight 4-bit values packed into one int32 along
        the contraction dimension, packed row i / nibble j holding K index 8i+j; dequant
        inside the loop as (w - zero) * scale; products accumulated in fp32.
-  [P3] GemLite README, "Packing": the HQQ convention (W_q - zeros) * scales ~= W.
+  [P3] GemLite README, "Packing": the HQQ convention (W_q - zeros) * scales ~= W; its
+       settings list takes any group size divisible by 32.
+  [P2] "Triton Kernel Matches bitsandbytes: Why Both Lose to Math", section "Three Kernel
+       Versions and Two Bugs": symmetric 4-bit codes carry a +8 zero point.
+  [P1] section "Code": the tests cover several group sizes and both symmetric and
+       asymmetric quantisation.
 
 Readings taken where the pages are silent (each one is listed in the design doc):
   R1  W is laid out [K, N] (input x output), so y[M,N] = x[M,K] @ W[K,N].
@@ -23,6 +28,9 @@ Readings taken where the pages are silent (each one is listed in the design doc):
   R4  A group whose fp16 scale rounds to zero gets scale 1.0.
   R5  The zero point is not clamped; |zero| <= 1024 is the supported domain.
   R6  Non-finite W, an fp16 scale overflow or |zero| > 1024 are errors.
+  R7  Symmetric mode: scale = max|w|/7 per (K-group, column) stored as fp16 (rne; 1.0 when
+      it rounds to zero), zero = 8, q = clamp(round(w/scale) + 8, 0, 15); the same fp32
+      steps as R2. Group sizes are multiples of 8 here (the library takes 32, 64, 128, 256).
 Everything the GPU path must reproduce bit for bit (codes, fp16 dequant) is defined
 here; the matmul is defined in fp64 on the exact fp32 dequantised weights.
 
@@ -45,13 +53,20 @@ def _check_group(K, group_size):
         raise ValueError("K must be a multiple of group_size")
 
 
-def quantize(W, group_size=GROUP_SIZE):
-    """Asymmetric per-(group, column) 4-bit quantisation (R2, R4-R6).
+SYM_ZERO = 8.0            # R7: [P2] "Three Kernel Versions and Two Bugs", the +8 zero point
+SYM_QPOS = 7              # R7: largest positive code offset in symmetric mode
+
+
+def quantize(W, group_size=GROUP_SIZE, symmetric=False):
+    """Per-(group, column) 4-bit quantisation: asymmetric min/max (R2, R4-R6) or symmetric
+    with a zero point of 8 (R7).
 
     W: float32 [K, N]. Returns (codes uint8 [K, N], scales fp16 [K/g, N], zeros fp16 [K/g, N]).
-    [P1] "The design" fixes the grouping (one scale and zero per 128 K-rows per column);
+    [P1] "The design" fixes the grouping (one scale and zero per group of K-rows per column);
     [P3] "Packing" fixes that (codes - zeros) * scales approximates W.
     """
+    if symmetric:
+        return _quantize_symmetric(W, group_size)
     W = np.asarray(W)
     if W.dtype != np.float32 or W.ndim != 2:
         raise ValueError("W must be a 2-D float32 array")
@@ -81,6 +96,32 @@ def quantize(W, group_size=GROUP_SIZE):
     q = np.rint(Wg / s[:, None, :]) + z[:, None, :]       # round first, then add the offset
     q = np.clip(q, 0, QMAX)
     codes = q.astype(np.uint8).reshape(K, N)
+    return codes, s16, z16
+
+
+def _quantize_symmetric(W, group_size):
+    """R7: scale = fp16(max|w| / 7), zero = 8, q = clamp(rne(w / scale) + 8, 0, 15)."""
+    W = np.asarray(W)
+    if W.dtype != np.float32 or W.ndim != 2:
+        raise ValueError("W must be a 2-D float32 array")
+    K, N = W.shape
+    _check_group(K, group_size)
+    if not np.all(np.isfinite(W)):
+        raise ValueError("W holds a non-finite value")
+    G = K // group_size
+    Wg = W.reshape(G, group_size, N)
+    amax = np.abs(Wg).max(axis=1)                         # exact
+    s32 = amax / np.float32(SYM_QPOS)                     # fp32 division
+    with np.errstate(over="ignore"):
+        s16 = s32.astype(np.float16)                      # round to nearest even
+    if not np.all(np.isfinite(s16)):
+        raise ValueError("scale overflows fp16")
+    s16 = np.where(s16 == 0, np.float16(1.0), s16)        # R4
+    s = s16.astype(np.float32)
+    q = np.rint(Wg / s[:, None, :]) + np.float32(SYM_ZERO)
+    q = np.clip(q, 0, QMAX)
+    codes = q.astype(np.uint8).reshape(K, N)
+    z16 = np.full((G, N), SYM_ZERO, dtype=np.float16)
     return codes, s16, z16
 
 
@@ -147,7 +188,7 @@ def matmul(x, qweight, scales, zeros, group_size=GROUP_SIZE):
     return x.astype(np.float64) @ w
 
 
-def quantize_pack(W, group_size=GROUP_SIZE):
+def quantize_pack(W, group_size=GROUP_SIZE, symmetric=False):
     """quantize then pack: W fp32 [K, N] -> (qweight int32 [K/8, N], scales, zeros)."""
-    codes, s16, z16 = quantize(W, group_size)
+    codes, s16, z16 = quantize(W, group_size, symmetric)
     return pack(codes), s16, z16

@@ -17,8 +17,8 @@ import numpy as np
 import synth
 
 
-def _exact_group_weight(K, N, centres, log2_spacing):
-    """W[k, n] = ((k + n) mod 16 - c_g) * 2**e_g for K-group g = k // 128.
+def _exact_group_weight(K, N, centres, log2_spacing, group_size=128):
+    """W[k, n] = ((k + n) mod 16 - c_g) * 2**e_g for K-group g = k // group_size.
 
     Each aligned block of 16 rows in a column visits every residue 0..15 once, so every
     group's min is -c_g * d_g and its max (15 - c_g) * d_g: the scale is exactly d_g
@@ -26,7 +26,7 @@ def _exact_group_weight(K, N, centres, log2_spacing):
     """
     k = np.arange(K)[:, None]
     n = np.arange(N)[None, :]
-    g = k // 128
+    g = k // group_size
     c = np.asarray(centres, dtype=np.float64)[g]
     d = np.exp2(np.asarray(log2_spacing, dtype=np.float64))[g]
     return (((k + n) % 16 - c) * d).astype(np.float32)
@@ -207,6 +207,85 @@ def pin_scale_rounding(o):
     assert codes[15, 0] == 15 and codes[16:, 0].max() == 0
 
 
+def pin_group_sizes(o):
+    """Groups of 32, 64 and 256 rows: per-group exact scale 2**e_g and zero c_g, and the
+    hand-summed y(ones) = sum_g (gs/16) * (120 - 16 c_g) * 2**e_g.
+
+    Group sizes divisible by 32 are what the GemLite README's settings accept; the
+    grouping itself is [P1] "The design" with another group height.
+    """
+    cases = [(32, 128, [8, 3, 12, 5], [-6, -5, -4, -7], -4.125),
+             (64, 256, [8, 3, 12, 5], [-6, -5, -4, -7], -8.25),
+             (256, 512, [4, 10], [-5, -6], 16 * 56 / 32 - 16 * 40 / 64)]
+    for gs, K, centres, log2d, y_ones in cases:
+        N = 6
+        W = _exact_group_weight(K, N, centres, log2d, gs)
+        codes, s, z = o.quantize(W, gs)
+        G = K // gs
+        assert s.shape == (G, N) and z.shape == (G, N)
+        for g in range(G):
+            assert np.all(s[g] == np.float16(2.0 ** log2d[g])) and np.all(z[g] == centres[g]), (gs, g)
+        assert np.array_equal(o.dequant(codes, s, z, gs), W)
+        qw = o.pack(codes)
+        ones = np.ones((1, K), dtype=np.float16)
+        assert np.array_equal(o.matmul(ones, qw, s, z, gs), np.full((1, N), y_ones)), gs
+        for k0 in (1, gs + 2, K - 1):
+            e = np.zeros((1, K), dtype=np.float16)
+            e[0, k0] = 1
+            g = k0 // gs
+            expect = (((k0 + np.arange(N)) % 16) - centres[g]) * 2.0 ** log2d[g]
+            assert np.array_equal(o.matmul(e, qw, s, z, gs)[0], expect), (gs, k0)
+
+
+def pin_symmetric_exact(o):
+    """Symmetric mode on W = ((k + n) mod 15 - 7) * 2**e_g: max|w| = 7 * 2**e_g in every
+    group, so the scale is exactly 2**e_g, the zero 8 and the codes (k + n) mod 15 + 1;
+    quantisation is lossless and x . dequant equals x . W computed from W itself.
+
+    [P2] "Three Kernel Versions and Two Bugs": symmetric codes carry a +8 zero point.
+    """
+    for gs, K, log2d in [(32, 128, [-6, -5, -7, -4]), (128, 256, [-5, -6])]:
+        N = 5
+        k = np.arange(K)[:, None]
+        n = np.arange(N)[None, :]
+        d = np.exp2(np.asarray(log2d, dtype=np.float64))[k // gs]
+        W = ((((k + n) % 15) - 7) * d).astype(np.float32)
+        codes, s, z = o.quantize(W, gs, symmetric=True)
+        for g in range(K // gs):
+            assert np.all(s[g] == np.float16(2.0 ** log2d[g])) and np.all(z[g] == 8), (gs, g)
+        assert np.array_equal(codes, (((k + n) % 15) + 1).astype(np.uint8))
+        qw, s2, z2 = o.quantize_pack(W, gs, symmetric=True)
+        x = synth.activations(3, K, wid=5)
+        y = o.matmul(x, qw, s2, z2, gs)
+        ref = x.astype(np.float64) @ W.astype(np.float64)
+        assert np.allclose(y, ref, rtol=0, atol=1e-12 * np.abs(ref).max()), gs
+
+
+def pin_symmetric_bounds(o):
+    """Symmetric invariants on the N(0, 0.02) draw: the stored scale is the nearest fp16 to
+    max|w| / 7, every code lies in 1..15 (|w| <= 7 s rounds to at most 7 away from 8),
+    the largest-magnitude element maps to 1 or 15, and |W - deq| <= s/2."""
+    for gs in (32, 128):
+        W = synth.weight(256, 48, wid=0)
+        codes, s16, z16 = o.quantize(W, gs, symmetric=True)
+        K, N = W.shape
+        G = K // gs
+        s = s16.astype(np.float64)
+        assert np.all(z16 == 8)
+        Wg = W.astype(np.float64).reshape(G, gs, N)
+        amax = np.abs(Wg).max(axis=1)
+        target = amax / 7.0
+        assert np.all(np.abs(s - target) <= target * 2.0 ** -11 * (1 + 2.0 ** -10))
+        cg = codes.reshape(G, gs, N)
+        assert cg.min() >= 1 and cg.max() <= 15
+        am = np.abs(Wg).argmax(axis=1)
+        top = np.take_along_axis(cg, am[:, None, :], axis=1)
+        assert np.all((top == 1) | (top == 15))
+        deq = o.dequant(codes, s16, z16, gs).astype(np.float64).reshape(G, gs, N)
+        slack = np.abs(Wg) * 2.0 ** -22
+        assert np.all(np.abs(Wg - deq) <= 0.5 * s[:, None, :] * (1 + 2.0 ** -10) + slack)
+
+
 ALL_PINS = [pin_hand_words, pin_roundtrip, pin_exact_group, pin_exact_products,
             pin_multigroup, pin_bounds_random, pin_fsum, pin_dequant_fp16_rounding,
-            pin_scale_rounding]
+            pin_scale_rounding, pin_group_sizes, pin_symmetric_exact, pin_symmetric_bounds]

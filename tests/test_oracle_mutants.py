@@ -60,6 +60,28 @@ MUTANTS = [
      "return dequant(codes, scales, zeros, group_size).astype(np.float16)",
      "d = dequant(codes, scales, zeros, group_size).astype(np.float64); "
      "return (np.sign(d) * np.floor(np.abs(d) * 2.0 ** 9 + 0.5) / 2.0 ** 9).astype(np.float16)"),
+    # group sizes other than 128
+    ("dequant broadcasts every group over 128 rows whatever the group size",
+     [("s = np.repeat(np.asarray(scales).astype(np.float32), group_size, axis=0)",
+       "s = np.repeat(np.asarray(scales).astype(np.float32), GROUP_SIZE, axis=0)[:K]"),
+      ("z = np.repeat(np.asarray(zeros).astype(np.float32), group_size, axis=0)",
+       "z = np.repeat(np.asarray(zeros).astype(np.float32), GROUP_SIZE, axis=0)[:K]")], None),
+    ("quantiser groups 128 rows whatever the group size",
+     "    G = K // group_size\n    Wg = W.reshape(G, group_size, N)                      # Wg",
+     "    G = K // GROUP_SIZE\n    Wg = W.reshape(G, GROUP_SIZE, N)                      # Wg"),
+    # symmetric mode
+    ("symmetric scale over 8 levels",
+     "s32 = amax / np.float32(SYM_QPOS)", "s32 = amax / np.float32(8)"),
+    ("symmetric zero point 7",
+     "q = np.rint(Wg / s[:, None, :]) + np.float32(SYM_ZERO)",
+     "q = np.rint(Wg / s[:, None, :]) + np.float32(7)"),
+    ("symmetric scale from the maximum instead of the largest magnitude",
+     "amax = np.abs(Wg).max(axis=1)", "amax = Wg.max(axis=1)"),
+    ("symmetric codes from floor",
+     "q = np.rint(Wg / s[:, None, :]) + np.float32(SYM_ZERO)",
+     "q = np.floor(Wg / s[:, None, :]) + np.float32(SYM_ZERO)"),
+    ("symmetric mode falls back to the asymmetric quantiser",
+     "        return _quantize_symmetric(W, group_size)", "        pass"),
     # matmul
     ("matmul accumulates in fp32",
      "w = dequant(codes, scales, zeros, group_size).astype(np.float64)\n    return x.astype(np.float64) @ w",
@@ -100,6 +122,6 @@ def test_mutant_is_caught(name, old, new):
     for pin in oracle_pins.ALL_PINS:
         try:
             pin(mod)
-        except AssertionError:
+        except Exception:            # a wrong value or a crash both expose the mutant
             caught.append(pin.__name__)
     assert caught, f"no pin caught the mutant: {name}"
