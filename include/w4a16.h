@@ -8,7 +8,8 @@
  * scale and one zero-point per group of 128 rows of the contraction dimension, eight
  * 4-bit values packed into one int32 along that dimension (packed row i, nibble j holds
  * K index 8*i + j), dequantised inside the product, fp32 accumulation.  The GemLite README
- * ("Packing") states the same (W_q - zeros) * scales convention.
+ * ("Packing") states the same (W_q - zeros) * scales convention, and its settings take
+ * other group sizes: the library accepts groups of 32, 64, 128 and 256 rows.
  *
  * Layouts (all row-major, contiguous, no padding):
  *   W        fp32  [K, N]        host; input x output (y = x . W)
@@ -94,7 +95,7 @@ typedef struct w4a16_plan {
  *
  *   W          host fp32 [K, N]
  *   K, N       K >= group_size, K % group_size == 0; N >= 1
- *   group_size must be 128
+ *   group_size 32, 64, 128 or 256
  *   qweight    host int32 [K/8, N]     (written)
  *   scales     host fp16 bits [K/g, N] (written)
  *   zeros      host fp16 bits [K/g, N] (written)
@@ -102,9 +103,28 @@ typedef struct w4a16_plan {
  * NONFINITE (NaN/Inf in W, scale overflow). Argument errors and NaN/Inf in W are found
  * before anything is written; after a scale overflow or an out-of-domain zero point
  * (found while packing) the contents of qweight / scales / zeros are unspecified.
+ * Same as w4a16_pack_ex(W, K, N, group_size, 0, qweight, scales, zeros).
  */
 int w4a16_pack(const float* W, int64_t K, int64_t N, int64_t group_size,
                int32_t* qweight, uint16_t* scales, uint16_t* zeros);
+
+/*
+ * w4a16_pack_ex - w4a16_pack with a choice of quantiser.
+ *   symmetric  0: the asymmetric min/max quantiser of w4a16_pack;
+ *              1: the symmetric one with the +8 zero point of "Triton Kernel Matches
+ *                 bitsandbytes: Why Both Lose to Math", section "Three Kernel Versions and
+ *                 Two Bugs", per (group, column):
+ *                   scale = fp16_rne(max|w| / 7)           (1.0 if that rounds to 0)
+ *                   zero  = 8
+ *                   q     = clamp(rne(w / scale) + 8, 0, 15)
+ *                 with the same fp32 steps. The output layout is unchanged (zeros holds 8),
+ *                 so w4a16_matmul runs both kinds of weights.
+ *   group_size 32, 64, 128 or 256.
+ * Other arguments, errors and ownership as w4a16_pack; INVALID_ARG when symmetric is not
+ * 0 or 1.
+ */
+int w4a16_pack_ex(const float* W, int64_t K, int64_t N, int64_t group_size, int symmetric,
+                  int32_t* qweight, uint16_t* scales, uint16_t* zeros);
 
 /*
  * w4a16_unpack - host inverse of the packing: codes[8i + j, n] = (qweight[i, n] >> 4j) & 15.
@@ -119,8 +139,8 @@ int w4a16_unpack(const int32_t* qweight, int64_t K, int64_t N, uint8_t* codes);
  * accumulation; y rounded to fp16 once at the end).
  *
  *   x, qweight, scales, zeros, y   device pointers (layouts above), 16-byte aligned
- *   M >= 1, N >= 4 with N % 4 == 0, K >= 128 with K % group_size == 0
- *   group_size must be 128
+ *   M >= 1, N >= 4 with N % 4 == 0, K >= 128 with K % 128 == 0 and K % group_size == 0
+ *   group_size 32, 64, 128 or 256
  *   stream     hipStream_t as void* (NULL = the null stream)
  * Asynchronous: returns once the kernel is enqueued on `stream`. y is fully overwritten.
  * The result is deterministic: the same call gives the same bits (split-K partial sums are
@@ -157,8 +177,8 @@ int w4a16_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, w4a16_plan_t
  *   codes  device uint8 [K, N] or NULL: codes[8i + j, n] = nibble j of qweight[i, n]
  *   w      device fp16 [K, N] or NULL: fp16_rne((q - zero) * scale), i.e. one rounding of
  *          the exact product (the fp16 weight the prefill kernel stages in LDS)
- *   qweight, scales, zeros as for w4a16_matmul; N % 4 == 0, K % group_size == 0,
- *   group_size == 128; at least one of codes / w non-NULL.
+ *   qweight, scales, zeros as for w4a16_matmul; N % 4 == 0, K % 128 == 0,
+ *   K % group_size == 0, group_size 32, 64, 128 or 256; at least one of codes / w non-NULL.
  * Asynchronous on `stream`. Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT, HIP.
  */
 int w4a16_dequant(const int32_t* qweight, const void* scales, const void* zeros,

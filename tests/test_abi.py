@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ["w4a16_pack", "w4a16_matmul", "w4a16_matmul_ex", "w4a16_plan",
+    for required in ["w4a16_pack", "w4a16_pack_ex", "w4a16_matmul", "w4a16_matmul_ex", "w4a16_plan",
                      "w4a16_dequant", "w4a16_unpack", "w4a16_strerror"]:
         assert required in names
 
@@ -65,7 +65,10 @@ def _mm(M, N, K, g=128, ptrs=None):
     (1, 0, 128, 128, lib.W4A16_ERR_INVALID_ARG),
     (1, 64, 0, 128, lib.W4A16_ERR_INVALID_ARG),
     (-3, 64, 128, 128, lib.W4A16_ERR_INVALID_ARG),
-    (1, 64, 128, 64, lib.W4A16_ERR_UNSUPPORTED),
+    (1, 64, 128, 96, lib.W4A16_ERR_UNSUPPORTED),
+    (1, 64, 128, 16, lib.W4A16_ERR_UNSUPPORTED),
+    (1, 64, 128, 256, lib.W4A16_ERR_UNSUPPORTED),
+    (1, 64, 192, 64, lib.W4A16_ERR_UNSUPPORTED),
     (1, 64, 200, 128, lib.W4A16_ERR_UNSUPPORTED),
     (1, 66, 128, 128, lib.W4A16_ERR_UNSUPPORTED),
     (1, 1 << 20, 1 << 16, 128, lib.W4A16_ERR_UNSUPPORTED),
@@ -136,6 +139,29 @@ def test_auto_plan_is_valid_and_covers_k(M, K, N):
         assert 1 <= pl["row_tiles"] <= (4 if pl["cols"] == 64 else 2)
         assert pl["row_tiles"] * 16 >= min(M, 64 if pl["cols"] == 64 else 32)
         assert pl["row_tiles"] == min(4 if pl["cols"] == 64 else 2, -(-M // 16))
+
+
+@pytest.mark.parametrize("g", [32, 64, 128, 256])
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (1, 4096, 14336), (1, 14336, 4096),
+                                   (16, 8192, 8192), (1, 2048, 1408), (4, 4096, 128256)])
+def test_auto_plan_per_group_size_is_built(M, K, N, g):
+    """Every group size gets a plan the library has compiled: 8-step segments only with
+    128-row groups (they span two groups of four K-steps)."""
+    pl = lib.w4a16_plan(M, N, K, group_size=g)
+    assert pl["kernel"] == lib.W4A16_KERNEL_SKINNY
+    assert pl["kc"] % pl["seg"] == 0
+    assert pl["seg"] != 8 or g == 128
+
+
+@pytest.mark.parametrize("g,ok", [(32, False), (64, False), (128, True), (256, False)])
+def test_forced_seg8_needs_128_row_groups(g, ok):
+    kw = dict(kernel=lib.W4A16_KERNEL_SKINNY, kc=8, seg=8, waves=4)
+    if ok:
+        assert lib.w4a16_plan(1, 4096, 4096, group_size=g, **kw)["seg"] == 8
+    else:
+        with pytest.raises(lib.W4A16Error) as e:
+            lib.w4a16_plan(1, 4096, 4096, group_size=g, **kw)
+        assert e.value.code == lib.W4A16_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("waves", [4, 8, 16])

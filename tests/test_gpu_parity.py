@@ -57,12 +57,12 @@ def check_y(y_gpu, y_ref, what=""):
     return float(err.max())
 
 
-def run(lib, x, qw, s, z, plan=None, y=None, stream=None):
+def run(lib, x, qw, s, z, plan=None, y=None, stream=None, group_size=128):
     out = lib.w4a16_matmul(dev(x) if isinstance(x, np.ndarray) else x,
                            dev(qw) if isinstance(qw, np.ndarray) else qw,
                            dev(s) if isinstance(s, np.ndarray) else s,
                            dev(z) if isinstance(z, np.ndarray) else z,
-                           y=y, plan=plan, stream=stream)
+                           y=y, plan=plan, stream=stream, group_size=group_size)
     torch.cuda.synchronize()
     return out
 
@@ -264,6 +264,93 @@ def test_matmul_prefill_kernel_forced(lib, M, K, N):
     x = synth.activations(M, K, wid=9)
     check_y(run(lib, x, qw, s, z, plan=dict(kernel=lib.W4A16_KERNEL_PREFILL)),
             oracle.matmul(x, qw, s, z), f"prefill forced M={M} K={K} N={N}")
+
+
+# ---------------------------------------------------------------------------------------
+# group sizes 32 / 64 / 256 and the symmetric (+8 zero point) quantiser
+
+FORMATS = [(32, False), (64, False), (256, False), (32, True), (128, True)]
+FMT_IDS = [f"g{g}{'-sym' if sym else ''}" for g, sym in FORMATS]
+
+
+@pytest.mark.parametrize("g,sym", FORMATS, ids=FMT_IDS)
+def test_dequant_bit_exact_formats(lib, g, sym):
+    W = synth.weight_custom(768, 200, seed=g, std=0.02)
+    qw, s, z = oracle.quantize_pack(W, g, sym)
+    print(f"\n[dequant] g={g} sym={sym}", flush=True)
+    c, w = lib.w4a16_dequant(dev(qw), dev(s), dev(z), group_size=g)
+    torch.cuda.synchronize()
+    codes_ref = oracle.unpack(qw)
+    assert np.array_equal(c.cpu().numpy(), codes_ref)
+    w_ref = oracle.dequant_fp16(codes_ref, s, z, g)
+    assert np.array_equal(w.cpu().numpy().view(np.uint16), w_ref.view(np.uint16))
+
+
+FMT_SHAPES = [(1, 4096, 4096), (5, 4096, 14336), (16, 14336, 4096), (1, 2048, 1408), (3, 1536, 2048)]
+
+
+@pytest.mark.parametrize("g,sym", FORMATS, ids=FMT_IDS)
+@pytest.mark.parametrize("M,K,N", FMT_SHAPES, ids=[f"M{m}-K{k}-N{n}" for m, k, n in FMT_SHAPES])
+def test_matmul_formats_decode(lib, M, K, N, g, sym):
+    print(f"\n[format] g={g} sym={sym} M={M} K={K} N={N} "
+          f"plan={lib.w4a16_plan(M, N, K, group_size=g)}", flush=True)
+    qw, s, z = oracle.quantize_pack(synth.weight(K, N, wid=0), g, sym)
+    x = synth.activations(M, K, wid=0)
+    check_y(run(lib, x, qw, s, z, group_size=g), oracle.matmul(x, qw, s, z, g),
+            f"g={g} sym={sym} M={M} K={K} N={N}")
+
+
+def _fmt_plans():
+    out = []
+    M, K, N = PLAN_MKN
+    import weight_only_bit_gemv_amd as L
+    for g in (32, 64, 256):
+        for c in (16, 32, 64):
+            for sg in (1, 2, 4):
+                for kc in _SEG_KC[sg][:2]:
+                    for rt in (1, 3 if c == 64 else 2):
+                        for w in (4, 8):
+                            p = dict(kernel=1, kc=kc, row_tiles=rt, waves=w, cols=c, seg=sg)
+                            try:
+                                L.w4a16_plan(M, N, K, group_size=g, **p)
+                            except L.W4A16Error:
+                                continue
+                            out.append((g, p))
+    return out
+
+
+FMT_PLANS = _fmt_plans()
+_FMT_CASE = {}
+
+
+@pytest.mark.parametrize("g,plan", FMT_PLANS,
+                         ids=[f"g{g}-c{p['cols']}-seg{p['seg']}-kc{p['kc']}-rt{p['row_tiles']}-w{p['waves']}"
+                              for g, p in FMT_PLANS])
+def test_matmul_every_segment_per_group_size(lib, g, plan):
+    """Segments of 1, 2 and 4 K-steps over groups of 1, 2, 4 and 8 K-steps (each segment
+    inside one group, or holding 2 or 4 whole groups)."""
+    M, K, N = PLAN_MKN
+    if g not in _FMT_CASE:
+        W = synth.weight_custom(K, N, seed=12, std=0.02)
+        qw, s, z = oracle.quantize_pack(W, g)
+        x = synth.activations(M, K, wid=8)
+        _FMT_CASE[g] = ([dev(x), dev(qw), dev(s), dev(z)], oracle.matmul(x, qw, s, z, g))
+    args, ref = _FMT_CASE[g]
+    print(f"\n[format plan] g={g} {plan}", flush=True)
+    check_y(run(lib, *args, plan=plan, group_size=g), ref, f"g={g} plan {plan}")
+
+
+FMT_PREFILL = [(3, 256, 100), (130, 512, 1412), (257, 1536, 260), (128, 4096, 256)]
+
+
+@pytest.mark.parametrize("g,sym", FORMATS, ids=FMT_IDS)
+@pytest.mark.parametrize("M,K,N", FMT_PREFILL, ids=[f"M{m}-K{k}-N{n}" for m, k, n in FMT_PREFILL])
+def test_matmul_formats_prefill_forced(lib, M, K, N, g, sym):
+    print(f"\n[format prefill] g={g} sym={sym} M={M} K={K} N={N}", flush=True)
+    qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=200 + M, std=0.02), g, sym)
+    x = synth.activations(M, K, wid=9)
+    check_y(run(lib, x, qw, s, z, plan=dict(kernel=lib.W4A16_KERNEL_PREFILL), group_size=g),
+            oracle.matmul(x, qw, s, z, g), f"prefill g={g} sym={sym} M={M} K={K} N={N}")
 
 
 @pytest.mark.parametrize("M,K,N", [(32, 8192, 8192), (128, 8192, 8192)])

@@ -14,9 +14,9 @@ def _same(a, b):
     return a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
-def _check(W):
-    qw, s, z = lib.w4a16_pack(W)
-    qo, so, zo = oracle.quantize_pack(W)
+def _check(W, group_size=128, symmetric=False):
+    qw, s, z = lib.w4a16_pack(W, group_size=group_size, symmetric=symmetric)
+    qo, so, zo = oracle.quantize_pack(W, group_size, symmetric)
     assert _same(qw, qo), "qweight differs"
     assert _same(s, so), "scales differ"
     assert _same(z, zo), "zeros differ"
@@ -38,6 +38,44 @@ def test_pack_matches_oracle_on_workload_draws(K, N):
                                       (1e-3, 0.0), (3e-7, 0.0)])
 def test_pack_matches_oracle_on_other_spreads(seed, std, mean):
     _check(synth.weight_custom(256, 40, seed=seed, std=std, mean=mean))
+
+
+@pytest.mark.parametrize("symmetric", [False, True])
+@pytest.mark.parametrize("g", [32, 64, 128, 256])
+@pytest.mark.parametrize("K,N", [(4096, 96), (768, 200), (256, 7)])
+def test_pack_group_sizes_and_modes_match_oracle(K, N, g, symmetric):
+    qw, s, z = _check(synth.weight(K, N, wid=2), g, symmetric)
+    assert s.shape == (K // g, N) and z.shape == (K // g, N)
+    if symmetric:
+        assert np.all(z == 8)
+
+
+@pytest.mark.parametrize("g", [32, 64, 128, 256])
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("std,mean", [(1.0, 0.0), (0.02, 1.0), (3e-7, 0.0)])
+def test_pack_symmetric_other_spreads(g, seed, std, mean):
+    _check(synth.weight_custom(512, 24, seed=seed, std=std, mean=mean), g, True)
+
+
+def test_pack_symmetric_ties_and_extremes():
+    """Symmetric mode: w/s = n + 0.5 ties go to even, +-max|w| map to codes 15 and 1."""
+    s = 2.0 ** -5
+    W = np.zeros((32, 4), dtype=np.float32)
+    W[0, :] = 7 * s                                   # max|w| = 7 s -> scale s
+    W[1, :] = -7 * s
+    W[2:6, :] = np.array([0.5, 1.5, -0.5, -2.5], dtype=np.float32)[:, None] * s
+    qw, sc, z = _check(W, 32, True)
+    codes = lib.w4a16_unpack(qw)
+    assert np.array_equal(codes[:6, 0], [15, 1, 8, 10, 8, 6])
+    assert np.all(sc == np.float16(s)) and np.all(z == 8)
+
+
+def test_pack_symmetric_zero_group_scale_one():
+    W = np.zeros((64, 3), dtype=np.float32)
+    W[:, 1] = -0.75
+    qw, s, z = _check(W, 64, True)
+    assert s[0, 0] == 1.0 and np.all(lib.w4a16_unpack(qw)[:, 0] == 8)
+    assert np.all(lib.w4a16_unpack(qw)[:, 1] == 1)      # -0.75 / (0.75 / 7) = -7
 
 
 def test_pack_exact_ties_round_half_even():
@@ -122,7 +160,10 @@ def test_pack_rejects_zero_out_of_domain():
 
 
 @pytest.mark.parametrize("K,N,g,code", [(100, 8, 128, lib.W4A16_ERR_UNSUPPORTED),
-                                        (256, 8, 64, lib.W4A16_ERR_UNSUPPORTED),
+                                        (256, 8, 96, lib.W4A16_ERR_UNSUPPORTED),
+                                        (256, 8, 16, lib.W4A16_ERR_UNSUPPORTED),
+                                        (256, 8, 512, lib.W4A16_ERR_UNSUPPORTED),
+                                        (96, 8, 64, lib.W4A16_ERR_UNSUPPORTED),
                                         (0, 8, 128, lib.W4A16_ERR_INVALID_ARG),
                                         (128, 0, 128, lib.W4A16_ERR_INVALID_ARG)])
 def test_pack_rejects_bad_shapes(K, N, g, code):
@@ -130,3 +171,10 @@ def test_pack_rejects_bad_shapes(K, N, g, code):
     with pytest.raises(lib.W4A16Error) as e:
         lib.w4a16_pack(W, group_size=g)
     assert e.value.code == code
+
+
+def test_pack_ex_rejects_bad_symmetric_flag():
+    W = np.zeros((128, 4), dtype=np.float32)
+    out = [np.empty((16, 4), np.int32), np.empty((1, 4), np.float16), np.empty((1, 4), np.float16)]
+    rc = lib.load().w4a16_pack_ex(W.ctypes.data, 128, 4, 128, 2, *(a.ctypes.data for a in out))
+    assert rc == lib.W4A16_ERR_INVALID_ARG

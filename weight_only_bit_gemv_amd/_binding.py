@@ -48,6 +48,7 @@ _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _SIGS = {
     "w4a16_pack": ([_P, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "w4a16_pack_ex": ([_P, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P], ctypes.c_int),
     "w4a16_unpack": ([_P, _I64, _I64, _P], ctypes.c_int),
     "w4a16_matmul": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
     "w4a16_matmul_ex": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P,
@@ -137,8 +138,9 @@ def _dev_ptr(t, name, dtype):
 
 # ---- host entry points ------------------------------------------------------------------
 
-def w4a16_pack(W, group_size=GROUP_SIZE):
-    """W fp32 [K, N] (NumPy) -> (qweight int32 [K/8, N], scales fp16, zeros fp16)."""
+def w4a16_pack(W, group_size=GROUP_SIZE, symmetric=False):
+    """W fp32 [K, N] (NumPy) -> (qweight int32 [K/8, N], scales fp16, zeros fp16).
+    symmetric=True selects the +8 zero-point quantiser (w4a16_pack_ex)."""
     W = np.ascontiguousarray(W, dtype=np.float32)
     if W.ndim != 2:
         raise ValueError("W must be 2-D")
@@ -147,9 +149,9 @@ def w4a16_pack(W, group_size=GROUP_SIZE):
     qweight = np.empty((K // 8, N), dtype=np.int32)
     scales = np.empty((max(G, 0), N), dtype=np.float16)
     zeros = np.empty((max(G, 0), N), dtype=np.float16)
-    rc = load().w4a16_pack(W.ctypes.data, K, N, group_size, qweight.ctypes.data,
-                           scales.ctypes.data, zeros.ctypes.data)
-    _check(rc, "w4a16_pack")
+    rc = load().w4a16_pack_ex(W.ctypes.data, K, N, group_size, 1 if symmetric else 0,
+                              qweight.ctypes.data, scales.ctypes.data, zeros.ctypes.data)
+    _check(rc, "w4a16_pack_ex")
     return qweight, scales, zeros
 
 

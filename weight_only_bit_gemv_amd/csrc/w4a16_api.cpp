@@ -41,10 +41,11 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int check_gpu_shape(int64_t M, int64_t N, int64_t K, int64_t group_size) {
     if (M < 1 || N < 1 || K < 1) return fail(W4A16_ERR_INVALID_ARG, "M, N, K must be >= 1 (got %lld, %lld, %lld)",
                                             (long long)M, (long long)N, (long long)K);
-    if (group_size != w4a16::kGroup)
-        return fail(W4A16_ERR_UNSUPPORTED, "group_size %lld not supported (128 only)", (long long)group_size);
-    if (K % group_size != 0)
-        return fail(W4A16_ERR_UNSUPPORTED, "K=%lld is not a multiple of group_size", (long long)K);
+    if (!w4a16::group_supported(group_size))
+        return fail(W4A16_ERR_UNSUPPORTED, "group_size %lld not supported (32, 64, 128 or 256)",
+                    (long long)group_size);
+    if (K % group_size != 0 || K % 128 != 0)
+        return fail(W4A16_ERR_UNSUPPORTED, "K=%lld must be a multiple of 128 and of group_size", (long long)K);
     if (N % 4 != 0) return fail(W4A16_ERR_UNSUPPORTED, "N=%lld is not a multiple of 4", (long long)N);
     const int64_t lim = INT32_MAX;
     if ((K / 8) * N > lim || M * K > lim || M * N > lim)
@@ -126,7 +127,7 @@ const TunedPlan* tuned_plan(int64_t M, int64_t N, int64_t K) {
 
 int64_t roundup4(int64_t v) { return ceil_div(v, 4) * 4; }
 
-void default_skinny_plan(int64_t M, int64_t N, int64_t K, w4a16_plan_t* pl) {
+void default_skinny_plan(int64_t M, int64_t N, int64_t K, int64_t group_steps, w4a16_plan_t* pl) {
     const TunedPlan* t = tuned_plan(M, N, K);
     const int64_t KS = K / w4a16::kKStep;
     if (pl->cols == 0) pl->cols = t ? t->cols : (N >= 8192 || K >= 8192) ? 64 : (M > 32 ? 32 : 16);
@@ -135,7 +136,9 @@ void default_skinny_plan(int64_t M, int64_t N, int64_t K, w4a16_plan_t* pl) {
         pl->kc = t ? t->kc : (int32_t)(KS <= 4 * 32 ? std::max<int64_t>(4, roundup4(ceil_div(KS, pl->waves))) : 32);
     if (pl->seg == 0) {
         int32_t seg = t ? t->seg : 4;
-        if (pl->kc % seg != 0 || (seg == 8 && KS % 8 != 0)) seg = pl->kc % 4 == 0 ? 4 : pl->kc;
+        // 8-step segments are built for 128-row groups only
+        if (pl->kc % seg != 0 || (seg == 8 && (KS % 8 != 0 || group_steps != 4)))
+            seg = pl->kc % 4 == 0 ? 4 : pl->kc;
         pl->seg = seg;
     }
 }
@@ -154,7 +157,8 @@ int64_t auto_kernel(int64_t M, int64_t N) {
     return (tiles >= kPrefillMinTiles || M > kSkinnyMaxM) ? W4A16_KERNEL_PREFILL : W4A16_KERNEL_SKINNY;
 }
 
-int complete_plan(int64_t M, int64_t N, int64_t K, w4a16_plan_t* pl) {
+int complete_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, w4a16_plan_t* pl) {
+    const int64_t group_steps = group_size / w4a16::kKStep;
     if (pl->kernel == W4A16_KERNEL_AUTO) pl->kernel = (int32_t)auto_kernel(M, N);
     if (pl->kernel == W4A16_KERNEL_PREFILL) {
         if (pl->tile != 0) return fail(W4A16_ERR_INVALID_ARG, "prefill tile %d is not built", pl->tile);
@@ -165,7 +169,7 @@ int complete_plan(int64_t M, int64_t N, int64_t K, w4a16_plan_t* pl) {
     }
     if (pl->kernel != W4A16_KERNEL_SKINNY)
         return fail(W4A16_ERR_INVALID_ARG, "unknown kernel id %d", pl->kernel);
-    default_skinny_plan(M, N, K, pl);
+    default_skinny_plan(M, N, K, group_steps, pl);
     if (pl->cols != 16 && pl->cols != 32 && pl->cols != 64)
         return fail(W4A16_ERR_INVALID_ARG, "cols must be 16, 32 or 64 (got %d)", pl->cols);
     const int lw = pl->cols / 16;
@@ -181,9 +185,10 @@ int complete_plan(int64_t M, int64_t N, int64_t K, w4a16_plan_t* pl) {
         return fail(W4A16_ERR_INVALID_ARG, "seg=8 needs K %% 256 == 0 (K=%lld)", (long long)K);
     if (pl->kc % pl->seg != 0)
         return fail(W4A16_ERR_INVALID_ARG, "kc=%d is not a multiple of seg=%d", pl->kc, pl->seg);
-    if (!w4a16::skinny_config_supported(pl->row_tiles, pl->waves, lw, pl->seg))
-        return fail(W4A16_ERR_INVALID_ARG, "waves=%d, row_tiles=%d, cols=%d, seg=%d is not built", pl->waves,
-                    pl->row_tiles, pl->cols, pl->seg);
+    if (!w4a16::skinny_config_supported(pl->row_tiles, pl->waves, lw, pl->seg,
+                                        (int)std::min<int64_t>(pl->seg, group_steps)))
+        return fail(W4A16_ERR_INVALID_ARG, "waves=%d, row_tiles=%d, cols=%d, seg=%d with %lld-row groups is not built",
+                    pl->waves, pl->row_tiles, pl->cols, pl->seg, (long long)group_size);
     const int64_t chunks = ceil_div(KS, pl->kc);
     const int64_t splits = ceil_div(chunks, pl->waves);
     if (pl->splits != 0 && pl->splits != splits)
@@ -257,7 +262,7 @@ int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const
     if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros) || !aligned16(y))
         return fail(W4A16_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
     w4a16_plan_t pl = forced ? *forced : w4a16_plan_t{};
-    rc = complete_plan(M, N, K, &pl);
+    rc = complete_plan(M, N, K, group_size, &pl);
     if (rc) return rc;
 
     if (pl.kernel == W4A16_KERNEL_PREFILL) {
@@ -271,6 +276,7 @@ int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const
         q.N = (int)N;
         q.K = (int)K;
         q.tile = pl.tile;
+        q.group_shift = w4a16::log2_exact(group_size);
         const int e = w4a16::launch_prefill(q, stream);
         if (e != (int)hipSuccess)
             return fail(W4A16_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString((hipError_t)e));
@@ -294,6 +300,7 @@ int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const
     p.waves = pl.waves;
     p.lw = pl.cols / 16;
     p.seg = pl.seg;
+    p.gshift = w4a16::log2_exact(group_size / w4a16::kKStep);
     uint64_t ws_bytes = 0, n_counters = 0;
     w4a16::skinny_workspace(p, &ws_bytes, &n_counters);
     if (ws_bytes) {
@@ -313,19 +320,26 @@ int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const
 
 extern "C" {
 
-int w4a16_pack(const float* W, int64_t K, int64_t N, int64_t group_size, int32_t* qweight,
-               uint16_t* scales, uint16_t* zeros) {
+int w4a16_pack_ex(const float* W, int64_t K, int64_t N, int64_t group_size, int symmetric,
+                  int32_t* qweight, uint16_t* scales, uint16_t* zeros) {
     if (!W || !qweight || !scales || !zeros) return fail(W4A16_ERR_INVALID_ARG, "null pointer argument");
     if (K < 1 || N < 1) return fail(W4A16_ERR_INVALID_ARG, "K and N must be >= 1");
-    if (group_size != w4a16::kGroup)
-        return fail(W4A16_ERR_UNSUPPORTED, "group_size %lld not supported (128 only)", (long long)group_size);
+    if (symmetric != 0 && symmetric != 1) return fail(W4A16_ERR_INVALID_ARG, "symmetric must be 0 or 1");
+    if (!w4a16::group_supported(group_size))
+        return fail(W4A16_ERR_UNSUPPORTED, "group_size %lld not supported (32, 64, 128 or 256)",
+                    (long long)group_size);
     if (K % group_size != 0)
         return fail(W4A16_ERR_UNSUPPORTED, "K=%lld is not a multiple of group_size", (long long)K);
-    const int rc = w4a16::pack_host(W, K, N, group_size, qweight, scales, zeros);
+    const int rc = w4a16::pack_host(W, K, N, group_size, symmetric == 1, qweight, scales, zeros);
     if (rc == W4A16_ERR_NONFINITE) return fail(rc, "non-finite weight or fp16 scale overflow");
     if (rc == W4A16_ERR_UNSUPPORTED) return fail(rc, "zero point outside |zero| <= 1024");
     if (rc) return fail(rc, "pack failed");
     return ok();
+}
+
+int w4a16_pack(const float* W, int64_t K, int64_t N, int64_t group_size, int32_t* qweight,
+               uint16_t* scales, uint16_t* zeros) {
+    return w4a16_pack_ex(W, K, N, group_size, 0, qweight, scales, zeros);
 }
 
 int w4a16_unpack(const int32_t* qweight, int64_t K, int64_t N, uint8_t* codes) {
@@ -352,7 +366,7 @@ int w4a16_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, w4a16_plan_t
     int rc = check_gpu_shape(M, N, K, group_size);
     if (rc) return rc;
     w4a16_plan_t pl = *plan;
-    rc = complete_plan(M, N, K, &pl);
+    rc = complete_plan(M, N, K, group_size, &pl);
     if (rc) return rc;
     *plan = pl;
     return ok();
@@ -369,7 +383,8 @@ int w4a16_dequant(const int32_t* qweight, const void* scales, const void* zeros,
     const int e = w4a16::launch_dequant(reinterpret_cast<const uint32_t*>(qweight),
                                         static_cast<const uint16_t*>(scales),
                                         static_cast<const uint16_t*>(zeros), codes,
-                                        static_cast<uint16_t*>(w), (int)N, (int)K, stream);
+                                        static_cast<uint16_t*>(w), (int)N, (int)K,
+                                        w4a16::log2_exact(group_size), stream);
     if (e != (int)hipSuccess)
         return fail(W4A16_ERR_HIP, "dequant kernel launch: %s", hipGetErrorString((hipError_t)e));
     return ok();

@@ -19,14 +19,15 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint4* __restrict__ 
                                                       const uint16_t* __restrict__ scales,
                                                       const uint16_t* __restrict__ zeros,
                                                       uint8_t* __restrict__ codes,
-                                                      uint16_t* __restrict__ w, int N, int K) {
+                                                      uint16_t* __restrict__ w, int N, int K,
+                                                      int group_shift) {
     const int nq = N >> 2;
     const size_t total = (size_t)(K >> 3) * nq;
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= total) return;
     const int i = (int)(idx / nq);                 // packed row
     const int n = (int)(idx % nq) * 4;             // first column
-    const int grp = (i * 8) / kGroup;
+    const int grp = (i * 8) >> group_shift;
     const uint4 wv = qw[idx];
     const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
     const uint2 sv = *reinterpret_cast<const uint2*>(scales + (size_t)grp * N + n);
@@ -57,12 +58,12 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint4* __restrict__ 
 }  // namespace
 
 int launch_dequant(const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
-                   uint8_t* codes, uint16_t* w, int N, int K, void* stream) {
+                   uint8_t* codes, uint16_t* w, int N, int K, int group_shift, void* stream) {
     const size_t total = (size_t)(K >> 3) * (size_t)(N >> 2);
     const unsigned blocks = (unsigned)((total + 255) / 256);
     hipLaunchKernelGGL(dequant_kernel, dim3(blocks), dim3(256), 0,
                        reinterpret_cast<hipStream_t>(stream),
-                       reinterpret_cast<const uint4*>(qweight), scales, zeros, codes, w, N, K);
+                       reinterpret_cast<const uint4*>(qweight), scales, zeros, codes, w, N, K, group_shift);
     return (int)hipGetLastError();
 }
 

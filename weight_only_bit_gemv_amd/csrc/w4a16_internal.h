@@ -10,13 +10,16 @@ namespace w4a16 {
 // ---- host packer (w4a16_pack.cpp) ----
 uint16_t f32_to_f16_rne(float f);
 float f16_to_f32(uint16_t h);
-int pack_host(const float* W, int64_t K, int64_t N, int64_t g,
+int pack_host(const float* W, int64_t K, int64_t N, int64_t g, bool symmetric,
               int32_t* qweight, uint16_t* scales, uint16_t* zeros);
 void unpack_host(const int32_t* qweight, int64_t K, int64_t N, uint8_t* codes);
 
 // ---- decode / skinny kernel (w4a16_skinny.hip) ----
 constexpr int kKStep = 32;           // K rows per MFMA step (4 packed rows)
-constexpr int kGroup = 128;          // K rows per scale/zero group
+constexpr int kGroup = 128;          // default K rows per scale/zero group
+// Supported group sizes: 32, 64, 128, 256 rows (1, 2, 4, 8 K-steps).
+inline bool group_supported(int64_t g) { return g == 32 || g == 64 || g == 128 || g == 256; }
+inline int log2_exact(int64_t v) { int r = 0; while ((int64_t(1) << r) < v) ++r; return r; }
 
 struct SkinnyParams {
     const uint16_t* x;        // fp16 [M, K]
@@ -35,6 +38,7 @@ struct SkinnyParams {
     int waves;                // wavefronts per work-group (4, 8 or 16), each on its own K range
     int lw;                   // packed words per lane per K-step (1, 2, 4): cols = 16 * lw
     int seg;                  // K-steps per software-pipeline segment (1, 2, 4, 8)
+    int gshift;               // log2(K-steps per scale/zero group): group of K-step ks = ks >> gshift
 };
 
 // Workspace a skinny launch needs (bytes of partials, number of counters).
@@ -45,7 +49,8 @@ inline void skinny_workspace(const SkinnyParams& p, uint64_t* ws_bytes, uint64_t
 }
 
 int launch_skinny(const SkinnyParams& p, void* stream);   // returns a hipError_t value
-bool skinny_config_supported(int row_tiles, int waves, int lw, int seg);
+// seg_group = min(seg, K-steps per group): K-steps of one group inside a segment.
+bool skinny_config_supported(int row_tiles, int waves, int lw, int seg, int seg_group);
 // per strip width (w4a16_skinny_lw{1,2,4}.hip); hipErrorInvalidValue for a config not built
 int launch_skinny_lw1(const SkinnyParams& p, void* stream);
 int launch_skinny_lw2(const SkinnyParams& p, void* stream);
@@ -64,12 +69,13 @@ struct PrefillParams {
     uint16_t* y;              // fp16 [M, N]
     int M, N, K;
     int tile;                 // tile configuration (0 only: 128 x 128)
+    int group_shift;          // log2(rows per scale/zero group)
 };
 
 int launch_prefill(const PrefillParams& p, void* stream);  // returns a hipError_t value
 
 // ---- dequant hook (w4a16_dequant.hip) ----
 int launch_dequant(const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
-                   uint8_t* codes, uint16_t* w, int N, int K, void* stream);
+                   uint8_t* codes, uint16_t* w, int N, int K, int group_shift, void* stream);
 
 }  // namespace w4a16

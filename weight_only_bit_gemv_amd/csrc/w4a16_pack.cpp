@@ -9,6 +9,14 @@
 //   q     = clamp(rne(w / scale) + zero, 0, 15)
 // with every step an IEEE fp32 operation. Build with -ffp-contract=off and without
 // fast-math so that no step is fused or reassociated.
+//
+// Symmetric mode (the +8 zero point of "Triton Kernel Matches bitsandbytes: Why Both Lose
+// to Math", section "Three Kernel Versions and Two Bugs"):
+//   scale = fp16_rne(max|w| / 7)        (1.0 when that rounds to zero)
+//   zero  = 8
+//   q     = clamp(rne(w / scale) + 8, 0, 15)
+// Group sizes: any multiple of 8 rows here; the library accepts 32, 64, 128 and 256 (the
+// GemLite README takes group sizes divisible by 32).
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -74,8 +82,8 @@ namespace {
 constexpr int kCols = 64;   // columns per work item of the packer's threads
 
 // Quantise and pack columns [n0, n1) of every K-group. Returns W4A16_OK or an error.
-int pack_columns(const float* W, int64_t K, int64_t N, int64_t g, int64_t n0, int64_t n1,
-                 int32_t* qweight, uint16_t* scales, uint16_t* zeros) {
+int pack_columns(const float* W, int64_t K, int64_t N, int64_t g, bool symmetric, int64_t n0,
+                 int64_t n1, int32_t* qweight, uint16_t* scales, uint16_t* zeros) {
     const int64_t nc = n1 - n0;
     float mn[kCols], mx[kCols], s[kCols], z[kCols];
     uint8_t q[kCols * 8];
@@ -90,13 +98,13 @@ int pack_columns(const float* W, int64_t K, int64_t N, int64_t g, int64_t n0, in
             }
         }
         for (int64_t c = 0; c < nc; ++c) {
-            const float range = mx[c] - mn[c];
-            const float s32 = range / 15.0f;
+            const float s32 = symmetric ? std::max(std::fabs(mn[c]), std::fabs(mx[c])) / 7.0f
+                                        : (mx[c] - mn[c]) / 15.0f;
             uint16_t s16 = f32_to_f16_rne(s32);
             if ((s16 & 0x7c00u) == 0x7c00u) return W4A16_ERR_NONFINITE;
             if ((s16 & 0x7fffu) == 0) s16 = 0x3c00u;             // 1.0 for a zero scale
             s[c] = f16_to_f32(s16);
-            z[c] = std::rint(-mn[c] / s[c]);
+            z[c] = symmetric ? 8.0f : std::rint(-mn[c] / s[c]);
             if (std::fabs(z[c]) > 1024.0f) return W4A16_ERR_UNSUPPORTED;
             scales[grp * N + n0 + c] = s16;
             zeros[grp * N + n0 + c] = f32_to_f16_rne(z[c]);
@@ -123,7 +131,7 @@ int pack_columns(const float* W, int64_t K, int64_t N, int64_t g, int64_t n0, in
 
 }  // namespace
 
-int pack_host(const float* W, int64_t K, int64_t N, int64_t g,
+int pack_host(const float* W, int64_t K, int64_t N, int64_t g, bool symmetric,
               int32_t* qweight, uint16_t* scales, uint16_t* zeros) {
     // Reject non-finite input up front so that no output is written on that error.
     {
@@ -140,7 +148,7 @@ int pack_host(const float* W, int64_t K, int64_t N, int64_t g,
         for (int64_t ch = t; ch < chunks; ch += nthreads) {
             const int64_t n0 = ch * kCols;
             const int64_t n1 = std::min<int64_t>(N, n0 + kCols);
-            const int rc = pack_columns(W, K, N, g, n0, n1, qweight, scales, zeros);
+            const int rc = pack_columns(W, K, N, g, symmetric, n0, n1, qweight, scales, zeros);
             if (rc != W4A16_OK) { status[t] = rc; return; }
         }
     };

@@ -88,7 +88,11 @@ __global__ __launch_bounds__(NT, OCC) void prefill_kernel(PrefillParams p) {
         uint2 sv, zv;
     };
     auto load_stage = [&](Regs& r, int kt) {
-        const int grp = (kt * BK) / kGroup;
+        // the thread's packed rows lie in one group: groups are >= 32 rows, packed rows
+        // br + (NT / BQ) * h of a stage differ by multiples of 8 * (NT / BQ) >= 64 rows only
+        // when BL > 1, which needs BN > 128 (not built)
+        static_assert(BL == 1, "one word quad per thread per stage");
+        const int grp = (kt * BK + 8 * br) >> p.group_shift;
 #pragma unroll
         for (int h = 0; h < BL; ++h) r.bw[h] = qw[(size_t)(kt * KCH + br + (NT / BQ) * h) * nq + (bnl >> 2)];
         r.sv = *reinterpret_cast<const uint2*>(p.scales + (size_t)grp * p.N + bnl);

@@ -38,7 +38,6 @@
 namespace w4a16 {
 namespace skinny {
 
-constexpr int kGS = kGroup / kKStep;    // K-steps per scale/zero group (4)
 // s_waitcnt immediate for vmcnt(0) with expcnt/lgkmcnt left at their maxima (gfx9 encoding).
 constexpr int kWaitVmcnt0 = 0 | (0x7 << 4) | (0xf << 8);
 // Buffer-instruction cache policy: sc1, the device-coherent level (another XCD's L2 may
@@ -70,24 +69,25 @@ __device__ __forceinline__ _Float16 half_at(uint2 v, int t) {
 }
 
 // One segment: U consecutive K-steps (U * 32 rows) of one wavefront: U packed word groups
-// per lane, the matching activations, and the scale/zero of every 128-row group the
-// segment touches (one when U <= 4, U/4 when U = 8; a segment never straddles a group).
+// per lane, the matching activations, and the scale/zero of every group the segment
+// touches: SG = min(U, K-steps per group) K-steps of one group each, U / SG groups (a
+// segment starts on a multiple of U, so it never straddles a group boundary).
 // The loads only issue memory requests: nothing in load() reads the returned registers,
 // so a wavefront can keep a prefetched segment in flight while it works on the current
 // one (the activation permutation happens in accumulate(), at first use).
-template <int MT, int LW, int U>
+template <int MT, int LW, int U, int SG>
 struct Segment {
     typedef typename Lanes<LW>::Words Words;
     typedef typename Lanes<LW>::Halves Halves;
-    static constexpr int NG = U > kGS ? U / kGS : 1;     // groups per segment
-    static constexpr int SG = U > kGS ? kGS : U;         // K-steps per group in the segment
+    static_assert(U % SG == 0, "a segment holds whole groups or lies inside one");
+    static constexpr int NG = U / SG;                    // groups per segment
     Words wv[U];
     uint4 xv[U][MT];
     Halves sv[NG], zv[NG];
 
     __device__ __forceinline__ void load(const uint32_t* __restrict__ wbase, const uint16_t* const* xrow,
                                          const SkinnyParams& p, int ks, int nl) {
-        const int grp = ks / kGS;
+        const int grp = ks >> p.gshift;
 #pragma unroll
         for (int u = 0; u < U; ++u)
             wv[u] = *reinterpret_cast<const Words*>(wbase + (size_t)(ks + u) * 4 * p.N);
@@ -213,9 +213,10 @@ __device__ __forceinline__ void partial_add(Row<LW>& r, __amdgpu_buffer_rsrc_t r
 // MT: 16-row MFMA tiles of M per work-group. LW: packed words per lane per K-step (strip
 // width 16*LW). U: K-steps per segment; the dispatcher keeps kc a multiple of U and, for
 // U = 8, K a multiple of 256, so every segment is exactly U K-steps inside whole groups and
-// the loop below needs no predicates. W: wavefronts per work-group.
+// the loop below needs no predicates. SG: min(U, K-steps per group). W: wavefronts per
+// work-group.
 // Dynamic LDS: (W - 1) * rows * CW floats, rows = min(16 * MT, M - row0).
-template <int MT, int LW, int U, int W>
+template <int MT, int LW, int U, int SG, int W>
 __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
     static_assert(U == 1 || U == 2 || U == 4 || U == 8, "segment of 1, 2, 4 or 8 K-steps");
     constexpr int CW = 16 * LW;
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
     // sched_barrier(0) after each load keeps the instruction scheduler from sinking the
     // prefetch below the arithmetic of the previous segment (it otherwise does so to save
     // registers, which leaves one segment in flight and drains the queue between segments).
-    Segment<MT, LW, U> sa, sb;
+    Segment<MT, LW, U, SG> sa, sb;
     const int nseg = (k1 - k0) / U;
     if (nseg > 0) sa.load(wbase, xrow, p, k0, nl);
     __builtin_amdgcn_sched_barrier(0);
@@ -385,12 +386,12 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
         __hip_atomic_store(&p.counters[counter], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MT, int LW, int U, int W>
+template <int MT, int LW, int U, int SG, int W>
 hipError_t launch_one(const SkinnyParams& p, hipStream_t s) {
     const dim3 grid((unsigned)(p.n_strips * p.splits), (unsigned)p.row_blocks);
     const int rows = std::min(16 * MT, p.M);
     const size_t lds = (size_t)(W - 1) * rows * 16 * LW * sizeof(float);
-    hipLaunchKernelGGL((skinny_kernel<MT, LW, U, W>), grid, dim3(64 * W), lds, s, p);
+    hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W>), grid, dim3(64 * W), lds, s, p);
     return hipGetLastError();
 }
 
