@@ -62,9 +62,9 @@ COPY_CAL_BYTES = 256 << 20     # calibration copy for the PMC byte counters
 METRIC = "W4A16 weight-stream HBM GB/s (% of peak) and us/call at M=1..16"
 
 
-def alg_bytes(M, K, N):
+def alg_bytes(M, K, N, group=GROUP):
     """Algorithmic bytes of one call: int4 weights, fp16 scales + zeros, fp16 x and y."""
-    return K * N // 2 + 2 * 2 * (K // GROUP) * N + 2 * M * K + 2 * M * N
+    return K * N // 2 + 2 * 2 * (K // group) * N + 2 * M * K + 2 * M * N
 
 
 def kernel_source_hash():
@@ -89,8 +89,10 @@ class Runner:
     items: list of (M, K, N, family key), launched in order by step().
     """
 
-    def __init__(self, torch, lib, dev, stream, families, items, rotate_bytes, replicate=None):
+    def __init__(self, torch, lib, dev, stream, families, items, rotate_bytes, replicate=None,
+                 group=GROUP, symmetric=False):
         self.torch, self.lib, self.dev, self.stream = torch, lib, dev, stream
+        self.group, self.symmetric = group, symmetric
         self.weights, self.host = {}, {}
         packed = {}
         for key, (K, N, wid, layer) in families.items():
@@ -102,7 +104,7 @@ class Runner:
             t0 = time.time()
             if (K, N, wid, layer) not in packed:
                 W = synth.weight(K, N, wid=wid, layer=layer)
-                packed[(K, N, wid, layer)] = lib.w4a16_pack(W)
+                packed[(K, N, wid, layer)] = lib.w4a16_pack(W, group_size=group, symmetric=symmetric)
                 del W
             qw, s, z = packed[(K, N, wid, layer)]
             self.host[key] = (qw, s, z)
@@ -120,7 +122,7 @@ class Runner:
         self.xk = [self.x[(M, K, wids[key])] for (M, K, N, key) in items]
         self.y = [torch.empty((M, N), dtype=torch.float16, device=dev) for (M, K, N, key) in items]
         self.cursor = {key: 0 for key in families}
-        self.step_bytes = sum(alg_bytes(M, K, N) for (M, K, N, key) in items)
+        self.step_bytes = sum(alg_bytes(M, K, N, group) for (M, K, N, key) in items)
         self.fn = lib.load().w4a16_matmul
         self.fn_ex = lib.load().w4a16_matmul_ex
         self.plans = {}
@@ -133,7 +135,7 @@ class Runner:
         self.cursor[key] = (c + 1) % len(self.weights[key])
         qw, s, z = self.weights[key][c]
         args = (self.xk[i].data_ptr(), qw.data_ptr(), s.data_ptr(), z.data_ptr(),
-                self.y[i].data_ptr(), M, N, K, GROUP, self.sptr)
+                self.y[i].data_ptr(), M, N, K, self.group, self.sptr)
         if plan is None:
             rc = self.fn(*args)
         else:
@@ -254,10 +256,11 @@ def per_item_times(torch, lib, runner, reps_per_copy=1):
         reps = len(runner.weights[key]) * reps_per_copy
         sec, _ = time_graph(torch, runner.stream, lambda: [runner.launch(i) for _ in range(reps)], 5)
         t = sec / reps
-        b = alg_bytes(M, K, N)
+        b = alg_bytes(M, K, N, runner.group)
         out.append({"M": M, "K": K, "N": N, "us": round(t * 1e6, 3),
                     "GBps": round(b / t / 1e9, 1), "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
-                    "TFLOPs": round(2 * M * K * N / t / 1e12, 3), "plan": lib.w4a16_plan(M, N, K)})
+                    "TFLOPs": round(2 * M * K * N / t / 1e12, 3),
+                    "plan": lib.w4a16_plan(M, N, K, group_size=runner.group)})
     return out
 
 
@@ -307,7 +310,7 @@ def dense_time(torch, x, ws, y, stream, reps):
 def dense_weights(torch, lib, runner, key):
     """fp16 weights [K, N] equal to the GPU's dequantised values, rotated like the int4 ones."""
     qw, s, z = runner.weights[key][0]
-    _, w16 = lib.w4a16_dequant(qw, s, z, codes=False)
+    _, w16 = lib.w4a16_dequant(qw, s, z, codes=False, group_size=runner.group)
     copies = max(2, -(-ROTATE_BYTES // (w16.numel() * 2)))
     return [w16] + [w16.clone() for _ in range(copies - 1)]
 
@@ -325,8 +328,8 @@ def cpu_baseline(runner, wid):
     for (M, K, N, key) in runner.items:
         qw, s, z = runner.host[key]
         x = synth.activations(M, K, wid=wid)
-        oracle.matmul(x, qw, s, z)
-        total_bytes += alg_bytes(M, K, N)
+        oracle.matmul(x, qw, s, z, runner.group)
+        total_bytes += alg_bytes(M, K, N, runner.group)
     dt = time.perf_counter() - t0
     return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": blas_threads,
             "kind": "oracle",
@@ -399,7 +402,12 @@ def run_decode(args):
     stream = torch.cuda.Stream(device=dev)
     fam, items, desc, replicate = workload_items(args.workload)
     rotate = 0 if args.workload == "chain_7b" else ROTATE_BYTES
-    runner = Runner(torch, lib, dev, stream, fam, items, rotate, replicate)
+    runner = Runner(torch, lib, dev, stream, fam, items, rotate, replicate, args.group_size,
+                    args.symmetric)
+    if args.group_size != GROUP or args.symmetric:
+        desc = (desc.replace("per 128-row group", "").rstrip(", ") +
+                f"; weight format: {'symmetric (zero 8)' if args.symmetric else 'asymmetric'}, "
+                f"group {args.group_size}")
     launches = len(items)
     steps = args.steps if args.workload != "chain_7b" else max(1, args.steps // 10)
     elapsed = timed_steps(torch, runner, steps, args.warmup)
@@ -435,13 +443,15 @@ def run_decode(args):
         "steps": steps, "warmup": args.warmup, "ms_per_step": round(elapsed / steps * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": desc, "launches_per_step": launches, "bytes_per_step": runner.step_bytes,
+        "config": {"workload": desc, "group_size": args.group_size, "symmetric": args.symmetric,
+                   "launches_per_step": launches, "bytes_per_step": runner.step_bytes,
                    "timing": "HIP graph of all steps, events on the launch stream",
                    "weight_copies_rotated": {str(k): len(v) for k, v in runner.weights.items()
                                              if args.workload != "chain_7b"}},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic() if args.workload == "decode_sweep" else None,
+                     "traffic": (load_traffic() if args.workload == "decode_sweep"
+                                 and args.group_size == GROUP and not args.symmetric else None),
                      "kernel": "skinny_kernel (decode weight stream, MFMA, split-K when K is deep)",
                      "avg_launch_us": round(avg_launch_s * 1e6, 3)},
         "measured_copy_GBps": round(copy_gbs, 1),
@@ -472,7 +482,8 @@ def run_prefill(args):
     for (K, N) in kns:
         fam = {(K, N): (K, N, wid, 0)}
         items = [(M, K, N, (K, N)) for M in ms]
-        runner = Runner(torch, lib, dev, stream, fam, items, ROTATE_BYTES // 2)
+        runner = Runner(torch, lib, dev, stream, fam, items, ROTATE_BYTES // 2, None, args.group_size,
+                        args.symmetric)
         with torch.cuda.stream(stream):
             runner.step()
         stream.synchronize()
@@ -487,9 +498,10 @@ def run_prefill(args):
             d = dense_time(torch, runner.xk[i], ws, y, stream, 2 * len(ws))
             fl = 2 * M * K * N
             row = {"M": M, "K": K, "N": N, "w4a16_us": round(t * 1e6, 2),
-                   "w4a16_TFLOPs": round(fl / t / 1e12, 2), "w4a16_GBps": round(alg_bytes(M, K, N) / t / 1e9, 1),
+                   "w4a16_TFLOPs": round(fl / t / 1e12, 2), "w4a16_GBps": round(alg_bytes(M, K, N, args.group_size) / t / 1e9, 1),
                    "dense_fp16_us": round(d * 1e6, 2), "dense_TFLOPs": round(fl / d / 1e12, 2),
-                   "speedup_vs_dense": round(d / t, 3), "plan": lib.w4a16_plan(M, N, K)}
+                   "speedup_vs_dense": round(d / t, 3),
+                   "plan": lib.w4a16_plan(M, N, K, group_size=args.group_size)}
             if 32 <= M <= 512:           # both kernels, where the dispatcher's threshold lies
                 for name, kern in (("skinny_us", lib.W4A16_KERNEL_SKINNY), ("prefill_us", lib.W4A16_KERNEL_PREFILL)):
                     sec, _ = time_graph(torch, stream, lambda: [runner.launch(i, dict(kernel=kern)) for _ in range(reps)],
@@ -508,7 +520,8 @@ def run_prefill(args):
               "warmup": 1, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
               "vs_baseline": None, "dtype": "f16", "data": "synthetic",
               "config": {"workload": "prefill crossover: M in 1..2048 on (8192,8192),(8192,28672),"
-                                     "(28672,8192) and the decode-sweep shapes"},
+                                     "(28672,8192) and the decode-sweep shapes",
+                         "group_size": args.group_size, "symmetric": args.symmetric},
               "roofline": {"bound": "mfma", "achieved": best["w4a16_TFLOPs"],
                            "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(best["w4a16_TFLOPs"] / MFMA_F16_PEAK_TFLOPS, 4),
@@ -639,6 +652,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_sweep",
                     choices=["decode_sweep", "gemv_4096", "moe_expert", "chain_7b", "prefill"])
+    ap.add_argument("--group-size", type=int, default=GROUP, choices=[32, 64, 128, 256],
+                    help="K rows per scale/zero group (decode workloads)")
+    ap.add_argument("--symmetric", action="store_true",
+                    help="symmetric quantiser (zero point 8) instead of min/max (decode workloads)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense fp16 baseline")
     ap.add_argument("--pmc-pass", action="store_true")

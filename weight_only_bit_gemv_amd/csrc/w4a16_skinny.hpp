@@ -366,21 +366,42 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);           // counter read before any partial load
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 
+    // The partials of kBatch splits x 4 rows are loaded together, then summed in split
+    // order 0..splits-1 (fixed, so the result does not depend on arrival order). Loads of a
+    // split index >= splits lie beyond the buffer resource's range and return 0, so the
+    // batch needs no predicate; rows >= M are read (inside the slab) but never stored.
     if (col_ok) {
+        constexpr int kBatch = 4;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
+            Row<LW> v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int t = 0; t < LW; ++t) v[r].v[t] = 0.f;
+            for (int s0 = 0; s0 < p.splits; s0 += kBatch) {
+                Row<LW> part[kBatch][4];
+#pragma unroll
+                for (int s = 0; s < kBatch; ++s)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+                        for (int t = 0; t < LW; ++t) part[s][r].v[t] = 0.f;
+                        partial_add<LW>(part[s][r], rs, ((s0 + s) * slab + (mt * 16 + lg * 4 + r) * CW + lc * LW) * 4);
+                    }
+#pragma unroll
+                for (int s = 0; s < kBatch; ++s)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+#pragma unroll
+                        for (int t = 0; t < LW; ++t) v[r].v[t] += part[s][r].v[t];
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int rl = mt * 16 + lg * 4 + r;
-                if (rl < rows) {
-                    Row<LW> v;
-#pragma unroll
-                    for (int t = 0; t < LW; ++t) v.v[t] = 0.f;
-                    for (int s = 0; s < p.splits; ++s)                 // fixed order 0..splits-1
-                        partial_add<LW>(v, rs, (s * slab + rl * CW + lc * LW) * 4);
-                    store_y<LW>(p.y + (size_t)(row0 + rl) * p.N + n, v);
-                }
+                if (rl < rows) store_y<LW>(p.y + (size_t)(row0 + rl) * p.N + n, v[r]);
             }
+        }
     }
     if (lane == 0)                                     // ready for the next call
         __hip_atomic_store(&p.counters[counter], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
