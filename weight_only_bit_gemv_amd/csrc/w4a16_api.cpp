@@ -88,15 +88,15 @@ const TunedPlan kTuned[] = {
     { 4096,   4096,  4, 16,  8, 16, 4},   // 5.72 us
     { 4096,   4096,  8, 16,  8, 16, 4},   // 6.19 us
     { 4096,   4096, 16, 16,  4, 32, 4},   // 7.22 us
-    { 4096,   4096, 32, 16,  4, 64, 4},   // 11.01 us
-    { 4096,   4096, 64, 32,  4, 64, 4},   // 11.87 us
+    { 4096,   4096, 32, 64,  4,  8, 2},   // 9.71 us (4 splits)
+    { 4096,   4096, 64, 32,  4, 48, 4},   // 11.79 us
     { 4096,  14336,  1, 64,  4, 32, 4},   // 9.01 us
     { 4096,  14336,  2, 64,  4, 32, 4},   // 9.13 us
     { 4096,  14336,  4, 64,  4, 32, 4},   // 9.30 us
     { 4096,  14336,  8, 64,  4, 32, 4},   // 9.69 us
     { 4096,  14336, 16, 64,  4, 32, 4},   // 10.35 us
     { 4096,  14336, 32, 64,  4, 32, 4},   // 14.79 us
-    { 4096,  14336, 64, 64,  4, 32, 4},   // 24.49 us
+    { 4096,  14336, 64, 64,  4, 48, 4},   // 23.98 us
     { 4096, 128256,  1, 64,  4, 32, 4},   // 54.97 us
     { 8192,   8192,  1, 32, 16, 16, 4},   // 10.61 us
     { 8192,   8192, 16, 32,  4, 64, 4},   // 13.64 us
@@ -106,13 +106,13 @@ const TunedPlan kTuned[] = {
     { 8192,  28672, 16, 64,  4, 64, 4},   // 33.76 us
     { 8192,  28672, 32, 64,  4, 64, 4},   // 48.56 us
     { 8192,  28672, 64, 64,  4, 64, 4},   // 80.77 us
-    {14336,   4096,  1, 64,  4, 32, 4},   // 11.19 us
-    {14336,   4096,  2,  64,  4, 32, 4},   // split K: steadier across machines than the fastest here
-    {14336,   4096,  4,  64,  4, 32, 4},   // split K: steadier across machines than the fastest here
-    {14336,   4096,  8, 64,  4, 32, 4},   // 14.82 us
-    {14336,   4096, 16, 64,  4, 32, 4},   // 15.53 us
-    {14336,   4096, 32, 64,  4, 32, 4},   // 24.09 us
-    {14336,   4096, 64, 32,  8, 64, 4},   // 34.00 us
+    {14336,   4096,  1, 64,  4, 28, 4},   // 10.56 us (4 splits of 112 K-steps)
+    {14336,   4096,  2, 64,  4, 28, 4},   // 10.72 us
+    {14336,   4096,  4, 64,  4, 28, 4},   // 11.04 us
+    {14336,   4096,  8, 64,  4, 28, 4},   // 11.09 us
+    {14336,   4096, 16, 64,  4, 28, 4},   // 11.65 us
+    {14336,   4096, 32, 64,  4, 28, 4},   // 16.54 us
+    {14336,   4096, 64, 64,  4, 28, 4},   // 26.29 us
     {28672,   8192,  1, 64,  8, 64, 4},   // 28.79 us
     {28672,   8192, 16, 64,  8, 64, 4},   // 36.51 us
     {28672,   8192, 32, 64,  8, 64, 4},   // 53.76 us
