@@ -502,11 +502,17 @@ def run_prefill(args):
                    "dense_fp16_us": round(d * 1e6, 2), "dense_TFLOPs": round(fl / d / 1e12, 2),
                    "speedup_vs_dense": round(d / t, 3),
                    "plan": lib.w4a16_plan(M, N, K, group_size=args.group_size)}
+            forced = []
             if 32 <= M <= 512:           # both kernels, where the dispatcher's threshold lies
-                for name, kern in (("skinny_us", lib.W4A16_KERNEL_SKINNY), ("prefill_us", lib.W4A16_KERNEL_PREFILL)):
-                    sec, _ = time_graph(torch, stream, lambda: [runner.launch(i, dict(kernel=kern)) for _ in range(reps)],
-                                        2, warm=1)
-                    row[name] = round(sec / reps * 1e6, 2)
+                forced.append(("skinny_us", dict(kernel=lib.W4A16_KERNEL_SKINNY)))
+            if M >= 32:                  # both prefill tiles
+                forced += [("prefill_lds_tile_us", dict(kernel=lib.W4A16_KERNEL_PREFILL, tile=lib.W4A16_TILE_LDS)),
+                           ("prefill_register_tile_us",
+                            dict(kernel=lib.W4A16_KERNEL_PREFILL, tile=lib.W4A16_TILE_REGISTER_B))]
+            for name, plan in forced:
+                sec, _ = time_graph(torch, stream, lambda: [runner.launch(i, plan) for _ in range(reps)],
+                                    2, warm=1)
+                row[name] = round(sec / reps * 1e6, 2)
             rows.append(row)
             if cross is None and d < t:
                 cross = M

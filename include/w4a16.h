@@ -50,8 +50,12 @@ extern "C" {
 /* Kernel selection for w4a16_matmul_ex / w4a16_plan. */
 #define W4A16_KERNEL_AUTO     0   /* shape-based dispatcher (what w4a16_matmul uses)        */
 #define W4A16_KERNEL_SKINNY   1   /* decode: weight stream, split-K, M <= 64 per row block  */
-#define W4A16_KERNEL_PREFILL  2   /* prefill: LDS-staged fp16 dequant tiles feeding MFMA;   */
-                                  /* 128 x 128 output tiles, no plan fields besides kernel */
+#define W4A16_KERNEL_PREFILL  2   /* prefill: fp16 dequant tiles feeding MFMA (tile below)  */
+
+/* Prefill tile configurations (w4a16_plan_t.tile; 0 = the dispatcher's choice). */
+#define W4A16_TILE_LDS         1  /* 128 x 128 output tile, weights and activations in LDS  */
+#define W4A16_TILE_REGISTER_B  2  /* 128 x 256 output tile, weights dequantised in registers,*/
+                                  /* activations in LDS (fewer LDS bytes per MFMA)          */
 
 /*
  * Execution plan of one w4a16_matmul call (what the dispatcher chose, or what a caller
@@ -63,7 +67,8 @@ extern "C" {
  *              waves; a caller may leave it 0 or give the matching value).
  *   row_tiles  SKINNY: 16-row MFMA tiles per work-group (1..4; default ceil(M/16) <= 4;
  *              at most 2 when cols < 64).
- *   tile       PREFILL: tile configuration id (0 = default).
+ *   tile       PREFILL: W4A16_TILE_LDS or W4A16_TILE_REGISTER_B (0: chosen from the
+ *              number of 128 x 256 output tiles; the register tile once there are >= 384).
  *   waves      SKINNY: wavefronts per work-group, 4, 8 or 16 (the cross-wave reduction
  *              must fit in 64 KiB of LDS: (waves-1) * 16*row_tiles * cols * 4 bytes).
  *   cols       SKINNY: output columns per work-group strip, 16, 32 or 64 (each lane loads

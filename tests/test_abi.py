@@ -92,7 +92,7 @@ def test_matmul_ex_rejects_bad_plans():
     so = B.load()
     for kw in [dict(kernel=7), dict(kernel=1, kc=3), dict(kernel=1, kc=6), dict(kernel=1, kc=-4),
                dict(kernel=1, row_tiles=5), dict(kernel=1, waves=6), dict(kernel=1, waves=16, row_tiles=2),
-               dict(kernel=1, kc=4, waves=4, splits=3), dict(kernel=2, tile=3), dict(kernel=2, kc=4),
+               dict(kernel=1, kc=4, waves=4, splits=3), dict(kernel=2, tile=3), dict(kernel=2, tile=-1), dict(kernel=2, kc=4),
                dict(kernel=2, waves=8)]:
         pl = B.w4a16_plan_t(**kw)
         rc = so.w4a16_matmul_ex(P[0], P[1], P[2], P[3], P[4], 1, 64, 128, 128, None,
@@ -125,6 +125,9 @@ def test_auto_plan_is_valid_and_covers_k(M, K, N):
     tiles = -(-M // 128) * -(-N // 128)
     expect_prefill = M >= 65 and (tiles >= 128 or M > 1024)
     assert pl["kernel"] == (lib.W4A16_KERNEL_PREFILL if expect_prefill else lib.W4A16_KERNEL_SKINNY)
+    if pl["kernel"] == lib.W4A16_KERNEL_PREFILL:
+        regb = -(-M // 128) * -(-N // 256) >= 384
+        assert pl["tile"] == (lib.W4A16_TILE_REGISTER_B if regb else lib.W4A16_TILE_LDS)
     if pl["kernel"] == lib.W4A16_KERNEL_SKINNY:
         kc, splits, W = pl["kc"], pl["splits"], pl["waves"]
         assert kc in (1, 2) or kc % 4 == 0
@@ -181,3 +184,12 @@ def test_one_hip_runtime_per_process():
         r = subprocess.run([sys.executable, "-c", src], cwd=ROOT, capture_output=True, text=True,
                            timeout=300)
         assert r.returncode == 0, f"{src}\n{r.stdout}\n{r.stderr}"
+
+
+def test_python_constants_match_header():
+    """The binding's W4A16_* integers are the header's #define values."""
+    text = open(HEADER).read()
+    defs = dict((k, int(v)) for k, v in re.findall(r"^#define (W4A16_\w+)\s+(-?\d+)", text, flags=re.M))
+    assert len(defs) >= 11
+    for name, value in defs.items():
+        assert getattr(lib, name) == value, name

@@ -262,7 +262,7 @@ def test_matmul_prefill_kernel_forced(lib, M, K, N):
     W = synth.weight_custom(K, N, seed=100 + M, std=0.02)
     qw, s, z = oracle.quantize_pack(W)
     x = synth.activations(M, K, wid=9)
-    check_y(run(lib, x, qw, s, z, plan=dict(kernel=lib.W4A16_KERNEL_PREFILL)),
+    check_y(run(lib, x, qw, s, z, plan=dict(kernel=lib.W4A16_KERNEL_PREFILL, tile=lib.W4A16_TILE_LDS)),
             oracle.matmul(x, qw, s, z), f"prefill forced M={M} K={K} N={N}")
 
 
@@ -349,8 +349,46 @@ def test_matmul_formats_prefill_forced(lib, M, K, N, g, sym):
     print(f"\n[format prefill] g={g} sym={sym} M={M} K={K} N={N}", flush=True)
     qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=200 + M, std=0.02), g, sym)
     x = synth.activations(M, K, wid=9)
-    check_y(run(lib, x, qw, s, z, plan=dict(kernel=lib.W4A16_KERNEL_PREFILL), group_size=g),
+    check_y(run(lib, x, qw, s, z, plan=dict(kernel=lib.W4A16_KERNEL_PREFILL, tile=lib.W4A16_TILE_LDS),
+                group_size=g),
             oracle.matmul(x, qw, s, z, g), f"prefill g={g} sym={sym} M={M} K={K} N={N}")
+
+
+PREFILL_RB = PREFILL_FORCED + [(511, 640, 516), (256, 1536, 260)]
+
+
+@pytest.mark.parametrize("M,K,N", PREFILL_RB, ids=[f"M{m}-K{k}-N{n}" for m, k, n in PREFILL_RB])
+def test_matmul_prefill_register_b_tile(lib, M, K, N):
+    """The 128 x 256 register tile (weights dequantised in registers): ragged M and N, N not
+    a multiple of 256 or of 64."""
+    print(f"\n[prefill register tile] M={M} K={K} N={N}", flush=True)
+    W = synth.weight_custom(K, N, seed=300 + M, std=0.02)
+    qw, s, z = oracle.quantize_pack(W)
+    x = synth.activations(M, K, wid=9)
+    check_y(run(lib, x, qw, s, z, plan=dict(kernel=lib.W4A16_KERNEL_PREFILL, tile=lib.W4A16_TILE_REGISTER_B)),
+            oracle.matmul(x, qw, s, z), f"prefill register tile M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("g,sym", FORMATS, ids=FMT_IDS)
+@pytest.mark.parametrize("M,K,N", FMT_PREFILL, ids=[f"M{m}-K{k}-N{n}" for m, k, n in FMT_PREFILL])
+def test_matmul_formats_prefill_register_b_tile(lib, M, K, N, g, sym):
+    print(f"\n[format prefill register tile] g={g} sym={sym} M={M} K={K} N={N}", flush=True)
+    qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=400 + M, std=0.02), g, sym)
+    x = synth.activations(M, K, wid=9)
+    check_y(run(lib, x, qw, s, z, plan=dict(kernel=lib.W4A16_KERNEL_PREFILL, tile=lib.W4A16_TILE_REGISTER_B), group_size=g),
+            oracle.matmul(x, qw, s, z, g), f"prefill register tile g={g} sym={sym} M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("M,K,N", PREFILL, ids=[f"M{m}-K{k}-N{n}" for m, k, n in PREFILL])
+def test_matmul_prefill_shapes_register_b_tile_sampled(lib, M, K, N):
+    wid = synth.WORKLOADS["prefill"]["wid"]
+    print(f"\n[prefill register tile] M={M} K={K} N={N}", flush=True)
+    qw, s, z = quantised(K, N, wid)
+    x = synth.activations(M, K, wid=wid)
+    y = run(lib, x, qw, s, z, plan=dict(kernel=lib.W4A16_KERNEL_PREFILL, tile=lib.W4A16_TILE_REGISTER_B))
+    cols = _sample_cols(N)
+    y_ref = oracle.matmul(x, qw[:, cols], s[:, cols], z[:, cols])
+    check_y(y[:, torch.from_numpy(cols).to(DEV)], y_ref, f"prefill register tile M={M} K={K} N={N}")
 
 
 @pytest.mark.parametrize("M,K,N", [(32, 8192, 8192), (128, 8192, 8192)])
@@ -413,13 +451,13 @@ def test_alternating_shapes_reuse_counters(lib):
             check_y(y, oracle.matmul(x, qw, s, z), f"alternating rep {rep}")
 
 
-@pytest.mark.parametrize("kernel", [1, 2])
-def test_exact_closed_form_on_gpu(lib, kernel):
+@pytest.mark.parametrize("kernel,tile", [(1, 0), (2, 1), (2, 2)])
+def test_exact_closed_form_on_gpu(lib, kernel, tile):
     """K=128 exact case (W = ((k+n) mod 16 - 8) / 64): y(ones) = -1 for every column."""
     k = np.arange(128)[:, None]
     n = np.arange(64)[None, :]
     W = (((k + n) % 16 - 8) / 64.0).astype(np.float32)
     qw, s, z = oracle.quantize_pack(W)
     x = np.ones((3, 128), dtype=np.float16)
-    y = run(lib, x, qw, s, z, plan=dict(kernel=kernel)).cpu().numpy()
+    y = run(lib, x, qw, s, z, plan=dict(kernel=kernel, tile=tile)).cpu().numpy()
     assert np.all(y == np.float16(-1.0))

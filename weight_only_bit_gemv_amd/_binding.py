@@ -22,6 +22,8 @@ W4A16_ERR_HIP = -5
 W4A16_KERNEL_AUTO = 0
 W4A16_KERNEL_SKINNY = 1
 W4A16_KERNEL_PREFILL = 2
+W4A16_TILE_LDS = 1
+W4A16_TILE_REGISTER_B = 2
 
 GROUP_SIZE = 128
 

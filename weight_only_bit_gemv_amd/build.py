@@ -21,7 +21,7 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["w4a16_skinny.hip", "w4a16_skinny_lw1.hip", "w4a16_skinny_lw2.hip", "w4a16_skinny_lw4.hip",
-               "w4a16_prefill.hip", "w4a16_dequant.hip"]
+               "w4a16_prefill.hip", "w4a16_prefill_rb.hip", "w4a16_dequant.hip"]
 # The packer must round every fp32 step on its own: no contraction, no fast-math.
 PACK_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math"]
 HIPCC_FLAGS = [
@@ -29,9 +29,9 @@ HIPCC_FLAGS = [
     # keep packed-fp32 VALU instructions out of the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-# MFMA accumulators in ordinary VGPRs (no accvgpr copies around the fp32 epilogue) for the
-# decode kernels, whose accumulators are few; the prefill kernel keeps its 128-256
-# accumulators per lane in AGPRs.
+# MFMA accumulators in ordinary VGPRs for every kernel: in AGPRs the compiler copies
+# accumulators between register files inside the prefill loops (accvgpr moves), which
+# costs more than the registers it frees.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 PER_FILE_FLAGS = {}
 

@@ -151,6 +151,16 @@ constexpr int64_t kPrefillMinM = 65;
 constexpr int64_t kPrefillMinTiles = 128;
 constexpr int64_t kSkinnyMaxM = 1024;
 
+// Prefill tile choice (measured on MI355X): the 128 x 256 tile with the weights in
+// registers reads a third of the LDS bytes per MFMA but has half as many work-groups; it
+// wins once they number at least kRegisterTileMinGroups (1.5 per compute unit), the 128 x
+// 128 LDS tile below that.
+constexpr int64_t kRegisterTileMinGroups = 384;
+
+int32_t auto_prefill_tile(int64_t M, int64_t N) {
+    return ceil_div(M, 128) * ceil_div(N, 256) >= kRegisterTileMinGroups ? W4A16_TILE_REGISTER_B : W4A16_TILE_LDS;
+}
+
 int64_t auto_kernel(int64_t M, int64_t N) {
     if (M < kPrefillMinM) return W4A16_KERNEL_SKINNY;
     const int64_t tiles = ceil_div(M, w4a16::kPrefillBM) * ceil_div(N, w4a16::kPrefillBN);
@@ -161,7 +171,9 @@ int complete_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, w4a16_pla
     const int64_t group_steps = group_size / w4a16::kKStep;
     if (pl->kernel == W4A16_KERNEL_AUTO) pl->kernel = (int32_t)auto_kernel(M, N);
     if (pl->kernel == W4A16_KERNEL_PREFILL) {
-        if (pl->tile != 0) return fail(W4A16_ERR_INVALID_ARG, "prefill tile %d is not built", pl->tile);
+        if (pl->tile == 0) pl->tile = auto_prefill_tile(M, N);
+        if (pl->tile != W4A16_TILE_LDS && pl->tile != W4A16_TILE_REGISTER_B)
+            return fail(W4A16_ERR_INVALID_ARG, "prefill tile %d is not built", pl->tile);
         if (pl->kc || pl->row_tiles || pl->waves || pl->splits || pl->cols || pl->seg)
             return fail(W4A16_ERR_INVALID_ARG, "kc/row_tiles/waves/splits/cols/seg apply to the skinny kernel only");
         if (ceil_div(M, w4a16::kPrefillBM) > 65535) return fail(W4A16_ERR_UNSUPPORTED, "grid too large");
