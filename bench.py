@@ -508,7 +508,9 @@ def run_prefill(args):
             if M >= 32:                  # both prefill tiles
                 forced += [("prefill_lds_tile_us", dict(kernel=lib.W4A16_KERNEL_PREFILL, tile=lib.W4A16_TILE_LDS)),
                            ("prefill_register_tile_us",
-                            dict(kernel=lib.W4A16_KERNEL_PREFILL, tile=lib.W4A16_TILE_REGISTER_B))]
+                            dict(kernel=lib.W4A16_KERNEL_PREFILL, tile=lib.W4A16_TILE_REGISTER_B)),
+                           ("prefill_async_tile_us",
+                            dict(kernel=lib.W4A16_KERNEL_PREFILL, tile=lib.W4A16_TILE_ASYNC))]
             for name, plan in forced:
                 sec, _ = time_graph(torch, stream, lambda: [runner.launch(i, plan) for _ in range(reps)],
                                     2, warm=1)
@@ -531,12 +533,15 @@ def run_prefill(args):
               "roofline": {"bound": "mfma", "achieved": best["w4a16_TFLOPs"],
                            "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(best["w4a16_TFLOPs"] / MFMA_F16_PEAK_TFLOPS, 4),
-                           "traffic": None, "kernel": "prefill_kernel", "shape": [best["M"], best["K"], best["N"]]},
+                           "traffic": None, "kernel": PREFILL_KERNEL_NAMES.get(best["plan"]["tile"], "prefill"),
+                           "shape": [best["M"], best["K"], best["N"]]},
               "rows": rows}
     print(json.dumps(result), flush=True)
 
 
 PREFILL_PMC_SHAPE = (2048, 8192, 28672)      # M, K, N of the prefill counter pass
+PREFILL_KERNEL_NAMES = {1: "prefill_kernel (128x128 LDS tile)", 2: "prefill_rb_kernel (128x256 register tile)",
+                        3: "prefill_async_kernel (128x256, direct-to-LDS ring)"}
 PREFILL_PMC_FILE = os.path.join(ROOT, "profiles", "prefill_counters_M2048_K8192_N28672.json")
 SIMDS = 1024                                  # 256 compute units x 4 SIMDs
 SCLK_GHZ = 2.4
@@ -561,20 +566,21 @@ def run_prefill_pmc_pass(args):
 def summarize_prefill_pmc(dirs):
     """MFMA and LDS counters of the prefill kernel (runs with --kernel-trace and --pmc)."""
     import csv
-    vals, durs = {}, []
+    vals, durs, names = {}, [], set()
     for d in dirs:
         for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for row in csv.DictReader(open(path)):
-                if "prefill_kernel" in row["Kernel_Name"]:
+                if "prefill" in row["Kernel_Name"]:
                     vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+                    names.add(row["Kernel_Name"])
         for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
             for row in csv.DictReader(open(path)):
-                if "prefill_kernel" in row["Kernel_Name"]:
+                if "prefill" in row["Kernel_Name"]:
                     durs.append(int(row["End_Timestamp"]) - int(row["Start_Timestamp"]))
     mean = {k: float(np.mean(v)) for k, v in vals.items()}
     M, K, N = PREFILL_PMC_SHAPE
     dur_ns = float(np.median(durs)) if durs else None
-    out = {"kernel_source_sha": kernel_source_hash(), "shape_MKN": [M, K, N],
+    out = {"kernel_source_sha": kernel_source_hash(), "shape_MKN": [M, K, N], "kernels": sorted(names),
            "counters_mean_per_dispatch": mean, "kernel_ns_median": dur_ns,
            "TFLOPs": round(2 * M * K * N / dur_ns / 1e3, 1) if dur_ns else None}
     if dur_ns and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:

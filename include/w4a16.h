@@ -56,6 +56,8 @@ extern "C" {
 #define W4A16_TILE_LDS         1  /* 128 x 128 output tile, weights and activations in LDS  */
 #define W4A16_TILE_REGISTER_B  2  /* 128 x 256 output tile, weights dequantised in registers,*/
                                   /* activations in LDS (fewer LDS bytes per MFMA)          */
+#define W4A16_TILE_ASYNC       3  /* 128 x 256 output tile, all operands loaded straight     */
+                                  /* into a 3-stage LDS ring (needs N % 8 == 0)             */
 
 /*
  * Execution plan of one w4a16_matmul call (what the dispatcher chose, or what a caller
@@ -67,8 +69,10 @@ extern "C" {
  *              waves; a caller may leave it 0 or give the matching value).
  *   row_tiles  SKINNY: 16-row MFMA tiles per work-group (1..4; default ceil(M/16) <= 4;
  *              at most 2 when cols < 64).
- *   tile       PREFILL: W4A16_TILE_LDS or W4A16_TILE_REGISTER_B (0: chosen from the
- *              number of 128 x 256 output tiles; the register tile once there are >= 384).
+ *   tile       PREFILL: W4A16_TILE_LDS, W4A16_TILE_REGISTER_B or W4A16_TILE_ASYNC (0: chosen
+ *              from the number G of 128 x 256 output tiles: ASYNC when G >= 224 and
+ *              N % 8 == 0, else REGISTER_B when G >= 384, else LDS). W4A16_TILE_ASYNC with
+ *              N % 8 != 0 is UNSUPPORTED.
  *   waves      SKINNY: wavefronts per work-group, 4, 8 or 16 (the cross-wave reduction
  *              must fit in 64 KiB of LDS: (waves-1) * 16*row_tiles * cols * 4 bytes).
  *   cols       SKINNY: output columns per work-group strip, 16, 32 or 64 (each lane loads

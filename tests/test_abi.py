@@ -92,7 +92,7 @@ def test_matmul_ex_rejects_bad_plans():
     so = B.load()
     for kw in [dict(kernel=7), dict(kernel=1, kc=3), dict(kernel=1, kc=6), dict(kernel=1, kc=-4),
                dict(kernel=1, row_tiles=5), dict(kernel=1, waves=6), dict(kernel=1, waves=16, row_tiles=2),
-               dict(kernel=1, kc=4, waves=4, splits=3), dict(kernel=2, tile=3), dict(kernel=2, tile=-1), dict(kernel=2, kc=4),
+               dict(kernel=1, kc=4, waves=4, splits=3), dict(kernel=2, tile=4), dict(kernel=2, tile=-1), dict(kernel=2, kc=4),
                dict(kernel=2, waves=8)]:
         pl = B.w4a16_plan_t(**kw)
         rc = so.w4a16_matmul_ex(P[0], P[1], P[2], P[3], P[4], 1, 64, 128, 128, None,
@@ -115,7 +115,7 @@ def test_dequant_rejects_bad_arguments():
 
 PLAN_SHAPES = [(m, k, n) for m in (1, 2, 4, 8, 16, 17, 33, 64, 65, 128, 2048)
                for (k, n) in [(4096, 4096), (4096, 14336), (14336, 4096), (2048, 1408),
-                              (768, 2048), (4096, 128256), (128, 4), (384, 100)]]
+                              (768, 2048), (4096, 128256), (128, 4), (384, 100), (4096, 28676)]]
 
 
 @pytest.mark.parametrize("M,K,N", PLAN_SHAPES)
@@ -126,8 +126,10 @@ def test_auto_plan_is_valid_and_covers_k(M, K, N):
     expect_prefill = M >= 65 and (tiles >= 128 or M > 1024)
     assert pl["kernel"] == (lib.W4A16_KERNEL_PREFILL if expect_prefill else lib.W4A16_KERNEL_SKINNY)
     if pl["kernel"] == lib.W4A16_KERNEL_PREFILL:
-        regb = -(-M // 128) * -(-N // 256) >= 384
-        assert pl["tile"] == (lib.W4A16_TILE_REGISTER_B if regb else lib.W4A16_TILE_LDS)
+        groups = -(-M // 128) * -(-N // 256)
+        expect = (lib.W4A16_TILE_ASYNC if groups >= 224 and N % 8 == 0 else
+                  lib.W4A16_TILE_REGISTER_B if groups >= 384 else lib.W4A16_TILE_LDS)
+        assert pl["tile"] == expect
     if pl["kernel"] == lib.W4A16_KERNEL_SKINNY:
         kc, splits, W = pl["kc"], pl["splits"], pl["waves"]
         assert kc in (1, 2) or kc % 4 == 0
@@ -193,3 +195,11 @@ def test_python_constants_match_header():
     assert len(defs) >= 11
     for name, value in defs.items():
         assert getattr(lib, name) == value, name
+
+
+def test_async_tile_needs_n_multiple_of_8():
+    with pytest.raises(lib.W4A16Error) as e:
+        lib.w4a16_plan(256, 1412, 1024, kernel=lib.W4A16_KERNEL_PREFILL, tile=lib.W4A16_TILE_ASYNC)
+    assert e.value.code == lib.W4A16_ERR_UNSUPPORTED
+    assert lib.w4a16_plan(256, 1416, 1024, kernel=lib.W4A16_KERNEL_PREFILL,
+                          tile=lib.W4A16_TILE_ASYNC)["tile"] == lib.W4A16_TILE_ASYNC

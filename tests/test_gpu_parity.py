@@ -391,6 +391,63 @@ def test_matmul_prefill_shapes_register_b_tile_sampled(lib, M, K, N):
     check_y(y[:, torch.from_numpy(cols).to(DEV)], y_ref, f"prefill register tile M={M} K={K} N={N}")
 
 
+PREFILL_ASYNC = [(1, 128, 8), (3, 256, 104), (130, 384, 1416), (257, 1408, 264), (64, 768, 2056),
+                 (128, 4096, 256), (200, 128, 136), (129, 2048, 1408), (511, 640, 520), (256, 1536, 264)]
+
+
+@pytest.mark.parametrize("M,K,N", PREFILL_ASYNC, ids=[f"M{m}-K{k}-N{n}" for m, k, n in PREFILL_ASYNC])
+def test_matmul_prefill_async_tile(lib, M, K, N):
+    """The 128 x 256 tile fed by direct global-to-LDS loads (three-stage ring): ragged M and
+    N (multiples of 8, not of 256), K from 2 to 64 stages."""
+    print(f"\n[prefill async tile] M={M} K={K} N={N}", flush=True)
+    W = synth.weight_custom(K, N, seed=500 + M, std=0.02)
+    qw, s, z = oracle.quantize_pack(W)
+    x = synth.activations(M, K, wid=9)
+    check_y(run(lib, x, qw, s, z, plan=dict(kernel=lib.W4A16_KERNEL_PREFILL, tile=lib.W4A16_TILE_ASYNC)),
+            oracle.matmul(x, qw, s, z), f"prefill async tile M={M} K={K} N={N}")
+
+
+FMT_ASYNC = [(3, 256, 104), (130, 512, 1416), (257, 1536, 264), (128, 4096, 256)]
+
+
+@pytest.mark.parametrize("g,sym", FORMATS, ids=FMT_IDS)
+@pytest.mark.parametrize("M,K,N", FMT_ASYNC, ids=[f"M{m}-K{k}-N{n}" for m, k, n in FMT_ASYNC])
+def test_matmul_formats_prefill_async_tile(lib, M, K, N, g, sym):
+    print(f"\n[format prefill async tile] g={g} sym={sym} M={M} K={K} N={N}", flush=True)
+    qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=600 + M, std=0.02), g, sym)
+    x = synth.activations(M, K, wid=9)
+    check_y(run(lib, x, qw, s, z, plan=dict(kernel=lib.W4A16_KERNEL_PREFILL, tile=lib.W4A16_TILE_ASYNC),
+                group_size=g),
+            oracle.matmul(x, qw, s, z, g), f"prefill async tile g={g} sym={sym} M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("M,K,N", PREFILL, ids=[f"M{m}-K{k}-N{n}" for m, k, n in PREFILL])
+def test_matmul_prefill_shapes_async_tile_sampled(lib, M, K, N):
+    wid = synth.WORKLOADS["prefill"]["wid"]
+    print(f"\n[prefill async tile] M={M} K={K} N={N}", flush=True)
+    qw, s, z = quantised(K, N, wid)
+    x = synth.activations(M, K, wid=wid)
+    y = run(lib, x, qw, s, z, plan=dict(kernel=lib.W4A16_KERNEL_PREFILL, tile=lib.W4A16_TILE_ASYNC))
+    cols = _sample_cols(N)
+    y_ref = oracle.matmul(x, qw[:, cols], s[:, cols], z[:, cols])
+    check_y(y[:, torch.from_numpy(cols).to(DEV)], y_ref, f"prefill async tile M={M} K={K} N={N}")
+
+
+def test_prefill_async_tile_repeated_calls_bitwise(lib):
+    """Same inputs, same bits: the ring's waits leave no stage to chance."""
+    M, K, N = 300, 2048, 1032
+    qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=7, std=0.02))
+    x = synth.activations(M, K, wid=9)
+    args = [dev(x), dev(qw), dev(s), dev(z)]
+    plan = dict(kernel=lib.W4A16_KERNEL_PREFILL, tile=lib.W4A16_TILE_ASYNC)
+    a = lib.w4a16_matmul(*args, plan=plan).clone()
+    for _ in range(5):
+        b = lib.w4a16_matmul(*args, plan=plan)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    check_y(a, oracle.matmul(x, qw, s, z), "async repeated")
+
+
 @pytest.mark.parametrize("M,K,N", [(32, 8192, 8192), (128, 8192, 8192)])
 def test_skinny_kernel_on_prefill_shapes(lib, M, K, N):
     """Both kernels must hold the bar where the dispatcher could pick either."""
@@ -451,7 +508,7 @@ def test_alternating_shapes_reuse_counters(lib):
             check_y(y, oracle.matmul(x, qw, s, z), f"alternating rep {rep}")
 
 
-@pytest.mark.parametrize("kernel,tile", [(1, 0), (2, 1), (2, 2)])
+@pytest.mark.parametrize("kernel,tile", [(1, 0), (2, 1), (2, 2), (2, 3)])
 def test_exact_closed_form_on_gpu(lib, kernel, tile):
     """K=128 exact case (W = ((k+n) mod 16 - 8) / 64): y(ones) = -1 for every column."""
     k = np.arange(128)[:, None]

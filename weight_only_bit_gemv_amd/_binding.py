@@ -24,6 +24,7 @@ W4A16_KERNEL_SKINNY = 1
 W4A16_KERNEL_PREFILL = 2
 W4A16_TILE_LDS = 1
 W4A16_TILE_REGISTER_B = 2
+W4A16_TILE_ASYNC = 3
 
 GROUP_SIZE = 128
 

@@ -151,14 +151,19 @@ constexpr int64_t kPrefillMinM = 65;
 constexpr int64_t kPrefillMinTiles = 128;
 constexpr int64_t kSkinnyMaxM = 1024;
 
-// Prefill tile choice (measured on MI355X): the 128 x 256 tile with the weights in
-// registers reads a third of the LDS bytes per MFMA but has half as many work-groups; it
-// wins once they number at least kRegisterTileMinGroups (1.5 per compute unit), the 128 x
-// 128 LDS tile below that.
+// Prefill tile choice (measured on MI355X). The 128 x 256 tiles read a third of the LDS
+// bytes per MFMA of the 128 x 128 tile but have half as many work-groups: the async tile
+// (direct-to-LDS loads) wins once they number at least kAsyncMinGroups; it needs N % 8 == 0,
+// and without it the register tile wins from kRegisterTileMinGroups. Below, the 128 x 128
+// tile.
+constexpr int64_t kAsyncMinGroups = 224;
 constexpr int64_t kRegisterTileMinGroups = 384;
 
 int32_t auto_prefill_tile(int64_t M, int64_t N) {
-    return ceil_div(M, 128) * ceil_div(N, 256) >= kRegisterTileMinGroups ? W4A16_TILE_REGISTER_B : W4A16_TILE_LDS;
+    const int64_t groups = ceil_div(M, 128) * ceil_div(N, 256);
+    if (groups >= kAsyncMinGroups && N % 8 == 0) return W4A16_TILE_ASYNC;
+    if (groups >= kRegisterTileMinGroups) return W4A16_TILE_REGISTER_B;
+    return W4A16_TILE_LDS;
 }
 
 int64_t auto_kernel(int64_t M, int64_t N) {
@@ -172,8 +177,10 @@ int complete_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, w4a16_pla
     if (pl->kernel == W4A16_KERNEL_AUTO) pl->kernel = (int32_t)auto_kernel(M, N);
     if (pl->kernel == W4A16_KERNEL_PREFILL) {
         if (pl->tile == 0) pl->tile = auto_prefill_tile(M, N);
-        if (pl->tile != W4A16_TILE_LDS && pl->tile != W4A16_TILE_REGISTER_B)
+        if (pl->tile != W4A16_TILE_LDS && pl->tile != W4A16_TILE_REGISTER_B && pl->tile != W4A16_TILE_ASYNC)
             return fail(W4A16_ERR_INVALID_ARG, "prefill tile %d is not built", pl->tile);
+        if (pl->tile == W4A16_TILE_ASYNC && N % 8 != 0)
+            return fail(W4A16_ERR_UNSUPPORTED, "the async prefill tile needs N %% 8 == 0 (N=%lld)", (long long)N);
         if (pl->kc || pl->row_tiles || pl->waves || pl->splits || pl->cols || pl->seg)
             return fail(W4A16_ERR_INVALID_ARG, "kc/row_tiles/waves/splits/cols/seg apply to the skinny kernel only");
         if (ceil_div(M, w4a16::kPrefillBM) > 65535) return fail(W4A16_ERR_UNSUPPORTED, "grid too large");

@@ -68,12 +68,13 @@ struct PrefillParams {
     const uint16_t* zeros;    // fp16 [K/g, N]
     uint16_t* y;              // fp16 [M, N]
     int M, N, K;
-    int tile;                 // W4A16_TILE_LDS (128 x 128) or W4A16_TILE_REGISTER_B (128 x 256)
+    int tile;                 // W4A16_TILE_LDS, W4A16_TILE_REGISTER_B or W4A16_TILE_ASYNC
     int group_shift;          // log2(rows per scale/zero group)
 };
 
 int launch_prefill(const PrefillParams& p, void* stream);  // returns a hipError_t value
 int launch_prefill_rb(const PrefillParams& p, void* stream);  // W4A16_TILE_REGISTER_B (w4a16_prefill_rb.hip)
+int launch_prefill_async(const PrefillParams& p, void* stream);  // W4A16_TILE_ASYNC (w4a16_prefill_async.hip)
 
 // ---- dequant hook (w4a16_dequant.hip) ----
 int launch_dequant(const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,

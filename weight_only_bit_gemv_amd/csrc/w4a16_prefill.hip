@@ -208,6 +208,7 @@ __global__ __launch_bounds__(NT, OCC) void prefill_kernel(PrefillParams p) {
 int launch_prefill(const PrefillParams& p, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (p.tile == W4A16_TILE_REGISTER_B) return launch_prefill_rb(p, stream);
+    if (p.tile == W4A16_TILE_ASYNC) return launch_prefill_async(p, stream);
     if (p.tile != W4A16_TILE_LDS) return (int)hipErrorInvalidValue;
     const dim3 grid((unsigned)((p.N + kPrefillBN - 1) / kPrefillBN), (unsigned)((p.M + kPrefillBM - 1) / kPrefillBM));
     hipLaunchKernelGGL((prefill_kernel<kPrefillBM, kPrefillBN, 2>), grid, dim3(NT), 0, s, p);
