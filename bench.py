@@ -56,8 +56,15 @@ SWEEP_KN = [(4096, 14336), (14336, 4096), (4096, 4096)]
 SWEEP_M = [1, 2, 4, 8, 16]
 ROTATE_BYTES = 1 << 30         # >= 4x the 256 MB Infinity Cache per shape family
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_skinny_decode_sweep.json")
+# sources that decide what the decode kernel does (kernel, unpack helpers, plan table): the
+# committed traffic counters stay valid while these are unchanged
 KERNEL_SOURCES = sorted(os.path.relpath(f, ROOT) for f in
-                        glob.glob(os.path.join(ROOT, "weight_only_bit_gemv_amd", "csrc", "*")))
+                        glob.glob(os.path.join(ROOT, "weight_only_bit_gemv_amd", "csrc", "w4a16_skinny*")) +
+                        [os.path.join(ROOT, "weight_only_bit_gemv_amd", "csrc", n)
+                         for n in ("w4a16_device.hpp", "w4a16_api.cpp")])
+PREFILL_SOURCES = sorted(os.path.relpath(f, ROOT) for f in
+                         glob.glob(os.path.join(ROOT, "weight_only_bit_gemv_amd", "csrc", "w4a16_prefill*")) +
+                         [os.path.join(ROOT, "weight_only_bit_gemv_amd", "csrc", "w4a16_device.hpp")])
 COPY_CAL_BYTES = 256 << 20     # calibration copy for the PMC byte counters
 METRIC = "W4A16 weight-stream HBM GB/s (% of peak) and us/call at M=1..16"
 
@@ -67,9 +74,9 @@ def alg_bytes(M, K, N, group=GROUP):
     return K * N // 2 + 2 * 2 * (K // group) * N + 2 * M * K + 2 * M * N
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=None):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -580,7 +587,7 @@ def summarize_prefill_pmc(dirs):
     mean = {k: float(np.mean(v)) for k, v in vals.items()}
     M, K, N = PREFILL_PMC_SHAPE
     dur_ns = float(np.median(durs)) if durs else None
-    out = {"kernel_source_sha": kernel_source_hash(), "shape_MKN": [M, K, N], "kernels": sorted(names),
+    out = {"kernel_source_sha": kernel_source_hash(PREFILL_SOURCES), "shape_MKN": [M, K, N], "kernels": sorted(names),
            "counters_mean_per_dispatch": mean, "kernel_ns_median": dur_ns,
            "TFLOPs": round(2 * M * K * N / dur_ns / 1e3, 1) if dur_ns else None}
     if dur_ns and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
