@@ -314,6 +314,32 @@ def dense_time(torch, x, ws, y, stream, reps):
     return e0.elapsed_time(e1) / 1e3 / reps
 
 
+def dequant_time(torch, lib, runner, key, stream, reps=4):
+    """Seconds per w4a16_dequant call writing the fp16 weights [K, N] (the first half of a
+    dequantise-then-dense-GEMM path), rotating over the weight copies."""
+    K, N = runner.weights[key][0][0].shape[0] * 8, runner.weights[key][0][0].shape[1]
+    w16 = torch.empty((K, N), dtype=torch.float16, device=runner.dev)
+    so = lib.load()
+
+    def call(i):
+        qw, s, z = runner.weights[key][i % len(runner.weights[key])]
+        rc = so.w4a16_dequant(qw.data_ptr(), s.data_ptr(), z.data_ptr(), None, w16.data_ptr(), N, K,
+                              runner.group, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"w4a16_dequant failed ({rc})")
+    with torch.cuda.stream(stream):
+        for i in range(2):
+            call(i)
+        stream.synchronize()
+        e0, e1 = events(torch, stream)
+        e0.record(stream)
+        for i in range(reps):
+            call(i)
+        e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / reps
+
+
 def dense_weights(torch, lib, runner, key):
     """fp16 weights [K, N] equal to the GPU's dequantised values, rotated like the int4 ones."""
     qw, s, z = runner.weights[key][0]
@@ -495,6 +521,7 @@ def run_prefill(args):
             runner.step()
         stream.synchronize()
         ws = dense_weights(torch, lib, runner, (K, N))
+        dq = dequant_time(torch, lib, runner, (K, N), stream)
         cross = None
         for i, M in enumerate(ms):
             log(f"[prefill] K={K} N={N} M={M}")
@@ -508,6 +535,8 @@ def run_prefill(args):
                    "w4a16_TFLOPs": round(fl / t / 1e12, 2), "w4a16_GBps": round(alg_bytes(M, K, N, args.group_size) / t / 1e9, 1),
                    "dense_fp16_us": round(d * 1e6, 2), "dense_TFLOPs": round(fl / d / 1e12, 2),
                    "speedup_vs_dense": round(d / t, 3),
+                   # dequantise to fp16 with the library's kernel, then the dense GEMM
+                   "dequant_then_dense_us": round((dq + d) * 1e6, 2),
                    "plan": lib.w4a16_plan(M, N, K, group_size=args.group_size)}
             forced = []
             if 32 <= M <= 512:           # both kernels, where the dispatcher's threshold lies

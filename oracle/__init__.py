@@ -4,5 +4,5 @@ This package is test infrastructure. Only the tests, the smoke entry point and t
 benchmark's CPU-baseline leg may import it; the product path never does.
 """
 from .w4a16_oracle import (  # noqa: F401
-    GROUP_SIZE, quantize, pack, unpack, dequant, dequant_fp16, matmul, quantize_pack,
+    GROUP_SIZE, NIBBLE_K, quantize, pack, unpack, dequant, dequant_fp16, matmul, quantize_pack,
 )

@@ -17,7 +17,7 @@ Sources (the pages this follows):
   [P1] section "Code": the tests cover several group sizes and both symmetric and
        asymmetric quantisation.
 
-Readings taken where the pages are silent (each one is listed in the design doc):
+Readings taken where the pages are silent:
   R1  W is laid out [K, N] (input x output), so y[M,N] = x[M,K] @ W[K,N].
   R2  Asymmetric min/max quantisation per (K-group, column): scale = (max-min)/15 stored
       as fp16 (round-to-nearest-even), zero = round(-min/scale) using the stored fp16
@@ -31,6 +31,12 @@ Readings taken where the pages are silent (each one is listed in the design doc):
   R7  Symmetric mode: scale = max|w|/7 per (K-group, column) stored as fp16 (rne; 1.0 when
       it rounds to zero), zero = 8, q = clamp(round(w/scale) + 8, 0, 15); the same fp32
       steps as R2. Group sizes are multiples of 8 here (the library takes 32, 64, 128, 256).
+  R8  Interleaved layout ([P1] "What's next": pre-permute the weights offline so they
+      reach the matrix instruction in the order it wants, with no runtime reshape): nibble p
+      of packed word i holds K index 8i + NIBBLE_K["interleaved"][p] = 8i + (0, 2, 4, 6, 1,
+      3, 5, 7)[p], i.e. even K offsets in nibbles 0..3 and odd ones in nibbles 4..7. Codes,
+      scales, zeros and the product are those of the linear layout; only the word packing
+      differs.
 Everything the GPU path must reproduce bit for bit (codes, fp16 dequant) is defined
 here; the matmul is defined in fp64 on the exact fp32 dequantised weights.
 
@@ -125,10 +131,18 @@ def _quantize_symmetric(W, group_size):
     return codes, s16, z16
 
 
-def pack(codes):
-    """Pack codes [K, N] (values 0..15) into int32 words [K/8, N]; nibble j at shift 4j (R3).
+# K offset (within the word's 8 K indices) held by nibble p (bits 4p..4p+3) of a word
+NIBBLE_K = {
+    "linear": (0, 1, 2, 3, 4, 5, 6, 7),        # R3: [P1] "The design", nibble j <-> K 8i + j
+    "interleaved": (0, 2, 4, 6, 1, 3, 5, 7),   # R8
+}
 
-    [P1] "The design": packed row i, nibble j holds K index 8*i + j.
+
+def pack(codes, layout="linear"):
+    """Pack codes [K, N] (values 0..15) into int32 words [K/8, N].
+
+    linear ([P1] "The design", R3): packed row i, nibble j holds K index 8*i + j.
+    interleaved (R8): nibble p holds K index 8*i + NIBBLE_K["interleaved"][p].
     """
     codes = np.asarray(codes)
     K, N = codes.shape
@@ -137,18 +151,18 @@ def pack(codes):
     if codes.max(initial=0) > QMAX:
         raise ValueError("codes must lie in 0..15")
     words = np.zeros((K // NIBBLES_PER_WORD, N), dtype=np.uint32)
-    for j in range(NIBBLES_PER_WORD):
-        words |= codes[j::NIBBLES_PER_WORD, :].astype(np.uint32) << np.uint32(4 * j)
+    for p, k in enumerate(NIBBLE_K[layout]):
+        words |= codes[k::NIBBLES_PER_WORD, :].astype(np.uint32) << np.uint32(4 * p)
     return words.view(np.int32)
 
 
-def unpack(qweight):
+def unpack(qweight, layout="linear"):
     """Inverse of pack: int32 [K/8, N] -> uint8 codes [K, N]. Shifts an unsigned view."""
     words = np.asarray(qweight).view(np.uint32)
     P, N = words.shape
     codes = np.zeros((P * NIBBLES_PER_WORD, N), dtype=np.uint8)
-    for j in range(NIBBLES_PER_WORD):
-        codes[j::NIBBLES_PER_WORD, :] = (words >> np.uint32(4 * j)) & np.uint32(0xF)
+    for p, k in enumerate(NIBBLE_K[layout]):
+        codes[k::NIBBLES_PER_WORD, :] = (words >> np.uint32(4 * p)) & np.uint32(0xF)
     return codes
 
 
@@ -172,7 +186,7 @@ def dequant_fp16(codes, scales, zeros, group_size=GROUP_SIZE):
     return dequant(codes, scales, zeros, group_size).astype(np.float16)
 
 
-def matmul(x, qweight, scales, zeros, group_size=GROUP_SIZE):
+def matmul(x, qweight, scales, zeros, group_size=GROUP_SIZE, layout="linear"):
     """y[m, n] = sum_k x[m, k] * dequant(W)[k, n], accumulated in fp64.
 
     x: fp16 [M, K]. Returns fp64 [M, N]. Every product of an fp16 activation and an fp32
@@ -181,14 +195,14 @@ def matmul(x, qweight, scales, zeros, group_size=GROUP_SIZE):
     x = np.asarray(x)
     if x.dtype != np.float16 or x.ndim != 2:
         raise ValueError("x must be a 2-D float16 array")
-    codes = unpack(qweight)
+    codes = unpack(qweight, layout)
     if x.shape[1] != codes.shape[0]:
         raise ValueError("x and qweight disagree on K")
     w = dequant(codes, scales, zeros, group_size).astype(np.float64)
     return x.astype(np.float64) @ w
 
 
-def quantize_pack(W, group_size=GROUP_SIZE, symmetric=False):
+def quantize_pack(W, group_size=GROUP_SIZE, symmetric=False, layout="linear"):
     """quantize then pack: W fp32 [K, N] -> (qweight int32 [K/8, N], scales, zeros)."""
     codes, s16, z16 = quantize(W, group_size, symmetric)
-    return pack(codes), s16, z16
+    return pack(codes, layout), s16, z16

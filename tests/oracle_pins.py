@@ -286,6 +286,32 @@ def pin_symmetric_bounds(o):
         assert np.all(np.abs(Wg - deq) <= 0.5 * s[:, None, :] * (1 + 2.0 ** -10) + slack)
 
 
-ALL_PINS = [pin_hand_words, pin_roundtrip, pin_exact_group, pin_exact_products,
+def pin_interleaved_words(o):
+    """Interleaved layout, words worked out by hand: nibble p holds K offset
+    (0, 2, 4, 6, 1, 3, 5, 7)[p] of its 8 K indices (even offsets low, odd offsets high)."""
+    codes = np.zeros((8, 5), dtype=np.uint8)
+    codes[:, 0] = np.arange(8)          # code k at K offset k -> nibbles 0,2,4,6,1,3,5,7 -> 0x75316420
+    codes[1, 1] = 1                     # K offset 1 -> nibble 4 -> 0x00010000
+    codes[7, 2] = 8                     # K offset 7 -> nibble 7 -> 0x80000000
+    codes[2, 3] = 0xA                   # K offset 2 -> nibble 1 -> 0x000000A0
+    codes[6, 4] = 0x3                   # K offset 6 -> nibble 3 -> 0x00003000
+    words = o.pack(codes, "interleaved")
+    expect = np.array([[0x75316420, 0x10000, -2**31, 0xA0, 0x3000]], dtype=np.int64)
+    assert np.array_equal(words.astype(np.int64), expect), [hex(int(w) & 0xFFFFFFFF) for w in words[0]]
+    assert np.array_equal(o.unpack(words, "interleaved"), codes)
+    for K, N, seed in [(8, 3, 4), (128, 17, 5)]:
+        c = synth.uniform_codes(K, N, seed)
+        assert np.array_equal(o.unpack(o.pack(c, "interleaved"), "interleaved"), c)
+    # same codes, other packing: the product is the linear layout's, exactly
+    W = synth.weight_custom(256, 12, seed=9, std=0.02)
+    x = synth.activations(3, 256, wid=6)
+    ql, s, z = o.quantize_pack(W)
+    qi, s2, z2 = o.quantize_pack(W, layout="interleaved")
+    assert np.array_equal(s, s2) and np.array_equal(z, z2)
+    assert not np.array_equal(ql, qi)
+    assert np.array_equal(o.matmul(x, ql, s, z), o.matmul(x, qi, s, z, layout="interleaved"))
+
+
+ALL_PINS = [pin_hand_words, pin_interleaved_words, pin_roundtrip, pin_exact_group, pin_exact_products,
             pin_multigroup, pin_bounds_random, pin_fsum, pin_dequant_fp16_rounding,
             pin_scale_rounding, pin_group_sizes, pin_symmetric_exact, pin_symmetric_bounds]

@@ -17,13 +17,17 @@ SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__
 MUTANTS = [
     # packing / unpacking
     ("nibble order reversed in pack",
-     "codes[j::NIBBLES_PER_WORD, :].astype(np.uint32) << np.uint32(4 * j)",
-     "codes[j::NIBBLES_PER_WORD, :].astype(np.uint32) << np.uint32(4 * (7 - j))"),
+     "codes[k::NIBBLES_PER_WORD, :].astype(np.uint32) << np.uint32(4 * p)",
+     "codes[k::NIBBLES_PER_WORD, :].astype(np.uint32) << np.uint32(4 * (7 - p))"),
     ("nibble order reversed in both pack and unpack",
-     "np.uint32(4 * j)", "np.uint32(4 * (7 - j))"),
+     "np.uint32(4 * p)", "np.uint32(4 * (7 - p))"),
     ("K split into 8 planes instead of 8 consecutive rows (pack and unpack)",
-     [("words |= codes[j::NIBBLES_PER_WORD, :]", "words |= codes[j * (K // 8):(j + 1) * (K // 8), :]"),
-      ("codes[j::NIBBLES_PER_WORD, :] = (words", "codes[j * P:(j + 1) * P, :] = (words")], None),
+     [("words |= codes[k::NIBBLES_PER_WORD, :]", "words |= codes[k * (K // 8):(k + 1) * (K // 8), :]"),
+      ("codes[k::NIBBLES_PER_WORD, :] = (words", "codes[k * P:(k + 1) * P, :] = (words")], None),
+    ("interleaved map inverted (the K-offset -> nibble map used as nibble -> K offset)",
+     '"interleaved": (0, 2, 4, 6, 1, 3, 5, 7)', '"interleaved": (0, 4, 1, 5, 2, 6, 3, 7)'),
+    ("matmul unpacks every layout as linear",
+     "codes = unpack(qweight, layout)", "codes = unpack(qweight)"),
     ("unpack mask 0x7",
      "& np.uint32(0xF)", "& np.uint32(0x7)"),
     # quantiser
