@@ -97,9 +97,10 @@ class Runner:
     """
 
     def __init__(self, torch, lib, dev, stream, families, items, rotate_bytes, replicate=None,
-                 group=GROUP, symmetric=False):
+                 group=GROUP, symmetric=False, layout="linear"):
         self.torch, self.lib, self.dev, self.stream = torch, lib, dev, stream
-        self.group, self.symmetric = group, symmetric
+        self.group, self.symmetric, self.layout = group, symmetric, layout
+        self.layout_id = lib._binding._layout_id(layout)
         self.weights, self.host = {}, {}
         packed = {}
         for key, (K, N, wid, layer) in families.items():
@@ -111,7 +112,8 @@ class Runner:
             t0 = time.time()
             if (K, N, wid, layer) not in packed:
                 W = synth.weight(K, N, wid=wid, layer=layer)
-                packed[(K, N, wid, layer)] = lib.w4a16_pack(W, group_size=group, symmetric=symmetric)
+                packed[(K, N, wid, layer)] = lib.w4a16_pack(W, group_size=group, symmetric=symmetric,
+                                                            layout=layout)
                 del W
             qw, s, z = packed[(K, N, wid, layer)]
             self.host[key] = (qw, s, z)
@@ -130,8 +132,7 @@ class Runner:
         self.y = [torch.empty((M, N), dtype=torch.float16, device=dev) for (M, K, N, key) in items]
         self.cursor = {key: 0 for key in families}
         self.step_bytes = sum(alg_bytes(M, K, N, group) for (M, K, N, key) in items)
-        self.fn = lib.load().w4a16_matmul
-        self.fn_ex = lib.load().w4a16_matmul_ex
+        self.fn = lib.load().w4a16_matmul_fmt
         self.plans = {}
         self.sptr = stream.cuda_stream
 
@@ -142,14 +143,14 @@ class Runner:
         self.cursor[key] = (c + 1) % len(self.weights[key])
         qw, s, z = self.weights[key][c]
         args = (self.xk[i].data_ptr(), qw.data_ptr(), s.data_ptr(), z.data_ptr(),
-                self.y[i].data_ptr(), M, N, K, self.group, self.sptr)
+                self.y[i].data_ptr(), M, N, K, self.group, self.layout_id, self.sptr)
         if plan is None:
-            rc = self.fn(*args)
+            rc = self.fn(*args, None)
         else:
             key_p = tuple(sorted(plan.items()))
             if key_p not in self.plans:
                 self.plans[key_p] = self.lib._binding._make_plan(plan)
-            rc = self.fn_ex(*args, ctypes.byref(self.plans[key_p]))
+            rc = self.fn(*args, ctypes.byref(self.plans[key_p]))
         if rc != 0:
             raise RuntimeError(f"w4a16_matmul failed ({rc}) for M={M} K={K} N={N}")
 
@@ -323,8 +324,8 @@ def dequant_time(torch, lib, runner, key, stream, reps=4):
 
     def call(i):
         qw, s, z = runner.weights[key][i % len(runner.weights[key])]
-        rc = so.w4a16_dequant(qw.data_ptr(), s.data_ptr(), z.data_ptr(), None, w16.data_ptr(), N, K,
-                              runner.group, stream.cuda_stream)
+        rc = so.w4a16_dequant_fmt(qw.data_ptr(), s.data_ptr(), z.data_ptr(), None, w16.data_ptr(), N, K,
+                                  runner.group, runner.layout_id, stream.cuda_stream)
         if rc != 0:
             raise RuntimeError(f"w4a16_dequant failed ({rc})")
     with torch.cuda.stream(stream):
@@ -343,7 +344,7 @@ def dequant_time(torch, lib, runner, key, stream, reps=4):
 def dense_weights(torch, lib, runner, key):
     """fp16 weights [K, N] equal to the GPU's dequantised values, rotated like the int4 ones."""
     qw, s, z = runner.weights[key][0]
-    _, w16 = lib.w4a16_dequant(qw, s, z, codes=False, group_size=runner.group)
+    _, w16 = lib.w4a16_dequant(qw, s, z, codes=False, group_size=runner.group, layout=runner.layout)
     copies = max(2, -(-ROTATE_BYTES // (w16.numel() * 2)))
     return [w16] + [w16.clone() for _ in range(copies - 1)]
 
@@ -361,7 +362,7 @@ def cpu_baseline(runner, wid):
     for (M, K, N, key) in runner.items:
         qw, s, z = runner.host[key]
         x = synth.activations(M, K, wid=wid)
-        oracle.matmul(x, qw, s, z, runner.group)
+        oracle.matmul(x, qw, s, z, runner.group, layout=runner.layout)
         total_bytes += alg_bytes(M, K, N, runner.group)
     dt = time.perf_counter() - t0
     return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": blas_threads,
@@ -436,11 +437,11 @@ def run_decode(args):
     fam, items, desc, replicate = workload_items(args.workload)
     rotate = 0 if args.workload == "chain_7b" else ROTATE_BYTES
     runner = Runner(torch, lib, dev, stream, fam, items, rotate, replicate, args.group_size,
-                    args.symmetric)
-    if args.group_size != GROUP or args.symmetric:
+                    args.symmetric, args.layout)
+    if args.group_size != GROUP or args.symmetric or args.layout != "linear":
         desc = (desc.replace("per 128-row group", "").rstrip(", ") +
                 f"; weight format: {'symmetric (zero 8)' if args.symmetric else 'asymmetric'}, "
-                f"group {args.group_size}")
+                f"group {args.group_size}, {args.layout} layout")
     launches = len(items)
     steps = args.steps if args.workload != "chain_7b" else max(1, args.steps // 10)
     elapsed = timed_steps(torch, runner, steps, args.warmup)
@@ -477,14 +478,15 @@ def run_decode(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": desc, "group_size": args.group_size, "symmetric": args.symmetric,
+                   "layout": args.layout,
                    "launches_per_step": launches, "bytes_per_step": runner.step_bytes,
                    "timing": "HIP graph of all steps, events on the launch stream",
                    "weight_copies_rotated": {str(k): len(v) for k, v in runner.weights.items()
                                              if args.workload != "chain_7b"}},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": (load_traffic() if args.workload == "decode_sweep"
-                                 and args.group_size == GROUP and not args.symmetric else None),
+                     "traffic": (load_traffic() if args.workload == "decode_sweep" and args.group_size == GROUP
+                                 and not args.symmetric and args.layout == "linear" else None),
                      "kernel": "skinny_kernel (decode weight stream, MFMA, split-K when K is deep)",
                      "avg_launch_us": round(avg_launch_s * 1e6, 3)},
         "measured_copy_GBps": round(copy_gbs, 1),
@@ -516,7 +518,7 @@ def run_prefill(args):
         fam = {(K, N): (K, N, wid, 0)}
         items = [(M, K, N, (K, N)) for M in ms]
         runner = Runner(torch, lib, dev, stream, fam, items, ROTATE_BYTES // 2, None, args.group_size,
-                        args.symmetric)
+                        args.symmetric, args.layout)
         with torch.cuda.stream(stream):
             runner.step()
         stream.synchronize()
@@ -565,7 +567,7 @@ def run_prefill(args):
               "vs_baseline": None, "dtype": "f16", "data": "synthetic",
               "config": {"workload": "prefill crossover: M in 1..2048 on (8192,8192),(8192,28672),"
                                      "(28672,8192) and the decode-sweep shapes",
-                         "group_size": args.group_size, "symmetric": args.symmetric},
+                         "group_size": args.group_size, "symmetric": args.symmetric, "layout": args.layout},
               "roofline": {"bound": "mfma", "achieved": best["w4a16_TFLOPs"],
                            "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(best["w4a16_TFLOPs"] / MFMA_F16_PEAK_TFLOPS, 4),
@@ -704,6 +706,8 @@ def main():
                     help="K rows per scale/zero group (decode workloads)")
     ap.add_argument("--symmetric", action="store_true",
                     help="symmetric quantiser (zero point 8) instead of min/max (decode workloads)")
+    ap.add_argument("--layout", default="linear", choices=["linear", "interleaved"],
+                    help="packing of the 4-bit codes in each int32 word")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense fp16 baseline")
     ap.add_argument("--pmc-pass", action="store_true")

@@ -52,6 +52,16 @@ extern "C" {
 #define W4A16_KERNEL_SKINNY   1   /* decode: weight stream, split-K, M <= 64 per row block  */
 #define W4A16_KERNEL_PREFILL  2   /* prefill: fp16 dequant tiles feeding MFMA (tile below)  */
 
+/* Packed-weight layouts: which K offset of its 8 K indices nibble p (bits 4p..4p+3) of a
+ * packed word holds. Codes, scales and zeros are the same in both; only the packing differs.
+ * LINEAR: offset p ("The design": packed row i, nibble j holds K index 8i + j).
+ * INTERLEAVED: offset (0, 2, 4, 6, 1, 3, 5, 7)[p] - even offsets in the low nibbles, odd
+ * in the high ones: the order in which the kernels' fp16 unpack yields consecutive K
+ * values, so neither operand is permuted (weights pre-permuted offline, as "Beating FP16
+ * with 4-bit Weights", section "What's next", proposes). */
+#define W4A16_LAYOUT_LINEAR       0
+#define W4A16_LAYOUT_INTERLEAVED  1
+
 /* Prefill tile configurations (w4a16_plan_t.tile; 0 = the dispatcher's choice). */
 #define W4A16_TILE_LDS         1  /* 128 x 128 output tile, weights and activations in LDS  */
 #define W4A16_TILE_REGISTER_B  2  /* 128 x 256 output tile, weights dequantised in registers,*/
@@ -129,11 +139,12 @@ int w4a16_pack(const float* W, int64_t K, int64_t N, int64_t group_size,
  *                 with the same fp32 steps. The output layout is unchanged (zeros holds 8),
  *                 so w4a16_matmul runs both kinds of weights.
  *   group_size 32, 64, 128 or 256.
+ *   layout     W4A16_LAYOUT_LINEAR or W4A16_LAYOUT_INTERLEAVED (packing of qweight).
  * Other arguments, errors and ownership as w4a16_pack; INVALID_ARG when symmetric is not
- * 0 or 1.
+ * 0 or 1 or layout is not a W4A16_LAYOUT_* value.
  */
 int w4a16_pack_ex(const float* W, int64_t K, int64_t N, int64_t group_size, int symmetric,
-                  int32_t* qweight, uint16_t* scales, uint16_t* zeros);
+                  int layout, int32_t* qweight, uint16_t* scales, uint16_t* zeros);
 
 /*
  * w4a16_unpack - host inverse of the packing: codes[8i + j, n] = (qweight[i, n] >> 4j) & 15.
@@ -141,6 +152,10 @@ int w4a16_pack_ex(const float* W, int64_t K, int64_t N, int64_t group_size, int 
  * Errors: INVALID_ARG.
  */
 int w4a16_unpack(const int32_t* qweight, int64_t K, int64_t N, uint8_t* codes);
+
+/* w4a16_unpack_ex - w4a16_unpack for either layout (codes in natural K order).
+ * Errors: INVALID_ARG (also for an unknown layout). */
+int w4a16_unpack_ex(const int32_t* qweight, int64_t K, int64_t N, int layout, uint8_t* codes);
 
 /*
  * w4a16_matmul - y = x . dequant(qweight, scales, zeros) on the GPU ("The design": the
@@ -175,6 +190,17 @@ int w4a16_matmul_ex(const void* x, const int32_t* qweight, const void* scales,
                     int64_t group_size, void* stream, const w4a16_plan_t* plan);
 
 /*
+ * w4a16_matmul_fmt - the general entry point: w4a16_matmul_ex for weights packed in either
+ * layout (w4a16_matmul and w4a16_matmul_ex are this call with W4A16_LAYOUT_LINEAR).
+ *   layout  W4A16_LAYOUT_LINEAR or W4A16_LAYOUT_INTERLEAVED, as given to w4a16_pack_ex
+ *   plan    NULL or a plan as for w4a16_matmul_ex
+ * Errors as w4a16_matmul_ex, plus INVALID_ARG for an unknown layout.
+ */
+int w4a16_matmul_fmt(const void* x, const int32_t* qweight, const void* scales,
+                     const void* zeros, void* y, int64_t M, int64_t N, int64_t K,
+                     int64_t group_size, int layout, void* stream, const w4a16_plan_t* plan);
+
+/*
  * w4a16_plan - the plan w4a16_matmul would use for (M, N, K, group_size), or the completed
  * version of a forced plan when `plan->kernel` is non-zero on entry. Host only; no HIP call.
  * Errors: INVALID_ARG, UNSUPPORTED.
@@ -183,7 +209,8 @@ int w4a16_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, w4a16_plan_t
 
 /*
  * w4a16_dequant - the GPU's unpack/dequant, exposed for bit-exact checks.
- *   codes  device uint8 [K, N] or NULL: codes[8i + j, n] = nibble j of qweight[i, n]
+ *   codes  device uint8 [K, N] or NULL, 4-byte aligned: codes[8i + j, n] = nibble j of
+ *          qweight[i, n]
  *   w      device fp16 [K, N] or NULL: fp16_rne((q - zero) * scale), i.e. one rounding of
  *          the exact product (the fp16 weight the prefill kernel stages in LDS)
  *   qweight, scales, zeros as for w4a16_matmul; N % 4 == 0, K % 128 == 0,
@@ -193,6 +220,13 @@ int w4a16_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, w4a16_plan_t
 int w4a16_dequant(const int32_t* qweight, const void* scales, const void* zeros,
                   uint8_t* codes, void* w, int64_t N, int64_t K, int64_t group_size,
                   void* stream);
+
+/* w4a16_dequant_fmt - w4a16_dequant for weights packed in either layout; codes and w are
+ * in natural K order whatever the layout. Errors as w4a16_dequant, plus INVALID_ARG for an
+ * unknown layout. */
+int w4a16_dequant_fmt(const int32_t* qweight, const void* scales, const void* zeros,
+                      uint8_t* codes, void* w, int64_t N, int64_t K, int64_t group_size,
+                      int layout, void* stream);
 
 /* w4a16_strerror - static description of an error code (never NULL). */
 const char* w4a16_strerror(int code);

@@ -23,7 +23,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ["w4a16_pack", "w4a16_pack_ex", "w4a16_matmul", "w4a16_matmul_ex", "w4a16_plan",
+    for required in ["w4a16_pack", "w4a16_pack_ex", "w4a16_unpack_ex", "w4a16_matmul_fmt",
+                     "w4a16_dequant_fmt", "w4a16_matmul", "w4a16_matmul_ex", "w4a16_plan",
                      "w4a16_dequant", "w4a16_unpack", "w4a16_strerror"]:
         assert required in names
 
@@ -203,3 +204,13 @@ def test_async_tile_needs_n_multiple_of_8():
     assert e.value.code == lib.W4A16_ERR_UNSUPPORTED
     assert lib.w4a16_plan(256, 1416, 1024, kernel=lib.W4A16_KERNEL_PREFILL,
                           tile=lib.W4A16_TILE_ASYNC)["tile"] == lib.W4A16_TILE_ASYNC
+
+
+def test_fmt_entry_points_reject_unknown_layout_and_misaligned_codes():
+    so = B.load()
+    assert so.w4a16_matmul_fmt(P[0], P[1], P[2], P[3], P[4], 1, 64, 128, 128, 2, None, None) == \
+        lib.W4A16_ERR_INVALID_ARG
+    assert so.w4a16_dequant_fmt(P[0], P[1], P[2], None, P[4], 64, 128, 128, -1, None) == \
+        lib.W4A16_ERR_INVALID_ARG
+    assert so.w4a16_dequant_fmt(P[0], P[1], P[2], ctypes.c_void_p(A + 2), None, 64, 128, 128, 0, None) == \
+        lib.W4A16_ERR_ALIGNMENT

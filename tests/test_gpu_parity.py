@@ -57,12 +57,12 @@ def check_y(y_gpu, y_ref, what=""):
     return float(err.max())
 
 
-def run(lib, x, qw, s, z, plan=None, y=None, stream=None, group_size=128):
+def run(lib, x, qw, s, z, plan=None, y=None, stream=None, group_size=128, layout="linear"):
     out = lib.w4a16_matmul(dev(x) if isinstance(x, np.ndarray) else x,
                            dev(qw) if isinstance(qw, np.ndarray) else qw,
                            dev(s) if isinstance(s, np.ndarray) else s,
                            dev(z) if isinstance(z, np.ndarray) else z,
-                           y=y, plan=plan, stream=stream, group_size=group_size)
+                           y=y, plan=plan, stream=stream, group_size=group_size, layout=layout)
     torch.cuda.synchronize()
     return out
 
@@ -446,6 +446,69 @@ def test_prefill_async_tile_repeated_calls_bitwise(lib):
         torch.cuda.synchronize()
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     check_y(a, oracle.matmul(x, qw, s, z), "async repeated")
+
+
+# ---------------------------------------------------------------------------------------
+# interleaved (pre-permuted) weight layout: every kernel, against the oracle
+
+@pytest.mark.parametrize("g", [32, 128])
+def test_dequant_bit_exact_interleaved(lib, g):
+    W = synth.weight_custom(768, 200, seed=40 + g, std=0.02)
+    qw, s, z = oracle.quantize_pack(W, g, layout="interleaved")
+    print(f"\n[dequant interleaved] g={g}", flush=True)
+    c, w = lib.w4a16_dequant(dev(qw), dev(s), dev(z), group_size=g, layout="interleaved")
+    torch.cuda.synchronize()
+    codes_ref = oracle.unpack(qw, "interleaved")
+    assert np.array_equal(c.cpu().numpy(), codes_ref)
+    w_ref = oracle.dequant_fp16(codes_ref, s, z, g)
+    assert np.array_equal(w.cpu().numpy().view(np.uint16), w_ref.view(np.uint16))
+
+
+IL_SHAPES = [(1, 4096, 4096), (5, 4096, 14336), (16, 14336, 4096), (37, 1024, 320), (3, 768, 2052)]
+
+
+@pytest.mark.parametrize("M,K,N", IL_SHAPES, ids=[f"M{m}-K{k}-N{n}" for m, k, n in IL_SHAPES])
+def test_matmul_interleaved_decode(lib, M, K, N):
+    print(f"\n[interleaved] M={M} K={K} N={N} plan={lib.w4a16_plan(M, N, K)}", flush=True)
+    qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=M, std=0.02), layout="interleaved")
+    x = synth.activations(M, K, wid=3)
+    check_y(run(lib, x, qw, s, z, layout="interleaved"), oracle.matmul(x, qw, s, z, layout="interleaved"),
+            f"interleaved M={M} K={K} N={N}")
+
+
+IL_PLANS = [dict(kernel=1, kc=kc, row_tiles=rt, waves=w, cols=c, seg=sg)
+            for c in (16, 32, 64) for sg, kc in ((1, 2), (2, 4), (4, 8), (8, 16)) for rt in (1, 2)
+            for w in (4, 8)]
+IL_PLANS = [p for p in IL_PLANS if _plan_is_built(p, PLAN_MKN[0], PLAN_MKN[2], PLAN_MKN[1])]
+_IL_CASE = {}
+
+
+@pytest.mark.parametrize("plan", IL_PLANS, ids=[f"c{p['cols']}-seg{p['seg']}-kc{p['kc']}-rt{p['row_tiles']}"
+                                                 f"-w{p['waves']}" for p in IL_PLANS])
+def test_matmul_interleaved_skinny_plans(lib, plan):
+    M, K, N = PLAN_MKN
+    if not _IL_CASE:
+        qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=13, std=0.02), layout="interleaved")
+        x = synth.activations(M, K, wid=8)
+        _IL_CASE.update(dev=[dev(x), dev(qw), dev(s), dev(z)],
+                        ref=oracle.matmul(x, qw, s, z, layout="interleaved"))
+    print(f"\n[interleaved plan] {plan}", flush=True)
+    check_y(run(lib, *_IL_CASE["dev"], plan=plan, layout="interleaved"), _IL_CASE["ref"], f"interleaved {plan}")
+
+
+IL_PREFILL = [(3, 256, 104), (130, 384, 1416), (257, 1408, 264), (200, 128, 136), (129, 2048, 1408)]
+
+
+@pytest.mark.parametrize("tile", [1, 2, 3])
+@pytest.mark.parametrize("g", [32, 128])
+@pytest.mark.parametrize("M,K,N", IL_PREFILL, ids=[f"M{m}-K{k}-N{n}" for m, k, n in IL_PREFILL])
+def test_matmul_interleaved_prefill_tiles(lib, M, K, N, g, tile):
+    print(f"\n[interleaved prefill] tile={tile} g={g} M={M} K={K} N={N}", flush=True)
+    qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=700 + M, std=0.02), g, layout="interleaved")
+    x = synth.activations(M, K, wid=9)
+    check_y(run(lib, x, qw, s, z, plan=dict(kernel=lib.W4A16_KERNEL_PREFILL, tile=tile), group_size=g,
+                layout="interleaved"),
+            oracle.matmul(x, qw, s, z, g, layout="interleaved"), f"interleaved tile={tile} g={g} M={M}")
 
 
 @pytest.mark.parametrize("M,K,N", [(32, 8192, 8192), (128, 8192, 8192)])

@@ -14,9 +14,9 @@ def _same(a, b):
     return a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
-def _check(W, group_size=128, symmetric=False):
-    qw, s, z = lib.w4a16_pack(W, group_size=group_size, symmetric=symmetric)
-    qo, so, zo = oracle.quantize_pack(W, group_size, symmetric)
+def _check(W, group_size=128, symmetric=False, layout="linear"):
+    qw, s, z = lib.w4a16_pack(W, group_size=group_size, symmetric=symmetric, layout=layout)
+    qo, so, zo = oracle.quantize_pack(W, group_size, symmetric, layout)
     assert _same(qw, qo), "qweight differs"
     assert _same(s, so), "scales differ"
     assert _same(z, zo), "zeros differ"
@@ -176,5 +176,31 @@ def test_pack_rejects_bad_shapes(K, N, g, code):
 def test_pack_ex_rejects_bad_symmetric_flag():
     W = np.zeros((128, 4), dtype=np.float32)
     out = [np.empty((16, 4), np.int32), np.empty((1, 4), np.float16), np.empty((1, 4), np.float16)]
-    rc = lib.load().w4a16_pack_ex(W.ctypes.data, 128, 4, 128, 2, *(a.ctypes.data for a in out))
+    rc = lib.load().w4a16_pack_ex(W.ctypes.data, 128, 4, 128, 2, 0, *(a.ctypes.data for a in out))
     assert rc == lib.W4A16_ERR_INVALID_ARG
+    rc = lib.load().w4a16_pack_ex(W.ctypes.data, 128, 4, 128, 0, 2, *(a.ctypes.data for a in out))
+    assert rc == lib.W4A16_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("symmetric", [False, True])
+@pytest.mark.parametrize("g", [32, 128])
+@pytest.mark.parametrize("K,N", [(4096, 96), (768, 200), (256, 7)])
+def test_pack_interleaved_layout_matches_oracle(K, N, g, symmetric):
+    W = synth.weight(K, N, wid=4)
+    qw, s, z = _check(W, g, symmetric, "interleaved")
+    ql, sl, zl = lib.w4a16_pack(W, group_size=g, symmetric=symmetric)
+    assert _same(s, sl) and _same(z, zl)                       # only the packing differs
+    assert np.array_equal(lib.w4a16_unpack(qw, "interleaved"), lib.w4a16_unpack(ql))
+
+
+def test_unpack_interleaved_matches_oracle():
+    codes = synth.uniform_codes(512, 37, seed=8)
+    qw = oracle.pack(codes, "interleaved")
+    assert np.array_equal(lib.w4a16_unpack(qw, "interleaved"), codes)
+    assert np.array_equal(lib.w4a16_unpack(qw, "interleaved"), oracle.unpack(qw, "interleaved"))
+
+
+def test_unpack_ex_rejects_unknown_layout():
+    qw = np.zeros((16, 4), np.int32)
+    out = np.empty((128, 4), np.uint8)
+    assert lib.load().w4a16_unpack_ex(qw.ctypes.data, 128, 4, 5, out.ctypes.data) == lib.W4A16_ERR_INVALID_ARG

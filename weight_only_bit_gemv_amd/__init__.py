@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     W4A16_OK, W4A16_ERR_INVALID_ARG, W4A16_ERR_UNSUPPORTED, W4A16_ERR_ALIGNMENT,
     W4A16_ERR_NONFINITE, W4A16_ERR_HIP, W4A16_KERNEL_AUTO, W4A16_KERNEL_SKINNY,
     W4A16_KERNEL_PREFILL, W4A16_TILE_LDS, W4A16_TILE_REGISTER_B, W4A16_TILE_ASYNC,
+    W4A16_LAYOUT_LINEAR, W4A16_LAYOUT_INTERLEAVED,
 )
 
 load()

@@ -25,6 +25,8 @@ W4A16_KERNEL_PREFILL = 2
 W4A16_TILE_LDS = 1
 W4A16_TILE_REGISTER_B = 2
 W4A16_TILE_ASYNC = 3
+W4A16_LAYOUT_LINEAR = 0
+W4A16_LAYOUT_INTERLEAVED = 1
 
 GROUP_SIZE = 128
 
@@ -51,13 +53,17 @@ _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _SIGS = {
     "w4a16_pack": ([_P, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
-    "w4a16_pack_ex": ([_P, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P], ctypes.c_int),
+    "w4a16_pack_ex": ([_P, _I64, _I64, _I64, ctypes.c_int, ctypes.c_int, _P, _P, _P], ctypes.c_int),
     "w4a16_unpack": ([_P, _I64, _I64, _P], ctypes.c_int),
+    "w4a16_unpack_ex": ([_P, _I64, _I64, ctypes.c_int, _P], ctypes.c_int),
     "w4a16_matmul": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
     "w4a16_matmul_ex": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P,
                          ctypes.POINTER(w4a16_plan_t)], ctypes.c_int),
+    "w4a16_matmul_fmt": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int, _P,
+                          ctypes.POINTER(w4a16_plan_t)], ctypes.c_int),
     "w4a16_plan": ([_I64, _I64, _I64, _I64, ctypes.POINTER(w4a16_plan_t)], ctypes.c_int),
     "w4a16_dequant": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "w4a16_dequant_fmt": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P], ctypes.c_int),
     "w4a16_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "w4a16_last_error_detail": ([], ctypes.c_char_p),
     "w4a16_version": ([], ctypes.c_int),
@@ -141,9 +147,22 @@ def _dev_ptr(t, name, dtype):
 
 # ---- host entry points ------------------------------------------------------------------
 
-def w4a16_pack(W, group_size=GROUP_SIZE, symmetric=False):
+_LAYOUTS = {"linear": 0, "interleaved": 1}
+
+
+def _layout_id(layout):
+    """"linear" / "interleaved" (or the W4A16_LAYOUT_* integer) -> the ABI's integer."""
+    if isinstance(layout, str):
+        if layout not in _LAYOUTS:
+            raise ValueError(f"unknown layout {layout!r}")
+        return _LAYOUTS[layout]
+    return int(layout)
+
+
+def w4a16_pack(W, group_size=GROUP_SIZE, symmetric=False, layout="linear"):
     """W fp32 [K, N] (NumPy) -> (qweight int32 [K/8, N], scales fp16, zeros fp16).
-    symmetric=True selects the +8 zero-point quantiser (w4a16_pack_ex)."""
+    symmetric=True selects the +8 zero-point quantiser; layout "interleaved" the
+    pre-permuted packing (w4a16_pack_ex)."""
     W = np.ascontiguousarray(W, dtype=np.float32)
     if W.ndim != 2:
         raise ValueError("W must be 2-D")
@@ -153,17 +172,19 @@ def w4a16_pack(W, group_size=GROUP_SIZE, symmetric=False):
     scales = np.empty((max(G, 0), N), dtype=np.float16)
     zeros = np.empty((max(G, 0), N), dtype=np.float16)
     rc = load().w4a16_pack_ex(W.ctypes.data, K, N, group_size, 1 if symmetric else 0,
-                              qweight.ctypes.data, scales.ctypes.data, zeros.ctypes.data)
+                              _layout_id(layout), qweight.ctypes.data, scales.ctypes.data,
+                              zeros.ctypes.data)
     _check(rc, "w4a16_pack_ex")
     return qweight, scales, zeros
 
 
-def w4a16_unpack(qweight):
-    """qweight int32 [K/8, N] (NumPy) -> codes uint8 [K, N]."""
+def w4a16_unpack(qweight, layout="linear"):
+    """qweight int32 [K/8, N] (NumPy) -> codes uint8 [K, N] in natural K order."""
     qweight = np.ascontiguousarray(qweight, dtype=np.int32)
     P, N = qweight.shape
     codes = np.empty((P * 8, N), dtype=np.uint8)
-    _check(load().w4a16_unpack(qweight.ctypes.data, P * 8, N, codes.ctypes.data), "w4a16_unpack")
+    _check(load().w4a16_unpack_ex(qweight.ctypes.data, P * 8, N, _layout_id(layout), codes.ctypes.data),
+           "w4a16_unpack_ex")
     return codes
 
 
@@ -182,12 +203,14 @@ def w4a16_plan(M, N, K, group_size=GROUP_SIZE, **plan):
 
 # ---- device entry points ------------------------------------------------------------------
 
-def w4a16_matmul(x, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, stream=None, plan=None):
+def w4a16_matmul(x, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, stream=None, plan=None,
+                 layout="linear"):
     """y[M, N] = x[M, K] . dequant(qweight, scales, zeros); torch tensors on one device.
 
     x fp16 [M, K]; qweight int32 [K/8, N]; scales, zeros fp16 [K/g, N]; y fp16 [M, N]
     (allocated when None). Enqueued on `stream` (default: torch's current stream).
-    `plan` (dict with kernel/kc/row_tiles/waves/tile) forces the execution plan.
+    `plan` (dict with kernel/kc/row_tiles/waves/tile) forces the execution plan; `layout`
+    names the packing of qweight ("linear" or "interleaved").
     """
     import torch
     if x.dim() != 2 or qweight.dim() != 2:
@@ -205,13 +228,18 @@ def w4a16_matmul(x, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, strea
     args = [_dev_ptr(x, "x", torch.float16), _dev_ptr(qweight, "qweight", torch.int32),
             _dev_ptr(scales, "scales", torch.float16), _dev_ptr(zeros, "zeros", torch.float16),
             _dev_ptr(y, "y", torch.float16), M, N, K, group_size, _stream_ptr(stream, x.device)]
-    if plan is None:
+    lay = _layout_id(layout)
+    if plan is None and lay == 0:
         rc = load().w4a16_matmul(*args)
         _check(rc, "w4a16_matmul")
-    else:
+    elif lay == 0:
         pl = _make_plan(plan)
         rc = load().w4a16_matmul_ex(*args, ctypes.byref(pl))
         _check(rc, "w4a16_matmul_ex")
+    else:
+        pl = ctypes.byref(_make_plan(plan)) if plan is not None else None
+        rc = load().w4a16_matmul_fmt(*args[:-1], lay, args[-1], pl)
+        _check(rc, "w4a16_matmul_fmt")
     return y
 
 
@@ -223,20 +251,21 @@ def w4a16_matmul_ex(x, qweight, scales, zeros, y=None, plan=None, group_size=GRO
 
 
 def w4a16_dequant(qweight, scales, zeros, codes=True, weights=True, group_size=GROUP_SIZE,
-                  stream=None):
-    """The GPU's unpack/dequant: returns (codes uint8 [K, N] or None, w fp16 [K, N] or None)."""
+                  stream=None, layout="linear"):
+    """The GPU's unpack/dequant: returns (codes uint8 [K, N] or None, w fp16 [K, N] or None),
+    both in natural K order."""
     import torch
     K = qweight.shape[0] * 8
     N = qweight.shape[1]
     c = torch.empty((K, N), dtype=torch.uint8, device=qweight.device) if codes else None
     w = torch.empty((K, N), dtype=torch.float16, device=qweight.device) if weights else None
-    rc = load().w4a16_dequant(_dev_ptr(qweight, "qweight", torch.int32),
-                              _dev_ptr(scales, "scales", torch.float16),
-                              _dev_ptr(zeros, "zeros", torch.float16),
-                              ctypes.c_void_p(c.data_ptr()) if c is not None else None,
-                              ctypes.c_void_p(w.data_ptr()) if w is not None else None,
-                              N, K, group_size, _stream_ptr(stream, qweight.device))
-    _check(rc, "w4a16_dequant")
+    rc = load().w4a16_dequant_fmt(_dev_ptr(qweight, "qweight", torch.int32),
+                                  _dev_ptr(scales, "scales", torch.float16),
+                                  _dev_ptr(zeros, "zeros", torch.float16),
+                                  ctypes.c_void_p(c.data_ptr()) if c is not None else None,
+                                  ctypes.c_void_p(w.data_ptr()) if w is not None else None,
+                                  N, K, group_size, _layout_id(layout), _stream_ptr(stream, qweight.device))
+    _check(rc, "w4a16_dequant_fmt")
     return c, w
 
 

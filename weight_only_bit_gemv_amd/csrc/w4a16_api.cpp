@@ -272,10 +272,11 @@ int get_workspace(void* stream, uint64_t bytes, uint64_t n_counters, Workspace* 
 }
 
 int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const void* zeros,
-                void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, void* stream,
+                void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, int layout, void* stream,
                 const w4a16_plan_t* forced) {
     if (!x || !qweight || !scales || !zeros || !y)
         return fail(W4A16_ERR_INVALID_ARG, "null pointer argument");
+    if (!w4a16::layout_supported(layout)) return fail(W4A16_ERR_INVALID_ARG, "unknown layout %d", layout);
     int rc = check_gpu_shape(M, N, K, group_size);
     if (rc) return rc;
     if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros) || !aligned16(y))
@@ -296,6 +297,7 @@ int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const
         q.K = (int)K;
         q.tile = pl.tile;
         q.group_shift = w4a16::log2_exact(group_size);
+        q.layout = layout;
         const int e = w4a16::launch_prefill(q, stream);
         if (e != (int)hipSuccess)
             return fail(W4A16_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString((hipError_t)e));
@@ -320,6 +322,7 @@ int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const
     p.lw = pl.cols / 16;
     p.seg = pl.seg;
     p.gshift = w4a16::log2_exact(group_size / w4a16::kKStep);
+    p.layout = layout;
     uint64_t ws_bytes = 0, n_counters = 0;
     w4a16::skinny_workspace(p, &ws_bytes, &n_counters);
     if (ws_bytes) {
@@ -340,16 +343,17 @@ int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const
 extern "C" {
 
 int w4a16_pack_ex(const float* W, int64_t K, int64_t N, int64_t group_size, int symmetric,
-                  int32_t* qweight, uint16_t* scales, uint16_t* zeros) {
+                  int layout, int32_t* qweight, uint16_t* scales, uint16_t* zeros) {
     if (!W || !qweight || !scales || !zeros) return fail(W4A16_ERR_INVALID_ARG, "null pointer argument");
     if (K < 1 || N < 1) return fail(W4A16_ERR_INVALID_ARG, "K and N must be >= 1");
     if (symmetric != 0 && symmetric != 1) return fail(W4A16_ERR_INVALID_ARG, "symmetric must be 0 or 1");
+    if (!w4a16::layout_supported(layout)) return fail(W4A16_ERR_INVALID_ARG, "unknown layout %d", layout);
     if (!w4a16::group_supported(group_size))
         return fail(W4A16_ERR_UNSUPPORTED, "group_size %lld not supported (32, 64, 128 or 256)",
                     (long long)group_size);
     if (K % group_size != 0)
         return fail(W4A16_ERR_UNSUPPORTED, "K=%lld is not a multiple of group_size", (long long)K);
-    const int rc = w4a16::pack_host(W, K, N, group_size, symmetric == 1, qweight, scales, zeros);
+    const int rc = w4a16::pack_host(W, K, N, group_size, symmetric == 1, layout, qweight, scales, zeros);
     if (rc == W4A16_ERR_NONFINITE) return fail(rc, "non-finite weight or fp16 scale overflow");
     if (rc == W4A16_ERR_UNSUPPORTED) return fail(rc, "zero point outside |zero| <= 1024");
     if (rc) return fail(rc, "pack failed");
@@ -358,26 +362,37 @@ int w4a16_pack_ex(const float* W, int64_t K, int64_t N, int64_t group_size, int 
 
 int w4a16_pack(const float* W, int64_t K, int64_t N, int64_t group_size, int32_t* qweight,
                uint16_t* scales, uint16_t* zeros) {
-    return w4a16_pack_ex(W, K, N, group_size, 0, qweight, scales, zeros);
+    return w4a16_pack_ex(W, K, N, group_size, 0, W4A16_LAYOUT_LINEAR, qweight, scales, zeros);
+}
+
+int w4a16_unpack_ex(const int32_t* qweight, int64_t K, int64_t N, int layout, uint8_t* codes) {
+    if (!qweight || !codes) return fail(W4A16_ERR_INVALID_ARG, "null pointer argument");
+    if (K < 8 || N < 1 || K % 8 != 0) return fail(W4A16_ERR_INVALID_ARG, "K must be a positive multiple of 8, N >= 1");
+    if (!w4a16::layout_supported(layout)) return fail(W4A16_ERR_INVALID_ARG, "unknown layout %d", layout);
+    w4a16::unpack_host(qweight, K, N, layout, codes);
+    return ok();
 }
 
 int w4a16_unpack(const int32_t* qweight, int64_t K, int64_t N, uint8_t* codes) {
-    if (!qweight || !codes) return fail(W4A16_ERR_INVALID_ARG, "null pointer argument");
-    if (K < 8 || N < 1 || K % 8 != 0) return fail(W4A16_ERR_INVALID_ARG, "K must be a positive multiple of 8, N >= 1");
-    w4a16::unpack_host(qweight, K, N, codes);
-    return ok();
+    return w4a16_unpack_ex(qweight, K, N, W4A16_LAYOUT_LINEAR, codes);
 }
 
 int w4a16_matmul(const void* x, const int32_t* qweight, const void* scales, const void* zeros,
                  void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, void* stream) {
-    return matmul_impl(x, qweight, scales, zeros, y, M, N, K, group_size, stream, nullptr);
+    return matmul_impl(x, qweight, scales, zeros, y, M, N, K, group_size, W4A16_LAYOUT_LINEAR, stream, nullptr);
 }
 
 int w4a16_matmul_ex(const void* x, const int32_t* qweight, const void* scales, const void* zeros,
                     void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, void* stream,
                     const w4a16_plan_t* plan) {
     if (!plan) return fail(W4A16_ERR_INVALID_ARG, "null plan");
-    return matmul_impl(x, qweight, scales, zeros, y, M, N, K, group_size, stream, plan);
+    return matmul_impl(x, qweight, scales, zeros, y, M, N, K, group_size, W4A16_LAYOUT_LINEAR, stream, plan);
+}
+
+int w4a16_matmul_fmt(const void* x, const int32_t* qweight, const void* scales, const void* zeros,
+                     void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, int layout, void* stream,
+                     const w4a16_plan_t* plan) {
+    return matmul_impl(x, qweight, scales, zeros, y, M, N, K, group_size, layout, stream, plan);
 }
 
 int w4a16_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, w4a16_plan_t* plan) {
@@ -391,22 +406,30 @@ int w4a16_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, w4a16_plan_t
     return ok();
 }
 
-int w4a16_dequant(const int32_t* qweight, const void* scales, const void* zeros, uint8_t* codes,
-                  void* w, int64_t N, int64_t K, int64_t group_size, void* stream) {
+int w4a16_dequant_fmt(const int32_t* qweight, const void* scales, const void* zeros, uint8_t* codes,
+                      void* w, int64_t N, int64_t K, int64_t group_size, int layout, void* stream) {
     if (!qweight || !scales || !zeros) return fail(W4A16_ERR_INVALID_ARG, "null pointer argument");
+    if (!w4a16::layout_supported(layout)) return fail(W4A16_ERR_INVALID_ARG, "unknown layout %d", layout);
     if (!codes && !w) return fail(W4A16_ERR_INVALID_ARG, "codes and w are both NULL");
     int rc = check_gpu_shape(1, N, K, group_size);
     if (rc) return rc;
     if (!aligned16(qweight) || !aligned16(scales) || !aligned16(zeros) || (w && !aligned16(w)))
         return fail(W4A16_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+    if (codes && reinterpret_cast<uintptr_t>(codes) % 4 != 0)
+        return fail(W4A16_ERR_ALIGNMENT, "codes must be 4-byte aligned");
     const int e = w4a16::launch_dequant(reinterpret_cast<const uint32_t*>(qweight),
                                         static_cast<const uint16_t*>(scales),
                                         static_cast<const uint16_t*>(zeros), codes,
                                         static_cast<uint16_t*>(w), (int)N, (int)K,
-                                        w4a16::log2_exact(group_size), stream);
+                                        w4a16::log2_exact(group_size), layout, stream);
     if (e != (int)hipSuccess)
         return fail(W4A16_ERR_HIP, "dequant kernel launch: %s", hipGetErrorString((hipError_t)e));
     return ok();
+}
+
+int w4a16_dequant(const int32_t* qweight, const void* scales, const void* zeros, uint8_t* codes,
+                  void* w, int64_t N, int64_t K, int64_t group_size, void* stream) {
+    return w4a16_dequant_fmt(qweight, scales, zeros, codes, w, N, K, group_size, W4A16_LAYOUT_LINEAR, stream);
 }
 
 const char* w4a16_strerror(int code) {

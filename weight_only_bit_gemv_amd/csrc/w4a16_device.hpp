@@ -82,13 +82,23 @@ __device__ __forceinline__ half8_t dequant_frag(uint32_t w, ZeroOffsets zo, _Flo
     return d * sv;
 }
 
-// Position in natural K order (0..7) of element e of an unpacked fragment.
+// Position in natural K order (0..7) of element e of an unpacked fragment of a word packed
+// in the linear layout (the interleaved layout's fragments are in natural order).
 __device__ __forceinline__ constexpr int frag_k(int e) { return (e >> 1) + ((e & 1) << 2); }
 
 // 8 consecutive fp16 activations (as 16 bytes) into the fragment K order.
 __device__ __forceinline__ half8_t permute_x(uint4 v) {
     const half8_t h = __builtin_bit_cast(half8_t, v);
     return __builtin_shufflevector(h, h, 0, 4, 1, 5, 2, 6, 3, 7);
+}
+
+// The activation fragment matching an unpacked word. NAT: the words are packed in the
+// interleaved layout (nibble p holds K offset (0, 2, 4, 6, 1, 3, 5, 7)[p]), whose unpack
+// already yields natural K order, so the activations stay as they are.
+template <bool NAT>
+__device__ __forceinline__ half8_t x_frag(uint4 v) {
+    if constexpr (NAT) return __builtin_bit_cast(half8_t, v);
+    else return permute_x(v);
 }
 
 }  // namespace w4a16

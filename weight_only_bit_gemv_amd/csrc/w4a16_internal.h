@@ -10,9 +10,14 @@ namespace w4a16 {
 // ---- host packer (w4a16_pack.cpp) ----
 uint16_t f32_to_f16_rne(float f);
 float f16_to_f32(uint16_t h);
-int pack_host(const float* W, int64_t K, int64_t N, int64_t g, bool symmetric,
+// K offset held by nibble p of a packed word, per W4A16_LAYOUT_*.
+constexpr int kNibbleK[2][8] = {{0, 1, 2, 3, 4, 5, 6, 7}, {0, 2, 4, 6, 1, 3, 5, 7}};
+inline bool layout_supported(int layout) {
+    return layout == W4A16_LAYOUT_LINEAR || layout == W4A16_LAYOUT_INTERLEAVED;
+}
+int pack_host(const float* W, int64_t K, int64_t N, int64_t g, bool symmetric, int layout,
               int32_t* qweight, uint16_t* scales, uint16_t* zeros);
-void unpack_host(const int32_t* qweight, int64_t K, int64_t N, uint8_t* codes);
+void unpack_host(const int32_t* qweight, int64_t K, int64_t N, int layout, uint8_t* codes);
 
 // ---- decode / skinny kernel (w4a16_skinny.hip) ----
 constexpr int kKStep = 32;           // K rows per MFMA step (4 packed rows)
@@ -39,6 +44,7 @@ struct SkinnyParams {
     int lw;                   // packed words per lane per K-step (1, 2, 4): cols = 16 * lw
     int seg;                  // K-steps per software-pipeline segment (1, 2, 4, 8)
     int gshift;               // log2(K-steps per scale/zero group): group of K-step ks = ks >> gshift
+    int layout;               // W4A16_LAYOUT_*
 };
 
 // Workspace a skinny launch needs (bytes of partials, number of counters).
@@ -70,6 +76,7 @@ struct PrefillParams {
     int M, N, K;
     int tile;                 // W4A16_TILE_LDS, W4A16_TILE_REGISTER_B or W4A16_TILE_ASYNC
     int group_shift;          // log2(rows per scale/zero group)
+    int layout;               // W4A16_LAYOUT_*
 };
 
 int launch_prefill(const PrefillParams& p, void* stream);  // returns a hipError_t value
@@ -78,6 +85,6 @@ int launch_prefill_async(const PrefillParams& p, void* stream);  // W4A16_TILE_A
 
 // ---- dequant hook (w4a16_dequant.hip) ----
 int launch_dequant(const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
-                   uint8_t* codes, uint16_t* w, int N, int K, int group_shift, void* stream);
+                   uint8_t* codes, uint16_t* w, int N, int K, int group_shift, int layout, void* stream);
 
 }  // namespace w4a16

@@ -17,6 +17,10 @@
 //   q     = clamp(rne(w / scale) + 8, 0, 15)
 // Group sizes: any multiple of 8 rows here; the library accepts 32, 64, 128 and 256 (the
 // GemLite README takes group sizes divisible by 32).
+//
+// Layouts: nibble j of a word holds K offset kNibbleK[layout][j] of its 8 K indices - j
+// itself (linear), or (0, 2, 4, 6, 1, 3, 5, 7)[j] (interleaved, the pre-permuted order of
+// "Beating FP16 with 4-bit Weights", section "What's next").
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -82,8 +86,8 @@ namespace {
 constexpr int kCols = 64;   // columns per work item of the packer's threads
 
 // Quantise and pack columns [n0, n1) of every K-group. Returns W4A16_OK or an error.
-int pack_columns(const float* W, int64_t K, int64_t N, int64_t g, bool symmetric, int64_t n0,
-                 int64_t n1, int32_t* qweight, uint16_t* scales, uint16_t* zeros) {
+int pack_columns(const float* W, int64_t K, int64_t N, int64_t g, bool symmetric, const int* nibble_k,
+                 int64_t n0, int64_t n1, int32_t* qweight, uint16_t* scales, uint16_t* zeros) {
     const int64_t nc = n1 - n0;
     float mn[kCols], mx[kCols], s[kCols], z[kCols];
     uint8_t q[kCols * 8];
@@ -121,7 +125,7 @@ int pack_columns(const float* W, int64_t K, int64_t N, int64_t g, bool symmetric
             int32_t* out = qweight + (grp * (g / 8) + i) * N + n0;
             for (int64_t c = 0; c < nc; ++c) {
                 uint32_t w = 0;
-                for (int j = 0; j < 8; ++j) w |= (uint32_t)q[c * 8 + j] << (4 * j);
+                for (int j = 0; j < 8; ++j) w |= (uint32_t)q[c * 8 + nibble_k[j]] << (4 * j);
                 out[c] = (int32_t)w;
             }
         }
@@ -131,7 +135,7 @@ int pack_columns(const float* W, int64_t K, int64_t N, int64_t g, bool symmetric
 
 }  // namespace
 
-int pack_host(const float* W, int64_t K, int64_t N, int64_t g, bool symmetric,
+int pack_host(const float* W, int64_t K, int64_t N, int64_t g, bool symmetric, int layout,
               int32_t* qweight, uint16_t* scales, uint16_t* zeros) {
     // Reject non-finite input up front so that no output is written on that error.
     {
@@ -148,7 +152,7 @@ int pack_host(const float* W, int64_t K, int64_t N, int64_t g, bool symmetric,
         for (int64_t ch = t; ch < chunks; ch += nthreads) {
             const int64_t n0 = ch * kCols;
             const int64_t n1 = std::min<int64_t>(N, n0 + kCols);
-            const int rc = pack_columns(W, K, N, g, symmetric, n0, n1, qweight, scales, zeros);
+            const int rc = pack_columns(W, K, N, g, symmetric, kNibbleK[layout], n0, n1, qweight, scales, zeros);
             if (rc != W4A16_OK) { status[t] = rc; return; }
         }
     };
@@ -166,11 +170,12 @@ int pack_host(const float* W, int64_t K, int64_t N, int64_t g, bool symmetric,
     return W4A16_OK;
 }
 
-void unpack_host(const int32_t* qweight, int64_t K, int64_t N, uint8_t* codes) {
+void unpack_host(const int32_t* qweight, int64_t K, int64_t N, int layout, uint8_t* codes) {
+    const int* nk = kNibbleK[layout];
     for (int64_t i = 0; i < K / 8; ++i)
         for (int64_t n = 0; n < N; ++n) {
             const uint32_t w = (uint32_t)qweight[i * N + n];
-            for (int j = 0; j < 8; ++j) codes[(i * 8 + j) * N + n] = (uint8_t)((w >> (4 * j)) & 0xFu);
+            for (int j = 0; j < 8; ++j) codes[(i * 8 + nk[j]) * N + n] = (uint8_t)((w >> (4 * j)) & 0xFu);
         }
 }
 

@@ -44,7 +44,7 @@ constexpr int NT = 256;                // threads per work-group
 // (measured with the SQ_LDS_BANK_CONFLICT counter; without it the stores conflict 4-way).
 __device__ __forceinline__ int bslot(int col, int chunk) { return chunk ^ ((col >> 3) & 7); }
 
-template <int BM, int BN, int OCC>
+template <int BM, int BN, int OCC, bool NAT>
 __global__ __launch_bounds__(NT, OCC) void prefill_kernel(PrefillParams p) {
     constexpr int WM = BM / 2;         // rows per wavefront
     constexpr int WN = BN / 2;         // columns per wavefront
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(NT, OCC) void prefill_kernel(PrefillParams p) {
     auto store_stage = [&](const Regs& r, int buf) {
 #pragma unroll
         for (int i = 0; i < AL; ++i)
-            a_lds[buf][(ar + (NT / KCH) * i) * LDSW + ac] = __builtin_bit_cast(uint4, permute_x(r.av[i]));
+            a_lds[buf][(ar + (NT / KCH) * i) * LDSW + ac] = __builtin_bit_cast(uint4, x_frag<NAT>(r.av[i]));
         const half2_t z01 = as_h2(r.zv.x), z23 = as_h2(r.zv.y);
         const half2_t s01 = as_h2(r.sv.x), s23 = as_h2(r.sv.y);
         const _Float16 zc[4] = {z01[0], z01[1], z23[0], z23[1]};
@@ -211,7 +211,10 @@ int launch_prefill(const PrefillParams& p, void* stream) {
     if (p.tile == W4A16_TILE_ASYNC) return launch_prefill_async(p, stream);
     if (p.tile != W4A16_TILE_LDS) return (int)hipErrorInvalidValue;
     const dim3 grid((unsigned)((p.N + kPrefillBN - 1) / kPrefillBN), (unsigned)((p.M + kPrefillBM - 1) / kPrefillBM));
-    hipLaunchKernelGGL((prefill_kernel<kPrefillBM, kPrefillBN, 2>), grid, dim3(NT), 0, s, p);
+    if (p.layout == W4A16_LAYOUT_INTERLEAVED)
+        hipLaunchKernelGGL((prefill_kernel<kPrefillBM, kPrefillBN, 2, true>), grid, dim3(NT), 0, s, p);
+    else
+        hipLaunchKernelGGL((prefill_kernel<kPrefillBM, kPrefillBN, 2, false>), grid, dim3(NT), 0, s, p);
     return (int)hipGetLastError();
 }
 

@@ -68,8 +68,12 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds_addr) : "memory");
 }
 
-// fp16 (q - z) * s of one word, reordered from [0, 4, 1, 5, 2, 6, 3, 7] to natural K order.
+// fp16 (q - z) * s of one word in natural K order. A word of the linear layout unpacks in
+// the order [0, 4, 1, 5, 2, 6, 3, 7] and is reordered; one of the interleaved layout (NAT)
+// unpacks in natural order already.
+template <bool NAT>
 __device__ __forceinline__ half8_t dequant_natural(uint32_t w, ZeroOffsets zo, _Float16 s, const UnpackConsts& uc) {
+    if constexpr (NAT) return dequant_frag(w, zo, s, uc);
     const uint4 u = __builtin_bit_cast(uint4, dequant_frag(w, zo, s, uc));   // (q0,q4) (q1,q5) (q2,q6) (q3,q7)
     const uint4 n = make_uint4(__builtin_amdgcn_perm(u.y, u.x, 0x05040100u),  // (q0, q1)
                                __builtin_amdgcn_perm(u.w, u.z, 0x05040100u),  // (q2, q3)
@@ -78,7 +82,7 @@ __device__ __forceinline__ half8_t dequant_natural(uint32_t w, ZeroOffsets zo, _
     return __builtin_bit_cast(half8_t, n);
 }
 
-template <bool G32>
+template <bool G32, bool NAT>
 __global__ __launch_bounds__(NT, 2) void prefill_async_kernel(PrefillParams p) {
     typedef Slot<G32> S;
     extern __shared__ uint4 lds[];                           // NS slots of S::kChunks chunks
@@ -142,10 +146,10 @@ __global__ __launch_bounds__(NT, 2) void prefill_async_kernel(PrefillParams p) {
         const uint4 bw = sl[kAChunks + (4 * j + lg) * 64 + wave * 16 + lr];
         const half2_t z01 = as_h2(zv.x), z23 = as_h2(zv.y);
         const half2_t s01 = as_h2(sv.x), s23 = as_h2(sv.y);
-        b[0] = dequant_natural(bw.x, zero_offsets(z01[0]), s01[0], uc);
-        b[1] = dequant_natural(bw.y, zero_offsets(z01[1]), s01[1], uc);
-        b[2] = dequant_natural(bw.z, zero_offsets(z23[0]), s23[0], uc);
-        b[3] = dequant_natural(bw.w, zero_offsets(z23[1]), s23[1], uc);
+        b[0] = dequant_natural<NAT>(bw.x, zero_offsets(z01[0]), s01[0], uc);
+        b[1] = dequant_natural<NAT>(bw.y, zero_offsets(z01[1]), s01[1], uc);
+        b[2] = dequant_natural<NAT>(bw.z, zero_offsets(z23[0]), s23[0], uc);
+        b[3] = dequant_natural<NAT>(bw.w, zero_offsets(z23[1]), s23[1], uc);
     };
     auto read_a = [&](const uint4* sl, int j, half8_t (&a)[TI]) {
 #pragma unroll
@@ -212,18 +216,18 @@ __global__ __launch_bounds__(NT, 2) void prefill_async_kernel(PrefillParams p) {
         }
 }
 
-template <bool G32>
+template <bool G32, bool NAT>
 int launch_async(const PrefillParams& p, hipStream_t s) {
     const size_t lds = (size_t)NS * Slot<G32>::kChunks * 16;
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [&] {
-        attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_async_kernel<G32>),
+        attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_async_kernel<G32, NAT>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     });
     if (attr != hipSuccess) return (int)attr;
     const dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM));
-    hipLaunchKernelGGL((prefill_async_kernel<G32>), grid, dim3(NT), lds, s, p);
+    hipLaunchKernelGGL((prefill_async_kernel<G32, NAT>), grid, dim3(NT), lds, s, p);
     return (int)hipGetLastError();
 }
 
@@ -232,7 +236,9 @@ int launch_async(const PrefillParams& p, hipStream_t s) {
 int launch_prefill_async(const PrefillParams& p, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (p.N % 8 != 0) return (int)hipErrorInvalidValue;
-    return p.group_shift == 5 ? launch_async<true>(p, s) : launch_async<false>(p, s);
+    const bool g32 = p.group_shift == 5, nat = p.layout == W4A16_LAYOUT_INTERLEAVED;
+    if (g32) return nat ? launch_async<true, true>(p, s) : launch_async<true, false>(p, s);
+    return nat ? launch_async<false, true>(p, s) : launch_async<false, false>(p, s);
 }
 
 }  // namespace w4a16

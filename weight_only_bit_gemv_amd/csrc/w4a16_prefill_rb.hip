@@ -41,7 +41,7 @@ constexpr int kRsrcRaw = 0x00020000;   // buffer resource word 3 for raw (untype
 // scales/zeros two stages ahead. Deeper register rings need more than 256 registers (a
 // three-set weight ring spills and measured slower). G32: 32-row groups (two scale/zero
 // loads per 64-row stage); otherwise a stage lies inside one group.
-template <int OCC, bool G32>
+template <int OCC, bool G32, bool NAT>
 __global__ __launch_bounds__(NT, OCC) void prefill_rb_kernel(PrefillParams p) {
     constexpr int BM = 128;
     constexpr int WNC = 64;                    // columns per wavefront
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(NT, OCC) void prefill_rb_kernel(PrefillParams p) {
     auto store_a = [&](const RegsA& r, int buf) {
 #pragma unroll
         for (int i = 0; i < AL; ++i)
-            a_lds[buf][(ar + (NT / KCH) * i) * LDSW + ac] = __builtin_bit_cast(uint4, permute_x(r.av[i]));
+            a_lds[buf][(ar + (NT / KCH) * i) * LDSW + ac] = __builtin_bit_cast(uint4, x_frag<NAT>(r.av[i]));
     };
     auto mma = [&](const RegsB& r, int buf) {
 #pragma unroll
@@ -190,8 +190,11 @@ __global__ __launch_bounds__(NT, OCC) void prefill_rb_kernel(PrefillParams p) {
 int launch_prefill_rb(const PrefillParams& p, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)((p.M + 127) / 128));
-    if (p.group_shift == 5) hipLaunchKernelGGL((prefill_rb_kernel<2, true>), grid, dim3(NT), 0, s, p);
-    else hipLaunchKernelGGL((prefill_rb_kernel<2, false>), grid, dim3(NT), 0, s, p);
+    const bool g32 = p.group_shift == 5, nat = p.layout == W4A16_LAYOUT_INTERLEAVED;
+    if (g32 && nat) hipLaunchKernelGGL((prefill_rb_kernel<2, true, true>), grid, dim3(NT), 0, s, p);
+    else if (g32) hipLaunchKernelGGL((prefill_rb_kernel<2, true, false>), grid, dim3(NT), 0, s, p);
+    else if (nat) hipLaunchKernelGGL((prefill_rb_kernel<2, false, true>), grid, dim3(NT), 0, s, p);
+    else hipLaunchKernelGGL((prefill_rb_kernel<2, false, false>), grid, dim3(NT), 0, s, p);
     return (int)hipGetLastError();
 }
 

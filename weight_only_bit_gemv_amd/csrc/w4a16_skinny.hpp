@@ -75,7 +75,7 @@ __device__ __forceinline__ _Float16 half_at(uint2 v, int t) {
 // The loads only issue memory requests: nothing in load() reads the returned registers,
 // so a wavefront can keep a prefetched segment in flight while it works on the current
 // one (the activation permutation happens in accumulate(), at first use).
-template <int MT, int LW, int U, int SG>
+template <int MT, int LW, int U, int SG, bool NAT>
 struct Segment {
     typedef typename Lanes<LW>::Words Words;
     typedef typename Lanes<LW>::Halves Halves;
@@ -116,7 +116,7 @@ struct Segment {
                 const int u = g * SG + uu;
                 half8_t xa[MT];
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) xa[mt] = permute_x(xv[u][mt]);
+                for (int mt = 0; mt < MT; ++mt) xa[mt] = x_frag<NAT>(xv[u][mt]);
 #pragma unroll
                 for (int t = 0; t < LW; ++t) {
                     const half8_t b = unpack_sub(word_at(wv[u], t), zo[t], uc);
@@ -214,9 +214,9 @@ __device__ __forceinline__ void partial_add(Row<LW>& r, __amdgpu_buffer_rsrc_t r
 // width 16*LW). U: K-steps per segment; the dispatcher keeps kc a multiple of U and, for
 // U = 8, K a multiple of 256, so every segment is exactly U K-steps inside whole groups and
 // the loop below needs no predicates. SG: min(U, K-steps per group). W: wavefronts per
-// work-group.
+// work-group. NAT: the weights are packed in the interleaved layout (no activation permute).
 // Dynamic LDS: (W - 1) * rows * CW floats, rows = min(16 * MT, M - row0).
-template <int MT, int LW, int U, int SG, int W>
+template <int MT, int LW, int U, int SG, int W, bool NAT>
 __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
     static_assert(U == 1 || U == 2 || U == 4 || U == 8, "segment of 1, 2, 4 or 8 K-steps");
     constexpr int CW = 16 * LW;
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
     // sched_barrier(0) after each load keeps the instruction scheduler from sinking the
     // prefetch below the arithmetic of the previous segment (it otherwise does so to save
     // registers, which leaves one segment in flight and drains the queue between segments).
-    Segment<MT, LW, U, SG> sa, sb;
+    Segment<MT, LW, U, SG, NAT> sa, sb;
     const int nseg = (k1 - k0) / U;
     if (nseg > 0) sa.load(wbase, xrow, p, k0, nl);
     __builtin_amdgcn_sched_barrier(0);
@@ -412,7 +412,10 @@ hipError_t launch_one(const SkinnyParams& p, hipStream_t s) {
     const dim3 grid((unsigned)(p.n_strips * p.splits), (unsigned)p.row_blocks);
     const int rows = std::min(16 * MT, p.M);
     const size_t lds = (size_t)(W - 1) * rows * 16 * LW * sizeof(float);
-    hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W>), grid, dim3(64 * W), lds, s, p);
+    if (p.layout == W4A16_LAYOUT_INTERLEAVED)
+        hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, true>), grid, dim3(64 * W), lds, s, p);
+    else
+        hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, false>), grid, dim3(64 * W), lds, s, p);
     return hipGetLastError();
 }
 
