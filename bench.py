@@ -548,6 +548,8 @@ def run_prefill(args):
                            ("prefill_register_tile_us",
                             dict(kernel=lib.W4A16_KERNEL_PREFILL, tile=lib.W4A16_TILE_REGISTER_B)),
                            ("prefill_async_tile_us",
+                            dict(kernel=lib.W4A16_KERNEL_PREFILL, tile=lib.W4A16_TILE_ASYNC, splits=1)),
+                           ("prefill_async_split_us",
                             dict(kernel=lib.W4A16_KERNEL_PREFILL, tile=lib.W4A16_TILE_ASYNC))]
             for name, plan in forced:
                 sec, _ = time_graph(torch, stream, lambda: [runner.launch(i, plan) for _ in range(reps)],

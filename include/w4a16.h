@@ -77,12 +77,15 @@ extern "C" {
  *              of 4 (a multiple of seg).
  *   splits     SKINNY: work-groups along K per column strip (output: derived from kc and
  *              waves; a caller may leave it 0 or give the matching value).
+ *              PREFILL with W4A16_TILE_ASYNC: work-groups along K per output tile, each over
+ *              an even number of 64-row stages (0: enough for 256 work-groups with >= 8
+ *              stages each; 1 when the tiles alone reach 256); at most K/128; the completed
+ *              plan holds the count actually used. Other tiles: 0 or 1 (output 1).
  *   row_tiles  SKINNY: 16-row MFMA tiles per work-group (1..4; default ceil(M/16) <= 4;
  *              at most 2 when cols < 64).
- *   tile       PREFILL: W4A16_TILE_LDS, W4A16_TILE_REGISTER_B or W4A16_TILE_ASYNC (0: chosen
- *              from the number G of 128 x 256 output tiles: ASYNC when G >= 224 and
- *              N % 8 == 0, else REGISTER_B when G >= 384, else LDS). W4A16_TILE_ASYNC with
- *              N % 8 != 0 is UNSUPPORTED.
+ *   tile       PREFILL: W4A16_TILE_LDS, W4A16_TILE_REGISTER_B or W4A16_TILE_ASYNC (0: ASYNC
+ *              when N % 8 == 0, else REGISTER_B when the 128 x 256 output tiles number
+ *              >= 384, else LDS). W4A16_TILE_ASYNC with N % 8 != 0 is UNSUPPORTED.
  *   waves      SKINNY: wavefronts per work-group, 4, 8 or 16 (the cross-wave reduction
  *              must fit in 64 KiB of LDS: (waves-1) * 16*row_tiles * cols * 4 bytes).
  *   cols       SKINNY: output columns per work-group strip, 16, 32 or 64 (each lane loads

@@ -114,7 +114,7 @@ def test_dequant_rejects_bad_arguments():
 
 # ---- dispatcher (host only) ----
 
-PLAN_SHAPES = [(m, k, n) for m in (1, 2, 4, 8, 16, 17, 33, 64, 65, 128, 2048)
+PLAN_SHAPES = [(m, k, n) for m in (1, 2, 4, 8, 16, 17, 33, 64, 65, 128, 129, 512, 2048)
                for (k, n) in [(4096, 4096), (4096, 14336), (14336, 4096), (2048, 1408),
                               (768, 2048), (4096, 128256), (128, 4), (384, 100), (4096, 28676)]]
 
@@ -124,13 +124,19 @@ def test_auto_plan_is_valid_and_covers_k(M, K, N):
     pl = lib.w4a16_plan(M, N, K)
     assert pl["kernel"] in (lib.W4A16_KERNEL_SKINNY, lib.W4A16_KERNEL_PREFILL)
     tiles = -(-M // 128) * -(-N // 128)
-    expect_prefill = M >= 65 and (tiles >= 128 or M > 1024)
+    if N % 8 == 0:
+        expect_prefill = M >= 65 and (M > 128 or K * N >= 1 << 25)
+    else:
+        expect_prefill = M >= 65 and (tiles >= 128 or M > 1024)
     assert pl["kernel"] == (lib.W4A16_KERNEL_PREFILL if expect_prefill else lib.W4A16_KERNEL_SKINNY)
     if pl["kernel"] == lib.W4A16_KERNEL_PREFILL:
         groups = -(-M // 128) * -(-N // 256)
-        expect = (lib.W4A16_TILE_ASYNC if groups >= 224 and N % 8 == 0 else
+        expect = (lib.W4A16_TILE_ASYNC if N % 8 == 0 else
                   lib.W4A16_TILE_REGISTER_B if groups >= 384 else lib.W4A16_TILE_LDS)
         assert pl["tile"] == expect
+        if expect == lib.W4A16_TILE_ASYNC:
+            want = 1 if groups >= 256 else min(-(-256 // groups), max(1, (K // 64) // 8))
+            assert pl["splits"] <= want and (pl["splits"] > 1) == (want > 1)
     if pl["kernel"] == lib.W4A16_KERNEL_SKINNY:
         kc, splits, W = pl["kc"], pl["splits"], pl["waves"]
         assert kc in (1, 2) or kc % 4 == 0
@@ -214,3 +220,16 @@ def test_fmt_entry_points_reject_unknown_layout_and_misaligned_codes():
         lib.W4A16_ERR_INVALID_ARG
     assert so.w4a16_dequant_fmt(P[0], P[1], P[2], ctypes.c_void_p(A + 2), None, 64, 128, 128, 0, None) == \
         lib.W4A16_ERR_ALIGNMENT
+
+
+def test_prefill_split_plans():
+    assert lib.w4a16_plan(512, 4096, 14336, kernel=2, tile=3)["splits"] == 4        # 64 tiles
+    assert lib.w4a16_plan(2048, 28672, 8192, kernel=2, tile=3)["splits"] == 1       # 1792 tiles
+    for S in (1, 2, 3, 5, 9, 100):
+        pl = lib.w4a16_plan(512, 4096, 14336, kernel=2, tile=3, splits=S)
+        per = 2 * -(-224 // (2 * pl["splits"]))
+        assert -(-224 // per) == pl["splits"] and 224 - (pl["splits"] - 1) * per >= 2
+    for kw in [dict(kernel=2, tile=1, splits=2), dict(kernel=2, tile=3, splits=113), dict(kernel=2, tile=3, splits=-1)]:
+        with pytest.raises(lib.W4A16Error) as e:
+            lib.w4a16_plan(512, 4096, 14336, **kw)
+        assert e.value.code == lib.W4A16_ERR_INVALID_ARG, kw

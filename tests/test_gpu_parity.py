@@ -449,6 +449,46 @@ def test_prefill_async_tile_repeated_calls_bitwise(lib):
 
 
 # ---------------------------------------------------------------------------------------
+# split-K on the async prefill tile
+
+SPLIT_CASES = [(130, 1024, 520, 2), (257, 2048, 264, 4), (64, 4096, 256, 8), (3, 768, 1032, 3),
+               (200, 14336, 1416, 7), (128, 256, 2056, 2)]
+
+
+@pytest.mark.parametrize("layout", ["linear", "interleaved"])
+@pytest.mark.parametrize("g", [32, 128])
+@pytest.mark.parametrize("M,K,N,splits", SPLIT_CASES, ids=[f"M{m}-K{k}-N{n}-S{s}" for m, k, n, s in SPLIT_CASES])
+def test_matmul_prefill_async_split_k(lib, M, K, N, splits, g, layout):
+    plan = dict(kernel=lib.W4A16_KERNEL_PREFILL, tile=lib.W4A16_TILE_ASYNC, splits=splits)
+    print(f"\n[prefill split-K] {lib.w4a16_plan(M, N, K, group_size=g, **plan)} g={g} {layout} "
+          f"M={M} K={K} N={N}", flush=True)
+    qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=800 + M, std=0.02), g, layout=layout)
+    x = synth.activations(M, K, wid=9)
+    check_y(run(lib, x, qw, s, z, plan=plan, group_size=g, layout=layout),
+            oracle.matmul(x, qw, s, z, g, layout=layout), f"split-K S={splits} g={g} M={M} K={K} N={N}")
+
+
+def test_prefill_split_k_deterministic_and_counters_reset(lib):
+    """Split-K sums in split order (bitwise repeatable); the arrival counters return to zero,
+    so shapes with other tile counts and a decode split-K call can follow on the stream."""
+    cases = [(512, 4096, 1024, 4), (130, 2048, 520, 3), (512, 4096, 1024, 4)]
+    data = []
+    for M, K, N, S in cases:
+        qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=M + S, std=0.02))
+        x = synth.activations(M, K, wid=9)
+        data.append((dict(kernel=2, tile=3, splits=S), [dev(x), dev(qw), dev(s), dev(z)], oracle.matmul(x, qw, s, z)))
+    first = [run(lib, *d, plan=p).clone() for p, d, _ in data]
+    for rep in range(3):
+        for (p, d, ref), a in zip(data, first):
+            b = run(lib, *d, plan=p)
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), (rep, p)
+            check_y(b, ref, f"split-K rep {rep} {p}")
+        qw, s, z = quantised(14336, 4096, 0)                  # decode split-K on the same stream
+        x = synth.activations(4, 14336, wid=0)
+        check_y(run(lib, x, qw, s, z), oracle.matmul(x, qw, s, z), "decode after prefill split-K")
+
+
+# ---------------------------------------------------------------------------------------
 # interleaved (pre-permuted) weight layout: every kernel, against the oracle
 
 @pytest.mark.parametrize("g", [32, 128])

@@ -143,46 +143,80 @@ void default_skinny_plan(int64_t M, int64_t N, int64_t K, int64_t group_steps, w
     }
 }
 
-// Kernel choice (measured crossover on MI355X): the weight-streaming kernel up to M = 64;
-// above, the LDS-tiled prefill kernel once its 128 x 128 output tiles number at least
-// kPrefillMinTiles (half a tile per compute unit; with fewer it leaves the chip idle and
-// streaming the weights once per 64 rows is faster), and always beyond M = 1024.
-constexpr int64_t kPrefillMinM = 65;
-constexpr int64_t kPrefillMinTiles = 128;
-constexpr int64_t kSkinnyMaxM = 1024;
+int64_t prefill_stages_per_split(int64_t stages, int64_t splits) { return 2 * ceil_div(stages, 2 * splits); }
 
-// Prefill tile choice (measured on MI355X). The 128 x 256 tiles read a third of the LDS
-// bytes per MFMA of the 128 x 128 tile but have half as many work-groups: the async tile
-// (direct-to-LDS loads) wins once they number at least kAsyncMinGroups; it needs N % 8 == 0,
-// and without it the register tile wins from kRegisterTileMinGroups. Below, the 128 x 128
-// tile.
-constexpr int64_t kAsyncMinGroups = 224;
+// Split-K for the async tile when its output tiles alone leave compute units idle: enough
+// splits for one work-group per compute unit, each at least kMinSplitStages stages long.
+constexpr int64_t kPrefillSplitTarget = 256;
+constexpr int64_t kMinSplitStages = 8;
+
+int64_t auto_prefill_splits(int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles = ceil_div(M, 128) * ceil_div(N, 256);
+    if (tiles >= kPrefillSplitTarget) return 1;
+    const int64_t by_occupancy = ceil_div(kPrefillSplitTarget, tiles);
+    const int64_t by_depth = std::max<int64_t>(1, (K / 64) / kMinSplitStages);
+    return std::min(by_occupancy, by_depth);
+}
+
+// Prefill tile choice (measured on MI355X): the async tile (direct-to-LDS loads, split-K
+// when its tiles underfill the chip) whenever N % 8 == 0; otherwise the register tile once
+// it has kRegisterTileMinGroups 128 x 256 work-groups, the 128 x 128 tile below that.
 constexpr int64_t kRegisterTileMinGroups = 384;
 
 int32_t auto_prefill_tile(int64_t M, int64_t N) {
-    const int64_t groups = ceil_div(M, 128) * ceil_div(N, 256);
-    if (groups >= kAsyncMinGroups && N % 8 == 0) return W4A16_TILE_ASYNC;
-    if (groups >= kRegisterTileMinGroups) return W4A16_TILE_REGISTER_B;
-    return W4A16_TILE_LDS;
+    if (N % 8 == 0) return W4A16_TILE_ASYNC;
+    return ceil_div(M, 128) * ceil_div(N, 256) >= kRegisterTileMinGroups ? W4A16_TILE_REGISTER_B : W4A16_TILE_LDS;
 }
 
-int64_t auto_kernel(int64_t M, int64_t N) {
+// Kernel choice (measured crossover on MI355X): the weight-streaming kernel up to M = 64.
+// Above, with N % 8 == 0 (async split-K prefill available): prefill from M = 65 when the
+// matrix has >= kPrefillLargeKN elements, from M = 129 otherwise (for small matrices the
+// streaming kernel still wins at M = 128). Without it: prefill once its 128 x 128 output
+// tiles number at least kPrefillMinTiles (half a tile per compute unit; with fewer it leaves
+// the chip idle and streaming the weights once per 64 rows is faster), and always beyond
+// M = 1024.
+constexpr int64_t kPrefillMinM = 65;
+constexpr int64_t kPrefillLargeKN = int64_t(1) << 25;
+constexpr int64_t kPrefillMinTiles = 128;
+constexpr int64_t kSkinnyMaxM = 1024;
+
+int64_t auto_kernel(int64_t M, int64_t N, int64_t K) {
     if (M < kPrefillMinM) return W4A16_KERNEL_SKINNY;
+    if (N % 8 == 0) return (M > 128 || K * N >= kPrefillLargeKN) ? W4A16_KERNEL_PREFILL : W4A16_KERNEL_SKINNY;
     const int64_t tiles = ceil_div(M, w4a16::kPrefillBM) * ceil_div(N, w4a16::kPrefillBN);
     return (tiles >= kPrefillMinTiles || M > kSkinnyMaxM) ? W4A16_KERNEL_PREFILL : W4A16_KERNEL_SKINNY;
 }
 
 int complete_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, w4a16_plan_t* pl) {
     const int64_t group_steps = group_size / w4a16::kKStep;
-    if (pl->kernel == W4A16_KERNEL_AUTO) pl->kernel = (int32_t)auto_kernel(M, N);
+    if (pl->kernel == W4A16_KERNEL_AUTO) pl->kernel = (int32_t)auto_kernel(M, N, K);
     if (pl->kernel == W4A16_KERNEL_PREFILL) {
         if (pl->tile == 0) pl->tile = auto_prefill_tile(M, N);
         if (pl->tile != W4A16_TILE_LDS && pl->tile != W4A16_TILE_REGISTER_B && pl->tile != W4A16_TILE_ASYNC)
             return fail(W4A16_ERR_INVALID_ARG, "prefill tile %d is not built", pl->tile);
         if (pl->tile == W4A16_TILE_ASYNC && N % 8 != 0)
             return fail(W4A16_ERR_UNSUPPORTED, "the async prefill tile needs N %% 8 == 0 (N=%lld)", (long long)N);
-        if (pl->kc || pl->row_tiles || pl->waves || pl->splits || pl->cols || pl->seg)
-            return fail(W4A16_ERR_INVALID_ARG, "kc/row_tiles/waves/splits/cols/seg apply to the skinny kernel only");
+        if (pl->kc || pl->row_tiles || pl->waves || pl->cols || pl->seg)
+            return fail(W4A16_ERR_INVALID_ARG, "kc/row_tiles/waves/cols/seg apply to the skinny kernel only");
+        if (pl->splits && pl->tile != W4A16_TILE_ASYNC)
+            return fail(W4A16_ERR_INVALID_ARG, "prefill splits apply to the async tile only");
+        if (pl->splits < 0) return fail(W4A16_ERR_INVALID_ARG, "splits must be >= 0");
+        const int64_t stages = K / 64;
+        if (pl->splits > stages / 2)
+            return fail(W4A16_ERR_INVALID_ARG, "splits=%d leaves fewer than 2 stages of 64 K rows per split",
+                        pl->splits);
+        if (pl->tile == W4A16_TILE_ASYNC) {
+            if (pl->splits == 0) pl->splits = (int32_t)auto_prefill_splits(M, N, K);
+            // settle on a split count whose stages per split (prefill_stages_per_split, even,
+            // which keeps the last split at >= 2 stages) cover K with exactly that many splits
+            for (;;) {
+                const int64_t s2 = ceil_div(stages, prefill_stages_per_split(stages, pl->splits));
+                if (s2 == pl->splits) break;
+                pl->splits = (int32_t)s2;
+            }
+        } else {
+            pl->splits = 1;
+        }
         if (ceil_div(M, w4a16::kPrefillBM) > 65535) return fail(W4A16_ERR_UNSUPPORTED, "grid too large");
         return W4A16_OK;
     }
@@ -298,6 +332,17 @@ int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const
         q.tile = pl.tile;
         q.group_shift = w4a16::log2_exact(group_size);
         q.layout = layout;
+        q.splits = std::max(1, pl.splits);
+        q.stages_per_split = (int)prefill_stages_per_split(K / 64, q.splits);
+        if (q.splits > 1) {
+            const int64_t tiles = ceil_div(M, 128) * ceil_div(N, 256);
+            Workspace w;
+            rc = get_workspace(stream, (uint64_t)tiles * q.splits * w4a16::kPrefillTileFloats * 4,
+                               (uint64_t)tiles, &w);
+            if (rc) return rc;
+            q.ws = w.partials;
+            q.counters = w.counters;
+        }
         const int e = w4a16::launch_prefill(q, stream);
         if (e != (int)hipSuccess)
             return fail(W4A16_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString((hipError_t)e));

@@ -77,7 +77,16 @@ struct PrefillParams {
     int tile;                 // W4A16_TILE_LDS, W4A16_TILE_REGISTER_B or W4A16_TILE_ASYNC
     int group_shift;          // log2(rows per scale/zero group)
     int layout;               // W4A16_LAYOUT_*
+    // split-K (W4A16_TILE_ASYNC only): work-groups along K per output tile, each over
+    // stages_per_split 64-row stages (the last over the rest, >= 2); fp32 partials of
+    // 128 x 256 per (tile, split) in ws, arrival counters per tile (zero between calls)
+    int splits;
+    int stages_per_split;
+    float* ws;
+    uint32_t* counters;
 };
+
+constexpr int kPrefillTileFloats = 128 * 256;   // one fp32 partial of the async tile
 
 int launch_prefill(const PrefillParams& p, void* stream);  // returns a hipError_t value
 int launch_prefill_rb(const PrefillParams& p, void* stream);  // W4A16_TILE_REGISTER_B (w4a16_prefill_rb.hip)

@@ -57,6 +57,11 @@ template <bool G32> struct Slot {
     static constexpr int kSzLanes = G32 ? 32 : 16;     // lanes per wavefront loading them
 };
 constexpr int kDmaPerStage = 4 + 2 + 1;  // per wavefront: activations, weights, scales/zeros
+constexpr int kRsrcRaw = 0x00020000;     // buffer resource word 3 for raw (untyped) access on gfx9
+constexpr int kCpolSc1 = 16;             // device-coherent (sc1) cache policy of a buffer access
+// s_waitcnt immediate for vmcnt(0) with expcnt/lgkmcnt left at their maxima (gfx9 encoding)
+constexpr int kWaitVmcnt0 = 0 | (0x7 << 4) | (0xf << 8);
+typedef uint32_t uint4_vec __attribute__((ext_vector_type(4)));
 static_assert(kDmaPerStage == 7, "the wait below counts 7 loads per stage");
 
 // Physical chunk of activation chunk `ch` (0..7) of tile row `row`: the 16 lanes that read
@@ -92,7 +97,10 @@ __global__ __launch_bounds__(NT, 2) void prefill_async_kernel(PrefillParams p) {
     const int lr = lane & 15, lg = lane >> 4;
     const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
     const int nw = n0 + wave * WNC + 4 * lr;                 // the lane's first output column
-    const int KT = p.K / 64;                                 // stages; even (K % 128 == 0)
+    // this work-group's stages: [kbase, kbase + KT) of the K / 64 stages (split-K), KT >= 2
+    const int split = blockIdx.z;
+    const int kbase = split * p.stages_per_split;
+    const int KT = min(p.stages_per_split, p.K / 64 - kbase);
     const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
     // Per-lane sources of stage 0; stage kt adds a uniform offset. Instruction i of a
@@ -189,17 +197,68 @@ __global__ __launch_bounds__(NT, 2) void prefill_async_kernel(PrefillParams p) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    issue(0, 0);
-    issue(1, 1);
+    issue(kbase, 0);
+    issue(kbase + 1, 1);
     for (int kt = 0; kt < KT; ++kt) {
         // this wavefront's loads of stage kt have landed (those of stage kt + 1 may not);
         // after the barrier every wavefront's have, and every wavefront is done with the
         // slot of stage kt - 1, which the next issue refills
         asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" : : : "memory");
-        issue(min(kt + 2, KT - 1), (kt + 2) % NS);           // past the end: a redundant copy
+        issue(kbase + min(kt + 2, KT - 1), (kt + 2) % NS);   // past the end: a redundant copy
         compute(kt % NS);
     }
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");       // no load may outlive the work-group
+
+    if (p.splits > 1) {
+        // Split-K: publish this work-group's fp32 partial; the last of the tile's work-groups
+        // to arrive sums all of them in split order (fixed, so the result does not depend
+        // on arrival order) and writes y. As in the decode kernel, partials are written and
+        // read with device-coherent (sc1) accesses and ordering needs only waits on this
+        // wavefront's memory operations plus a work-group barrier before the ticket.
+        __shared__ uint32_t ticket_lds;
+        const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            p.ws + (size_t)tile * p.splits * kPrefillTileFloats, 0, p.splits * kPrefillTileFloats * 4, kRsrcRaw);
+        // float4 (i, t) of this lane: partial offset ((wave * TI + i) * 4 + t) * 64 + lane
+        auto off = [&](int s, int i, int t) {
+            return (s * (kPrefillTileFloats / 4) + ((wave * TI + i) * 4 + t) * 64 + lane) * 16;
+        };
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint4_vec, acc[i][t]), rs, off(split, i, t), 0,
+                                                       kCpolSc1);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);              // this wavefront's partial stores have completed
+        __syncthreads();                                       // ... and every wavefront's
+        if (tid == 0)
+            ticket_lds = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (ticket_lds != (uint32_t)(p.splits - 1)) return;
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        // sum in split order, half the row tiles at a time (register budget)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int i = 4 * h; i < 4 * h + 4; ++i)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) acc[i][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < p.splits; ++s) {
+                floatx4 v[4][4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        v[i][t] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs, off(s, 4 * h + i, t), 0, kCpolSc1));
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) acc[4 * h + i][t] += v[i][t];
+            }
+        }
+        if (tid == 0)                                          // ready for the next call
+            __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     // epilogue: lane holds rows 4*lg + r of columns nw + t (t = 0..3) of each row tile
     if (nw >= p.N) return;
@@ -226,7 +285,7 @@ int launch_async(const PrefillParams& p, hipStream_t s) {
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     });
     if (attr != hipSuccess) return (int)attr;
-    const dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM));
+    const dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM), (unsigned)p.splits);
     hipLaunchKernelGGL((prefill_async_kernel<G32, NAT>), grid, dim3(NT), lds, s, p);
     return (int)hipGetLastError();
 }
@@ -235,7 +294,8 @@ int launch_async(const PrefillParams& p, hipStream_t s) {
 
 int launch_prefill_async(const PrefillParams& p, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (p.N % 8 != 0) return (int)hipErrorInvalidValue;
+    if (p.N % 8 != 0 || p.splits < 1 || p.stages_per_split < 2 || (p.splits > 1 && (!p.ws || !p.counters)))
+        return (int)hipErrorInvalidValue;
     const bool g32 = p.group_shift == 5, nat = p.layout == W4A16_LAYOUT_INTERLEAVED;
     if (g32) return nat ? launch_async<true, true>(p, s) : launch_async<true, false>(p, s);
     return nat ? launch_async<false, true>(p, s) : launch_async<false, false>(p, s);
