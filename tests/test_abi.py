@@ -135,8 +135,13 @@ def test_auto_plan_is_valid_and_covers_k(M, K, N):
                   lib.W4A16_TILE_REGISTER_B if groups >= 384 else lib.W4A16_TILE_LDS)
         assert pl["tile"] == expect
         if expect == lib.W4A16_TILE_ASYNC:
-            want = 1 if groups >= 256 else min(-(-256 // groups), max(1, (K // 64) // 8))
+            stages = K // 64
+            want = 1 if groups > 256 else min(max(1, (256 + groups // 2) // groups), max(1, stages // 16))
+            if groups * want <= 256 and stages // want > 128:
+                want *= 2                                # two work-groups per compute unit
             assert pl["splits"] <= want and (pl["splits"] > 1) == (want > 1)
+            per = 2 * -(-stages // (2 * pl["splits"]))   # even stages per split, all covered
+            assert -(-stages // per) == pl["splits"]
     if pl["kernel"] == lib.W4A16_KERNEL_SKINNY:
         kc, splits, W = pl["kc"], pl["splits"], pl["waves"]
         assert kc in (1, 2) or kc % 4 == 0
@@ -233,3 +238,4 @@ def test_prefill_split_plans():
         with pytest.raises(lib.W4A16Error) as e:
             lib.w4a16_plan(512, 4096, 14336, **kw)
         assert e.value.code == lib.W4A16_ERR_INVALID_ARG, kw
+

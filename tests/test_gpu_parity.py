@@ -398,7 +398,8 @@ PREFILL_ASYNC = [(1, 128, 8), (3, 256, 104), (130, 384, 1416), (257, 1408, 264),
 @pytest.mark.parametrize("M,K,N", PREFILL_ASYNC, ids=[f"M{m}-K{k}-N{n}" for m, k, n in PREFILL_ASYNC])
 def test_matmul_prefill_async_tile(lib, M, K, N):
     """The 128 x 256 tile fed by direct global-to-LDS loads (three-stage ring): ragged M and
-    N (multiples of 8, not of 256), K from 2 to 64 stages."""
+    N (multiples of 8, not of 256), K from 2 to 64 stages (fewer stages than ring slots
+    included)."""
     print(f"\n[prefill async tile] M={M} K={K} N={N}", flush=True)
     W = synth.weight_custom(K, N, seed=500 + M, std=0.02)
     qw, s, z = oracle.quantize_pack(W)

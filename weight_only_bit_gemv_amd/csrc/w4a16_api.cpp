@@ -145,17 +145,24 @@ void default_skinny_plan(int64_t M, int64_t N, int64_t K, int64_t group_steps, w
 
 int64_t prefill_stages_per_split(int64_t stages, int64_t splits) { return 2 * ceil_div(stages, 2 * splits); }
 
-// Split-K for the async tile when its output tiles alone leave compute units idle: enough
-// splits for one work-group per compute unit, each at least kMinSplitStages stages long.
+// Split-K for the async tile (measured on MI355X over the prefill shapes, M = 128 .. 2048):
+// when its output tiles number at most one per compute unit, about one work-group per
+// compute unit (splits = 256 / tiles, rounded), each split at least kMinSplitStages stages
+// long; and when every split is then still longer than kLongSplitStages stages, twice as
+// many, so that two work-groups share each compute unit. More splits cost more than they
+// gain: the last work-group of a tile sums all of the tile's fp32 partials alone.
 constexpr int64_t kPrefillSplitTarget = 256;
-constexpr int64_t kMinSplitStages = 8;
+constexpr int64_t kMinSplitStages = 16;
+constexpr int64_t kLongSplitStages = 128;
 
 int64_t auto_prefill_splits(int64_t M, int64_t N, int64_t K) {
     const int64_t tiles = ceil_div(M, 128) * ceil_div(N, 256);
-    if (tiles >= kPrefillSplitTarget) return 1;
-    const int64_t by_occupancy = ceil_div(kPrefillSplitTarget, tiles);
-    const int64_t by_depth = std::max<int64_t>(1, (K / 64) / kMinSplitStages);
-    return std::min(by_occupancy, by_depth);
+    const int64_t stages = K / 64;
+    if (tiles > kPrefillSplitTarget) return 1;
+    int64_t s = std::max<int64_t>(1, (kPrefillSplitTarget + tiles / 2) / tiles);
+    s = std::min(s, std::max<int64_t>(1, stages / kMinSplitStages));
+    if (tiles * s <= kPrefillSplitTarget && stages / s > kLongSplitStages) s *= 2;
+    return s;
 }
 
 // Prefill tile choice (measured on MI355X): the async tile (direct-to-LDS loads, split-K

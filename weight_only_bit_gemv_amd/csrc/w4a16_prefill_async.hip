@@ -1,5 +1,5 @@
 // Prefill-sized W4A16 kernel for gfx950, tile W4A16_TILE_ASYNC: every operand reaches LDS
-// through direct global-to-LDS loads, three stages in flight.
+// through direct global-to-LDS loads into a ring of LDS stages.
 //
 // What it computes: y = x . dequant(Wq) ("Beating FP16 with 4-bit Weights: A Portable W4A16
 // GEMM in Triton", section "The design": each packed int32 is loaded once, its eight
@@ -8,32 +8,45 @@
 //
 // Tiling as the register tile: a work-group computes 128 x 256 of y with 4 wavefronts side
 // by side along N, each owning all 128 rows x 64 columns (8 x 4 tiles of
-// v_mfma_f32_16x16x32_f16, 128 fp32 accumulators per lane), two work-groups per compute
-// unit. What differs is how the operands arrive: global_load_lds_dwordx4 writes 16 bytes
-// per lane straight into LDS (lane i of an instruction lands at the wavefront's LDS base +
-// 16 i) without passing through registers, so the pipeline depth is bounded by LDS, not by
-// the 256 VGPRs the accumulators already half fill. Each 64-row K stage of a work-group
-// (activations 128 x 64 fp16, packed weights 8 rows x 256 columns, scales and zeros of
-// its groups) lands in one of three LDS slots; the loads of stage k + 2 are issued while
-// stage k is multiplied.
+// v_mfma_f32_16x16x32_f16, 128 fp32 accumulators per lane). What differs is how the
+// operands arrive: global_load_lds_dwordx4 writes 16 bytes per lane straight into LDS
+// (lane i of an instruction lands at the wavefront's LDS base + 16 i) without passing
+// through registers, so the pipeline depth is bounded by LDS, not by the 256 VGPRs the
+// accumulators already half fill. Each 64-row K stage of a work-group (activations
+// 128 x 64 fp16, packed weights 8 rows x 256 columns, scales and zeros of its groups) lands
+// in one slot of a three-slot LDS ring (77-80 KB, room for two work-groups per compute
+// unit). A six-slot ring (one work-group per compute unit, five stages in flight) measured
+// no faster on any prefill shape: the loads are not what a lone work-group waits for.
 //
 // The activations land in LDS in their natural K order (a direct load cannot permute), so
 // the weights are put into that order instead: the magic-number unpack yields the codes of
 // a word in the order [0, 4, 1, 5, 2, 6, 3, 7], and four byte permutes per word reorder the
 // dequantised halves to [0 .. 7].
 //
+// Schedule. A stage is two K-steps of 32 rows, each 32 MFMAs per wavefront. While the
+// MFMAs of one K-step run, the operands of the next are prepared: its weights, scales and
+// zeros are read from LDS and dequantised (about 70 VALU), and each activation fragment is
+// re-read as soon as the four MFMAs that use it have issued. The next K-step may belong to
+// the next stage, so the stage boundary falls between the two K-steps of a stage: after
+// the first K-step's MFMAs every wavefront waits for the next stage's loads, a barrier
+// makes them visible (and ends every read of the current slot), the current slot is
+// refilled with the stage NS ahead, and the second K-step's MFMAs overlap the next stage's
+// first operands. The matrix cores then see one unbroken stream of MFMAs per wavefront,
+// which matters when a compute unit holds a single work-group and no other wavefront can
+// fill the gaps.
+//
 // Synchronisation is explicit. The loads are issued from inline assembly, invisible to the
 // compiler's wait-count pass (which otherwise waits for every outstanding load before each
 // LDS read it cannot prove disjoint from them, draining the pipeline); every wavefront
 // issues the same number of loads per stage (kDmaPerStage), so "s_waitcnt vmcnt(n)" with n
-// the loads of one later stage means "this wavefront's loads of the current stage have
-// landed", and the barrier that follows makes every wavefront's loads of it visible. The
-// barrier also orders the reads of the slot about to be refilled before the loads that
-// refill it. No load the compiler issues itself is in flight in the loop (nothing else
+// the loads of the stages issued after the one awaited means "this wavefront's loads of
+// that stage have landed", and the barrier that follows makes every wavefront's loads of
+// it visible. No load the compiler issues itself is in flight in the loop (nothing else
 // loads from global memory there), so its own wait counts are unaffected.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "w4a16_device.hpp"
 #include "w4a16_internal.h"
@@ -47,7 +60,7 @@ constexpr int BM = 128;                // rows of M per work-group
 constexpr int WNC = 64;                // columns per wavefront
 constexpr int BN = 4 * WNC;            // columns per work-group
 constexpr int TI = BM / 16;            // 16-row MFMA tiles per wavefront
-constexpr int NS = 3;                  // LDS slots (stages in flight)
+constexpr int NS = 3;                  // LDS ring slots
 // LDS slot layout in 16-byte chunks
 constexpr int kAChunks = BM * 8;       // activations: 128 rows x 8 chunks (64 fp16), swizzled
 constexpr int kBChunks = 8 * (BN / 4); // packed weights: 8 rows x 64 column quads
@@ -62,30 +75,64 @@ constexpr int kCpolSc1 = 16;             // device-coherent (sc1) cache policy o
 // s_waitcnt immediate for vmcnt(0) with expcnt/lgkmcnt left at their maxima (gfx9 encoding)
 constexpr int kWaitVmcnt0 = 0 | (0x7 << 4) | (0xf << 8);
 typedef uint32_t uint4_vec __attribute__((ext_vector_type(4)));
-static_assert(kDmaPerStage == 7, "the wait below counts 7 loads per stage");
+static_assert(kDmaPerStage == 7, "stage_barrier counts 7 loads per stage");
+
+// Wait until this wavefront has at most LATER stages of loads outstanding (the stages
+// issued after the one awaited) and every one of its LDS reads has completed, then barrier.
+template <int LATER>
+__device__ __forceinline__ void stage_barrier() {
+    static_assert(LATER == 1 || LATER == 2, "the ring waits with one or two later stages in flight");
+    if constexpr (LATER == 1) asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" : : : "memory");
+    if constexpr (LATER == 2) asm volatile("s_waitcnt vmcnt(14) lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
 
 // Physical chunk of activation chunk `ch` (0..7) of tile row `row`: the 16 lanes that read
 // one chunk of 16 consecutive rows hit 16 different 16-byte bank groups.
 __device__ __forceinline__ int a_slot(int row, int ch) { return row * 8 + (ch ^ ((row >> 1) & 7)); }
 
-// 16 bytes per lane from global memory to LDS (wave-uniform LDS base in M0).
+// 16 bytes per lane from global memory to LDS (wave-uniform LDS base in M0; the one wait
+// state between the M0 write and the LDS-DMA load is the s_nop).
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds_addr) : "memory");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds_addr) : "memory");
 }
 
-// fp16 (q - z) * s of one word in natural K order. A word of the linear layout unpacks in
-// the order [0, 4, 1, 5, 2, 6, 3, 7] and is reordered; one of the interleaved layout (NAT)
-// unpacks in natural order already.
-template <bool NAT>
-__device__ __forceinline__ half8_t dequant_natural(uint32_t w, ZeroOffsets zo, _Float16 s, const UnpackConsts& uc) {
-    if constexpr (NAT) return dequant_frag(w, zo, s, uc);
-    const uint4 u = __builtin_bit_cast(uint4, dequant_frag(w, zo, s, uc));   // (q0,q4) (q1,q5) (q2,q6) (q3,q7)
-    const uint4 n = make_uint4(__builtin_amdgcn_perm(u.y, u.x, 0x05040100u),  // (q0, q1)
-                               __builtin_amdgcn_perm(u.w, u.z, 0x05040100u),  // (q2, q3)
-                               __builtin_amdgcn_perm(u.y, u.x, 0x07060302u),  // (q4, q5)
-                               __builtin_amdgcn_perm(u.w, u.z, 0x07060302u)); // (q6, q7)
-    return __builtin_bit_cast(half8_t, n);
+// The same for the lanes in `lanes` only. EXEC is switched inside the one asm statement,
+// so the compiler sees straight-line code (a branch here would split the loop into blocks
+// across which it moves the dequantisation away from the MFMAs it should overlap).
+__device__ __forceinline__ void dma16_lanes(const void* gptr, uint32_t lds_addr, uint64_t lanes) {
+    uint64_t saved;
+    asm volatile("s_mov_b64 %0, exec\n\ts_mov_b64 exec, %3\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, off\n\ts_mov_b64 exec, %0"
+                 : "=&s"(saved) : "v"(gptr), "s"(lds_addr), "s"(lanes) : "memory");
 }
+
+// Half H of the fp16 (q - z) * s of one word, in natural K order: H = 0 dequantises the
+// codes at K offsets 0, 1, 4, 5 of the fragment, H = 1 those at 2, 3, 6, 7 (the magic-number
+// unpack of device.hpp, split in two so that the work spreads over more MFMAs). A word of
+// the linear layout unpacks as the pairs (q0, q4) (q1, q5) (q2, q6) (q3, q7) and two byte
+// permutes per half reorder them; one of the interleaved layout (NAT) unpacks in natural
+// order already.
+template <bool NAT, int H>
+__device__ __forceinline__ void dequant_half(uint32_t w, const ZeroOffsets& zo, half2_t s2, const UnpackConsts& c,
+                                             uint4& out) {
+    const uint32_t v = H ? w >> 8 : w;
+    const half2_t lo = (as_h2((v & c.mask_lo) | c.bias1024) - zo.lo) * s2;   // codes 2H, 2H + 4
+    const half2_t hi = (as_h2((v & c.mask_hi) | c.bias64) - zo.hi) * s2;     // codes 2H + 1, 2H + 5
+    if constexpr (NAT) {
+        (H ? out.z : out.x) = as_u32(lo);
+        (H ? out.w : out.y) = as_u32(hi);
+    } else {
+        (H ? out.y : out.x) = __builtin_amdgcn_perm(as_u32(hi), as_u32(lo), 0x05040100u);   // (q2H, q2H+1)
+        (H ? out.w : out.z) = __builtin_amdgcn_perm(as_u32(hi), as_u32(lo), 0x07060302u);   // (q2H+4, q2H+5)
+    }
+}
+
+// The packed weights, scales and zeros of one K-step of a lane's four columns, as read from
+// LDS.
+struct BRaw {
+    uint2 s, z;
+    uint4 w;
+};
 
 template <bool G32, bool NAT>
 __global__ __launch_bounds__(NT, 2) void prefill_async_kernel(PrefillParams p) {
@@ -97,7 +144,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_async_kernel(PrefillParams p) {
     const int lr = lane & 15, lg = lane >> 4;
     const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
     const int nw = n0 + wave * WNC + 4 * lr;                 // the lane's first output column
-    // this work-group's stages: [kbase, kbase + KT) of the K / 64 stages (split-K), KT >= 2
+    // this work-group's stages: [kbase, kbase + KT) of the K / 64 stages (split-K), KT >= 1
     const int split = blockIdx.z;
     const int kbase = split * p.stages_per_split;
     const int KT = min(p.stages_per_split, p.K / 64 - kbase);
@@ -134,8 +181,8 @@ __global__ __launch_bounds__(NT, 2) void prefill_async_kernel(PrefillParams p) {
         for (int i = 0; i < 2; ++i)
             dma16(b_src[i] + (size_t)kt * 8 * p.N, sb + (uint32_t)(kAChunks + (4 * i + wave) * 64) * 16u);
         const size_t grp = G32 ? (size_t)(2 * kt + sz_group) : (size_t)((kt * 64) >> p.group_shift);
-        if (lane < S::kSzLanes)
-            dma16(sz_src + grp * p.N, sb + (uint32_t)(kAChunks + kBChunks + wave * S::kSzLanes) * 16u);
+        dma16_lanes(sz_src + grp * p.N, sb + (uint32_t)(kAChunks + kBChunks + wave * S::kSzLanes) * 16u,
+                    (uint64_t(1) << S::kSzLanes) - 1);
     };
 
     const UnpackConsts uc = unpack_consts();
@@ -145,68 +192,80 @@ __global__ __launch_bounds__(NT, 2) void prefill_async_kernel(PrefillParams p) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[i][t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // The B operands of one K-step: 4 words of the lane's columns, dequantised to natural
-    // K order with their group's scales and zeros.
-    auto load_b = [&](const uint4* sl, int j, half8_t (&b)[4]) {
+    // The B operands of one K-step: the 4 words of the lane's columns, dequantised to
+    // natural K order with their group's scales and zeros.
+    auto read_b = [&](const uint4* sl, int j) {
         const uint4* szl = sl + kAChunks + kBChunks + (G32 ? j * 64 : 0) + wave * 8 + (lr >> 1);
-        const uint2 sv = reinterpret_cast<const uint2*>(szl)[lr & 1];
-        const uint2 zv = reinterpret_cast<const uint2*>(szl + 32)[lr & 1];
-        const uint4 bw = sl[kAChunks + (4 * j + lg) * 64 + wave * 16 + lr];
-        const half2_t z01 = as_h2(zv.x), z23 = as_h2(zv.y);
-        const half2_t s01 = as_h2(sv.x), s23 = as_h2(sv.y);
-        b[0] = dequant_natural<NAT>(bw.x, zero_offsets(z01[0]), s01[0], uc);
-        b[1] = dequant_natural<NAT>(bw.y, zero_offsets(z01[1]), s01[1], uc);
-        b[2] = dequant_natural<NAT>(bw.z, zero_offsets(z23[0]), s23[0], uc);
-        b[3] = dequant_natural<NAT>(bw.w, zero_offsets(z23[1]), s23[1], uc);
+        BRaw r;
+        r.s = reinterpret_cast<const uint2*>(szl)[lr & 1];
+        r.z = reinterpret_cast<const uint2*>(szl + 32)[lr & 1];
+        r.w = sl[kAChunks + (4 * j + lg) * 64 + wave * 16 + lr];
+        return r;
     };
-    auto read_a = [&](const uint4* sl, int j, half8_t (&a)[TI]) {
-#pragma unroll
-        for (int i = 0; i < TI; ++i) a[i] = __builtin_bit_cast(half8_t, sl[a_slot(16 * i + lr, 4 * j + lg)]);
+    auto dequant_word = [&](const BRaw& r, int t, uint4& b) {   // t: compile-time after unrolling
+        const half2_t zp = as_h2(t < 2 ? r.z.x : r.z.y), sp = as_h2(t < 2 ? r.s.x : r.s.y);
+        const _Float16 z = zp[t & 1], sc = sp[t & 1];
+        const ZeroOffsets zo = zero_offsets(z);
+        const uint32_t w = t == 0 ? r.w.x : t == 1 ? r.w.y : t == 2 ? r.w.z : r.w.w;
+        dequant_half<NAT, 0>(w, zo, half2_t{sc, sc}, uc, b);
+        dequant_half<NAT, 1>(w, zo, half2_t{sc, sc}, uc, b);
     };
-    auto mfma_step = [&](const half8_t (&a)[TI], const half8_t (&b)[4]) {
+    auto read_a = [&](const uint4* sl, int j, int i) {
+        return __builtin_bit_cast(half8_t, sl[a_slot(16 * i + lr, 4 * j + lg)]);
+    };
+    // The 32 MFMAs of one K-step on (a, b), in 8 chunks of 4 (one activation fragment each).
+    // NEXT: the chunks also prepare the next K-step, K-step nj of slot nsl: its weights,
+    // scales and zeros are read from LDS before the first chunk, their words dequantised in
+    // chunks 1 to 4 (one each; chunk 0 covers the read latency), and fragment i is re-read
+    // into a[i] in chunk i, after its four MFMAs. Scheduling barriers between the chunks
+    // keep the compiler from gathering the VALU work in one place.
+    auto kstep = [&](half8_t (&a)[TI], const uint4 (&b)[4], auto next, const uint4* nsl, int nj, uint4 (&nb)[4]) {
+        constexpr bool NEXT = decltype(next)::value;
+        BRaw r;
+        if constexpr (NEXT) r = read_b(nsl, nj);
 #pragma unroll
-        for (int i = 0; i < TI; ++i)
+        for (int i = 0; i < TI; ++i) {
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[t], acc[i][t], 0, 0, 0);
-    };
-    // Per K-step all eight activation fragments are read first (the MFMAs then consume them
-    // as they arrive). Within a stage the dequantisation of K-step 1 (its LDS reads and
-    // about 70 VALU) runs between the 32 MFMAs of K-step 0: one MFMA, then two VALU,
-    // repeated, so the matrix core does not wait for the unpack; K-step 0's dequantisation
-    // comes first, alone.
-    auto compute = [&](int slot) {
-        const uint4* sl = lds + slot * S::kChunks;
-        half8_t a[TI], b0[4], b1[4];
-        load_b(sl, 0, b0);
-        read_a(sl, 0, a);
-        __builtin_amdgcn_sched_barrier(0);
-        load_b(sl, 1, b1);
-        mfma_step(a, b0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // K-step 1's weight, scale, zero reads
-#pragma unroll
-        for (int i = 0; i < 4 * TI; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // 3 VALU
+                acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], __builtin_bit_cast(half8_t, b[t]), acc[i][t], 0,
+                                                                   0, 0);
+            if constexpr (NEXT) {
+                a[i] = read_a(nsl, nj, i);
+                if (i >= 1 && i <= 4) dequant_word(r, i - 1, nb[i - 1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        read_a(sl, 1, a);
-        mfma_step(a, b1);
-        __builtin_amdgcn_sched_group_barrier(0x100, TI, 0);  // all activation reads first
-        __builtin_amdgcn_sched_group_barrier(0x008, 4 * TI, 0);
-        __builtin_amdgcn_sched_barrier(0);
     };
 
-    issue(kbase, 0);
-    issue(kbase + 1, 1);
-    for (int kt = 0; kt < KT; ++kt) {
-        // this wavefront's loads of stage kt have landed (those of stage kt + 1 may not);
-        // after the barrier every wavefront's have, and every wavefront is done with the
-        // slot of stage kt - 1, which the next issue refills
-        asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" : : : "memory");
-        issue(kbase + min(kt + 2, KT - 1), (kt + 2) % NS);   // past the end: a redundant copy
-        compute(kt % NS);
+    // Prologue: NS stages in flight, the first K-step's operands in registers. Past the
+    // work-group's last stage the ring is fed copies of that stage (never read): every
+    // wavefront then issues kDmaPerStage loads per stage, the waits have fixed counts and
+    // the loop body is one basic block.
+#pragma unroll
+    for (int s = 0; s < NS; ++s) issue(kbase + min(s, KT - 1), s);
+    stage_barrier<NS - 1>();
+    half8_t a[TI];
+    uint4 b0[4], b1[4];
+    {
+        const BRaw r = read_b(lds, 0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) dequant_word(r, t, b0[t]);
     }
+#pragma unroll
+    for (int i = 0; i < TI; ++i) a[i] = read_a(lds, 0, i);
+
+    int slot = 0;
+    for (int kt = 0; kt + 1 < KT; ++kt) {
+        kstep(a, b0, std::true_type{}, lds + slot * S::kChunks, 1, b1);   // K-step 0; prepares K-step 1
+        // stage kt + 1 has landed and every wavefront is done with this slot, which takes
+        // stage kt + NS
+        stage_barrier<NS - 2>();
+        issue(kbase + min(kt + NS, KT - 1), slot);
+        slot = slot + 1 == NS ? 0 : slot + 1;
+        kstep(a, b1, std::true_type{}, lds + slot * S::kChunks, 0, b0);   // K-step 1; prepares the next stage's K-step 0
+    }
+    kstep(a, b0, std::true_type{}, lds + slot * S::kChunks, 1, b1);       // the last stage
+    kstep(a, b1, std::false_type{}, lds, 0, b0);
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");       // no load may outlive the work-group
 
     if (p.splits > 1) {
@@ -294,7 +353,7 @@ int launch_async(const PrefillParams& p, hipStream_t s) {
 
 int launch_prefill_async(const PrefillParams& p, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (p.N % 8 != 0 || p.splits < 1 || p.stages_per_split < 2 || (p.splits > 1 && (!p.ws || !p.counters)))
+    if (p.N % 8 != 0 || p.splits < 1 || p.stages_per_split < 1 || (p.splits > 1 && (!p.ws || !p.counters)))
         return (int)hipErrorInvalidValue;
     const bool g32 = p.group_shift == 5, nat = p.layout == W4A16_LAYOUT_INTERLEAVED;
     if (g32) return nat ? launch_async<true, true>(p, s) : launch_async<true, false>(p, s);
