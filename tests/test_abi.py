@@ -238,4 +238,3 @@ def test_prefill_split_plans():
         with pytest.raises(lib.W4A16Error) as e:
             lib.w4a16_plan(512, 4096, 14336, **kw)
         assert e.value.code == lib.W4A16_ERR_INVALID_ARG, kw
-

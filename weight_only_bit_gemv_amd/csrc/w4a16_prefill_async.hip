@@ -268,6 +268,22 @@ __global__ __launch_bounds__(NT, 2) void prefill_async_kernel(PrefillParams p) {
     kstep(a, b1, std::false_type{}, lds, 0, b0);
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");       // no load may outlive the work-group
 
+    // y rows 4*lg + r of row tile i, columns nw .. nw + 3, from fp32 values v[t][r]
+    auto store_rows = [&](int i, const floatx4 (&v)[4]) {
+        if (nw >= p.N) return;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = m0 + 16 * i + 4 * lg + r;
+            if (row < p.M) {
+                const half2_t lo = half2_t{(_Float16)v[0][r], (_Float16)v[1][r]};
+                const half2_t hi = half2_t{(_Float16)v[2][r], (_Float16)v[3][r]};
+                *reinterpret_cast<uint2*>(p.y + (size_t)row * p.N + nw) = make_uint2(as_u32(lo), as_u32(hi));
+            }
+        }
+    };
+    // row tiles with at least one row < M (the rest of the tile is never stored)
+    const int live_tiles = min(TI, (p.M - m0 + 15) / 16);
+
     if (p.splits > 1) {
         // Split-K: publish this work-group's fp32 partial; the last of the tile's work-groups
         // to arrive sums all of them in split order (fixed, so the result does not depend
@@ -278,60 +294,64 @@ __global__ __launch_bounds__(NT, 2) void prefill_async_kernel(PrefillParams p) {
         const int tile = blockIdx.y * gridDim.x + blockIdx.x;
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             p.ws + (size_t)tile * p.splits * kPrefillTileFloats, 0, p.splits * kPrefillTileFloats * 4, kRsrcRaw);
-        // float4 (i, t) of this lane: partial offset ((wave * TI + i) * 4 + t) * 64 + lane
+        // float4 (i, t) of this lane: partial offset ((wave * TI + i) * 4 + t) * 64 + lane;
+        // offsets of splits >= p.splits lie past the buffer's end, where loads return 0
         auto off = [&](int s, int i, int t) {
             return (s * (kPrefillTileFloats / 4) + ((wave * TI + i) * 4 + t) * 64 + lane) * 16;
         };
 #pragma unroll
         for (int i = 0; i < TI; ++i)
+            if (i < live_tiles)
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint4_vec, acc[i][t]), rs, off(split, i, t), 0,
-                                                       kCpolSc1);
+                for (int t = 0; t < 4; ++t)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint4_vec, acc[i][t]), rs, off(split, i, t), 0,
+                                                           kCpolSc1);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);              // this wavefront's partial stores have completed
         __syncthreads();                                       // ... and every wavefront's
         if (tid == 0)
             ticket_lds = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         if (ticket_lds != (uint32_t)(p.splits - 1)) return;
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        // sum in split order, half the row tiles at a time (register budget)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int i = 4 * h; i < 4 * h + 4; ++i)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) acc[i][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-            for (int s = 0; s < p.splits; ++s) {
-                floatx4 v[4][4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        v[i][t] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs, off(s, 4 * h + i, t), 0, kCpolSc1));
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) acc[4 * h + i][t] += v[i][t];
-            }
-        }
         if (tid == 0)                                          // ready for the next call
             __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // Sum in split order, two row tiles at a time, the loads of four splits in flight
+        // together (the partials reach this compute unit only as fast as enough of them are
+        // outstanding); each pair of row tiles is stored as soon as it is summed.
+#pragma unroll
+        for (int i0 = 0; i0 < TI; i0 += 2) {
+            if (i0 >= live_tiles) break;
+            floatx4 sum[2][4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) sum[i][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int s0 = 0; s0 < p.splits; s0 += 4) {
+                floatx4 v[4][2][4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            v[u][i][t] = __builtin_bit_cast(
+                                floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs, off(s0 + u, i0 + i, t), 0, kCpolSc1));
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (s0 + u < p.splits)
+#pragma unroll
+                        for (int i = 0; i < 2; ++i)
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) sum[i][t] += v[u][i][t];
+            }
+            store_rows(i0, sum[0]);
+            store_rows(i0 + 1, sum[1]);
+        }
+        return;
     }
 
     // epilogue: lane holds rows 4*lg + r of columns nw + t (t = 0..3) of each row tile
-    if (nw >= p.N) return;
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = m0 + 16 * i + 4 * lg + r;
-            if (row < p.M) {
-                const half2_t lo = half2_t{(_Float16)acc[i][0][r], (_Float16)acc[i][1][r]};
-                const half2_t hi = half2_t{(_Float16)acc[i][2][r], (_Float16)acc[i][3][r]};
-                *reinterpret_cast<uint2*>(p.y + (size_t)row * p.N + nw) = make_uint2(as_u32(lo), as_u32(hi));
-            }
-        }
+    for (int i = 0; i < TI; ++i) store_rows(i, acc[i]);
 }
 
 template <bool G32, bool NAT>
