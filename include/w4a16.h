@@ -24,7 +24,8 @@
  * a caller buffer after a call returns. It owns one split-K workspace (fp32 partial sums
  * and arrival counters) per (device, stream) pair, allocated on first use and grown when a
  * larger one is needed; two calls on one stream are ordered by the stream, so they never
- * share it concurrently.
+ * share it concurrently. A workspace that grows keeps its earlier buffers allocated until
+ * the process ends, so a graph captured on the stream before the growth stays valid.
  *
  * Errors: every entry point returns W4A16_OK (0) or a negative W4A16_ERR_* code and never
  * throws. Arguments are validated before any HIP call is made; a call rejected by
@@ -175,7 +176,9 @@ int w4a16_unpack_ex(const int32_t* qweight, int64_t K, int64_t N, int layout, ui
  * Graph capture: a plan with splits > 1 uses the library's split-K workspace for `stream`;
  * if it is not yet large enough it is allocated (hipMalloc) on the call. Under stream
  * capture that allocation is not possible, and the call returns HIP without enqueueing
- * anything: make one call of the shape on the stream before capturing.
+ * anything (the capture itself stays usable): make one call of the shape on the stream
+ * before capturing. The captured kernels use that stream's workspace: replay the graph on
+ * the capturing stream, or at least never concurrently with other calls on it.
  * Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT (no HIP call made), HIP (launch failure,
  * workspace allocation failure, or a workspace that would have to grow during capture).
  */

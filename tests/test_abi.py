@@ -114,8 +114,8 @@ def test_dequant_rejects_bad_arguments():
 
 # ---- dispatcher (host only) ----
 
-PLAN_SHAPES = [(m, k, n) for m in (1, 2, 4, 8, 16, 17, 33, 64, 65, 128, 129, 512, 2048)
-               for (k, n) in [(4096, 4096), (4096, 14336), (14336, 4096), (2048, 1408),
+PLAN_SHAPES = [(m, k, n) for m in (1, 2, 4, 8, 16, 17, 33, 48, 49, 64, 65, 128, 129, 512, 2048)
+               for (k, n) in [(4096, 4096), (4096, 14336), (14336, 4096), (2048, 1408), (8192, 28672),
                               (768, 2048), (4096, 128256), (128, 4), (384, 100), (4096, 28676)]]
 
 
@@ -125,7 +125,7 @@ def test_auto_plan_is_valid_and_covers_k(M, K, N):
     assert pl["kernel"] in (lib.W4A16_KERNEL_SKINNY, lib.W4A16_KERNEL_PREFILL)
     tiles = -(-M // 128) * -(-N // 128)
     if N % 8 == 0:
-        expect_prefill = M >= 65 and (M > 128 or K * N >= 1 << 25)
+        expect_prefill = (M >= 65 and (M > 128 or K * N >= 1 << 25)) or (M >= 49 and K * N >= 1 << 27)
     else:
         expect_prefill = M >= 65 and (tiles >= 128 or M > 1024)
     assert pl["kernel"] == (lib.W4A16_KERNEL_PREFILL if expect_prefill else lib.W4A16_KERNEL_SKINNY)

@@ -9,6 +9,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <vector>
 #include <utility>
 
 #include "w4a16_internal.h"
@@ -175,21 +176,28 @@ int32_t auto_prefill_tile(int64_t M, int64_t N) {
     return ceil_div(M, 128) * ceil_div(N, 256) >= kRegisterTileMinGroups ? W4A16_TILE_REGISTER_B : W4A16_TILE_LDS;
 }
 
-// Kernel choice (measured crossover on MI355X): the weight-streaming kernel up to M = 64.
-// Above, with N % 8 == 0 (async split-K prefill available): prefill from M = 65 when the
-// matrix has >= kPrefillLargeKN elements, from M = 129 otherwise (for small matrices the
-// streaming kernel still wins at M = 128). Without it: prefill once its 128 x 128 output
-// tiles number at least kPrefillMinTiles (half a tile per compute unit; with fewer it leaves
-// the chip idle and streaming the weights once per 64 rows is faster), and always beyond
-// M = 1024.
+// Kernel choice (measured crossover on MI355X): the weight-streaming kernel up to M = 64
+// (up to M = 48 for the largest matrices, >= kPrefillHugeKN elements, where the split-K
+// prefill streams the weights faster at M = 64). Above, with N % 8 == 0 (async split-K
+// prefill available): prefill from M = 65 when the matrix has >= kPrefillLargeKN elements,
+// from M = 129 otherwise (for small matrices the streaming kernel still wins at M = 128).
+// Without it: prefill once its 128 x 128 output tiles number at least kPrefillMinTiles (half
+// a tile per compute unit; with fewer it leaves the chip idle and streaming the weights once
+// per 64 rows is faster), and always beyond M = 1024.
 constexpr int64_t kPrefillMinM = 65;
+constexpr int64_t kPrefillMinMHuge = 49;
 constexpr int64_t kPrefillLargeKN = int64_t(1) << 25;
+constexpr int64_t kPrefillHugeKN = int64_t(1) << 27;
 constexpr int64_t kPrefillMinTiles = 128;
 constexpr int64_t kSkinnyMaxM = 1024;
 
 int64_t auto_kernel(int64_t M, int64_t N, int64_t K) {
+    if (N % 8 == 0) {
+        if (M >= kPrefillMinMHuge && K * N >= kPrefillHugeKN) return W4A16_KERNEL_PREFILL;
+        if (M < kPrefillMinM) return W4A16_KERNEL_SKINNY;
+        return (M > 128 || K * N >= kPrefillLargeKN) ? W4A16_KERNEL_PREFILL : W4A16_KERNEL_SKINNY;
+    }
     if (M < kPrefillMinM) return W4A16_KERNEL_SKINNY;
-    if (N % 8 == 0) return (M > 128 || K * N >= kPrefillLargeKN) ? W4A16_KERNEL_PREFILL : W4A16_KERNEL_SKINNY;
     const int64_t tiles = ceil_div(M, w4a16::kPrefillBM) * ceil_div(N, w4a16::kPrefillBN);
     return (tiles >= kPrefillMinTiles || M > kSkinnyMaxM) ? W4A16_KERNEL_PREFILL : W4A16_KERNEL_SKINNY;
 }
@@ -271,6 +279,11 @@ struct Workspace {
 
 std::mutex g_ws_mu;
 std::map<std::pair<int, void*>, Workspace> g_ws;
+// Buffers of workspaces that have grown. A graph captured on the stream before the growth
+// holds their addresses and may be replayed later, so they are never freed (they stay
+// allocated until the process ends); growth at least doubles, which bounds what is kept
+// to the size of the current workspace.
+std::vector<void*> g_retired;
 
 int get_workspace(void* stream, uint64_t bytes, uint64_t n_counters, Workspace* out) {
     int dev = 0;
@@ -285,28 +298,30 @@ int get_workspace(void* stream, uint64_t bytes, uint64_t n_counters, Workspace* 
             return fail(W4A16_ERR_HIP, "split-K workspace of %llu bytes is not allocated for this stream and "
                         "cannot be allocated during graph capture: make one call of this shape on the "
                         "stream before capturing", (unsigned long long)bytes);
-        if (w.partials || w.counters) {
-            // Earlier launches on this stream may still read the old buffers.
-            e = hipStreamSynchronize(s);
-            if (e != hipSuccess) return fail(W4A16_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
-            (void)hipFree(w.partials);
-            (void)hipFree(w.counters);
-            w = Workspace{};
-        }
-        const uint64_t nb = std::max<uint64_t>(bytes, 1u << 20);
-        const uint64_t nc = std::max<uint64_t>(n_counters, 4096);
-        e = hipMalloc(reinterpret_cast<void**>(&w.partials), nb);
-        if (e != hipSuccess) { w = Workspace{}; return fail(W4A16_ERR_HIP, "hipMalloc workspace: %s", hipGetErrorString(e)); }
-        e = hipMalloc(reinterpret_cast<void**>(&w.counters), nc * sizeof(uint32_t));
+        const uint64_t nb = std::max<uint64_t>({bytes, 2 * w.partial_bytes, 1u << 20});
+        const uint64_t nc = std::max<uint64_t>({n_counters, 2 * w.n_counters, 4096});
+        Workspace g;
+        e = hipMalloc(reinterpret_cast<void**>(&g.partials), nb);
+        if (e != hipSuccess) return fail(W4A16_ERR_HIP, "hipMalloc workspace: %s", hipGetErrorString(e));
+        e = hipMalloc(reinterpret_cast<void**>(&g.counters), nc * sizeof(uint32_t));
         if (e != hipSuccess) {
-            (void)hipFree(w.partials);
-            w = Workspace{};
+            (void)hipFree(g.partials);
             return fail(W4A16_ERR_HIP, "hipMalloc counters: %s", hipGetErrorString(e));
         }
-        e = hipMemsetAsync(w.counters, 0, nc * sizeof(uint32_t), s);
-        if (e != hipSuccess) return fail(W4A16_ERR_HIP, "hipMemsetAsync: %s", hipGetErrorString(e));
-        w.partial_bytes = nb;
-        w.n_counters = nc;
+        // zero once; every kernel that takes a counter returns it to zero
+        e = hipMemsetAsync(g.counters, 0, nc * sizeof(uint32_t), s);
+        if (e != hipSuccess) {
+            (void)hipFree(g.partials);
+            (void)hipFree(g.counters);
+            return fail(W4A16_ERR_HIP, "hipMemsetAsync: %s", hipGetErrorString(e));
+        }
+        g.partial_bytes = nb;
+        g.n_counters = nc;
+        // launches already enqueued on the stream, and graphs captured on it, keep using
+        // the old buffers: retire them instead of freeing them
+        if (w.partials) g_retired.push_back(w.partials);
+        if (w.counters) g_retired.push_back(w.counters);
+        w = g;
     }
     *out = w;
     return W4A16_OK;
