@@ -108,10 +108,9 @@ __device__ __forceinline__ void dma16_lanes(const void* gptr, uint32_t lds_addr,
 
 // Half H of the fp16 (q - z) * s of one word, in natural K order: H = 0 dequantises the
 // codes at K offsets 0, 1, 4, 5 of the fragment, H = 1 those at 2, 3, 6, 7 (the magic-number
-// unpack of device.hpp, split in two so that the work spreads over more MFMAs). A word of
-// the linear layout unpacks as the pairs (q0, q4) (q1, q5) (q2, q6) (q3, q7) and two byte
-// permutes per half reorder them; one of the interleaved layout (NAT) unpacks in natural
-// order already.
+// unpack of device.hpp, one pair of halves at a time). A word of the linear layout unpacks
+// as the pairs (q0, q4) (q1, q5) (q2, q6) (q3, q7) and two byte permutes per half reorder
+// them; one of the interleaved layout (NAT) unpacks in natural order already.
 template <bool NAT, int H>
 __device__ __forceinline__ void dequant_half(uint32_t w, const ZeroOffsets& zo, half2_t s2, const UnpackConsts& c,
                                              uint4& out) {
