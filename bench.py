@@ -158,6 +158,29 @@ class Runner:
         for i in range(len(self.items)):
             self.launch(i)
 
+    def launch_w4a8(self, i, quantize=False):
+        """Enqueue item i on the W4A8 path: the per-row E4M3 activation quantiser (when
+        `quantize`, else once, up front) and the 8-bit product, same weights as launch()."""
+        M, K, N, key = self.items[i]
+        so = self.lib.load()
+        if not hasattr(self, "xq"):
+            self.xq, self.sx = {}, {}
+        if quantize or i not in self.xq:
+            if i not in self.xq:
+                self.xq[i] = self.torch.empty((M, K), dtype=self.torch.uint8, device=self.dev)
+                self.sx[i] = self.torch.empty((M,), dtype=self.torch.float32, device=self.dev)
+            rc = so.w4a8_quantize_activations(self.xk[i].data_ptr(), self.xq[i].data_ptr(), self.sx[i].data_ptr(),
+                                              M, K, self.sptr)
+            if rc != 0:
+                raise RuntimeError(f"w4a8_quantize_activations failed ({rc}) for M={M} K={K}")
+        c = self.cursor[key]
+        self.cursor[key] = (c + 1) % len(self.weights[key])
+        qw, s, z = self.weights[key][c]
+        rc = so.w4a8_matmul(self.xq[i].data_ptr(), self.sx[i].data_ptr(), qw.data_ptr(), s.data_ptr(), z.data_ptr(),
+                            self.y[i].data_ptr(), M, N, K, self.group, self.layout_id, self.sptr)
+        if rc != 0:
+            raise RuntimeError(f"w4a8_matmul failed ({rc}) for M={M} K={K} N={N}")
+
 
 def events(torch, stream):
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -555,6 +578,18 @@ def run_prefill(args):
                 sec, _ = time_graph(torch, stream, lambda: [runner.launch(i, plan) for _ in range(reps)],
                                     2, warm=1)
                 row[name] = round(sec / reps * 1e6, 2)
+            if M >= 32 and N % 8 == 0 and args.group_size in (128, 256):
+                # W4A8 (E4M3 activations): the 8-bit product alone, and with the per-row
+                # activation quantiser in front of it
+                with torch.cuda.stream(stream):
+                    runner.launch_w4a8(i)
+                stream.synchronize()
+                sec, _ = time_graph(torch, stream, lambda: [runner.launch_w4a8(i) for _ in range(reps)], 2, warm=1)
+                row["w4a8_us"] = round(sec / reps * 1e6, 2)
+                row["w4a8_TFLOPs"] = round(fl / (sec / reps) / 1e12, 2)
+                sec, _ = time_graph(torch, stream, lambda: [runner.launch_w4a8(i, quantize=True) for _ in range(reps)],
+                                    2, warm=1)
+                row["w4a8_with_quantize_us"] = round(sec / reps * 1e6, 2)
             rows.append(row)
             if cross is None and d < t:
                 cross = M

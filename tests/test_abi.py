@@ -18,14 +18,15 @@ HEADER = os.path.join(ROOT, "include", "w4a16.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(w4a16_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(w4a(?:16|8)_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ["w4a16_pack", "w4a16_pack_ex", "w4a16_unpack_ex", "w4a16_matmul_fmt",
                      "w4a16_dequant_fmt", "w4a16_matmul", "w4a16_matmul_ex", "w4a16_plan",
-                     "w4a16_dequant", "w4a16_unpack", "w4a16_strerror"]:
+                     "w4a16_dequant", "w4a16_unpack", "w4a16_strerror", "w4a8_quantize_activations",
+                     "w4a8_matmul"]:
         assert required in names
 
 
@@ -35,7 +36,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(so, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (w4a16_\w+)$", out, flags=re.M))
+    exported = set(re.findall(r"\bT (w4a(?:16|8)_\w+)$", out, flags=re.M))
     assert set(declared_functions()) <= exported
 
 
@@ -238,3 +239,28 @@ def test_prefill_split_plans():
         with pytest.raises(lib.W4A16Error) as e:
             lib.w4a16_plan(512, 4096, 14336, **kw)
         assert e.value.code == lib.W4A16_ERR_INVALID_ARG, kw
+
+
+def test_w4a8_entry_points_reject_bad_arguments():
+    so = B.load()
+    q = so.w4a8_quantize_activations
+    assert q(None, P[1], P[2], 4, 256, None) == lib.W4A16_ERR_INVALID_ARG
+    assert q(P[0], P[1], P[2], 0, 256, None) == lib.W4A16_ERR_INVALID_ARG
+    assert q(P[0], P[1], P[2], 4, 200, None) == lib.W4A16_ERR_UNSUPPORTED
+    assert q(ctypes.c_void_p(A + 8), P[1], P[2], 4, 256, None) == lib.W4A16_ERR_ALIGNMENT
+    assert q(P[0], P[1], ctypes.c_void_p(A + 2), 4, 256, None) == lib.W4A16_ERR_ALIGNMENT
+    m = so.w4a8_matmul
+
+    def call(M=4, N=64, K=256, g=128, layout=0, ptrs=None):
+        pp = ptrs or [P[0], P[1], P[2], P[3], P[4], ctypes.c_void_p(A + 0x5000)]
+        return m(*pp, M, N, K, g, layout, None)
+    assert call(M=0) == lib.W4A16_ERR_INVALID_ARG
+    assert call(layout=3) == lib.W4A16_ERR_INVALID_ARG
+    assert call(g=64) == lib.W4A16_ERR_UNSUPPORTED                 # 8-bit MFMA spans 128 rows
+    assert call(g=32) == lib.W4A16_ERR_UNSUPPORTED
+    assert call(N=60) == lib.W4A16_ERR_UNSUPPORTED                 # N % 8
+    assert call(K=200) == lib.W4A16_ERR_UNSUPPORTED
+    bad = [P[0], P[1], P[2], P[3], ctypes.c_void_p(A + 0x4008), ctypes.c_void_p(A + 0x5000)]
+    assert call(ptrs=bad) == lib.W4A16_ERR_ALIGNMENT
+    nul = [P[0], None, P[2], P[3], P[4], ctypes.c_void_p(A + 0x5000)]
+    assert call(ptrs=nul) == lib.W4A16_ERR_INVALID_ARG

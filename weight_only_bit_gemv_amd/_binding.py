@@ -64,6 +64,8 @@ _SIGS = {
     "w4a16_plan": ([_I64, _I64, _I64, _I64, ctypes.POINTER(w4a16_plan_t)], ctypes.c_int),
     "w4a16_dequant": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "w4a16_dequant_fmt": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P], ctypes.c_int),
+    "w4a8_quantize_activations": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
+    "w4a8_matmul": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int, _P], ctypes.c_int),
     "w4a16_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "w4a16_last_error_detail": ([], ctypes.c_char_p),
     "w4a16_version": ([], ctypes.c_int),
@@ -267,6 +269,44 @@ def w4a16_dequant(qweight, scales, zeros, codes=True, weights=True, group_size=G
                                   N, K, group_size, _layout_id(layout), _stream_ptr(stream, qweight.device))
     _check(rc, "w4a16_dequant_fmt")
     return c, w
+
+
+def w4a8_quantize(x, stream=None):
+    """Per-row E4M3 quantisation of fp16 activations on the device: returns (xq uint8
+    [M, K], sx float32 [M]) with x ~= dec(xq) * sx[:, None]."""
+    import torch
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    M, K = x.shape
+    xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    sx = torch.empty((M,), dtype=torch.float32, device=x.device)
+    rc = load().w4a8_quantize_activations(_dev_ptr(x, "x", torch.float16), _dev_ptr(xq, "xq", torch.uint8),
+                                          _dev_ptr(sx, "sx", torch.float32), M, K, _stream_ptr(stream, x.device))
+    _check(rc, "w4a8_quantize_activations")
+    return xq, sx
+
+
+def w4a8_matmul(xq, sx, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, layout="linear", stream=None):
+    """y[M, N] = sx * (dec(xq) . dec(E4M3(q - z))) per group times its scales (W4A8)."""
+    import torch
+    if xq.dim() != 2 or qweight.dim() != 2 or sx.dim() != 1:
+        raise ValueError("xq and qweight must be 2-D, sx 1-D")
+    M, K = xq.shape
+    N = qweight.shape[1]
+    if qweight.shape[0] * 8 != K or sx.shape[0] != M:
+        raise ValueError("xq, sx and qweight disagree on M or K")
+    if scales.shape != (K // group_size, N) or zeros.shape != (K // group_size, N):
+        raise ValueError("scales/zeros must be [K/group_size, N]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=xq.device)
+    elif y.shape != (M, N):
+        raise ValueError("y must be [M, N]")
+    rc = load().w4a8_matmul(_dev_ptr(xq, "xq", torch.uint8), _dev_ptr(sx, "sx", torch.float32),
+                            _dev_ptr(qweight, "qweight", torch.int32), _dev_ptr(scales, "scales", torch.float16),
+                            _dev_ptr(zeros, "zeros", torch.float16), _dev_ptr(y, "y", torch.float16), M, N, K,
+                            group_size, _layout_id(layout), _stream_ptr(stream, xq.device))
+    _check(rc, "w4a8_matmul")
+    return y
 
 
 def w4a16_version():

@@ -92,6 +92,21 @@ int launch_prefill(const PrefillParams& p, void* stream);  // returns a hipError
 int launch_prefill_rb(const PrefillParams& p, void* stream);  // W4A16_TILE_REGISTER_B (w4a16_prefill_rb.hip)
 int launch_prefill_async(const PrefillParams& p, void* stream);  // W4A16_TILE_ASYNC (w4a16_prefill_async.hip)
 
+// ---- W4A8: E4M3 activations x 4-bit weights (w4a8_prefill.hip) ----
+struct W4A8Params {
+    const uint8_t* xq;        // E4M3 codes [M, K]
+    const float* sx;          // fp32 row scales [M]
+    const uint32_t* qweight;  // int32 [K/8, N]
+    const uint16_t* scales;   // fp16 [K/g, N]
+    const uint16_t* zeros;    // fp16 [K/g, N]
+    uint16_t* y;              // fp16 [M, N]
+    int M, N, K;
+    int group_shift;          // log2(rows per group): 7 or 8
+    int layout;               // W4A16_LAYOUT_*
+};
+int launch_w4a8_quantize(const uint16_t* x, uint8_t* xq, float* sx, int M, int K, void* stream);
+int launch_w4a8(const W4A8Params& p, void* stream);   // returns a hipError_t value
+
 // ---- dequant hook (w4a16_dequant.hip) ----
 int launch_dequant(const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                    uint8_t* codes, uint16_t* w, int N, int K, int group_shift, int layout, void* stream);

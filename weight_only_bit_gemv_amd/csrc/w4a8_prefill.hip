@@ -1,0 +1,305 @@
+// W4A8 on gfx950: 8-bit floating-point (E4M3) activations x the 4-bit weights of the W4A16
+// path, on the 8-bit matrix cores ("Beating FP16 with 4-bit Weights: A Portable W4A16 GEMM
+// in Triton", section "What's next": FP8 activations for a W4A8 variant; the GemLite
+// README lists FP8 x Wn with activations quantised dynamically, one scale per row).
+//
+// Two kernels:
+//   quantize_rows_kernel  x fp16 [M, K] -> codes xq [M, K] (E4M3) and row scales sx [M]:
+//                         sx = amax / 448 (1 for a zero row), xq = E4M3(x / sx), nearest-
+//                         even, saturating (the hardware conversion rounds to nearest even;
+//                         values are clamped to +-448 first, as it returns NaN above 464).
+//   w4a8_kernel           y = sx * sum_g s_g * sum_{k in g} dec(xq) * dec(E4M3(q - z)).
+//
+// The product kernel keeps the tiling of the async W4A16 tile (a work-group computes
+// 128 x 256 of y, 4 wavefronts side by side along N, each 128 rows x 64 columns as 8 x 4
+// tiles of 16 x 16) and its direct global-to-LDS loads, but a stage is one 128-row K group:
+// one v_mfma_f32_16x16x128_f8f6f4 per tile covers it. In that instruction lane (r, g)
+// (r = lane % 16, g = lane / 16) holds 32 bytes of row r of A and of column r of B, and
+// byte j of A pairs with byte j of B: the kernel gives byte j the K index 32 g + j on both
+// sides (activation bytes as they lie in memory, weight bytes from packed rows 4g .. 4g+3).
+// Each tile's product over the group comes out with a zero accumulator and is added to the
+// fp32 result times the group's scale of its column (four FMAs per instruction); the row
+// scale multiplies the result once at the end.
+//
+// Weight operand: the magic-number unpack of device.hpp gives q - z exactly in fp16, and
+// v_cvt_scalef32_pk_fp8_f16 (scale 1) rounds pairs of it to E4M3 (nearest even). q - z is
+// exact in E4M3 when |q - z| <= 16. The zero point is first clamped to [-448, 463]: that
+// keeps every |q - z| below 464 (the conversion's NaN threshold) and gives exactly the
+// saturated value for zero points beyond it.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "w4a16_device.hpp"
+#include "w4a16_internal.h"
+
+namespace w4a16 {
+
+namespace {
+
+typedef int int8v __attribute__((ext_vector_type(8)));
+typedef short short2v __attribute__((ext_vector_type(2)));
+typedef uint32_t uint4_vec __attribute__((ext_vector_type(4)));
+
+constexpr float kE4M3Max = 448.0f;
+
+// ---- activation quantiser ---------------------------------------------------------------
+
+constexpr int QT = 256;   // threads per row
+
+__global__ __launch_bounds__(QT) void quantize_rows_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ xq,
+                                                          float* __restrict__ sx, int K) {
+    const int m = blockIdx.x;
+    const uint4* row = reinterpret_cast<const uint4*>(x + (size_t)m * K);   // 8 fp16 per uint4
+    const int n8 = K / 8;
+    float amax = 0.f;
+    for (int i = threadIdx.x; i < n8; i += QT) {
+        const half8_t h = __builtin_bit_cast(half8_t, row[i]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)h[e]));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    __shared__ float wmax[QT / 64];
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float s = amax > 0.f ? amax / kE4M3Max : 1.0f;
+    if (threadIdx.x == 0) sx[m] = s;
+    uint2* out = reinterpret_cast<uint2*>(xq + (size_t)m * K);              // 8 codes per uint2
+    for (int i = threadIdx.x; i < n8; i += QT) {
+        const half8_t h = __builtin_bit_cast(half8_t, row[i]);
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = fminf(fmaxf((float)h[e] / s, -kE4M3Max), kE4M3Max);
+        int lo = 0, hi = 0;
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], lo, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], hi, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], hi, true);
+        out[i] = make_uint2((uint32_t)lo, (uint32_t)hi);
+    }
+}
+
+// ---- product kernel ---------------------------------------------------------------------
+
+constexpr int NT = 256;                // threads per work-group
+constexpr int BM = 128;                // rows of M per work-group
+constexpr int WNC = 64;                // columns per wavefront
+constexpr int BN = 4 * WNC;            // columns per work-group
+constexpr int TI = BM / 16;            // 16-row tiles per wavefront
+constexpr int KS = 128;                // K rows per stage (one 8-bit MFMA, one group of 128)
+constexpr int NS = 2;                  // LDS ring slots
+// LDS slot in 16-byte chunks: activations 128 rows x 8 chunks (128 codes), swizzled; packed
+// weights 16 rows x 64 column quads; scales then zeros of the stage's group, 32 chunks of 8
+// columns each
+constexpr int kAChunks = BM * 8;
+constexpr int kBChunks = (KS / 8) * (BN / 4);
+constexpr int kSzChunks = 64;
+constexpr int kChunks = kAChunks + kBChunks + kSzChunks;
+constexpr int kDmaPerStage = 4 + 4 + 1;  // per wavefront: activations, weights, scales/zeros
+static_assert(kDmaPerStage == 9, "stage_barrier_one_later counts 9 loads per stage");
+
+// Wait until this wavefront has at most one later stage of loads outstanding and every one
+// of its LDS reads has completed, then barrier.
+__device__ __forceinline__ void stage_barrier_one_later() {
+    asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
+__device__ __forceinline__ void reads_done_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
+
+// Physical chunk of activation chunk `ch` (0..7) of tile row `row` (XOR swizzle: the lanes
+// that read one chunk of 16 consecutive rows hit different 16-byte bank groups).
+__device__ __forceinline__ int a_slot(int row, int ch) { return row * 8 + (ch ^ ((row >> 1) & 7)); }
+
+// 16 bytes per lane from global memory (wave-uniform base in SGPRs + a 32-bit per-lane byte
+// offset) to LDS (wave-uniform LDS base in M0; the s_nop is the one wait state the M0 write
+// needs before an LDS-DMA load). Per-lane offsets instead of 64-bit pointers keep the
+// addresses of the 9 loads of a stage in 9 VGPRs.
+__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_addr)
+                 : "memory");
+}
+__device__ __forceinline__ void dma16_lanes(uint32_t voff, const void* sbase, uint32_t lds_addr, uint64_t lanes) {
+    uint64_t saved;
+    asm volatile("s_mov_b64 %0, exec\n\ts_mov_b64 exec, %4\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, %2\n\ts_mov_b64 exec, %0"
+                 : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(lds_addr), "s"(lanes) : "memory");
+}
+
+// E4M3 codes of q - z for the 8 codes of word w, in natural K order (two dwords).
+template <bool NAT>
+__device__ __forceinline__ uint2 fp8_word(uint32_t w, const ZeroOffsets& zo, const UnpackConsts& c) {
+    const half8_t d = unpack_sub(w, zo, c);   // linear: (q0,q4) (q1,q5) (q2,q6) (q3,q7); NAT: (q0,q1) .. (q6,q7)
+    short2v p0 = {0, 0}, p1 = {0, 0};
+    p0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(p0, half2_t{d[0], d[1]}, 1.0f, false);
+    p0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(p0, half2_t{d[2], d[3]}, 1.0f, true);
+    p1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(p1, half2_t{d[4], d[5]}, 1.0f, false);
+    p1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(p1, half2_t{d[6], d[7]}, 1.0f, true);
+    const uint32_t u0 = __builtin_bit_cast(uint32_t, p0), u1 = __builtin_bit_cast(uint32_t, p1);
+    if constexpr (NAT) return make_uint2(u0, u1);
+    // u0 = bytes (q0, q4, q1, q5), u1 = (q2, q6, q3, q7)
+    return make_uint2(__builtin_amdgcn_perm(u1, u0, 0x06040200u),    // (q0, q1, q2, q3)
+                      __builtin_amdgcn_perm(u1, u0, 0x07050301u));   // (q4, q5, q6, q7)
+}
+
+template <bool NAT>
+__global__ __launch_bounds__(NT, 2) void w4a8_kernel(W4A8Params p) {
+    extern __shared__ uint4 lds[];                           // NS slots of kChunks chunks
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+    const int nw = n0 + wave * WNC + 4 * lr;                 // the lane's first output column
+    const int KT = p.K / KS;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+    // per-lane byte offsets of the loads (a stage moves only the wave-uniform bases);
+    // instruction i of a wavefront fills chunks (4 i + wave) * 64 + lane of its region
+    uint32_t a_off[4], b_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = (4 * i + wave) * 64 + lane;
+        const int row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
+        a_off[i] = (uint32_t)(min(m0 + row, p.M - 1) * p.K + ch * 16);       // rows >= M: never stored
+        const int col = n0 + 4 * lane;
+        b_off[i] = (uint32_t)(((4 * i + wave) * p.N + (col < p.N ? col : 0)) * 4);   // columns >= N: never stored
+    }
+    // scales/zeros: lanes 0..15 of wavefront w load chunk 16 w + lane (scales for chunks
+    // 0..31, i.e. wavefronts 0 and 1, zeros for 32..63), 8 columns each (N % 8 == 0)
+    const int sz_col = n0 + ((wave * 16 + lane) & 31) * 8;
+    const uint32_t sz_off = (uint32_t)((sz_col < p.N ? sz_col : 0) * 2);
+    const uint16_t* sz_base = wave >= 2 ? p.zeros : p.scales;
+
+    auto issue = [&](int kt, int slot) {
+        const uint32_t sb = lds_base + (uint32_t)(slot * kChunks) * 16u;
+        const uint8_t* xa = p.xq + (size_t)kt * KS;
+        const uint32_t* wb = p.qweight + (size_t)kt * (KS / 8) * p.N;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(a_off[i], xa, sb + (uint32_t)((4 * i + wave) * 64) * 16u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(b_off[i], wb, sb + (uint32_t)(kAChunks + (4 * i + wave) * 64) * 16u);
+        const size_t grp = (size_t)((kt * KS) >> p.group_shift);
+        dma16_lanes(sz_off, sz_base + grp * p.N, sb + (uint32_t)(kAChunks + kBChunks + wave * 16) * 16u, 0xFFFFull);
+    };
+
+    const UnpackConsts uc = unpack_consts();
+    floatx4 acc[TI][4];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[i][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const uint4* sl) {
+        // the lane's four columns: scales and zero offsets of the group
+        const uint4* szl = sl + kAChunks + kBChunks + wave * 8 + (lr >> 1);
+        const uint2 sv = reinterpret_cast<const uint2*>(szl)[lr & 1];
+        const uint2 zv = reinterpret_cast<const uint2*>(szl + 32)[lr & 1];
+        const half2_t s01 = as_h2(sv.x), s23 = as_h2(sv.y), z01 = as_h2(zv.x), z23 = as_h2(zv.y);
+        const float sc[4] = {(float)s01[0], (float)s01[1], (float)s23[0], (float)s23[1]};
+        const _Float16 zc[4] = {z01[0], z01[1], z23[0], z23[1]};
+        // B operands: packed rows 4 lg + r (r = 0..3) give K 32 lg + 8 r .. + 7 of the 4 columns
+        uint4 raw[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) raw[r] = sl[kAChunks + (4 * lg + r) * 64 + wave * 16 + lr];
+        int8v b[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const _Float16 zt = (_Float16)fminf(fmaxf((float)zc[t], -448.0f), 463.0f);
+            const ZeroOffsets zo = zero_offsets(zt);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t w = t == 0 ? raw[r].x : t == 1 ? raw[r].y : t == 2 ? raw[r].z : raw[r].w;
+                const uint2 q8 = fp8_word<NAT>(w, zo, uc);
+                b[t][2 * r] = (int)q8.x;
+                b[t][2 * r + 1] = (int)q8.y;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // row tile i: its activation fragment (read one tile ahead), 4 MFMAs with a zero
+        // accumulator, then the group's scale of each column into the fp32 result
+        auto read_a = [&](int i) {
+            const int row = 16 * i + lr;
+            const uint4 a0 = sl[a_slot(row, 2 * lg)], a1 = sl[a_slot(row, 2 * lg + 1)];
+            return int8v{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        };
+        int8v a = read_a(0);
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+            int8v a_next = a;
+            if (i + 1 < TI) a_next = read_a(i + 1);
+            floatx4 g[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                g[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[t], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0,
+                                                                        0, 0);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][t][e] = fmaf(sc[t], g[t][e], acc[i][t][e]);
+            a = a_next;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Two-slot ring: stage kt + 1 loads while stage kt is computed. Past the last stage the
+    // ring is fed copies of it (never read), so every wait has the same count and the loop
+    // body is one basic block (branches in it make the compiler split and spill).
+    issue(0, 0);
+    issue(min(1, KT - 1), 1);
+    for (int kt = 0; kt < KT; ++kt) {
+        stage_barrier_one_later();                          // stage kt has landed
+        compute(lds + (kt & 1) * kChunks);
+        reads_done_barrier();                               // every wavefront is done with this slot
+        issue(min(kt + 2, KT - 1), kt & 1);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");       // no load may outlive the work-group
+
+    // epilogue: row scale, fp16; lane holds rows 4 lg + r of columns nw .. nw + 3 per tile
+    if (nw >= p.N) return;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = m0 + 16 * i + 4 * lg + r;
+            if (row < p.M) {
+                const float s = p.sx[row];
+                const half2_t lo = half2_t{(_Float16)(acc[i][0][r] * s), (_Float16)(acc[i][1][r] * s)};
+                const half2_t hi = half2_t{(_Float16)(acc[i][2][r] * s), (_Float16)(acc[i][3][r] * s)};
+                *reinterpret_cast<uint2*>(p.y + (size_t)row * p.N + nw) = make_uint2(as_u32(lo), as_u32(hi));
+            }
+        }
+}
+
+template <bool NAT>
+int launch_w4a8_t(const W4A8Params& p, hipStream_t s) {
+    const size_t lds = (size_t)NS * kChunks * 16;
+    static std::once_flag once;
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [&] {
+        attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&w4a8_kernel<NAT>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    });
+    if (attr != hipSuccess) return (int)attr;
+    const dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM), 1);
+    hipLaunchKernelGGL((w4a8_kernel<NAT>), grid, dim3(NT), lds, s, p);
+    return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_w4a8_quantize(const uint16_t* x, uint8_t* xq, float* sx, int M, int K, void* stream) {
+    hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)M), dim3(QT), 0, reinterpret_cast<hipStream_t>(stream),
+                       x, xq, sx, K);
+    return (int)hipGetLastError();
+}
+
+int launch_w4a8(const W4A8Params& p, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (p.N % 8 != 0 || p.K % KS != 0 || (p.group_shift != 7 && p.group_shift != 8)) return (int)hipErrorInvalidValue;
+    return p.layout == W4A16_LAYOUT_INTERLEAVED ? launch_w4a8_t<true>(p, s) : launch_w4a8_t<false>(p, s);
+}
+
+}  // namespace w4a16
