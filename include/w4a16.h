@@ -263,12 +263,23 @@ int w4a8_quantize_activations(const void* x, uint8_t* xq, float* sx, int64_t M, 
  * q - z is exact in E4M3 when |q - z| <= 16, i.e. for zero points in [-1, 16] (every
  * asymmetric group that contains 0, every symmetric group); otherwise it is rounded to E4M3
  * (nearest even, saturating at +-448) as part of the method.
- * Asynchronous on `stream`; deterministic (no atomics, no split-K). Errors: INVALID_ARG,
- * UNSUPPORTED (group size, N % 8, K, size), ALIGNMENT, HIP.
+ * Asynchronous on `stream`; deterministic (split-K partial sums are combined in a fixed
+ * order). When the output tiles underfill the chip the K range is split over several
+ * work-groups (w4a8_matmul_ex forces the count). Errors: INVALID_ARG, UNSUPPORTED (group
+ * size, N % 8, K, size), ALIGNMENT, HIP (launch or workspace failure).
  */
 int w4a8_matmul(const uint8_t* xq, const float* sx, const int32_t* qweight, const void* scales,
                 const void* zeros, void* y, int64_t M, int64_t N, int64_t K, int64_t group_size,
                 int layout, void* stream);
+
+/* w4a8_matmul_ex - w4a8_matmul with the split-K count forced: `splits` work-groups along K
+ * per 128 x 256 output tile (0: the library's choice; 1..K/128), summed in split order
+ * (deterministic). With splits > 1 the call uses the split-K workspace of `stream` (see
+ * w4a16_matmul on graph capture). Errors as w4a8_matmul, plus INVALID_ARG for splits out of
+ * range. */
+int w4a8_matmul_ex(const uint8_t* xq, const float* sx, const int32_t* qweight, const void* scales,
+                   const void* zeros, void* y, int64_t M, int64_t N, int64_t K, int64_t group_size,
+                   int layout, int splits, void* stream);
 
 /* w4a16_strerror - static description of an error code (never NULL). */
 const char* w4a16_strerror(int code);

@@ -264,3 +264,7 @@ def test_w4a8_entry_points_reject_bad_arguments():
     assert call(ptrs=bad) == lib.W4A16_ERR_ALIGNMENT
     nul = [P[0], None, P[2], P[3], P[4], ctypes.c_void_p(A + 0x5000)]
     assert call(ptrs=nul) == lib.W4A16_ERR_INVALID_ARG
+    ex = so.w4a8_matmul_ex
+    pp = [P[0], P[1], P[2], P[3], P[4], ctypes.c_void_p(A + 0x5000)]
+    assert ex(*pp, 4, 64, 256, 128, 0, -1, None) == lib.W4A16_ERR_INVALID_ARG
+    assert ex(*pp, 4, 64, 256, 128, 0, 3, None) == lib.W4A16_ERR_INVALID_ARG      # > K / 128

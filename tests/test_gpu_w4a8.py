@@ -145,3 +145,37 @@ def test_w4a8_prefill_shapes_sampled(lib, M, K, N):
     cols = np.unique(np.concatenate([np.arange(0, N, max(1, N // 40)), [N - 1]]))
     y_ref = oracle.matmul_w4a8(xq_ref, sx_ref, qw[:, cols], s[:, cols], z[:, cols])
     check_y(y[:, torch.from_numpy(cols).to(DEV)], y_ref, f"w4a8 prefill M={M} K={K} N={N}")
+
+
+SPLITS = [(130, 1024, 520, 2), (257, 2048, 264, 4), (64, 4096, 256, 8), (3, 768, 1032, 3), (200, 14336, 1416, 7),
+          (128, 256, 2056, 2), (70, 8192, 512, 0), (1, 4096, 4096, 0)]
+
+
+@pytest.mark.parametrize("layout", ["linear", "interleaved"])
+@pytest.mark.parametrize("M,K,N,splits", SPLITS, ids=[f"M{m}-K{k}-N{n}-S{s}" for m, k, n, s in SPLITS])
+def test_w4a8_split_k(lib, M, K, N, splits, layout):
+    print(f"\n[w4a8 split-K] S={splits} {layout} M={M} K={K} N={N}", flush=True)
+    qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=990 + M, std=0.02), 128, False, layout)
+    x = synth.activations(M, K, wid=9)
+    xq, sx = oracle.quantize_activations(x)
+    args = [dev(xq), dev(sx), dev(qw), dev(s), dev(z)]
+    y = lib.w4a8_matmul(*args, layout=layout, splits=splits).clone()
+    check_y(y, oracle.matmul_w4a8(xq, sx, qw, s, z, 128, layout), f"w4a8 split-K S={splits}")
+    for _ in range(2):                                   # same bits again: counters were reset
+        assert torch.equal(lib.w4a8_matmul(*args, layout=layout, splits=splits).view(torch.int16), y.view(torch.int16))
+
+
+def test_w4a8_split_k_shares_counters_with_w4a16(lib):
+    """W4A8 and W4A16 split-K calls alternate on one stream: each returns the arrival
+    counters to zero for the other."""
+    M, K, N = 96, 4096, 1024
+    qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=3, std=0.02))
+    x = synth.activations(M, K, wid=9)
+    xq, sx = oracle.quantize_activations(x)
+    a8 = [dev(xq), dev(sx), dev(qw), dev(s), dev(z)]
+    a16 = [dev(x), dev(qw), dev(s), dev(z)]
+    ref8 = oracle.matmul_w4a8(xq, sx, qw, s, z)
+    ref16 = oracle.matmul(x, qw, s, z)
+    for rep in range(3):
+        check_y(lib.w4a8_matmul(*a8, splits=4), ref8, f"w4a8 rep {rep}")
+        check_y(lib.w4a16_matmul(*a16, plan=dict(kernel=2, tile=3, splits=3)), ref16, f"w4a16 rep {rep}")

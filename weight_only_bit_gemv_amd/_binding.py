@@ -66,6 +66,8 @@ _SIGS = {
     "w4a16_dequant_fmt": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P], ctypes.c_int),
     "w4a8_quantize_activations": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
     "w4a8_matmul": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int, _P], ctypes.c_int),
+    "w4a8_matmul_ex": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int, ctypes.c_int, _P],
+                       ctypes.c_int),
     "w4a16_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "w4a16_last_error_detail": ([], ctypes.c_char_p),
     "w4a16_version": ([], ctypes.c_int),
@@ -286,8 +288,10 @@ def w4a8_quantize(x, stream=None):
     return xq, sx
 
 
-def w4a8_matmul(xq, sx, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, layout="linear", stream=None):
-    """y[M, N] = sx * (dec(xq) . dec(E4M3(q - z))) per group times its scales (W4A8)."""
+def w4a8_matmul(xq, sx, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, layout="linear", stream=None,
+                splits=0):
+    """y[M, N] = sx * (dec(xq) . dec(E4M3(q - z))) per group times its scales (W4A8);
+    `splits` forces the split-K count (0: the library's choice)."""
     import torch
     if xq.dim() != 2 or qweight.dim() != 2 or sx.dim() != 1:
         raise ValueError("xq and qweight must be 2-D, sx 1-D")
@@ -301,11 +305,11 @@ def w4a8_matmul(xq, sx, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, l
         y = torch.empty((M, N), dtype=torch.float16, device=xq.device)
     elif y.shape != (M, N):
         raise ValueError("y must be [M, N]")
-    rc = load().w4a8_matmul(_dev_ptr(xq, "xq", torch.uint8), _dev_ptr(sx, "sx", torch.float32),
-                            _dev_ptr(qweight, "qweight", torch.int32), _dev_ptr(scales, "scales", torch.float16),
-                            _dev_ptr(zeros, "zeros", torch.float16), _dev_ptr(y, "y", torch.float16), M, N, K,
-                            group_size, _layout_id(layout), _stream_ptr(stream, xq.device))
-    _check(rc, "w4a8_matmul")
+    rc = load().w4a8_matmul_ex(_dev_ptr(xq, "xq", torch.uint8), _dev_ptr(sx, "sx", torch.float32),
+                               _dev_ptr(qweight, "qweight", torch.int32), _dev_ptr(scales, "scales", torch.float16),
+                               _dev_ptr(zeros, "zeros", torch.float16), _dev_ptr(y, "y", torch.float16), M, N, K,
+                               group_size, _layout_id(layout), splits, _stream_ptr(stream, xq.device))
+    _check(rc, "w4a8_matmul_ex")
     return y
 
 

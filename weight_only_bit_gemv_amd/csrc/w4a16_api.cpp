@@ -166,6 +166,18 @@ int64_t auto_prefill_splits(int64_t M, int64_t N, int64_t K) {
     return s;
 }
 
+// Split-K of the W4A8 product (stages of 128 K rows): the same rule as the async W4A16 tile
+// in K rows (at least 1024 rows per split; doubled while the splits stay longer than 8192).
+int64_t auto_w4a8_splits(int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles = ceil_div(M, 128) * ceil_div(N, 256);
+    const int64_t stages = K / 128;
+    if (tiles > kPrefillSplitTarget) return 1;
+    int64_t s = std::max<int64_t>(1, (kPrefillSplitTarget + tiles / 2) / tiles);
+    s = std::min(s, std::max<int64_t>(1, stages / 8));
+    if (tiles * s <= kPrefillSplitTarget && stages / s > 64) s *= 2;
+    return s;
+}
+
 // Prefill tile choice (measured on MI355X): the async tile (direct-to-LDS loads, split-K
 // when its tiles underfill the chip) whenever N % 8 == 0; otherwise the register tile once
 // it has kRegisterTileMinGroups 128 x 256 work-groups, the 128 x 128 tile below that.
@@ -513,8 +525,9 @@ int w4a8_quantize_activations(const void* x, uint8_t* xq, float* sx, int64_t M, 
     return ok();
 }
 
-int w4a8_matmul(const uint8_t* xq, const float* sx, const int32_t* qweight, const void* scales, const void* zeros,
-                void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, int layout, void* stream) {
+int w4a8_matmul_ex(const uint8_t* xq, const float* sx, const int32_t* qweight, const void* scales, const void* zeros,
+                   void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, int layout, int splits,
+                   void* stream) {
     if (!xq || !sx || !qweight || !scales || !zeros || !y) return fail(W4A16_ERR_INVALID_ARG, "null pointer argument");
     if (!w4a16::layout_supported(layout)) return fail(W4A16_ERR_INVALID_ARG, "unknown layout %d", layout);
     int rc = check_gpu_shape(M, N, K, group_size);
@@ -538,9 +551,30 @@ int w4a8_matmul(const uint8_t* xq, const float* sx, const int32_t* qweight, cons
     p.K = (int)K;
     p.group_shift = w4a16::log2_exact(group_size);
     p.layout = layout;
+    const int64_t stages = K / 128;
+    if (splits < 0 || splits > stages)
+        return fail(W4A16_ERR_INVALID_ARG, "splits=%d must lie in 0..K/128 (%lld)", splits, (long long)stages);
+    int64_t S = splits ? splits : auto_w4a8_splits(M, N, K);
+    const int64_t per = ceil_div(stages, S);
+    S = ceil_div(stages, per);                                 // every split non-empty
+    p.splits = (int)S;
+    p.stages_per_split = (int)per;
+    if (S > 1) {
+        const int64_t tiles = ceil_div(M, 128) * ceil_div(N, 256);
+        Workspace w;
+        rc = get_workspace(stream, (uint64_t)tiles * S * w4a16::kPrefillTileFloats * 4, (uint64_t)tiles, &w);
+        if (rc) return rc;
+        p.ws = w.partials;
+        p.counters = w.counters;
+    }
     const int e = w4a16::launch_w4a8(p, stream);
     if (e != (int)hipSuccess) return fail(W4A16_ERR_HIP, "W4A8 kernel launch: %s", hipGetErrorString((hipError_t)e));
     return ok();
+}
+
+int w4a8_matmul(const uint8_t* xq, const float* sx, const int32_t* qweight, const void* scales, const void* zeros,
+                void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, int layout, void* stream) {
+    return w4a8_matmul_ex(xq, sx, qweight, scales, zeros, y, M, N, K, group_size, layout, 0, stream);
 }
 
 const char* w4a16_strerror(int code) {

@@ -42,6 +42,10 @@ typedef short short2v __attribute__((ext_vector_type(2)));
 typedef uint32_t uint4_vec __attribute__((ext_vector_type(4)));
 
 constexpr float kE4M3Max = 448.0f;
+constexpr int kRsrcRaw = 0x00020000;     // buffer resource word 3 for raw (untyped) access on gfx9
+constexpr int kCpolSc1 = 16;             // device-coherent (sc1) cache policy of a buffer access
+// s_waitcnt immediate for vmcnt(0) with expcnt/lgkmcnt left at their maxima (gfx9 encoding)
+constexpr int kWaitVmcnt0 = 0 | (0x7 << 4) | (0xf << 8);
 
 // ---- activation quantiser ---------------------------------------------------------------
 
@@ -153,7 +157,10 @@ __global__ __launch_bounds__(NT, 2) void w4a8_kernel(W4A8Params p) {
     const int lr = lane & 15, lg = lane >> 4;
     const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
     const int nw = n0 + wave * WNC + 4 * lr;                 // the lane's first output column
-    const int KT = p.K / KS;
+    // this work-group's stages: [kbase, kbase + KT) of the K / 128 stages (split-K), KT >= 1
+    const int split = blockIdx.z;
+    const int kbase = split * p.stages_per_split;
+    const int KT = min(p.stages_per_split, p.K / KS - kbase);
     const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
     // per-lane byte offsets of the loads (a stage moves only the wave-uniform bases);
@@ -247,30 +254,97 @@ __global__ __launch_bounds__(NT, 2) void w4a8_kernel(W4A8Params p) {
     // Two-slot ring: stage kt + 1 loads while stage kt is computed. Past the last stage the
     // ring is fed copies of it (never read), so every wait has the same count and the loop
     // body is one basic block (branches in it make the compiler split and spill).
-    issue(0, 0);
-    issue(min(1, KT - 1), 1);
+    issue(kbase, 0);
+    issue(kbase + min(1, KT - 1), 1);
     for (int kt = 0; kt < KT; ++kt) {
         stage_barrier_one_later();                          // stage kt has landed
         compute(lds + (kt & 1) * kChunks);
         reads_done_barrier();                               // every wavefront is done with this slot
-        issue(min(kt + 2, KT - 1), kt & 1);
+        issue(kbase + min(kt + 2, KT - 1), kt & 1);
     }
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");       // no load may outlive the work-group
 
-    // epilogue: row scale, fp16; lane holds rows 4 lg + r of columns nw .. nw + 3 per tile
-    if (nw >= p.N) return;
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
+    // y rows 4 lg + r of row tile i, columns nw .. nw + 3, from fp32 sums v[t][r] times the
+    // row scale
+    auto store_rows = [&](int i, const floatx4 (&v)[4]) {
+        if (nw >= p.N) return;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = m0 + 16 * i + 4 * lg + r;
             if (row < p.M) {
                 const float s = p.sx[row];
-                const half2_t lo = half2_t{(_Float16)(acc[i][0][r] * s), (_Float16)(acc[i][1][r] * s)};
-                const half2_t hi = half2_t{(_Float16)(acc[i][2][r] * s), (_Float16)(acc[i][3][r] * s)};
+                const half2_t lo = half2_t{(_Float16)(v[0][r] * s), (_Float16)(v[1][r] * s)};
+                const half2_t hi = half2_t{(_Float16)(v[2][r] * s), (_Float16)(v[3][r] * s)};
                 *reinterpret_cast<uint2*>(p.y + (size_t)row * p.N + nw) = make_uint2(as_u32(lo), as_u32(hi));
             }
         }
+    };
+    const int live_tiles = min(TI, (p.M - m0 + 15) / 16);   // row tiles with a row < M
+
+    if (p.splits > 1) {
+        // Split-K, as on the async W4A16 tile: every work-group publishes its fp32 partial
+        // with device-coherent (sc1) stores; the last of the tile's work-groups to arrive
+        // sums all of them in split order (so the result does not depend on arrival order),
+        // two row tiles at a time with four splits' loads in flight, and writes y.
+        __shared__ uint32_t ticket_lds;
+        const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            p.ws + (size_t)tile * p.splits * kPrefillTileFloats, 0, p.splits * kPrefillTileFloats * 4, kRsrcRaw);
+        // float4 (i, t) of this lane: partial offset ((wave * TI + i) * 4 + t) * 64 + lane;
+        // offsets of splits >= p.splits lie past the buffer's end, where loads return 0
+        auto off = [&](int s, int i, int t) {
+            return (s * (kPrefillTileFloats / 4) + ((wave * TI + i) * 4 + t) * 64 + lane) * 16;
+        };
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+            if (i < live_tiles)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint4_vec, acc[i][t]), rs, off(split, i, t), 0,
+                                                           kCpolSc1);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);              // this wavefront's partial stores have completed
+        __syncthreads();                                       // ... and every wavefront's
+        if (tid == 0)
+            ticket_lds = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (ticket_lds != (uint32_t)(p.splits - 1)) return;
+        if (tid == 0)                                          // ready for the next call
+            __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int i0 = 0; i0 < TI; i0 += 2) {
+            if (i0 >= live_tiles) break;
+            floatx4 sum[2][4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) sum[i][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int s0 = 0; s0 < p.splits; s0 += 4) {
+                floatx4 v[4][2][4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            v[u][i][t] = __builtin_bit_cast(
+                                floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs, off(s0 + u, i0 + i, t), 0, kCpolSc1));
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (s0 + u < p.splits)
+#pragma unroll
+                        for (int i = 0; i < 2; ++i)
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) sum[i][t] += v[u][i][t];
+            }
+            store_rows(i0, sum[0]);
+            store_rows(i0 + 1, sum[1]);
+        }
+        return;
+    }
+
+    // epilogue: lane holds rows 4 lg + r of columns nw .. nw + 3 of each row tile
+#pragma unroll
+    for (int i = 0; i < TI; ++i) store_rows(i, acc[i]);
 }
 
 template <bool NAT>
@@ -283,7 +357,7 @@ int launch_w4a8_t(const W4A8Params& p, hipStream_t s) {
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     });
     if (attr != hipSuccess) return (int)attr;
-    const dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM), 1);
+    const dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM), (unsigned)p.splits);
     hipLaunchKernelGGL((w4a8_kernel<NAT>), grid, dim3(NT), lds, s, p);
     return (int)hipGetLastError();
 }
@@ -298,7 +372,9 @@ int launch_w4a8_quantize(const uint16_t* x, uint8_t* xq, float* sx, int M, int K
 
 int launch_w4a8(const W4A8Params& p, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (p.N % 8 != 0 || p.K % KS != 0 || (p.group_shift != 7 && p.group_shift != 8)) return (int)hipErrorInvalidValue;
+    if (p.N % 8 != 0 || p.K % KS != 0 || (p.group_shift != 7 && p.group_shift != 8) || p.splits < 1 ||
+        p.stages_per_split < 1 || (p.splits > 1 && (!p.ws || !p.counters)))
+        return (int)hipErrorInvalidValue;
     return p.layout == W4A16_LAYOUT_INTERLEAVED ? launch_w4a8_t<true>(p, s) : launch_w4a8_t<false>(p, s);
 }
 
