@@ -60,8 +60,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_skinny_decode_sweep.json"
 # committed traffic counters stay valid while these are unchanged
 KERNEL_SOURCES = sorted(os.path.relpath(f, ROOT) for f in
                         glob.glob(os.path.join(ROOT, "weight_only_bit_gemv_amd", "csrc", "w4a16_skinny*")) +
-                        [os.path.join(ROOT, "weight_only_bit_gemv_amd", "csrc", n)
-                         for n in ("w4a16_device.hpp", "w4a16_api.cpp")])
+                        [os.path.join(ROOT, "weight_only_bit_gemv_amd", "csrc", "w4a16_device.hpp")])
 PREFILL_SOURCES = sorted(os.path.relpath(f, ROOT) for f in
                          glob.glob(os.path.join(ROOT, "weight_only_bit_gemv_amd", "csrc", "w4a16_prefill*")) +
                          [os.path.join(ROOT, "weight_only_bit_gemv_amd", "csrc", "w4a16_device.hpp")])
@@ -79,6 +78,16 @@ def kernel_source_hash(sources=None):
     for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def decode_kernel_hash():
+    """What the decode sweep's traffic depends on: the decode kernel's sources and the plan the
+    dispatcher picks for each of the sweep's calls (not the rest of the dispatcher's code)."""
+    import weight_only_bit_gemv_amd as lib
+    h = hashlib.sha256(kernel_source_hash().encode())
+    for (M, K, N, _) in workload_items("decode_sweep")[1]:
+        h.update(json.dumps(lib.w4a16_plan(M, N, K), sort_keys=True).encode())
     return h.hexdigest()[:16]
 
 
@@ -403,7 +412,7 @@ def load_traffic():
         d = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if d.get("kernel_source_sha") != kernel_source_hash():
+    if d.get("kernel_source_sha") != decode_kernel_hash():
         return None
     return d.get("traffic_bytes_per_launch")
 
@@ -618,6 +627,8 @@ PREFILL_PMC_SHAPE = (2048, 8192, 28672)      # M, K, N of the prefill counter pa
 PREFILL_KERNEL_NAMES = {1: "prefill_kernel (128x128 LDS tile)", 2: "prefill_rb_kernel (128x256 register tile)",
                         3: "prefill_async_kernel (128x256, direct-to-LDS ring)"}
 PREFILL_PMC_FILE = os.path.join(ROOT, "profiles", "prefill_counters_M2048_K8192_N28672.json")
+W4A8_PMC_FILE = os.path.join(ROOT, "profiles", "w4a8_counters_M2048_K8192_N28672.json")
+W4A8_SOURCES = [os.path.join("weight_only_bit_gemv_amd", "csrc", n) for n in ("w4a8_prefill.hip", "w4a16_device.hpp")]
 SIMDS = 1024                                  # 256 compute units x 4 SIMDs
 SCLK_GHZ = 2.4
 
@@ -632,39 +643,46 @@ def run_prefill_pmc_pass(args):
     wid = synth.WORKLOADS["prefill"]["wid"]
     runner = Runner(torch, lib, dev, stream, {(K, N): (K, N, wid, 0)}, [(M, K, N, (K, N))], 0)
     with torch.cuda.stream(stream):
+        if args.w4a8:
+            runner.launch_w4a8(0)                   # quantise once, outside the counted launches
         for _ in range(args.steps):
-            runner.launch(0, dict(kernel=lib.W4A16_KERNEL_PREFILL))
+            if args.w4a8:
+                runner.launch_w4a8(0)
+            else:
+                runner.launch(0, dict(kernel=lib.W4A16_KERNEL_PREFILL))
     stream.synchronize()
-    log(f"[pmc] {args.steps} prefill launches done")
+    log(f"[pmc] {args.steps} {'W4A8' if args.w4a8 else 'prefill'} launches done")
 
 
-def summarize_prefill_pmc(dirs):
-    """MFMA and LDS counters of the prefill kernel (runs with --kernel-trace and --pmc)."""
+def summarize_prefill_pmc(dirs, w4a8=False):
+    """MFMA and LDS counters of the prefill kernel, or of the W4A8 product kernel (runs with
+    --kernel-trace and --pmc)."""
     import csv
+    tag = "w4a8_kernel" if w4a8 else "prefill"
     vals, durs, names = {}, [], set()
     for d in dirs:
         for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for row in csv.DictReader(open(path)):
-                if "prefill" in row["Kernel_Name"]:
+                if tag in row["Kernel_Name"]:
                     vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
                     names.add(row["Kernel_Name"])
         for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
             for row in csv.DictReader(open(path)):
-                if "prefill" in row["Kernel_Name"]:
+                if tag in row["Kernel_Name"]:
                     durs.append(int(row["End_Timestamp"]) - int(row["Start_Timestamp"]))
     mean = {k: float(np.mean(v)) for k, v in vals.items()}
     M, K, N = PREFILL_PMC_SHAPE
     dur_ns = float(np.median(durs)) if durs else None
-    out = {"kernel_source_sha": kernel_source_hash(PREFILL_SOURCES), "shape_MKN": [M, K, N], "kernels": sorted(names),
-           "counters_mean_per_dispatch": mean, "kernel_ns_median": dur_ns,
+    out = {"kernel_source_sha": kernel_source_hash(W4A8_SOURCES if w4a8 else PREFILL_SOURCES), "shape_MKN": [M, K, N],
+           "kernels": sorted(names), "counters_mean_per_dispatch": mean, "kernel_ns_median": dur_ns,
            "TFLOPs": round(2 * M * K * N / dur_ns / 1e3, 1) if dur_ns else None}
     if dur_ns and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
-        # busy cycles summed over SIMDs (16 per 16x16x32 f16 MFMA) against every SIMD busy
-        # for the whole kernel at the nominal clock
+        # busy cycles summed over SIMDs against every SIMD busy for the whole kernel at the
+        # nominal clock
         out["mfma_busy_fraction"] = round(mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (dur_ns * SCLK_GHZ * SIMDS), 4)
     if "SQ_LDS_BANK_CONFLICT" in mean and "SQ_LDS_IDX_ACTIVE" in mean:
         out["lds_bank_conflict_over_active"] = round(mean["SQ_LDS_BANK_CONFLICT"] / mean["SQ_LDS_IDX_ACTIVE"], 4)
-    with open(PREFILL_PMC_FILE, "w") as f:
+    with open(W4A8_PMC_FILE if w4a8 else PREFILL_PMC_FILE, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out, indent=1))
@@ -719,7 +737,7 @@ def summarize_pmc(dirs):
     launches = len(SWEEP_M) * len(SWEEP_KN)
     alg = sum(alg_bytes(M, K, N) for (K, N) in SWEEP_KN for M in SWEEP_M) / launches
     traffic = out["FETCH_SIZE"]["kernel_bytes_mean"] + out["WRITE_SIZE"]["kernel_bytes_mean"]
-    summary = {"kernel_source_sha": kernel_source_hash(),
+    summary = {"kernel_source_sha": decode_kernel_hash(),
                "workload": "decode_sweep (15 shapes), mean over dispatches",
                "traffic_bytes_per_launch": round(traffic),
                "algorithmic_bytes_per_launch": round(alg),
@@ -750,12 +768,14 @@ def main():
     ap.add_argument("--pmc-pass", action="store_true")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR")
     ap.add_argument("--summarize-prefill-pmc", nargs="+", metavar="DIR")
+    ap.add_argument("--w4a8", action="store_true",
+                    help="with --pmc-pass/--summarize-prefill-pmc: the W4A8 product kernel instead")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc)
         return 0
     if args.summarize_prefill_pmc:
-        summarize_prefill_pmc(args.summarize_prefill_pmc)
+        summarize_prefill_pmc(args.summarize_prefill_pmc, args.w4a8)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the W4A16 path is built and timed on a single "
