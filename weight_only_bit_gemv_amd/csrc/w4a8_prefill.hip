@@ -15,8 +15,13 @@
 // tiles of 16 x 16) and its direct global-to-LDS loads, but a stage is one 128-row K group:
 // one v_mfma_f32_16x16x128_f8f6f4 per tile covers it. In that instruction lane (r, g)
 // (r = lane % 16, g = lane / 16) holds 32 bytes of row r of A and of column r of B, and
-// byte j of A pairs with byte j of B: the kernel gives byte j the K index 32 g + j on both
-// sides (activation bytes as they lie in memory, weight bytes from packed rows 4g .. 4g+3).
+// byte j of A pairs with byte j of B, so any assignment of K indices to (g, j) works if both
+// sides use it. The kernel gives bytes 0..15 of lane group g the K indices 16 g .. 16 g + 15
+// and bytes 16..31 the indices 64 + 16 g .. 64 + 16 g + 15: the activation bytes are then
+// the 16-byte LDS chunks g and 4 + g of the row (the four lane groups of one instruction
+// read four neighbouring chunks, which a bank-conflict probe showed conflict-free, while
+// chunks 2g and 2g + 1 conflict two ways), and the weight bytes come from packed rows
+// 2g, 2g + 1, 8 + 2g and 9 + 2g.
 // Each tile's product over the group comes out with a zero accumulator and is added to the
 // fp32 result times the group's scale of its column (four FMAs per instruction); the row
 // scale multiplies the result once at the end.
@@ -207,10 +212,11 @@ __global__ __launch_bounds__(NT, 2) void w4a8_kernel(W4A8Params p) {
         const half2_t s01 = as_h2(sv.x), s23 = as_h2(sv.y), z01 = as_h2(zv.x), z23 = as_h2(zv.y);
         const float sc[4] = {(float)s01[0], (float)s01[1], (float)s23[0], (float)s23[1]};
         const _Float16 zc[4] = {z01[0], z01[1], z23[0], z23[1]};
-        // B operands: packed rows 4 lg + r (r = 0..3) give K 32 lg + 8 r .. + 7 of the 4 columns
+        // B operands: byte 8r .. 8r + 7 of the lane's 32 come from packed row
+        // (r < 2 ? 2 lg + r : 8 + 2 lg + r - 2) (K 16 lg + 8r .. resp. 64 + 16 lg + 8(r-2) ..)
         uint4 raw[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) raw[r] = sl[kAChunks + (4 * lg + r) * 64 + wave * 16 + lr];
+        for (int r = 0; r < 4; ++r) raw[r] = sl[kAChunks + ((r < 2 ? 0 : 6) + 2 * lg + r) * 64 + wave * 16 + lr];
         int8v b[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -229,7 +235,7 @@ __global__ __launch_bounds__(NT, 2) void w4a8_kernel(W4A8Params p) {
         // accumulator, then the group's scale of each column into the fp32 result
         auto read_a = [&](int i) {
             const int row = 16 * i + lr;
-            const uint4 a0 = sl[a_slot(row, 2 * lg)], a1 = sl[a_slot(row, 2 * lg + 1)];
+            const uint4 a0 = sl[a_slot(row, lg)], a1 = sl[a_slot(row, 4 + lg)];
             return int8v{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
         };
         int8v a = read_a(0);
