@@ -141,10 +141,14 @@ __device__ __forceinline__ void dma16_lanes(uint32_t voff, const void* sbase, ui
 template <bool NAT>
 __device__ __forceinline__ uint2 fp8_word(uint32_t w, const ZeroOffsets& zo, const UnpackConsts& c) {
     const half8_t d = unpack_sub(w, zo, c);   // linear: (q0,q4) (q1,q5) (q2,q6) (q3,q7); NAT: (q0,q1) .. (q6,q7)
-    short2v p0 = {0, 0}, p1 = {0, 0};
-    p0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(p0, half2_t{d[0], d[1]}, 1.0f, false);
+    // Each conversion writes one half of its destination and keeps the other. The first of
+    // each pair starts from its own (dying) source register, whose other half the second
+    // conversion overwrites: no register has to be cleared first.
+    const half2_t d01 = half2_t{d[0], d[1]}, d45 = half2_t{d[4], d[5]};
+    short2v p0 = __builtin_bit_cast(short2v, d01), p1 = __builtin_bit_cast(short2v, d45);
+    p0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(p0, d01, 1.0f, false);
     p0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(p0, half2_t{d[2], d[3]}, 1.0f, true);
-    p1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(p1, half2_t{d[4], d[5]}, 1.0f, false);
+    p1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(p1, d45, 1.0f, false);
     p1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(p1, half2_t{d[6], d[7]}, 1.0f, true);
     const uint32_t u0 = __builtin_bit_cast(uint32_t, p0), u1 = __builtin_bit_cast(uint32_t, p1);
     if constexpr (NAT) return make_uint2(u0, u1);
@@ -231,14 +235,23 @@ __global__ __launch_bounds__(NT, 2) void w4a8_kernel(W4A8Params p) {
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        // row tile i: its activation fragment (read one tile ahead), 4 MFMAs with a zero
-        // accumulator, then the group's scale of each column into the fp32 result
+        // row tile i: its activation fragment (read one tile ahead) and 4 MFMAs with a zero
+        // accumulator; the group's scale of each column takes tile i's products into the fp32
+        // result after tile i + 1's MFMAs are issued, so the FMAs never wait on a matrix
+        // instruction that has just started
         auto read_a = [&](int i) {
             const int row = 16 * i + lr;
             const uint4 a0 = sl[a_slot(row, lg)], a1 = sl[a_slot(row, 4 + lg)];
             return int8v{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
         };
+        auto scale_into = [&](int i, const floatx4 (&g)[4]) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][t][e] = fmaf(sc[t], g[t][e], acc[i][t][e]);
+        };
         int8v a = read_a(0);
+        floatx4 gp[4];
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
             int8v a_next = a;
@@ -248,13 +261,14 @@ __global__ __launch_bounds__(NT, 2) void w4a8_kernel(W4A8Params p) {
             for (int t = 0; t < 4; ++t)
                 g[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[t], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0,
                                                                         0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i > 0) scale_into(i - 1, gp);
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[i][t][e] = fmaf(sc[t], g[t][e], acc[i][t][e]);
+            for (int t = 0; t < 4; ++t) gp[t] = g[t];
             a = a_next;
             __builtin_amdgcn_sched_barrier(0);
         }
+        scale_into(TI - 1, gp);
     };
 
     // Two-slot ring: stage kt + 1 loads while stage kt is computed. Past the last stage the
