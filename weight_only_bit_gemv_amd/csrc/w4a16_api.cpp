@@ -277,6 +277,12 @@ int complete_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, w4a16_pla
     pl->splits = (int32_t)splits;
     if (n_strips * splits > INT32_MAX || row_blocks > 65535)
         return fail(W4A16_ERR_UNSUPPORTED, "grid too large");
+    // The kernel addresses a wavefront's weights (kc K-steps of 16 N bytes), a row block's
+    // activations (16 row_tiles rows of 2 K bytes) and the scales/zeros with 32-bit byte
+    // offsets into buffer resources.
+    if (16 * N * (pl->kc + 1) > INT32_MAX || 32 * (int64_t)pl->row_tiles * K > INT32_MAX ||
+        (K / group_size) * N * 2 > INT32_MAX)
+        return fail(W4A16_ERR_UNSUPPORTED, "shape too large for the skinny kernel's 32-bit offsets (kc=%d)", pl->kc);
     return W4A16_OK;
 }
 

@@ -68,6 +68,36 @@ __device__ __forceinline__ _Float16 half_at(uint2 v, int t) {
     return half_at(t < 2 ? v.x : v.y, t & 1);
 }
 
+// The weight, activation and scale/zero streams of one wavefront as buffer resources:
+// the scalar base of the weights and activations sits at the wavefront's first K-step,
+// every lane adds a fixed 32-bit byte offset, and the K-step (or group) offset is a scalar
+// register, so the loop carries no 64-bit address arithmetic. A load beyond a resource's
+// range returns 0 instead of faulting.
+template <int MT>
+struct Streams {
+    __amdgpu_buffer_rsrc_t w, x, s, z;
+    int w_lane;          // bytes: packed row lg, column nl
+    int w_step;          // bytes per K-step: 4 packed rows of N words
+    int x_lane[MT];      // bytes: activation row of each M tile, K offset 8 lg
+    int sz_lane;         // bytes: column nl
+    int sz_step;         // bytes per group row: N halves
+    int gshift;          // log2(K-steps per group)
+};
+
+template <int LW>
+__device__ __forceinline__ typename Lanes<LW>::Words load_words(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    if constexpr (LW == 4) return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    else if constexpr (LW == 2) return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+    else return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+template <int LW>
+__device__ __forceinline__ typename Lanes<LW>::Halves load_halves(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    if constexpr (LW == 4) return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+    else if constexpr (LW == 2) return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
 // One segment: U consecutive K-steps (U * 32 rows) of one wavefront: U packed word groups
 // per lane, the matching activations, and the scale/zero of every group the segment
 // touches: SG = min(U, K-steps per group) K-steps of one group each, U / SG groups (a
@@ -85,22 +115,23 @@ struct Segment {
     uint4 xv[U][MT];
     Halves sv[NG], zv[NG];
 
-    __device__ __forceinline__ void load(const uint32_t* __restrict__ wbase, const uint16_t* const* xrow,
-                                         const SkinnyParams& p, int ks, int nl) {
-        const int grp = ks >> p.gshift;
+    // j: K-step of the segment's start counted from the wavefront's first K-step (weights and
+    // activations); ks: the same K-step counted from 0 (scale/zero group).
+    __device__ __forceinline__ void load(const Streams<MT>& st, int ks, int j) {
+        const int grp = ks >> st.gshift;
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            wv[u] = *reinterpret_cast<const Words*>(wbase + (size_t)(ks + u) * 4 * p.N);
+        for (int u = 0; u < U; ++u) wv[u] = load_words<LW>(st.w, st.w_lane, (j + u) * st.w_step);
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-            sv[g] = *reinterpret_cast<const Halves*>(p.scales + (size_t)(grp + g) * p.N + nl);
-            zv[g] = *reinterpret_cast<const Halves*>(p.zeros + (size_t)(grp + g) * p.N + nl);
+            sv[g] = load_halves<LW>(st.s, st.sz_lane, (grp + g) * st.sz_step);
+            zv[g] = load_halves<LW>(st.z, st.sz_lane, (grp + g) * st.sz_step);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-                xv[u][mt] = *reinterpret_cast<const uint4*>(xrow[mt] + (size_t)(ks + u) * kKStep);
+                xv[u][mt] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          st.x, st.x_lane[mt], (j + u) * kKStep * 2, 0));
     }
 
     // acc += scale * sum over each group of x * (q - zero), per column, in fp32.
@@ -244,15 +275,33 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
     const int chunk = split * W + wave;
     const int k0 = min(chunk * p.kc, KS);
     const int k1 = min(k0 + p.kc, KS);
-    const uint32_t* __restrict__ wbase = p.qweight + (size_t)lg * p.N + nl;
+    // Resources: weights from packed row 4 k0 on (clamped to the 32-bit range; a wavefront's
+    // own K range is far smaller), activations from row row0 on, scales/zeros whole. The
+    // lane offsets stay below 2^31: the dispatcher keeps 16 N kc, 2 K rows and 2 N K/g in
+    // range.
+    Streams<MT> st;
+    {
+        const size_t w_rows = (size_t)(p.K / 8 - 4 * k0) * p.N * 4;
+        st.w = __builtin_amdgcn_make_buffer_rsrc((void*)(p.qweight + (size_t)4 * k0 * p.N), 0,
+                                                 (int)min(w_rows, (size_t)0xffffffffu), kRsrcWord3);
+        st.x = __builtin_amdgcn_make_buffer_rsrc((void*)(p.x + (size_t)row0 * p.K + (size_t)k0 * kKStep), 0,
+                                                 (int)min(((size_t)(p.M - row0) * p.K - (size_t)k0 * kKStep) * 2, (size_t)0xffffffffu), kRsrcWord3);
+        const int sz_bytes = (p.K >> (p.gshift + 5)) * p.N * 2;
+        st.s = __builtin_amdgcn_make_buffer_rsrc((void*)p.scales, 0, sz_bytes, kRsrcWord3);
+        st.z = __builtin_amdgcn_make_buffer_rsrc((void*)p.zeros, 0, sz_bytes, kRsrcWord3);
+    }
+    st.w_lane = (lg * p.N + nl) * 4;
+    st.w_step = 16 * p.N;
     // A-operand rows beyond M only feed output rows beyond M, which are never stored, so
     // their loads are clamped to row M-1 instead of being predicated (a predicated load
     // would put a branch between a segment's loads and their use, and the compiler then
     // waits for every outstanding load at the branch's end).
-    const uint16_t* xrow[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-        xrow[mt] = p.x + (size_t)min(row0 + mt * 16 + lc, p.M - 1) * p.K + lg * 8;
+        st.x_lane[mt] = ((min(row0 + mt * 16 + lc, p.M - 1) - row0) * p.K + lg * 8) * 2;
+    st.sz_lane = nl * 2;
+    st.sz_step = p.N * 2;
+    st.gshift = p.gshift;
     const UnpackConsts uc = unpack_consts();
 
     floatx4 acc[MT][LW];
@@ -271,19 +320,19 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
     // registers, which leaves one segment in flight and drains the queue between segments).
     Segment<MT, LW, U, SG, NAT> sa, sb;
     const int nseg = (k1 - k0) / U;
-    if (nseg > 0) sa.load(wbase, xrow, p, k0, nl);
+    if (nseg > 0) sa.load(st, k0, 0);
     __builtin_amdgcn_sched_barrier(0);
     int i = 0;
     for (; i + 2 < nseg; i += 2) {
-        sb.load(wbase, xrow, p, k0 + (i + 1) * U, nl);
+        sb.load(st, k0 + (i + 1) * U, (i + 1) * U);
         __builtin_amdgcn_sched_barrier(0);
         sa.accumulate(acc, uc);
-        sa.load(wbase, xrow, p, k0 + (i + 2) * U, nl);
+        sa.load(st, k0 + (i + 2) * U, (i + 2) * U);
         __builtin_amdgcn_sched_barrier(0);
         sb.accumulate(acc, uc);
     }
     if (i + 1 < nseg) {
-        sb.load(wbase, xrow, p, k0 + (i + 1) * U, nl);
+        sb.load(st, k0 + (i + 1) * U, (i + 1) * U);
         __builtin_amdgcn_sched_barrier(0);
         sa.accumulate(acc, uc);
         sb.accumulate(acc, uc);
