@@ -268,3 +268,13 @@ def test_w4a8_entry_points_reject_bad_arguments():
     pp = [P[0], P[1], P[2], P[3], P[4], ctypes.c_void_p(A + 0x5000)]
     assert ex(*pp, 4, 64, 256, 128, 0, -1, None) == lib.W4A16_ERR_INVALID_ARG
     assert ex(*pp, 4, 64, 256, 128, 0, 3, None) == lib.W4A16_ERR_INVALID_ARG      # > K / 128
+
+
+def test_skinny_plan_offsets_fit_31_bits():
+    """The decode kernel addresses a wavefront's weights with 32-bit byte offsets: a forced
+    K range of kc K-steps must keep 16 N (kc + 1) bytes below 2^31."""
+    N, K = 1 << 20, 4096                                   # 16 N * 129 > 2^31 - 1 >= 16 N * 128
+    with pytest.raises(lib.W4A16Error) as e:
+        lib.w4a16_plan(1, N, K, kernel=lib.W4A16_KERNEL_SKINNY, kc=128, waves=4)
+    assert e.value.code == lib.W4A16_ERR_UNSUPPORTED
+    assert lib.w4a16_plan(1, N, K, kernel=lib.W4A16_KERNEL_SKINNY, kc=124, waves=4)["kc"] == 124
