@@ -75,7 +75,10 @@ extern "C" {
  * forces through w4a16_matmul_ex). Fields a caller sets to 0 are chosen by the library.
  *   kernel     W4A16_KERNEL_*.
  *   kc         SKINNY: K-steps of 32 rows that one wavefront streams: 1, 2 or a multiple
- *              of 4 (a multiple of seg).
+ *              of 4 (a multiple of seg). The kernel addresses a wavefront's weights with
+ *              32-bit byte offsets: 16 * N * (kc + 1) must stay below 2^31, else
+ *              UNSUPPORTED (also when 32 * row_tiles * K or 2 * N * K / group_size
+ *              reaches 2^31).
  *   splits     SKINNY: work-groups along K per column strip (output: derived from kc and
  *              waves; a caller may leave it 0 or give the matching value).
  *              PREFILL with W4A16_TILE_ASYNC: work-groups along K per output tile, each over
