@@ -179,3 +179,17 @@ def test_w4a8_split_k_shares_counters_with_w4a16(lib):
     for rep in range(3):
         check_y(lib.w4a8_matmul(*a8, splits=4), ref8, f"w4a8 rep {rep}")
         check_y(lib.w4a16_matmul(*a16, plan=dict(kernel=2, tile=3, splits=3)), ref16, f"w4a16 rep {rep}")
+
+
+@pytest.mark.parametrize("layout", ["linear", "interleaved"])
+@pytest.mark.parametrize("M,K,N,splits", [(70, 1280, 264, 3), (200, 2560, 520, 4), (5, 768, 136, 2)],
+                         ids=["M70-K1280-S3", "M200-K2560-S4", "M5-K768-S2"])
+def test_w4a8_split_k_groups_of_256(lib, M, K, N, splits, layout):
+    """Groups of 256 rows span two 128-row stages; a split may start in the middle of a
+    group, and both halves still take that group's scale."""
+    print(f"\n[w4a8 split-K g=256] S={splits} {layout} M={M} K={K} N={N}", flush=True)
+    qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=1200 + M, std=0.02), 256, False, layout)
+    x = synth.activations(M, K, wid=9)
+    xq, sx = oracle.quantize_activations(x)
+    y = lib.w4a8_matmul(dev(xq), dev(sx), dev(qw), dev(s), dev(z), group_size=256, layout=layout, splits=splits)
+    check_y(y, oracle.matmul_w4a8(xq, sx, qw, s, z, 256, layout), f"w4a8 g=256 split-K S={splits}")
