@@ -84,11 +84,15 @@ struct Streams {
     int gshift;          // log2(K-steps per group)
 };
 
+// Weights are read once per call: non-temporal loads (cache policy nt) keep them from
+// displacing the activations and partial sums in the caches.
+constexpr int kCpolNt = 2;
+
 template <int LW>
 __device__ __forceinline__ typename Lanes<LW>::Words load_words(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    if constexpr (LW == 4) return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-    else if constexpr (LW == 2) return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
-    else return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    if constexpr (LW == 4) return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCpolNt));
+    else if constexpr (LW == 2) return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kCpolNt));
+    else return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kCpolNt);
 }
 
 template <int LW>
