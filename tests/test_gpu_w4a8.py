@@ -129,12 +129,13 @@ def test_w4a8_end_to_end_and_repeatable(lib):
         assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
-PREFILL = [(2048, 8192, 28672), (512, 28672, 8192), (128, 8192, 8192)]
+PREFILL = [(2048, 8192, 28672), (512, 28672, 8192), (128, 8192, 8192), (32, 8192, 28672), (64, 28672, 8192)]
 
 
 @pytest.mark.parametrize("M,K,N", PREFILL, ids=[f"M{m}-K{k}-N{n}" for m, k, n in PREFILL])
 def test_w4a8_prefill_shapes_sampled(lib, M, K, N):
-    """The prefill workload's shapes at full size, checked on sampled columns."""
+    """The prefill workload's shapes at full size, checked on sampled columns (M = 32 and 64
+    run the 32- and 64-row work-group tiles)."""
     wid = synth.WORKLOADS["prefill"]["wid"]
     print(f"\n[w4a8 prefill] M={M} K={K} N={N}", flush=True)
     qw, s, z = oracle.quantize_pack(synth.weight(K, N, wid=wid))

@@ -103,9 +103,10 @@ struct W4A8Params {
     int M, N, K;
     int group_shift;          // log2(rows per group): 7 or 8
     int layout;               // W4A16_LAYOUT_*
+    int bm;                   // rows of M per work-group: 32, 64 or 128
     // split-K as on the async W4A16 tile: work-groups along K per output tile, each over
     // stages_per_split 128-row stages (the last over the rest, >= 1); fp32 partials of
-    // 128 x 256 per (tile, split) in ws, arrival counters per tile (zero between calls)
+    // up to 128 x 256 per (tile, split) in ws, arrival counters per tile (zero between calls)
     int splits;
     int stages_per_split;
     float* ws;

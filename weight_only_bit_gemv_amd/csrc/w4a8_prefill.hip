@@ -93,26 +93,26 @@ __global__ __launch_bounds__(QT) void quantize_rows_kernel(const uint16_t* __res
 // ---- product kernel ---------------------------------------------------------------------
 
 constexpr int NT = 256;                // threads per work-group
-constexpr int BM = 128;                // rows of M per work-group
 constexpr int WNC = 64;                // columns per wavefront
 constexpr int BN = 4 * WNC;            // columns per work-group
-constexpr int TI = BM / 16;            // 16-row tiles per wavefront
 constexpr int KS = 128;                // K rows per stage (one 8-bit MFMA, one group of 128)
 constexpr int NS = 2;                  // LDS ring slots
-// LDS slot in 16-byte chunks: activations 128 rows x 8 chunks (128 codes), swizzled; packed
-// weights 16 rows x 64 column quads; scales then zeros of the stage's group, 32 chunks of 8
-// columns each
-constexpr int kAChunks = BM * 8;
+// A work-group computes BM rows (32, 64 or 128: the library takes the smallest that holds M,
+// so small M does not pay for padding rows) x 256 columns. LDS slot in 16-byte chunks:
+// activations BM rows x 8 chunks (128 codes), swizzled; packed weights 16 rows x 64 column
+// quads; scales then zeros of the stage's group, 32 chunks of 8 columns each.
 constexpr int kBChunks = (KS / 8) * (BN / 4);
 constexpr int kSzChunks = 64;
-constexpr int kChunks = kAChunks + kBChunks + kSzChunks;
-constexpr int kDmaPerStage = 4 + 4 + 1;  // per wavefront: activations, weights, scales/zeros
-static_assert(kDmaPerStage == 9, "stage_barrier_one_later counts 9 loads per stage");
+constexpr int a_chunks(int bm) { return bm * 8; }
+constexpr int slot_chunks(int bm) { return a_chunks(bm) + kBChunks + kSzChunks; }
+// loads per wavefront and stage: activations (BM / 32), weights (4), scales/zeros (1)
+constexpr int dma_per_stage(int bm) { return bm / 32 + 4 + 1; }
 
-// Wait until this wavefront has at most one later stage of loads outstanding and every one
-// of its LDS reads has completed, then barrier.
+// Wait until this wavefront has at most one later stage of loads (N) outstanding and every
+// one of its LDS reads has completed, then barrier.
+template <int N>
 __device__ __forceinline__ void stage_barrier_one_later() {
-    asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" : : : "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 __device__ __forceinline__ void reads_done_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
@@ -157,8 +157,13 @@ __device__ __forceinline__ uint2 fp8_word(uint32_t w, const ZeroOffsets& zo, con
                       __builtin_amdgcn_perm(u1, u0, 0x07050301u));   // (q4, q5, q6, q7)
 }
 
-template <bool NAT>
+template <bool NAT, int BM>
 __global__ __launch_bounds__(NT, 2) void w4a8_kernel(W4A8Params p) {
+    static_assert(BM == 32 || BM == 64 || BM == 128, "work-group rows");
+    constexpr int TI = BM / 16;                              // 16-row tiles per wavefront
+    constexpr int NA = BM / 32;                              // activation loads per wavefront and stage
+    constexpr int kAChunks = a_chunks(BM);
+    constexpr int kChunks = slot_chunks(BM);
     extern __shared__ uint4 lds[];                           // NS slots of kChunks chunks
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -174,12 +179,15 @@ __global__ __launch_bounds__(NT, 2) void w4a8_kernel(W4A8Params p) {
 
     // per-lane byte offsets of the loads (a stage moves only the wave-uniform bases);
     // instruction i of a wavefront fills chunks (4 i + wave) * 64 + lane of its region
-    uint32_t a_off[4], b_off[4];
+    uint32_t a_off[NA], b_off[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NA; ++i) {
         const int c = (4 * i + wave) * 64 + lane;
         const int row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
         a_off[i] = (uint32_t)(min(m0 + row, p.M - 1) * p.K + ch * 16);       // rows >= M: never stored
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
         const int col = n0 + 4 * lane;
         b_off[i] = (uint32_t)(((4 * i + wave) * p.N + (col < p.N ? col : 0)) * 4);   // columns >= N: never stored
     }
@@ -194,7 +202,7 @@ __global__ __launch_bounds__(NT, 2) void w4a8_kernel(W4A8Params p) {
         const uint8_t* xa = p.xq + (size_t)kt * KS;
         const uint32_t* wb = p.qweight + (size_t)kt * (KS / 8) * p.N;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16(a_off[i], xa, sb + (uint32_t)((4 * i + wave) * 64) * 16u);
+        for (int i = 0; i < NA; ++i) dma16(a_off[i], xa, sb + (uint32_t)((4 * i + wave) * 64) * 16u);
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma16(b_off[i], wb, sb + (uint32_t)(kAChunks + (4 * i + wave) * 64) * 16u);
         const size_t grp = (size_t)((kt * KS) >> p.group_shift);
@@ -277,7 +285,7 @@ __global__ __launch_bounds__(NT, 2) void w4a8_kernel(W4A8Params p) {
     issue(kbase, 0);
     issue(kbase + min(1, KT - 1), 1);
     for (int kt = 0; kt < KT; ++kt) {
-        stage_barrier_one_later();                          // stage kt has landed
+        stage_barrier_one_later<dma_per_stage(BM)>();       // stage kt has landed
         compute(lds + (kt & 1) * kChunks);
         reads_done_barrier();                               // every wavefront is done with this slot
         issue(kbase + min(kt + 2, KT - 1), kt & 1);
@@ -367,18 +375,18 @@ __global__ __launch_bounds__(NT, 2) void w4a8_kernel(W4A8Params p) {
     for (int i = 0; i < TI; ++i) store_rows(i, acc[i]);
 }
 
-template <bool NAT>
+template <bool NAT, int BM>
 int launch_w4a8_t(const W4A8Params& p, hipStream_t s) {
-    const size_t lds = (size_t)NS * kChunks * 16;
+    const size_t lds = (size_t)NS * slot_chunks(BM) * 16;
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [&] {
-        attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&w4a8_kernel<NAT>),
+        attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&w4a8_kernel<NAT, BM>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     });
     if (attr != hipSuccess) return (int)attr;
     const dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM), (unsigned)p.splits);
-    hipLaunchKernelGGL((w4a8_kernel<NAT>), grid, dim3(NT), lds, s, p);
+    hipLaunchKernelGGL((w4a8_kernel<NAT, BM>), grid, dim3(NT), lds, s, p);
     return (int)hipGetLastError();
 }
 
@@ -393,9 +401,12 @@ int launch_w4a8_quantize(const uint16_t* x, uint8_t* xq, float* sx, int M, int K
 int launch_w4a8(const W4A8Params& p, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (p.N % 8 != 0 || p.K % KS != 0 || (p.group_shift != 7 && p.group_shift != 8) || p.splits < 1 ||
-        p.stages_per_split < 1 || (p.splits > 1 && (!p.ws || !p.counters)))
+        p.stages_per_split < 1 || (p.splits > 1 && (!p.ws || !p.counters)) || (p.bm != 32 && p.bm != 64 && p.bm != 128))
         return (int)hipErrorInvalidValue;
-    return p.layout == W4A16_LAYOUT_INTERLEAVED ? launch_w4a8_t<true>(p, s) : launch_w4a8_t<false>(p, s);
+    const bool nat = p.layout == W4A16_LAYOUT_INTERLEAVED;
+    if (p.bm == 32) return nat ? launch_w4a8_t<true, 32>(p, s) : launch_w4a8_t<false, 32>(p, s);
+    if (p.bm == 64) return nat ? launch_w4a8_t<true, 64>(p, s) : launch_w4a8_t<false, 64>(p, s);
+    return nat ? launch_w4a8_t<true, 128>(p, s) : launch_w4a8_t<false, 128>(p, s);
 }
 
 }  // namespace w4a16
