@@ -115,7 +115,7 @@ def test_dequant_rejects_bad_arguments():
 
 # ---- dispatcher (host only) ----
 
-PLAN_SHAPES = [(m, k, n) for m in (1, 2, 4, 8, 16, 17, 33, 48, 49, 64, 65, 128, 129, 512, 2048)
+PLAN_SHAPES = [(m, k, n) for m in (1, 2, 4, 8, 16, 17, 23, 24, 33, 48, 49, 63, 64, 65, 128, 129, 512, 2048)
                for (k, n) in [(4096, 4096), (4096, 14336), (14336, 4096), (2048, 1408), (8192, 28672),
                               (768, 2048), (4096, 128256), (128, 4), (384, 100), (4096, 28676)]]
 
@@ -126,7 +126,8 @@ def test_auto_plan_is_valid_and_covers_k(M, K, N):
     assert pl["kernel"] in (lib.W4A16_KERNEL_SKINNY, lib.W4A16_KERNEL_PREFILL)
     tiles = -(-M // 128) * -(-N // 128)
     if N % 8 == 0:
-        expect_prefill = (M >= 65 and (M > 128 or K * N >= 1 << 25)) or (M >= 49 and K * N >= 1 << 27)
+        expect_prefill = ((M >= 65 and (M > 128 or K * N >= 1 << 25)) or (M >= 24 and K * N >= 1 << 27) or
+                          (M >= 64 and K * N >= 1 << 25 and K <= N))
     else:
         expect_prefill = M >= 65 and (tiles >= 128 or M > 1024)
     assert pl["kernel"] == (lib.W4A16_KERNEL_PREFILL if expect_prefill else lib.W4A16_KERNEL_SKINNY)
@@ -137,8 +138,13 @@ def test_auto_plan_is_valid_and_covers_k(M, K, N):
         assert pl["tile"] == expect
         if expect == lib.W4A16_TILE_ASYNC:
             stages = K // 64
-            want = 1 if groups > 256 else min(max(1, (256 + groups // 2) // groups), max(1, stages // 16))
-            if groups * want <= 256 and stages // want > 128:
+            bm = 32 if M <= 32 else 64 if M <= 64 else 128           # rows per work-group
+            target, min_stages = (512, 12) if bm < 128 else (256, 16)
+            groups = -(-M // bm) * -(-N // 256)
+            want = 1 if groups > target else min(max(1, (target + groups // 2) // groups), max(1, stages // min_stages))
+            if bm < 128:
+                want = 1 << (want.bit_length() - 1)                 # power of two
+            if groups * want <= target and stages // want > 128:
                 want *= 2                                # two work-groups per compute unit
             assert pl["splits"] <= want and (pl["splits"] > 1) == (want > 1)
             per = 2 * -(-stages // (2 * pl["splits"]))   # even stages per split, all covered

@@ -156,13 +156,28 @@ constexpr int64_t kPrefillSplitTarget = 256;
 constexpr int64_t kMinSplitStages = 16;
 constexpr int64_t kLongSplitStages = 128;
 
+// Rows of M per work-group of the async tile: the smallest of 32, 64 and 128 that holds M
+// (a 128-row tile at M = 64 spends half its MFMAs on padding rows).
+int async_rows(int64_t M) { return M <= 32 ? 32 : M <= 64 ? 64 : 128; }
+
+// The 32- and 64-row work-groups (M <= 64) are lighter: they aim at 512 work-groups, each
+// split at least kMinSplitStagesSmall stages long, rounded down to a power of two (a sweep
+// of 1..32 splits on the six prefill shapes at M = 24..64 picked these counts or came within
+// 3 % of them; uneven splits measured worse than their power-of-two neighbours).
+constexpr int64_t kMinSplitStagesSmall = 12;
+
 int64_t auto_prefill_splits(int64_t M, int64_t N, int64_t K) {
-    const int64_t tiles = ceil_div(M, 128) * ceil_div(N, 256);
+    const int bm = async_rows(M);
+    const bool small = bm < 128;
+    const int64_t target = small ? 2 * kPrefillSplitTarget : kPrefillSplitTarget;
+    const int64_t tiles = ceil_div(M, bm) * ceil_div(N, 256);
     const int64_t stages = K / 64;
-    if (tiles > kPrefillSplitTarget) return 1;
-    int64_t s = std::max<int64_t>(1, (kPrefillSplitTarget + tiles / 2) / tiles);
-    s = std::min(s, std::max<int64_t>(1, stages / kMinSplitStages));
-    if (tiles * s <= kPrefillSplitTarget && stages / s > kLongSplitStages) s *= 2;
+    if (tiles > target) return 1;
+    int64_t s = std::max<int64_t>(1, (target + tiles / 2) / tiles);
+    s = std::min(s, std::max<int64_t>(1, stages / (small ? kMinSplitStagesSmall : kMinSplitStages)));
+    if (small)
+        while (s & (s - 1)) s &= s - 1;                      // largest power of two <= s
+    if (tiles * s <= target && stages / s > kLongSplitStages) s *= 2;
     return s;
 }
 
@@ -199,16 +214,19 @@ int32_t auto_prefill_tile(int64_t M, int64_t N) {
     return ceil_div(M, 128) * ceil_div(N, 256) >= kRegisterTileMinGroups ? W4A16_TILE_REGISTER_B : W4A16_TILE_LDS;
 }
 
-// Kernel choice (measured crossover on MI355X): the weight-streaming kernel up to M = 64
-// (up to M = 48 for the largest matrices, >= kPrefillHugeKN elements, where the split-K
-// prefill streams the weights faster at M = 64). Above, with N % 8 == 0 (async split-K
-// prefill available): prefill from M = 65 when the matrix has >= kPrefillLargeKN elements,
+// Kernel choice (measured crossover on MI355X): with N % 8 == 0 (the async split-K prefill
+// tile, whose 32- and 64-row work-groups serve small M): prefill from M = 24 for the largest
+// matrices (>= kPrefillHugeKN elements: 8192x28672 at M = 24..32 41-44 us against 43-50 us
+// streaming), from M = 64 for matrices of >= kPrefillLargeKN elements that are at least as
+// wide as deep (8192^2 and 4096x14336 at M = 64: 25.3 / 22.3 us against 27.7 / 23.9), from
+// M = 65 for the deeper ones (14336x4096 streams faster at M = 64: 26.2 against 29.5 us),
 // from M = 129 otherwise (for small matrices the streaming kernel still wins at M = 128).
 // Without it: prefill once its 128 x 128 output tiles number at least kPrefillMinTiles (half
 // a tile per compute unit; with fewer it leaves the chip idle and streaming the weights once
 // per 64 rows is faster), and always beyond M = 1024.
 constexpr int64_t kPrefillMinM = 65;
-constexpr int64_t kPrefillMinMHuge = 49;
+constexpr int64_t kPrefillMinMWide = 64;
+constexpr int64_t kPrefillMinMHuge = 24;
 constexpr int64_t kPrefillLargeKN = int64_t(1) << 25;
 constexpr int64_t kPrefillHugeKN = int64_t(1) << 27;
 constexpr int64_t kPrefillMinTiles = 128;
@@ -217,6 +235,7 @@ constexpr int64_t kSkinnyMaxM = 1024;
 int64_t auto_kernel(int64_t M, int64_t N, int64_t K) {
     if (N % 8 == 0) {
         if (M >= kPrefillMinMHuge && K * N >= kPrefillHugeKN) return W4A16_KERNEL_PREFILL;
+        if (M >= kPrefillMinMWide && K * N >= kPrefillLargeKN && K <= N) return W4A16_KERNEL_PREFILL;
         if (M < kPrefillMinM) return W4A16_KERNEL_SKINNY;
         return (M > 128 || K * N >= kPrefillLargeKN) ? W4A16_KERNEL_PREFILL : W4A16_KERNEL_SKINNY;
     }
@@ -383,10 +402,11 @@ int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const
         q.tile = pl.tile;
         q.group_shift = w4a16::log2_exact(group_size);
         q.layout = layout;
+        q.bm = pl.tile == W4A16_TILE_ASYNC ? async_rows(M) : 128;
         q.splits = std::max(1, pl.splits);
         q.stages_per_split = (int)prefill_stages_per_split(K / 64, q.splits);
         if (q.splits > 1) {
-            const int64_t tiles = ceil_div(M, 128) * ceil_div(N, 256);
+            const int64_t tiles = ceil_div(M, q.bm) * ceil_div(N, 256);
             Workspace w;
             rc = get_workspace(stream, (uint64_t)tiles * q.splits * w4a16::kPrefillTileFloats * 4,
                                (uint64_t)tiles, &w);

@@ -77,9 +77,10 @@ struct PrefillParams {
     int tile;                 // W4A16_TILE_LDS, W4A16_TILE_REGISTER_B or W4A16_TILE_ASYNC
     int group_shift;          // log2(rows per scale/zero group)
     int layout;               // W4A16_LAYOUT_*
+    int bm;                   // W4A16_TILE_ASYNC: rows of M per work-group, 32, 64 or 128
     // split-K (W4A16_TILE_ASYNC only): work-groups along K per output tile, each over
     // stages_per_split 64-row stages (the last over the rest, >= 2); fp32 partials of
-    // 128 x 256 per (tile, split) in ws, arrival counters per tile (zero between calls)
+    // up to 128 x 256 per (tile, split) in ws, arrival counters per tile (zero between calls)
     int splits;
     int stages_per_split;
     float* ws;

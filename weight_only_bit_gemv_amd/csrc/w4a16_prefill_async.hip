@@ -56,34 +56,34 @@ namespace w4a16 {
 namespace {
 
 constexpr int NT = 256;                // threads per work-group
-constexpr int BM = 128;                // rows of M per work-group
 constexpr int WNC = 64;                // columns per wavefront
 constexpr int BN = 4 * WNC;            // columns per work-group
-constexpr int TI = BM / 16;            // 16-row MFMA tiles per wavefront
 constexpr int NS = 3;                  // LDS ring slots
-// LDS slot layout in 16-byte chunks
-constexpr int kAChunks = BM * 8;       // activations: 128 rows x 8 chunks (64 fp16), swizzled
-constexpr int kBChunks = 8 * (BN / 4); // packed weights: 8 rows x 64 column quads
-template <bool G32> struct Slot {
+// A work-group computes BM rows (32, 64 or 128: the library takes the smallest that holds
+// M) x 256 columns. LDS slot layout in 16-byte chunks: activations BM rows x 8 chunks (64
+// fp16), swizzled; packed weights 8 rows x 64 column quads; scales and zeros.
+constexpr int kBChunks = 8 * (BN / 4);
+template <bool G32, int BM> struct Slot {
+    static constexpr int kAChunks = BM * 8;
     static constexpr int kSzChunks = G32 ? 128 : 64;   // per group: 32 scale + 32 zero chunks
     static constexpr int kChunks = kAChunks + kBChunks + kSzChunks;
     static constexpr int kSzLanes = G32 ? 32 : 16;     // lanes per wavefront loading them
+    // loads per wavefront and stage: activations (BM / 32), weights (2), scales/zeros (1)
+    static constexpr int kDmaPerStage = BM / 32 + 2 + 1;
 };
-constexpr int kDmaPerStage = 4 + 2 + 1;  // per wavefront: activations, weights, scales/zeros
 constexpr int kRsrcRaw = 0x00020000;     // buffer resource word 3 for raw (untyped) access on gfx9
 constexpr int kCpolSc1 = 16;             // device-coherent (sc1) cache policy of a buffer access
 // s_waitcnt immediate for vmcnt(0) with expcnt/lgkmcnt left at their maxima (gfx9 encoding)
 constexpr int kWaitVmcnt0 = 0 | (0x7 << 4) | (0xf << 8);
 typedef uint32_t uint4_vec __attribute__((ext_vector_type(4)));
-static_assert(kDmaPerStage == 7, "stage_barrier counts 7 loads per stage");
 
-// Wait until this wavefront has at most LATER stages of loads outstanding (the stages
-// issued after the one awaited) and every one of its LDS reads has completed, then barrier.
-template <int LATER>
+// Wait until this wavefront has at most LATER stages of DMA loads each outstanding (the
+// stages issued after the one awaited) and every one of its LDS reads has completed, then
+// barrier.
+template <int LATER, int DMA>
 __device__ __forceinline__ void stage_barrier() {
     static_assert(LATER == 1 || LATER == 2, "the ring waits with one or two later stages in flight");
-    if constexpr (LATER == 1) asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" : : : "memory");
-    if constexpr (LATER == 2) asm volatile("s_waitcnt vmcnt(14) lgkmcnt(0)\n\ts_barrier" : : : "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(LATER * DMA) : "memory");
 }
 
 // Physical chunk of activation chunk `ch` (0..7) of tile row `row`: the 16 lanes that read
@@ -133,9 +133,13 @@ struct BRaw {
     uint4 w;
 };
 
-template <bool G32, bool NAT>
+template <bool G32, bool NAT, int BM>
 __global__ __launch_bounds__(NT, 2) void prefill_async_kernel(PrefillParams p) {
-    typedef Slot<G32> S;
+    static_assert(BM == 32 || BM == 64 || BM == 128, "work-group rows");
+    typedef Slot<G32, BM> S;
+    constexpr int TI = BM / 16;                              // 16-row MFMA tiles per wavefront
+    constexpr int NA = BM / 32;                              // activation loads per wavefront and stage
+    constexpr int kAChunks = S::kAChunks;
     extern __shared__ uint4 lds[];                           // NS slots of S::kChunks chunks
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -151,9 +155,9 @@ __global__ __launch_bounds__(NT, 2) void prefill_async_kernel(PrefillParams p) {
 
     // Per-lane sources of stage 0; stage kt adds a uniform offset. Instruction i of a
     // wavefront fills chunks (4 i + wave) * 64 + lane of its region.
-    const uint16_t* a_src[4];
+    const uint16_t* a_src[NA];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NA; ++i) {
         const int c = (4 * i + wave) * 64 + lane;
         const int row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);   // inverse of a_slot
         a_src[i] = p.x + (size_t)min(m0 + row, p.M - 1) * p.K + ch * 8;   // rows >= M: not stored
@@ -175,7 +179,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_async_kernel(PrefillParams p) {
     auto issue = [&](int kt, int slot) {
         const uint32_t sb = lds_base + (uint32_t)(slot * S::kChunks) * 16u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16(a_src[i] + (size_t)kt * 64, sb + (uint32_t)((4 * i + wave) * 64) * 16u);
+        for (int i = 0; i < NA; ++i) dma16(a_src[i] + (size_t)kt * 64, sb + (uint32_t)((4 * i + wave) * 64) * 16u);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
             dma16(b_src[i] + (size_t)kt * 8 * p.N, sb + (uint32_t)(kAChunks + (4 * i + wave) * 64) * 16u);
@@ -212,11 +216,12 @@ __global__ __launch_bounds__(NT, 2) void prefill_async_kernel(PrefillParams p) {
     auto read_a = [&](const uint4* sl, int j, int i) {
         return __builtin_bit_cast(half8_t, sl[a_slot(16 * i + lr, 4 * j + lg)]);
     };
-    // The 32 MFMAs of one K-step on (a, b), in 8 chunks of 4 (one activation fragment each).
-    // NEXT: the chunks also prepare the next K-step, K-step nj of slot nsl: its weights,
-    // scales and zeros are read from LDS before the first chunk, their words dequantised in
-    // chunks 1 to 4 (one each; chunk 0 covers the read latency), and fragment i is re-read
-    // into a[i] in chunk i, after its four MFMAs. Scheduling barriers between the chunks
+    // The 4 TI MFMAs of one K-step on (a, b), in TI chunks of 4 (one activation fragment
+    // each). NEXT: the chunks also prepare the next K-step, K-step nj of slot nsl: its
+    // weights, scales and zeros are read from LDS before the first chunk, their words
+    // dequantised in chunks 1 to 4 (one each; chunk 0 covers the read latency; after the
+    // last chunk when there are fewer), and fragment i is re-read into a[i] in chunk i,
+    // after its four MFMAs. Scheduling barriers between the chunks
     // keep the compiler from gathering the VALU work in one place.
     auto kstep = [&](half8_t (&a)[TI], const uint4 (&b)[4], auto next, const uint4* nsl, int nj, uint4 (&nb)[4]) {
         constexpr bool NEXT = decltype(next)::value;
@@ -234,6 +239,11 @@ __global__ __launch_bounds__(NT, 2) void prefill_async_kernel(PrefillParams p) {
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        // with fewer than 5 row tiles the chunks cover words 0 .. TI - 2; the rest follow
+        if constexpr (NEXT) {
+#pragma unroll
+            for (int t = (TI - 1 < 4 ? TI - 1 : 4); t < 4; ++t) dequant_word(r, t, nb[t]);
+        }
     };
 
     // Prologue: NS stages in flight, the first K-step's operands in registers. Past the
@@ -242,7 +252,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_async_kernel(PrefillParams p) {
     // the loop body is one basic block.
 #pragma unroll
     for (int s = 0; s < NS; ++s) issue(kbase + min(s, KT - 1), s);
-    stage_barrier<NS - 1>();
+    stage_barrier<NS - 1, S::kDmaPerStage>();
     half8_t a[TI];
     uint4 b0[4], b1[4];
     {
@@ -258,7 +268,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_async_kernel(PrefillParams p) {
         kstep(a, b0, std::true_type{}, lds + slot * S::kChunks, 1, b1);   // K-step 0; prepares K-step 1
         // stage kt + 1 has landed and every wavefront is done with this slot, which takes
         // stage kt + NS
-        stage_barrier<NS - 2>();
+        stage_barrier<NS - 2, S::kDmaPerStage>();
         issue(kbase + min(kt + NS, KT - 1), slot);
         slot = slot + 1 == NS ? 0 : slot + 1;
         kstep(a, b1, std::true_type{}, lds + slot * S::kChunks, 0, b0);   // K-step 1; prepares the next stage's K-step 0
@@ -353,18 +363,18 @@ __global__ __launch_bounds__(NT, 2) void prefill_async_kernel(PrefillParams p) {
     for (int i = 0; i < TI; ++i) store_rows(i, acc[i]);
 }
 
-template <bool G32, bool NAT>
+template <bool G32, bool NAT, int BM>
 int launch_async(const PrefillParams& p, hipStream_t s) {
-    const size_t lds = (size_t)NS * Slot<G32>::kChunks * 16;
+    const size_t lds = (size_t)NS * Slot<G32, BM>::kChunks * 16;
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [&] {
-        attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_async_kernel<G32, NAT>),
+        attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_async_kernel<G32, NAT, BM>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     });
     if (attr != hipSuccess) return (int)attr;
     const dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM), (unsigned)p.splits);
-    hipLaunchKernelGGL((prefill_async_kernel<G32, NAT>), grid, dim3(NT), lds, s, p);
+    hipLaunchKernelGGL((prefill_async_kernel<G32, NAT, BM>), grid, dim3(NT), lds, s, p);
     return (int)hipGetLastError();
 }
 
@@ -372,11 +382,20 @@ int launch_async(const PrefillParams& p, hipStream_t s) {
 
 int launch_prefill_async(const PrefillParams& p, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (p.N % 8 != 0 || p.splits < 1 || p.stages_per_split < 1 || (p.splits > 1 && (!p.ws || !p.counters)))
+    if (p.N % 8 != 0 || p.splits < 1 || p.stages_per_split < 1 || (p.splits > 1 && (!p.ws || !p.counters)) ||
+        (p.bm != 32 && p.bm != 64 && p.bm != 128))
         return (int)hipErrorInvalidValue;
     const bool g32 = p.group_shift == 5, nat = p.layout == W4A16_LAYOUT_INTERLEAVED;
-    if (g32) return nat ? launch_async<true, true>(p, s) : launch_async<true, false>(p, s);
-    return nat ? launch_async<false, true>(p, s) : launch_async<false, false>(p, s);
+#define W4A16_ASYNC_BM(BM_)                                                                       \
+    if (p.bm == BM_) {                                                                            \
+        if (g32) return nat ? launch_async<true, true, BM_>(p, s) : launch_async<true, false, BM_>(p, s); \
+        return nat ? launch_async<false, true, BM_>(p, s) : launch_async<false, false, BM_>(p, s);       \
+    }
+    W4A16_ASYNC_BM(32)
+    W4A16_ASYNC_BM(64)
+    W4A16_ASYNC_BM(128)
+#undef W4A16_ASYNC_BM
+    return (int)hipErrorInvalidValue;
 }
 
 }  // namespace w4a16
