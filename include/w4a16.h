@@ -67,8 +67,9 @@ extern "C" {
 #define W4A16_TILE_LDS         1  /* 128 x 128 output tile, weights and activations in LDS  */
 #define W4A16_TILE_REGISTER_B  2  /* 128 x 256 output tile, weights dequantised in registers,*/
                                   /* activations in LDS (fewer LDS bytes per MFMA)          */
-#define W4A16_TILE_ASYNC       3  /* 128 x 256 output tile, all operands loaded straight     */
-                                  /* into a 3-stage LDS ring (needs N % 8 == 0)             */
+#define W4A16_TILE_ASYNC       3  /* 128 x 256 output tile (64 or 32 rows when M is that     */
+                                  /* small), all operands loaded straight into a 3-stage    */
+                                  /* LDS ring (needs N % 8 == 0)                            */
 
 /*
  * Execution plan of one w4a16_matmul call (what the dispatcher chose, or what a caller
@@ -82,9 +83,11 @@ extern "C" {
  *   splits     SKINNY: work-groups along K per column strip (output: derived from kc and
  *              waves; a caller may leave it 0 or give the matching value).
  *              PREFILL with W4A16_TILE_ASYNC: work-groups along K per output tile, each over
- *              an even number of 64-row stages (0: enough for 256 work-groups with >= 8
- *              stages each; 1 when the tiles alone reach 256); at most K/128; the completed
- *              plan holds the count actually used. Other tiles: 0 or 1 (output 1).
+ *              an even number of 64-row stages (0: about 256 work-groups with >= 16 stages
+ *              each, or for M <= 64, whose work-groups hold 32 or 64 rows, about 512 with
+ *              >= 12 stages each and a power of two; 1 when the tiles alone reach that);
+ *              at most K/128; the completed plan holds the count actually used. Other
+ *              tiles: 0 or 1 (output 1).
  *   row_tiles  SKINNY: 16-row MFMA tiles per work-group (1..4; default ceil(M/16) <= 4;
  *              at most 2 when cols < 64).
  *   tile       PREFILL: W4A16_TILE_LDS, W4A16_TILE_REGISTER_B or W4A16_TILE_ASYNC (0: ASYNC
@@ -276,7 +279,8 @@ int w4a8_matmul(const uint8_t* xq, const float* sx, const int32_t* qweight, cons
                 int layout, void* stream);
 
 /* w4a8_matmul_ex - w4a8_matmul with the split-K count forced: `splits` work-groups along K
- * per 128 x 256 output tile (0: the library's choice; 1..K/128), summed in split order
+ * per output tile of 128 x 256 (64 or 32 rows when M is that small; 0: the library's
+ * choice; 1..K/128), summed in split order
  * (deterministic). With splits > 1 the call uses the split-K workspace of `stream` (see
  * w4a16_matmul on graph capture). Errors as w4a8_matmul, plus INVALID_ARG for splits out of
  * range. */

@@ -6,16 +6,17 @@
 // nibbles are dequantised with the group's scale and zero, and the products accumulate in
 // fp32 on the matrix cores).
 //
-// Tiling as the register tile: a work-group computes 128 x 256 of y with 4 wavefronts side
-// by side along N, each owning all 128 rows x 64 columns (8 x 4 tiles of
-// v_mfma_f32_16x16x32_f16, 128 fp32 accumulators per lane). What differs is how the
+// Tiling as the register tile: a work-group computes BM x 256 of y (BM = 128; 64 or 32 rows
+// when M is that small) with 4 wavefronts side by side along N, each owning all BM rows x
+// 64 columns (BM/16 x 4 tiles of v_mfma_f32_16x16x32_f16, 128 fp32 accumulators per lane at
+// BM = 128). What differs is how the
 // operands arrive: global_load_lds_dwordx4 writes 16 bytes per lane straight into LDS
 // (lane i of an instruction lands at the wavefront's LDS base + 16 i) without passing
 // through registers, so the pipeline depth is bounded by LDS, not by the 256 VGPRs the
 // accumulators already half fill. Each 64-row K stage of a work-group (activations
-// 128 x 64 fp16, packed weights 8 rows x 256 columns, scales and zeros of its groups) lands
-// in one slot of a three-slot LDS ring (77-80 KB, room for two work-groups per compute
-// unit). A six-slot ring (one work-group per compute unit, five stages in flight) measured
+// BM x 64 fp16, packed weights 8 rows x 256 columns, scales and zeros of its groups) lands
+// in one slot of a three-slot LDS ring (77-80 KB at BM = 128, room for two work-groups per
+// compute unit). A six-slot ring (one work-group per compute unit, five stages in flight) measured
 // no faster on any prefill shape: the loads are not what a lone work-group waits for.
 //
 // The activations land in LDS in their natural K order (a direct load cannot permute), so

@@ -11,8 +11,9 @@
 //   w4a8_kernel           y = sx * sum_g s_g * sum_{k in g} dec(xq) * dec(E4M3(q - z)).
 //
 // The product kernel keeps the tiling of the async W4A16 tile (a work-group computes
-// 128 x 256 of y, 4 wavefronts side by side along N, each 128 rows x 64 columns as 8 x 4
-// tiles of 16 x 16) and its direct global-to-LDS loads, but a stage is one 128-row K group:
+// BM x 256 of y, BM = 128, or 64 or 32 when M is that small, 4 wavefronts side by side
+// along N, each BM rows x 64 columns as BM/16 x 4 tiles of 16 x 16) and its direct
+// global-to-LDS loads, but a stage is one 128-row K group:
 // one v_mfma_f32_16x16x128_f8f6f4 per tile covers it. In that instruction lane (r, g)
 // (r = lane % 16, g = lane / 16) holds 32 bytes of row r of A and of column r of B, and
 // byte j of A pairs with byte j of B, so any assignment of K indices to (g, j) works if both
