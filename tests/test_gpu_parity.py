@@ -623,3 +623,26 @@ def test_exact_closed_form_on_gpu(lib, kernel, tile):
     x = np.ones((3, 128), dtype=np.float16)
     y = run(lib, x, qw, s, z, plan=dict(kernel=kernel, tile=tile)).cpu().numpy()
     assert np.all(y == np.float16(-1.0))
+
+
+# ---------------------------------------------------------------------------------------
+# the dispatcher's switch points between the decode kernel and the async prefill tile
+
+DISPATCH_EDGES = [(23, 8192, 16384, 1), (24, 8192, 16384, 2),     # K*N = 2^27: prefill from M = 24
+                  (63, 4096, 8192, 1), (64, 4096, 8192, 2),       # 2^25, K <= N: from M = 64
+                  (64, 8192, 4096, 1), (65, 8192, 4096, 2)]       # 2^25, K > N: from M = 65
+
+
+@pytest.mark.parametrize("M,K,N,kernel", DISPATCH_EDGES, ids=[f"M{m}-K{k}-N{n}" for m, k, n, _ in DISPATCH_EDGES])
+def test_dispatch_edges_automatic_plan(lib, M, K, N, kernel):
+    """On either side of each switch point the automatic plan picks the documented kernel
+    (the prefill tile with its 32-, 64- or 128-row work-groups) and matches the oracle."""
+    pl = lib.w4a16_plan(M, N, K)
+    print(f"\n[dispatch edge] M={M} K={K} N={N} plan={pl}", flush=True)
+    assert pl["kernel"] == kernel
+    qw, s, z = quantised(K, N, wid=3)
+    x = synth.activations(M, K, wid=3)
+    y = run(lib, x, qw, s, z)
+    cols = _sample_cols(N)
+    check_y(y[:, torch.from_numpy(cols).to(DEV)], oracle.matmul(x, qw[:, cols], s[:, cols], z[:, cols]),
+            f"dispatch edge M={M} K={K} N={N}")
