@@ -115,7 +115,7 @@ def test_dequant_rejects_bad_arguments():
 
 # ---- dispatcher (host only) ----
 
-PLAN_SHAPES = [(m, k, n) for m in (1, 2, 4, 8, 16, 17, 23, 24, 33, 48, 49, 63, 64, 65, 128, 129, 512, 2048)
+PLAN_SHAPES = [(m, k, n) for m in (1, 2, 4, 8, 16, 17, 23, 24, 33, 48, 49, 63, 64, 65, 96, 97, 128, 129, 512, 2048)
                for (k, n) in [(4096, 4096), (4096, 14336), (14336, 4096), (2048, 1408), (8192, 28672),
                               (768, 2048), (4096, 128256), (128, 4), (384, 100), (4096, 28676)]]
 

@@ -393,7 +393,8 @@ def test_matmul_prefill_shapes_register_b_tile_sampled(lib, M, K, N):
 
 PREFILL_ASYNC = [(1, 128, 8), (3, 256, 104), (130, 384, 1416), (257, 1408, 264), (64, 768, 2056),
                  (128, 4096, 256), (200, 128, 136), (129, 2048, 1408), (511, 640, 520), (256, 1536, 264),
-                 (32, 512, 264), (17, 2048, 136), (40, 1024, 520), (65, 640, 264)]   # 32-, 64- and 128-row tiles
+                 (32, 512, 264), (17, 2048, 136), (40, 1024, 520), (65, 640, 264), (96, 1024, 136),
+                 (90, 2048, 520)]   # 32-, 64- and 128-row tiles
 
 
 @pytest.mark.parametrize("M,K,N", PREFILL_ASYNC, ids=[f"M{m}-K{k}-N{n}" for m, k, n in PREFILL_ASYNC])
