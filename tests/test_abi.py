@@ -284,3 +284,12 @@ def test_skinny_plan_offsets_fit_31_bits():
         lib.w4a16_plan(1, N, K, kernel=lib.W4A16_KERNEL_SKINNY, kc=128, waves=4)
     assert e.value.code == lib.W4A16_ERR_UNSUPPORTED
     assert lib.w4a16_plan(1, N, K, kernel=lib.W4A16_KERNEL_SKINNY, kc=124, waves=4)["kc"] == 124
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """Without the built library (and no build allowed) the binding raises instead of
+    falling back to anything else."""
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", os.path.join(os.path.dirname(B.LIB_PATH), "missing", "libw4a16.so"))
+    with pytest.raises(ImportError):
+        B.load(build_if_missing=False)
