@@ -21,7 +21,6 @@ void unpack_host(const int32_t* qweight, int64_t K, int64_t N, int layout, uint8
 
 // ---- decode / skinny kernel (w4a16_skinny.hip) ----
 constexpr int kKStep = 32;           // K rows per MFMA step (4 packed rows)
-constexpr int kGroup = 128;          // default K rows per scale/zero group
 // Supported group sizes: 32, 64, 128, 256 rows (1, 2, 4, 8 K-steps).
 inline bool group_supported(int64_t g) { return g == 32 || g == 64 || g == 128 || g == 256; }
 inline int log2_exact(int64_t v) { int r = 0; while ((int64_t(1) << r) < v) ++r; return r; }
@@ -65,7 +64,6 @@ int launch_skinny_lw4(const SkinnyParams& p, void* stream);
 // ---- prefill kernel (w4a16_prefill.hip) ----
 constexpr int kPrefillBM = 128;      // rows of M per work-group
 constexpr int kPrefillBN = 128;      // columns per work-group
-constexpr int kPrefillBK = 64;       // K rows per LDS stage
 
 struct PrefillParams {
     const uint16_t* x;        // fp16 [M, K]
