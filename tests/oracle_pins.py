@@ -312,6 +312,87 @@ def pin_interleaved_words(o):
     assert np.array_equal(o.matmul(x, ql, s, z), o.matmul(x, qi, s, z, layout="interleaved"))
 
 
+def pin_round_then_add_odd_zero(o):
+    """Codes are rounded first and offset by the zero after: q = rne(w/s) + z.
+
+    One group, s = 2**-6 exactly (min -3s, max 12s: (max - min)/15 = s) and zero
+    rne(3) = 3, an odd zero, so the two orders differ on every half-way w/s. Worked by
+    hand, w/s -> rne(w/s) + 3 (rne(w/s + 3) in brackets):
+      -3 -> 0 (0), -1.5 -> -2 + 3 = 1 (rne(1.5) = 2), -0.5 -> -0 + 3 = 3 (rne(2.5) = 2),
+      0.5 -> 0 + 3 = 3 (rne(3.5) = 4), 1.5 -> 2 + 3 = 5 (rne(4.5) = 4),
+      2.5 -> 2 + 3 = 5 (rne(5.5) = 6), 12 -> 15 (15); the other rows hold 0 -> 3.
+    Round-half-away codes would give 0.5 -> 4 and 2.5 -> 6 instead.
+    """
+    d = 2.0 ** -6
+    ratios = [-3.0, -1.5, -0.5, 0.5, 1.5, 2.5, 12.0]
+    W = np.zeros((128, 1), dtype=np.float32)
+    W[:len(ratios), 0] = np.asarray(ratios) * d
+    codes, s, z = o.quantize(W)
+    assert s[0, 0] == np.float16(d) and z[0, 0] == 3, (s, z)
+    expect = np.full(128, 3, dtype=np.uint8)
+    expect[:len(ratios)] = [0, 1, 3, 3, 5, 5, 15]
+    assert np.array_equal(codes[:, 0], expect), codes[:8, 0]
+    # the dequantised values follow from the codes: (q - 3) * 2**-6
+    deq = o.dequant(codes, s, z)[:len(ratios), 0]
+    assert np.array_equal(deq, np.array([-3, -2, 0, 0, 2, 2, 12], dtype=np.float32) * np.float32(d))
+
+
+def pin_zero_point_tie(o):
+    """The zero point is rounded half to even: rne(-min/s) at exact ties.
+
+    Three columns, each with scale 2**-6 exactly (max - min = 15 s):
+      min -2.5s, max 12.5s: zero rne(2.5) = 2 (half-up or half-away: 3); codes of the
+        min and max rne(-2.5) + 2 = 0 and rne(12.5) + 2 = 14;
+      min -0.5s, max 14.5s: zero rne(0.5) = 0 (half-up: 1); codes 0 and rne(14.5) = 14;
+      min -3.5s, max 11.5s: zero rne(3.5) = 4 (half-down or truncation: 3); codes
+        rne(-3.5) + 4 = 0 and rne(11.5) + 4 = 16 -> clamped to 15.
+    """
+    d = 2.0 ** -6
+    lo = [-2.5, -0.5, -3.5]
+    W = np.zeros((128, 3), dtype=np.float32)
+    for n, a in enumerate(lo):
+        W[0, n] = a * d
+        W[1, n] = (a + 15.0) * d
+    codes, s, z = o.quantize(W)
+    assert np.all(s[0] == np.float16(d)), s
+    assert z[0].tolist() == [2.0, 0.0, 4.0], z
+    assert codes[0].tolist() == [0, 0, 0] and codes[1].tolist() == [14, 14, 15], codes[:2]
+    assert codes[2:].tolist() == [[2, 0, 4]] * 126
+
+
+def pin_true_division(o):
+    """w / scale is one correctly rounded fp32 division, not w times a rounded 1/scale.
+
+    Asymmetric: scale 1070 * 2**-10 (an fp16 value; a group with min 0 and max 15 scale
+    stores it exactly, zero 0) and w = 8025 * 2**-10 - 2**-21, one fp32 step below
+    7.5 * scale. The exact quotient 7.5 - 2**-21 / scale lies nearer to the fp32 value
+    7.5 - 2**-21 than to 7.5, so w / scale rounds below 7.5 and the code is 7; the
+    reciprocal fl32(1 / scale) times w rounds to exactly 7.5, which half-even takes to 8.
+    Symmetric: scale 141 * 2**-7 (max |w| = 7 scale) and w = 916.5 * 2**-7 + 2**-21, one
+    step above 6.5 * scale: the quotient rounds above 6.5, code rne(6.5+) + 8 = 15 (and
+    -w gives 1); the reciprocal route lands on exactly 6.5 and gives 14 (and 2).
+    These values were found by a search over fp16 scales for a quotient within an fp32
+    step of a half-way point; the reasoning above is what fixes the expected codes.
+    """
+    s_a = 1070 * 2.0 ** -10
+    W = np.zeros((128, 1), dtype=np.float32)
+    W[0, 0] = 15 * s_a
+    W[1, 0] = np.float32(8025 * 2.0 ** -10) - np.float32(2.0 ** -21)
+    codes, s, z = o.quantize(W)
+    assert s[0, 0] == np.float16(s_a) and z[0, 0] == 0, (s, z)
+    assert codes[0, 0] == 15 and codes[1, 0] == 7, codes[:2, 0]
+    s_s = 141 * 2.0 ** -7
+    W = np.zeros((128, 2), dtype=np.float32)
+    W[0, :] = 7 * s_s
+    w = np.float32(916.5 * 2.0 ** -7) + np.float32(2.0 ** -21)
+    W[1, 0] = w
+    W[1, 1] = -w
+    codes, s, z = o.quantize(W, 128, symmetric=True)
+    assert np.all(s[0] == np.float16(s_s)) and np.all(z == 8), (s, z)
+    assert codes[0].tolist() == [15, 15] and codes[1].tolist() == [15, 1], codes[:2]
+
+
 ALL_PINS = [pin_hand_words, pin_interleaved_words, pin_roundtrip, pin_exact_group, pin_exact_products,
             pin_multigroup, pin_bounds_random, pin_fsum, pin_dequant_fp16_rounding,
-            pin_scale_rounding, pin_group_sizes, pin_symmetric_exact, pin_symmetric_bounds]
+            pin_scale_rounding, pin_group_sizes, pin_symmetric_exact, pin_symmetric_bounds,
+            pin_round_then_add_odd_zero, pin_zero_point_tie, pin_true_division]

@@ -48,6 +48,22 @@ MUTANTS = [
     ("groups interleaved along K (k mod G) instead of contiguous",
      "Wg = W.reshape(G, group_size, N)",
      "Wg = W.reshape(group_size, G, N).transpose(1, 0, 2)"),
+    ("codes rounded after adding the zero: rne(w/s + z)",
+     "q = np.rint(Wg / s[:, None, :]) + z[:, None, :]",
+     "q = np.rint(Wg / s[:, None, :] + z[:, None, :])"),
+    ("codes rounded half away from zero",
+     "q = np.rint(Wg / s[:, None, :]) + z[:, None, :]",
+     "t = Wg / s[:, None, :]; q = np.trunc(t + np.copysign(np.float32(0.5), t)) + z[:, None, :]"),
+    ("zero point rounded half up",
+     "z = np.rint(-mn / s)", "z = np.floor(-mn / s + np.float32(0.5))"),
+    ("zero point rounded half down",
+     "z = np.rint(-mn / s)", "z = np.ceil(-mn / s - np.float32(0.5))"),
+    ("codes from w times a rounded reciprocal of the scale",
+     "q = np.rint(Wg / s[:, None, :]) + z[:, None, :]",
+     "q = np.rint(Wg * (np.float32(1) / s)[:, None, :]) + z[:, None, :]"),
+    ("symmetric codes from w times a rounded reciprocal of the scale",
+     "q = np.rint(Wg / s[:, None, :]) + np.float32(SYM_ZERO)",
+     "q = np.rint(Wg * (np.float32(1) / s)[:, None, :]) + np.float32(SYM_ZERO)"),
     ("range from max only",
      "rng = mx - mn", "rng = mx - np.float32(0)"),
     # dequant
