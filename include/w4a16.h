@@ -157,13 +157,17 @@ int w4a16_pack_ex(const float* W, int64_t K, int64_t N, int64_t group_size, int 
                   int layout, int32_t* qweight, uint16_t* scales, uint16_t* zeros);
 
 /*
- * w4a16_unpack - host inverse of the packing: codes[8i + j, n] = (qweight[i, n] >> 4j) & 15.
+ * w4a16_unpack - host inverse of the packing that "Beating FP16 with 4-bit Weights", section
+ * "The design", defines (eight codes per int32 along K, packed row i / nibble j holding K
+ * index 8i + j): codes[8i + j, n] = (qweight[i, n] >> 4j) & 15.
  *   qweight host int32 [K/8, N]; codes host uint8 [K, N] (written). K % 8 == 0.
  * Errors: INVALID_ARG.
  */
 int w4a16_unpack(const int32_t* qweight, int64_t K, int64_t N, uint8_t* codes);
 
-/* w4a16_unpack_ex - w4a16_unpack for either layout (codes in natural K order).
+/* w4a16_unpack_ex - w4a16_unpack for either layout (codes in natural K order): the linear
+ * packing of "The design", or the interleaved one that section "What's next" of the same page
+ * motivates (weights pre-permuted offline into the order the matrix instruction consumes).
  * Errors: INVALID_ARG (also for an unknown layout). */
 int w4a16_unpack_ex(const int32_t* qweight, int64_t K, int64_t N, int layout, uint8_t* codes);
 
@@ -193,7 +197,10 @@ int w4a16_matmul(const void* x, const int32_t* qweight, const void* scales,
                  int64_t group_size, void* stream);
 
 /*
- * w4a16_matmul_ex - w4a16_matmul with the plan forced by the caller (tuning and tests).
+ * w4a16_matmul_ex - w4a16_matmul with the plan forced by the caller (tuning and tests). The
+ * product is the one of "The design"; the plan is what "Things I got wrong along the way" on
+ * the same page says must be tuned per shape (block sizes and the split-K factor, whose best
+ * value differed between attention and FFN projections).
  * plan->kernel == W4A16_KERNEL_AUTO behaves as w4a16_matmul. Fields left 0 are filled by
  * the dispatcher. Errors as w4a16_matmul, plus INVALID_ARG for an unusable plan.
  */
@@ -203,7 +210,9 @@ int w4a16_matmul_ex(const void* x, const int32_t* qweight, const void* scales,
 
 /*
  * w4a16_matmul_fmt - the general entry point: w4a16_matmul_ex for weights packed in either
- * layout (w4a16_matmul and w4a16_matmul_ex are this call with W4A16_LAYOUT_LINEAR).
+ * layout (w4a16_matmul and w4a16_matmul_ex are this call with W4A16_LAYOUT_LINEAR). The
+ * product is that of "Beating FP16 with 4-bit Weights", section "The design"; the interleaved
+ * layout is the offline pre-permutation its section "What's next" proposes.
  *   layout  W4A16_LAYOUT_LINEAR or W4A16_LAYOUT_INTERLEAVED, as given to w4a16_pack_ex
  *   plan    NULL or a plan as for w4a16_matmul_ex
  * Errors as w4a16_matmul_ex, plus INVALID_ARG for an unknown layout.
@@ -215,12 +224,18 @@ int w4a16_matmul_fmt(const void* x, const int32_t* qweight, const void* scales,
 /*
  * w4a16_plan - the plan w4a16_matmul would use for (M, N, K, group_size), or the completed
  * version of a forced plan when `plan->kernel` is non-zero on entry. Host only; no HIP call.
+ * The choice is per shape, from measurements, as "Beating FP16 with 4-bit Weights", section
+ * "Things I got wrong along the way", asks (autotune per shape; the best split factor is not
+ * the same for every projection), and as "Triton Kernel Matches bitsandbytes: Why Both Lose to
+ * Math", section "Three Kernel Versions and Two Bugs", bears out (split-K lost on some shapes).
  * Errors: INVALID_ARG, UNSUPPORTED.
  */
 int w4a16_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, w4a16_plan_t* plan);
 
 /*
- * w4a16_dequant - the GPU's unpack/dequant, exposed for bit-exact checks.
+ * w4a16_dequant - the GPU's unpack/dequant, exposed for bit-exact checks: the unpack and the
+ * (q - zero) * scale dequantisation of "Beating FP16 with 4-bit Weights", section "The
+ * design", that the product kernels perform in registers.
  *   codes  device uint8 [K, N] or NULL, 4-byte aligned: codes[8i + j, n] = nibble j of
  *          qweight[i, n]
  *   w      device fp16 [K, N] or NULL: fp16_rne((q - zero) * scale), i.e. one rounding of
@@ -233,9 +248,10 @@ int w4a16_dequant(const int32_t* qweight, const void* scales, const void* zeros,
                   uint8_t* codes, void* w, int64_t N, int64_t K, int64_t group_size,
                   void* stream);
 
-/* w4a16_dequant_fmt - w4a16_dequant for weights packed in either layout; codes and w are
- * in natural K order whatever the layout. Errors as w4a16_dequant, plus INVALID_ARG for an
- * unknown layout. */
+/* w4a16_dequant_fmt - w4a16_dequant for weights packed in either layout ("The design" and
+ * the pre-permuted layout of "What's next" on the same page); codes and w are in natural K
+ * order whatever the layout. Errors as w4a16_dequant, plus INVALID_ARG for an unknown
+ * layout. */
 int w4a16_dequant_fmt(const int32_t* qweight, const void* scales, const void* zeros,
                       uint8_t* codes, void* w, int64_t N, int64_t K, int64_t group_size,
                       int layout, void* stream);

@@ -293,3 +293,33 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(B, "LIB_PATH", os.path.join(os.path.dirname(B.LIB_PATH), "missing", "libw4a16.so"))
     with pytest.raises(ImportError):
         B.load(build_if_missing=False)
+
+
+def test_offsets_beyond_31_bits_are_rejected():
+    """The W4A8 kernel addresses 16 packed rows of weights (64 N bytes) and the split
+    partials of an output tile (128 KiB each, for W4A8 and the async W4A16 tile) with
+    32-bit offsets: shapes or split counts past that are rejected before any HIP call."""
+    so = B.load()
+    pp = [P[0], P[1], P[2], P[3], P[4], ctypes.c_void_p(A + 0x5000)]
+    assert so.w4a8_matmul_ex(*pp, 1, 1 << 25, 128, 128, 0, 0, None) == lib.W4A16_ERR_UNSUPPORTED
+    assert "32-bit" in B.load().w4a16_last_error_detail().decode()
+    assert so.w4a8_matmul_ex(*pp, 1, 8, 1 << 21, 128, 0, 16384, None) == lib.W4A16_ERR_UNSUPPORTED
+    with pytest.raises(lib.W4A16Error) as e:
+        lib.w4a16_plan(1, 8, 1 << 21, kernel=2, tile=3, splits=16384)
+    assert e.value.code == lib.W4A16_ERR_UNSUPPORTED
+    assert lib.w4a16_plan(1, 8, 1 << 21, kernel=2, tile=3, splits=16383)["splits"] <= 16383
+
+
+def test_binding_dequant_checks_scale_shapes():
+    """w4a16_dequant's binding checks scales/zeros against [K/group_size, N] on the host: the
+    C entry point cannot see buffer sizes, and short scales would be read past their end."""
+    torch = pytest.importorskip("torch")
+    qw = torch.zeros((32, 64), dtype=torch.int32)          # K = 256, N = 64
+    good = torch.zeros((2, 64), dtype=torch.float16)
+    for s, z, g in [(torch.zeros((1, 64), dtype=torch.float16), good, 128),
+                    (good, torch.zeros((2, 60), dtype=torch.float16), 128),
+                    (good, good, 64), (good, good, 96)]:
+        with pytest.raises(ValueError):
+            lib.w4a16_dequant(qw, s, z, group_size=g)
+    with pytest.raises(ValueError):
+        lib.w4a16_dequant(torch.zeros(64, dtype=torch.int32), good, good)

@@ -259,8 +259,14 @@ def w4a16_dequant(qweight, scales, zeros, codes=True, weights=True, group_size=G
     """The GPU's unpack/dequant: returns (codes uint8 [K, N] or None, w fp16 [K, N] or None),
     both in natural K order."""
     import torch
+    if qweight.dim() != 2:
+        raise ValueError("qweight must be 2-D")
     K = qweight.shape[0] * 8
     N = qweight.shape[1]
+    if group_size <= 0 or K % group_size != 0:
+        raise ValueError(f"K={K} is not a multiple of group_size={group_size}")
+    if scales.shape != (K // group_size, N) or zeros.shape != (K // group_size, N):
+        raise ValueError("scales/zeros must be [K/group_size, N]")
     c = torch.empty((K, N), dtype=torch.uint8, device=qweight.device) if codes else None
     w = torch.empty((K, N), dtype=torch.float16, device=qweight.device) if weights else None
     rc = load().w4a16_dequant_fmt(_dev_ptr(qweight, "qweight", torch.int32),

@@ -126,6 +126,35 @@ const TunedPlan* tuned_plan(int64_t M, int64_t N, int64_t K) {
     return nullptr;
 }
 
+}  // namespace
+
+namespace w4a16 {
+
+// Built configurations of the decode kernel (the instances in w4a16_skinny_lw{1,2,4}.hip);
+// host logic only, shared by plan completion and the launcher.
+bool skinny_config_supported(int row_tiles, int waves, int lw, int seg, int seg_group) {
+    if (lw != 1 && lw != 2 && lw != 4) return false;
+    if (seg != 1 && seg != 2 && seg != 4 && seg != 8) return false;
+    // built (segment, K-steps of one group in it) pairs: every segment inside one group,
+    // 4-step segments over 2 or 4 groups (64- and 32-row groups), 8-step over 2 groups
+    if (!(seg_group == seg || (seg == 4 && (seg_group == 1 || seg_group == 2)) ||
+          (seg == 2 && seg_group == 1) || (seg == 8 && seg_group == 4)))
+        return false;
+    if (seg == 8 && seg_group == 8) return false;
+    if (waves != 4 && waves != 8 && waves != 16) return false;
+    if (row_tiles < 1 || row_tiles > (lw == 4 ? 4 : 2)) return false;
+    // built (row_tiles, waves) pairs: the LDS of the wave reduction, (waves - 1) * 16 *
+    // row_tiles rows of 16 * lw floats, stays within 64 KiB, and register use stays low
+    // enough for at least two work-groups' worth of waves per compute unit
+    if (row_tiles >= 3 && waves != 4) return false;
+    if (row_tiles == 2 && waves == 16) return false;
+    return (waves - 1) * 16 * row_tiles * 16 * lw * 4 <= 64 * 1024;
+}
+
+}  // namespace w4a16
+
+namespace {
+
 int64_t roundup4(int64_t v) { return ceil_div(v, 4) * 4; }
 
 void default_skinny_plan(int64_t M, int64_t N, int64_t K, int64_t group_steps, w4a16_plan_t* pl) {
@@ -264,6 +293,10 @@ int complete_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, w4a16_pla
                         pl->splits);
         if (pl->tile == W4A16_TILE_ASYNC) {
             if (pl->splits == 0) pl->splits = (int32_t)auto_prefill_splits(M, N, K);
+            // the kernel addresses a tile's split partials (128 KiB each) with 32-bit offsets
+            if ((int64_t)pl->splits * w4a16::kPrefillTileFloats * 4 > INT32_MAX)
+                return fail(W4A16_ERR_UNSUPPORTED, "splits=%d exceeds the async tile's 32-bit workspace offsets",
+                            pl->splits);
             // settle on a split count whose stages per split (prefill_stages_per_split, even,
             // which keeps the last split at >= 2 stages) cover K with exactly that many splits
             for (;;) {
@@ -572,6 +605,9 @@ int w4a8_matmul_ex(const uint8_t* xq, const float* sx, const int32_t* qweight, c
     if (group_size != 128 && group_size != 256)
         return fail(W4A16_ERR_UNSUPPORTED, "W4A8 takes groups of 128 or 256 rows (got %lld)", (long long)group_size);
     if (N % 8 != 0) return fail(W4A16_ERR_UNSUPPORTED, "W4A8 needs N %% 8 == 0 (N=%lld)", (long long)N);
+    // a wavefront addresses 16 packed rows of the weights (64 N bytes) with 32-bit offsets
+    if (64 * N > INT32_MAX)
+        return fail(W4A16_ERR_UNSUPPORTED, "N=%lld exceeds the W4A8 kernel's 32-bit weight offsets", (long long)N);
     if (ceil_div(M, 128) > 65535) return fail(W4A16_ERR_UNSUPPORTED, "grid too large");
     if (!aligned16(xq) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros) || !aligned16(y) ||
         reinterpret_cast<uintptr_t>(sx) % 4 != 0)
@@ -595,6 +631,9 @@ int w4a8_matmul_ex(const uint8_t* xq, const float* sx, const int32_t* qweight, c
     int64_t S = splits ? splits : auto_w4a8_splits(M, N, K, p.bm);
     const int64_t per = ceil_div(stages, S);
     S = ceil_div(stages, per);                                 // every split non-empty
+    if (S * w4a16::kPrefillTileFloats * 4 > INT32_MAX)         // partials addressed with 32-bit offsets
+        return fail(W4A16_ERR_UNSUPPORTED, "%lld splits exceed the W4A8 kernel's 32-bit workspace offsets",
+                    (long long)S);
     p.splits = (int)S;
     p.stages_per_split = (int)per;
     if (S > 1) {
