@@ -68,3 +68,16 @@ def weight_custom(K, N, seed, std=0.02, mean=0.0):
     W = rng.standard_normal((K, N), dtype=np.float32) * np.float32(std)
     W += np.float32(mean)
     return W
+
+
+def scales_zeros_custom(G, N, seed, log2_lo=-12.0, log2_hi=-9.0, zero_limit=1024):
+    """Hand-built per-(group, column) parameters for packed weights that no quantiser run
+    would produce: fp16 scales log-uniform in [2**log2_lo, 2**log2_hi] and integer zero
+    points uniform in [-zero_limit, zero_limit], with the first columns of group 0 set to
+    the values at and next to the ends of that range (-1024, 1024, -1, 0, 15, 16)."""
+    rng = np.random.default_rng((6, G, N, seed))
+    s = np.exp2(rng.uniform(log2_lo, log2_hi, size=(G, N))).astype(np.float16)
+    z = rng.integers(-zero_limit, zero_limit + 1, size=(G, N)).astype(np.float16)
+    edges = np.array([-zero_limit, zero_limit, -1, 0, 15, 16], dtype=np.float16)
+    z[0, :min(N, len(edges))] = edges[:min(N, len(edges))]
+    return s, z
