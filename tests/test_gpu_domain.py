@@ -16,15 +16,22 @@ Each case runs every kernel with its plan forced: the decode kernel with 16-, 32
 tile, the register tile, and the async tile with 32/64- and 128-row work-groups, with and
 without split-K; group sizes 32, 64, 128 and 256; linear and interleaved packing.
 
-Two bars per output element:
-  * the stated one, |y - y_ref| <= 1e-2 + 5e-3 |y_ref| against the fp64 oracle;
-  * a bound derived from the arithmetic the kernel performs, which stays meaningful where
-    y is tiny (subnormal scales): against y_w = x . w' in fp64, where w' is the weight the
-    kernel multiplies (the exact (q - z) s for the decode kernel, which applies the scale
-    to each group's fp32 partial sum; fp16_rne((q - z) s) for the prefill tiles, which
-    stage fp16 weights), |y - y_w| <= 2K 2**-23 sum_k |x_k w'_k| + 2**-11 |y_w| + 2**-25
-    (fp32 accumulation of exact products with at most 2K roundings, whatever the order,
-    then one fp16 rounding of the output, subnormal outputs included).
+Two bars per output element. Let w' be the weight the kernel multiplies: the exact
+(q - z) s for the decode kernel, which applies each group's scale to its fp32 partial sum,
+and fp16_rne((q - z) s) for the prefill tiles, which stage fp16 weights as "The design"
+dequantises them (both values come from the oracle: dequant and dequant_fp16), and let
+y_w = x . w' in fp64.
+  * The stated bar against the exact fp64 oracle, |y - y_ref| <= 1e-2 + 5e-3 |y_ref|,
+    widened by |y_w - y_ref|: the deviation that the fp16 weights themselves cause, which
+    is zero for the decode kernel. On these domains that deviation alone exceeds the bar
+    (computed from the oracle on the CPU, K = 2048: 2.3x the bar for N(+1, 0.02), 10x for
+    N(-3, 5), 1.7x for the far zero points), since each fp16 weight carries a relative
+    error up to 2**-11 while |y| can be small by cancellation; on the workload's N(0, 0.02)
+    weights it does not, and every other test holds the unwidened bar.
+  * A bound derived from the arithmetic the kernel performs, which stays meaningful where
+    y is tiny (subnormal scales): |y - y_w| <= 2K 2**-23 sum_k |x_k w'_k| + 2**-11 |y_w| +
+    2**-25 (fp32 accumulation of exact products with at most 2K roundings, whatever the
+    order, then one fp16 rounding of the output, subnormal outputs included).
 """
 import numpy as np
 import pytest
@@ -98,12 +105,13 @@ def weights(domain, g, layout):
 def check(y_gpu, x, y_ref, w_kernel, what):
     y = y_gpu.detach().cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(y)), f"{what}: non-finite output"
-    err = np.abs(y - y_ref)
-    bar = ATOL + RTOL * np.abs(y_ref)
-    worst = np.unravel_index(np.argmax(err - bar), err.shape)
-    assert np.all(err <= bar), f"{what}: max err {err.max():.3e} at {worst} (y={y[worst]}, ref={y_ref[worst]})"
     x64 = x.astype(np.float64)
     y_w = x64 @ w_kernel
+    err = np.abs(y - y_ref)
+    bar = ATOL + RTOL * np.abs(y_ref) + np.abs(y_w - y_ref)
+    worst = np.unravel_index(np.argmax(err - bar), err.shape)
+    assert np.all(err <= bar), (f"{what}: error {err[worst]:.3e} > {bar[worst]:.3e} at {worst} "
+                                f"(y={y[worst]}, ref={y_ref[worst]}, y_w={y_w[worst]})")
     mag = np.abs(x64) @ np.abs(w_kernel)
     tight = 2 * K * 2.0 ** -23 * mag + 2.0 ** -11 * np.abs(y_w) + 2.0 ** -25
     e2 = np.abs(y - y_w)
