@@ -222,6 +222,26 @@ int w4a16_matmul_fmt(const void* x, const int32_t* qweight, const void* scales,
                      int64_t group_size, int layout, void* stream, const w4a16_plan_t* plan);
 
 /*
+ * w4a16_matmul_noalloc - w4a16_matmul_fmt that allocates nothing, for callers that cannot
+ * call hipMalloc: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * device allocation. Same arguments, plans, kernels and results as w4a16_matmul_fmt; a plan
+ * with split-K keeps its fp32 partials and arrival counters in a static scratch array of the
+ * library (one per device, held until the process ends: 64 MiB of partials and 65536
+ * counters) instead of the per-stream workspace. No hipMalloc, hipFree or other allocating
+ * call is made. The first call on a device takes the array's device address and clears its
+ * counters with a kernel on `stream`; every kernel returns the counters it takes to zero.
+ * Every call on one device shares that device's array: calls that overlap in time on one
+ * device (on different streams, or graphs replayed concurrently) race and give undefined
+ * results; calls ordered on one stream do not.
+ * Errors as w4a16_matmul_fmt, plus UNSUPPORTED (before any HIP call) when the plan needs
+ * more partials or counters than the scratch holds: force fewer splits (plan->splits for the
+ * async prefill tile, larger kc or more waves for the decode kernel).
+ */
+int w4a16_matmul_noalloc(const void* x, const int32_t* qweight, const void* scales,
+                         const void* zeros, void* y, int64_t M, int64_t N, int64_t K,
+                         int64_t group_size, int layout, void* stream, const w4a16_plan_t* plan);
+
+/*
  * w4a16_plan - the plan w4a16_matmul would use for (M, N, K, group_size), or the completed
  * version of a forced plan when `plan->kernel` is non-zero on entry. Host only; no HIP call.
  * The choice is per shape, from measurements, as "Beating FP16 with 4-bit Weights", section

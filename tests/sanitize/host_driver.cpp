@@ -42,6 +42,7 @@ int launch_dequant(const uint32_t*, const uint16_t*, const uint16_t*, uint8_t*, 
 }
 int launch_w4a8_quantize(const uint16_t*, uint8_t*, float*, int, int, void*) { reached("launch_w4a8_quantize"); }
 int launch_w4a8(const W4A8Params&, void*) { reached("launch_w4a8"); }
+int scratch_workspace(void*, float**, uint32_t**) { reached("scratch_workspace"); }
 }  // namespace w4a16
 
 static int g_checks = 0;
@@ -166,6 +167,12 @@ static void device_call_errors() {
            W4A16_ERR_INVALID_ARG, "matmul_ex null plan");
     expect(w4a16_matmul_fmt(p[0], (const int32_t*)p[1], p[2], p[3], p[4], 1, 64, 1024, 128, 2, nullptr, nullptr),
            W4A16_ERR_INVALID_ARG, "matmul_fmt layout=2");
+    const w4a16_plan_t many_splits{2, 0, 64, 0, 3, 0, 0, 0};   // 64 tiles x 64 splits x 128 KiB > the scratch
+    expect(w4a16_matmul_noalloc(p[0], (const int32_t*)p[1], p[2], p[3], p[4], 130, 8192, 8192, 128, 0, nullptr,
+                                &many_splits),
+           W4A16_ERR_UNSUPPORTED, "noalloc plan beyond the static scratch");
+    expect(w4a16_matmul_noalloc(p[0], nullptr, p[2], p[3], p[4], 1, 64, 128, 128, 0, nullptr, nullptr),
+           W4A16_ERR_INVALID_ARG, "noalloc null qweight");
     w4a16_plan_t async{2, 0, 0, 0, 3, 0, 0, 0};
     expect(w4a16_matmul_ex(p[0], (const int32_t*)p[1], p[2], p[3], p[4], 1, 60, 1024, 128, nullptr, &async),
            W4A16_ERR_UNSUPPORTED, "async tile N%8");

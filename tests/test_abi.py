@@ -323,3 +323,15 @@ def test_binding_dequant_checks_scale_shapes():
             lib.w4a16_dequant(qw, s, z, group_size=g)
     with pytest.raises(ValueError):
         lib.w4a16_dequant(torch.zeros(64, dtype=torch.int32), good, good)
+
+
+def test_noalloc_rejects_plans_beyond_the_scratch():
+    """w4a16_matmul_noalloc takes only plans whose split-K partials fit its static scratch;
+    a larger one is rejected before any HIP call (the fake pointers are never used)."""
+    so = B.load()
+    pl = B.w4a16_plan_t(kernel=2, tile=3, splits=64)      # 64 output tiles x 64 splits x 128 KiB
+    rc = so.w4a16_matmul_noalloc(P[0], P[1], P[2], P[3], P[4], 130, 8192, 8192, 128, 0, None, ctypes.byref(pl))
+    assert rc == lib.W4A16_ERR_UNSUPPORTED
+    assert "static scratch" in so.w4a16_last_error_detail().decode()
+    assert so.w4a16_matmul_noalloc(P[0], None, P[2], P[3], P[4], 1, 64, 128, 128, 0, None,
+                                   None) == lib.W4A16_ERR_INVALID_ARG

@@ -61,6 +61,8 @@ _SIGS = {
                          ctypes.POINTER(w4a16_plan_t)], ctypes.c_int),
     "w4a16_matmul_fmt": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int, _P,
                           ctypes.POINTER(w4a16_plan_t)], ctypes.c_int),
+    "w4a16_matmul_noalloc": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int, _P,
+                              ctypes.POINTER(w4a16_plan_t)], ctypes.c_int),
     "w4a16_plan": ([_I64, _I64, _I64, _I64, ctypes.POINTER(w4a16_plan_t)], ctypes.c_int),
     "w4a16_dequant": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "w4a16_dequant_fmt": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P], ctypes.c_int),
@@ -244,6 +246,30 @@ def w4a16_matmul(x, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, strea
         pl = ctypes.byref(_make_plan(plan)) if plan is not None else None
         rc = load().w4a16_matmul_fmt(*args[:-1], lay, args[-1], pl)
         _check(rc, "w4a16_matmul_fmt")
+    return y
+
+
+def w4a16_matmul_noalloc(x, qweight, scales, zeros, y, group_size=GROUP_SIZE, stream=None, plan=None,
+                         layout="linear"):
+    """w4a16_matmul through the entry point that allocates nothing (split-K partials in the
+    library's static scratch). y fp16 [M, N] must be given: nothing is allocated here either."""
+    import torch
+    if x.dim() != 2 or qweight.dim() != 2:
+        raise ValueError("x and qweight must be 2-D")
+    M, K = x.shape
+    N = qweight.shape[1]
+    if qweight.shape[0] * 8 != K:
+        raise ValueError(f"qweight rows {qweight.shape[0]} do not match K={K}")
+    if scales.shape != (K // group_size, N) or zeros.shape != (K // group_size, N):
+        raise ValueError("scales/zeros must be [K/group_size, N]")
+    if y is None or y.shape != (M, N):
+        raise ValueError("y must be an fp16 [M, N] tensor")
+    pl = ctypes.byref(_make_plan(plan)) if plan is not None else None
+    rc = load().w4a16_matmul_noalloc(_dev_ptr(x, "x", torch.float16), _dev_ptr(qweight, "qweight", torch.int32),
+                                     _dev_ptr(scales, "scales", torch.float16), _dev_ptr(zeros, "zeros", torch.float16),
+                                     _dev_ptr(y, "y", torch.float16), M, N, K, group_size, _layout_id(layout),
+                                     _stream_ptr(stream, x.device), pl)
+    _check(rc, "w4a16_matmul_noalloc")
     return y
 
 

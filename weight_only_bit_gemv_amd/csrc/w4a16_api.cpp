@@ -408,9 +408,35 @@ int get_workspace(void* stream, uint64_t bytes, uint64_t n_counters, Workspace* 
     return W4A16_OK;
 }
 
+// Split-K buffers of one call: the library's per-(device, stream) workspace, or for
+// w4a16_matmul_noalloc the static per-device scratch, whose size bounds the plans it takes
+// (checked before any HIP call).
+int call_workspace(bool noalloc, void* stream, uint64_t bytes, uint64_t n_counters, float** ws,
+                   uint32_t** counters) {
+    if (noalloc) {
+        if (bytes > w4a16::kScratchPartialBytes || n_counters * 4 > w4a16::kScratchCounterBytes)
+            return fail(W4A16_ERR_UNSUPPORTED,
+                        "the plan needs %llu bytes of split-K partials and %llu counters; the static scratch "
+                        "holds %llu bytes and %llu counters (force fewer splits)",
+                        (unsigned long long)bytes, (unsigned long long)n_counters,
+                        (unsigned long long)w4a16::kScratchPartialBytes,
+                        (unsigned long long)(w4a16::kScratchCounterBytes / 4));
+        const int e = w4a16::scratch_workspace(stream, ws, counters);
+        if (e != (int)hipSuccess)
+            return fail(W4A16_ERR_HIP, "static scratch: %s", hipGetErrorString((hipError_t)e));
+        return W4A16_OK;
+    }
+    Workspace w;
+    const int rc = get_workspace(stream, bytes, n_counters, &w);
+    if (rc) return rc;
+    *ws = w.partials;
+    *counters = w.counters;
+    return W4A16_OK;
+}
+
 int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const void* zeros,
                 void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, int layout, void* stream,
-                const w4a16_plan_t* forced) {
+                const w4a16_plan_t* forced, bool noalloc = false) {
     if (!x || !qweight || !scales || !zeros || !y)
         return fail(W4A16_ERR_INVALID_ARG, "null pointer argument");
     if (!w4a16::layout_supported(layout)) return fail(W4A16_ERR_INVALID_ARG, "unknown layout %d", layout);
@@ -440,12 +466,9 @@ int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const
         q.stages_per_split = (int)prefill_stages_per_split(K / 64, q.splits);
         if (q.splits > 1) {
             const int64_t tiles = ceil_div(M, q.bm) * ceil_div(N, 256);
-            Workspace w;
-            rc = get_workspace(stream, (uint64_t)tiles * q.splits * w4a16::kPrefillTileFloats * 4,
-                               (uint64_t)tiles, &w);
+            rc = call_workspace(noalloc, stream, (uint64_t)tiles * q.splits * w4a16::kPrefillTileFloats * 4,
+                                (uint64_t)tiles, &q.ws, &q.counters);
             if (rc) return rc;
-            q.ws = w.partials;
-            q.counters = w.counters;
         }
         const int e = w4a16::launch_prefill(q, stream);
         if (e != (int)hipSuccess)
@@ -475,11 +498,8 @@ int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const
     uint64_t ws_bytes = 0, n_counters = 0;
     w4a16::skinny_workspace(p, &ws_bytes, &n_counters);
     if (ws_bytes) {
-        Workspace w;
-        rc = get_workspace(stream, ws_bytes, n_counters, &w);
+        rc = call_workspace(noalloc, stream, ws_bytes, n_counters, &p.ws, &p.counters);
         if (rc) return rc;
-        p.ws = w.partials;
-        p.counters = w.counters;
     }
     const int e = w4a16::launch_skinny(p, stream);
     if (e != (int)hipSuccess)
@@ -542,6 +562,12 @@ int w4a16_matmul_fmt(const void* x, const int32_t* qweight, const void* scales, 
                      void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, int layout, void* stream,
                      const w4a16_plan_t* plan) {
     return matmul_impl(x, qweight, scales, zeros, y, M, N, K, group_size, layout, stream, plan);
+}
+
+int w4a16_matmul_noalloc(const void* x, const int32_t* qweight, const void* scales, const void* zeros,
+                         void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, int layout, void* stream,
+                         const w4a16_plan_t* plan) {
+    return matmul_impl(x, qweight, scales, zeros, y, M, N, K, group_size, layout, stream, plan, true);
 }
 
 int w4a16_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, w4a16_plan_t* plan) {

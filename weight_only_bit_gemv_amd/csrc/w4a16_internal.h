@@ -114,6 +114,13 @@ struct W4A8Params {
 int launch_w4a8_quantize(const uint16_t* x, uint8_t* xq, float* sx, int M, int K, void* stream);
 int launch_w4a8(const W4A8Params& p, void* stream);   // returns a hipError_t value
 
+// ---- static scratch of w4a16_matmul_noalloc (w4a16_noalloc.hip) ----
+constexpr uint64_t kScratchCounterBytes = 256ull << 10;   // 65536 arrival counters
+constexpr uint64_t kScratchPartialBytes = 64ull << 20;    // fp32 split-K partials
+// Device addresses of this device's counters and partials (the counters are cleared on the
+// device's first call, by a kernel on `stream`). Returns a hipError_t value.
+int scratch_workspace(void* stream, float** partials, uint32_t** counters);
+
 // ---- dequant hook (w4a16_dequant.hip) ----
 int launch_dequant(const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                    uint8_t* codes, uint16_t* w, int N, int K, int group_shift, int layout, void* stream);
