@@ -222,6 +222,44 @@ int w4a16_matmul_fmt(const void* x, const int32_t* qweight, const void* scales,
                      int64_t group_size, int layout, void* stream, const w4a16_plan_t* plan);
 
 /*
+ * w4a16_matrix_t - one weight matrix of a grouped product (w4a16_matmul_grouped): device
+ * pointers in the layouts above, N its output columns (N >= 4, N % 4 == 0).
+ */
+typedef struct w4a16_matrix {
+    const int32_t* qweight;   /* int32 [K/8, N] */
+    const void* scales;       /* fp16 [K/g, N]  */
+    const void* zeros;        /* fp16 [K/g, N]  */
+    void* y;                  /* fp16 [M, N], fully overwritten */
+    int64_t N;
+} w4a16_matrix_t;
+
+/*
+ * w4a16_matmul_grouped - y_i = x . dequant(W_i) for 1..4 weight matrices that share the
+ * activations x (M, K, group size and layout), in one launch of the decode kernel: the
+ * projections that read one input, such as the query, key and value projections of an
+ * attention layer or the gate and up projections of an FFN. "Beating FP16 with 4-bit
+ * Weights", section "Takeaways", calls decode a parallelism problem, and "Triton Kernel
+ * Matches bitsandbytes: Why Both Lose to Math", section "Limitations and Next Steps", names
+ * launch overhead among the costs of a decode step: one launch over the matrices' combined
+ * columns pays the per-launch cost once and gives the chip more work-groups.
+ *   x        device fp16 [M, K], 16-byte aligned
+ *   mats     host array of n_mats w4a16_matrix_t (read during the call only)
+ *   n_mats   1..4
+ *   plan     NULL or a forced plan. The plan is chosen (or completed) for M, the summed N and
+ *            K; when it selects the decode kernel (W4A16_KERNEL_SKINNY) one launch covers
+ *            every matrix with that plan, and each y_i is bitwise equal to
+ *            w4a16_matmul_fmt(x, W_i, ...) under the same plan. When it selects the prefill
+ *            kernel, each matrix is launched on its own (with the forced plan, or with the
+ *            dispatcher's plan for its shape), as the prefill tiles fill the chip per matrix.
+ * Asynchronous on `stream`; split-K uses the stream's workspace as w4a16_matmul does.
+ * Errors: INVALID_ARG (null pointers, n_mats, layout, plan), UNSUPPORTED (a matrix's shape,
+ * or the summed N, outside what w4a16_matmul accepts), ALIGNMENT, HIP; all found before any
+ * launch except HIP errors of a later matrix when the prefill kernel is launched per matrix.
+ */
+int w4a16_matmul_grouped(const void* x, const w4a16_matrix_t* mats, int n_mats, int64_t M, int64_t K,
+                         int64_t group_size, int layout, void* stream, const w4a16_plan_t* plan);
+
+/*
  * w4a16_matmul_noalloc - w4a16_matmul_fmt that allocates nothing, for callers that cannot
  * call hipMalloc: code under HIP graph capture, tight serving loops, harnesses that forbid
  * device allocation. Same arguments, plans, kernels and results as w4a16_matmul_fmt; a plan

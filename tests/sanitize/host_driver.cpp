@@ -173,6 +173,23 @@ static void device_call_errors() {
            W4A16_ERR_UNSUPPORTED, "noalloc plan beyond the static scratch");
     expect(w4a16_matmul_noalloc(p[0], nullptr, p[2], p[3], p[4], 1, 64, 128, 128, 0, nullptr, nullptr),
            W4A16_ERR_INVALID_ARG, "noalloc null qweight");
+    w4a16_matrix_t gm[5];
+    for (int i = 0; i < 5; ++i)
+        gm[i] = w4a16_matrix_t{(const int32_t*)p[1], p[2], p[3], p[4], 64};
+    expect(w4a16_matmul_grouped(p[0], gm, 5, 1, 4096, 128, 0, nullptr, nullptr), W4A16_ERR_INVALID_ARG,
+           "grouped 5 matrices");
+    expect(w4a16_matmul_grouped(p[0], gm, 0, 1, 4096, 128, 0, nullptr, nullptr), W4A16_ERR_INVALID_ARG,
+           "grouped 0 matrices");
+    gm[2].N = 62;
+    expect(w4a16_matmul_grouped(p[0], gm, 3, 1, 4096, 128, 0, nullptr, nullptr), W4A16_ERR_UNSUPPORTED,
+           "grouped N%4");
+    gm[2].N = 64;
+    gm[1].zeros = mis;
+    expect(w4a16_matmul_grouped(p[0], gm, 3, 1, 4096, 128, 0, nullptr, nullptr), W4A16_ERR_ALIGNMENT,
+           "grouped misaligned zeros");
+    gm[1].zeros = p[3];
+    expect(w4a16_matmul_grouped(p[0], gm, 3, 1, 4096, 100, 0, nullptr, nullptr), W4A16_ERR_UNSUPPORTED,
+           "grouped g=100");
     w4a16_plan_t async{2, 0, 0, 0, 3, 0, 0, 0};
     expect(w4a16_matmul_ex(p[0], (const int32_t*)p[1], p[2], p[3], p[4], 1, 60, 1024, 128, nullptr, &async),
            W4A16_ERR_UNSUPPORTED, "async tile N%8");

@@ -335,3 +335,32 @@ def test_noalloc_rejects_plans_beyond_the_scratch():
     assert "static scratch" in so.w4a16_last_error_detail().decode()
     assert so.w4a16_matmul_noalloc(P[0], None, P[2], P[3], P[4], 1, 64, 128, 128, 0, None,
                                    None) == lib.W4A16_ERR_INVALID_ARG
+
+
+def test_grouped_rejects_bad_arguments():
+    """w4a16_matmul_grouped validates every matrix (and the summed N) before any launch."""
+    so = B.load()
+
+    def mats(*ns, bad=None):
+        arr = (B.w4a16_matrix_t * len(ns))()
+        for i, n in enumerate(ns):
+            base = A + 0x10000 * (i + 1)
+            arr[i] = B.w4a16_matrix_t(base, base + 0x1000, base + 0x2000, base + 0x3000, n)
+        if bad is not None:
+            setattr(arr[bad[0]], bad[1], bad[2])
+        return arr
+
+    def call(arr, n=None, M=1, K=4096, g=128, layout=0, x=P[0], plan=None):
+        return so.w4a16_matmul_grouped(x, arr, len(arr) if n is None else n, M, K, g, layout, None, plan)
+    assert call(mats(64), n=0) == lib.W4A16_ERR_INVALID_ARG
+    assert call(mats(64, 64, 64, 64, 64)) == lib.W4A16_ERR_INVALID_ARG            # at most 4
+    assert call(mats(64, 64), x=None) == lib.W4A16_ERR_INVALID_ARG
+    assert call(mats(64, 64, bad=(1, "zeros", None))) == lib.W4A16_ERR_INVALID_ARG
+    assert call(mats(64, 62)) == lib.W4A16_ERR_UNSUPPORTED                         # N % 4
+    assert call(mats(64, 64), K=200) == lib.W4A16_ERR_UNSUPPORTED
+    assert call(mats(64, 64), layout=5) == lib.W4A16_ERR_INVALID_ARG
+    assert call(mats(64, 64, bad=(0, "y", A + 0x3008))) == lib.W4A16_ERR_ALIGNMENT
+    assert call(mats(64, 64), x=ctypes.c_void_p(A + 4)) == lib.W4A16_ERR_ALIGNMENT
+    bad_plan = B.w4a16_plan_t(kernel=1, cols=24)
+    assert call(mats(64, 64), plan=ctypes.byref(bad_plan)) == lib.W4A16_ERR_INVALID_ARG
+    assert so.w4a16_matmul_grouped(P[0], None, 1, 1, 4096, 128, 0, None, None) == lib.W4A16_ERR_INVALID_ARG

@@ -48,6 +48,11 @@ class w4a16_plan_t(ctypes.Structure):
                 "cols": self.cols, "seg": self.seg}
 
 
+class w4a16_matrix_t(ctypes.Structure):
+    _fields_ = [("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("N", ctypes.c_int64)]
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -61,6 +66,8 @@ _SIGS = {
                          ctypes.POINTER(w4a16_plan_t)], ctypes.c_int),
     "w4a16_matmul_fmt": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int, _P,
                           ctypes.POINTER(w4a16_plan_t)], ctypes.c_int),
+    "w4a16_matmul_grouped": ([_P, ctypes.POINTER(w4a16_matrix_t), ctypes.c_int, _I64, _I64, _I64, ctypes.c_int, _P,
+                              ctypes.POINTER(w4a16_plan_t)], ctypes.c_int),
     "w4a16_matmul_noalloc": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int, _P,
                               ctypes.POINTER(w4a16_plan_t)], ctypes.c_int),
     "w4a16_plan": ([_I64, _I64, _I64, _I64, ctypes.POINTER(w4a16_plan_t)], ctypes.c_int),
@@ -247,6 +254,40 @@ def w4a16_matmul(x, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, strea
         rc = load().w4a16_matmul_fmt(*args[:-1], lay, args[-1], pl)
         _check(rc, "w4a16_matmul_fmt")
     return y
+
+
+def w4a16_matmul_grouped(x, weights, ys=None, group_size=GROUP_SIZE, stream=None, plan=None, layout="linear"):
+    """y_i = x . dequant(W_i) for the matrices in `weights` (a list of (qweight, scales, zeros),
+    1..4 of them) in one call of w4a16_matmul_grouped; returns the list of y_i (allocated when
+    `ys` is None)."""
+    import torch
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    M, K = x.shape
+    if not 1 <= len(weights) <= 4:
+        raise ValueError("1..4 weight matrices")
+    if ys is None:
+        ys = [torch.empty((M, qw.shape[1]), dtype=torch.float16, device=x.device) for qw, _, _ in weights]
+    arr = (w4a16_matrix_t * len(weights))()
+    for i, ((qw, s, z), y) in enumerate(zip(weights, ys)):
+        N = qw.shape[1]
+        if qw.dim() != 2 or qw.shape[0] * 8 != K:
+            raise ValueError(f"matrix {i}: qweight must be [K/8, N] with K={K}")
+        if scales_shape_bad(s, z, K, N, group_size):
+            raise ValueError(f"matrix {i}: scales/zeros must be [K/group_size, N]")
+        if y.shape != (M, N):
+            raise ValueError(f"matrix {i}: y must be [M, N]")
+        arr[i] = w4a16_matrix_t(_dev_ptr(qw, "qweight", torch.int32), _dev_ptr(s, "scales", torch.float16),
+                                _dev_ptr(z, "zeros", torch.float16), _dev_ptr(y, "y", torch.float16), N)
+    pl = ctypes.byref(_make_plan(plan)) if plan is not None else None
+    rc = load().w4a16_matmul_grouped(_dev_ptr(x, "x", torch.float16), arr, len(weights), M, K, group_size,
+                                     _layout_id(layout), _stream_ptr(stream, x.device), pl)
+    _check(rc, "w4a16_matmul_grouped")
+    return ys
+
+
+def scales_shape_bad(scales, zeros, K, N, group_size):
+    return group_size <= 0 or scales.shape != (K // group_size, N) or zeros.shape != (K // group_size, N)
 
 
 def w4a16_matmul_noalloc(x, qweight, scales, zeros, y, group_size=GROUP_SIZE, stream=None, plan=None,

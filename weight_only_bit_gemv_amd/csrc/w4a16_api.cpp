@@ -91,6 +91,7 @@ const TunedPlan kTuned[] = {
     { 4096,   4096, 16, 16,  4, 32, 4},   // 7.22 us
     { 4096,   4096, 32, 64,  4,  8, 2},   // 9.71 us (4 splits)
     { 4096,   4096, 64, 32,  4, 48, 4},   // 11.79 us
+    { 4096,  12288,  1, 64, 16,  8, 4},   // 8.28 us (q, k, v of 4096 x 4096 in one grouped launch)
     { 4096,  14336,  1, 64,  4, 32, 4},   // 9.01 us
     { 4096,  14336,  2, 64,  4, 32, 4},   // 9.13 us
     { 4096,  14336,  4, 64,  4, 32, 4},   // 9.30 us
@@ -434,6 +435,49 @@ int call_workspace(bool noalloc, void* stream, uint64_t bytes, uint64_t n_counte
     return W4A16_OK;
 }
 
+// One launch of the decode kernel over 1..kMaxGroupMats matrices that share x (validated,
+// plan completed for M, the summed N and K): their column strips are numbered one after the
+// other, so each work-group finds its matrix from its strip.
+int launch_skinny_mats(const void* x, const w4a16_matrix_t* mats, int n_mats, int64_t M, int64_t K,
+                       int64_t group_size, int layout, void* stream, const w4a16_plan_t& pl, bool noalloc) {
+    w4a16::SkinnyParams p{};
+    p.x = static_cast<const uint16_t*>(x);
+    p.n_mats = n_mats;
+    int64_t strips = 0;
+    for (int i = 0; i < w4a16::kMaxGroupMats; ++i) {
+        const w4a16_matrix_t& m = mats[std::min(i, n_mats - 1)];       // unused entries repeat the last
+        p.mat[i].qweight = reinterpret_cast<const uint32_t*>(m.qweight);
+        p.mat[i].scales = static_cast<const uint16_t*>(m.scales);
+        p.mat[i].zeros = static_cast<const uint16_t*>(m.zeros);
+        p.mat[i].y = static_cast<uint16_t*>(m.y);
+        p.mat[i].N = (int)m.N;
+        p.mat[i].strip0 = (int)strips;
+        if (i < n_mats) strips += ceil_div(m.N, pl.cols);
+    }
+    p.M = (int)M;
+    p.K = (int)K;
+    p.kc = pl.kc;
+    p.splits = pl.splits;
+    p.n_strips = (int)strips;
+    p.row_tiles = pl.row_tiles;
+    p.row_blocks = (int)ceil_div(M, 16 * (int64_t)pl.row_tiles);
+    p.waves = pl.waves;
+    p.lw = pl.cols / 16;
+    p.seg = pl.seg;
+    p.gshift = w4a16::log2_exact(group_size / w4a16::kKStep);
+    p.layout = layout;
+    uint64_t ws_bytes = 0, n_counters = 0;
+    w4a16::skinny_workspace(p, &ws_bytes, &n_counters);
+    if (ws_bytes) {
+        const int rc = call_workspace(noalloc, stream, ws_bytes, n_counters, &p.ws, &p.counters);
+        if (rc) return rc;
+    }
+    const int e = w4a16::launch_skinny(p, stream);
+    if (e != (int)hipSuccess)
+        return fail(W4A16_ERR_HIP, "skinny kernel launch: %s", hipGetErrorString((hipError_t)e));
+    return ok();
+}
+
 int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const void* zeros,
                 void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, int layout, void* stream,
                 const w4a16_plan_t* forced, bool noalloc = false) {
@@ -476,35 +520,8 @@ int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const
         return ok();
     }
 
-    w4a16::SkinnyParams p{};
-    p.x = static_cast<const uint16_t*>(x);
-    p.qweight = reinterpret_cast<const uint32_t*>(qweight);
-    p.scales = static_cast<const uint16_t*>(scales);
-    p.zeros = static_cast<const uint16_t*>(zeros);
-    p.y = static_cast<uint16_t*>(y);
-    p.M = (int)M;
-    p.N = (int)N;
-    p.K = (int)K;
-    p.kc = pl.kc;
-    p.splits = pl.splits;
-    p.n_strips = (int)ceil_div(N, pl.cols);
-    p.row_tiles = pl.row_tiles;
-    p.row_blocks = (int)ceil_div(M, 16 * (int64_t)pl.row_tiles);
-    p.waves = pl.waves;
-    p.lw = pl.cols / 16;
-    p.seg = pl.seg;
-    p.gshift = w4a16::log2_exact(group_size / w4a16::kKStep);
-    p.layout = layout;
-    uint64_t ws_bytes = 0, n_counters = 0;
-    w4a16::skinny_workspace(p, &ws_bytes, &n_counters);
-    if (ws_bytes) {
-        rc = call_workspace(noalloc, stream, ws_bytes, n_counters, &p.ws, &p.counters);
-        if (rc) return rc;
-    }
-    const int e = w4a16::launch_skinny(p, stream);
-    if (e != (int)hipSuccess)
-        return fail(W4A16_ERR_HIP, "skinny kernel launch: %s", hipGetErrorString((hipError_t)e));
-    return ok();
+    const w4a16_matrix_t one{qweight, scales, zeros, y, N};
+    return launch_skinny_mats(x, &one, 1, M, K, group_size, layout, stream, pl, noalloc);
 }
 
 }  // namespace
@@ -562,6 +579,49 @@ int w4a16_matmul_fmt(const void* x, const int32_t* qweight, const void* scales, 
                      void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, int layout, void* stream,
                      const w4a16_plan_t* plan) {
     return matmul_impl(x, qweight, scales, zeros, y, M, N, K, group_size, layout, stream, plan);
+}
+
+int w4a16_matmul_grouped(const void* x, const w4a16_matrix_t* mats, int n_mats, int64_t M, int64_t K,
+                         int64_t group_size, int layout, void* stream, const w4a16_plan_t* plan) {
+    if (!x || !mats) return fail(W4A16_ERR_INVALID_ARG, "null pointer argument");
+    if (n_mats < 1 || n_mats > w4a16::kMaxGroupMats)
+        return fail(W4A16_ERR_INVALID_ARG, "n_mats=%d must lie in 1..%d", n_mats, w4a16::kMaxGroupMats);
+    if (!w4a16::layout_supported(layout)) return fail(W4A16_ERR_INVALID_ARG, "unknown layout %d", layout);
+    int64_t n_total = 0;
+    for (int i = 0; i < n_mats; ++i) {
+        const w4a16_matrix_t& m = mats[i];
+        if (!m.qweight || !m.scales || !m.zeros || !m.y)
+            return fail(W4A16_ERR_INVALID_ARG, "null pointer in matrix %d", i);
+        int rc = check_gpu_shape(M, m.N, K, group_size);
+        if (rc) return rc;
+        if (!aligned16(m.qweight) || !aligned16(m.scales) || !aligned16(m.zeros) || !aligned16(m.y))
+            return fail(W4A16_ERR_ALIGNMENT, "device pointers of matrix %d must be 16-byte aligned", i);
+        n_total += m.N;
+    }
+    int rc = check_gpu_shape(M, n_total, K, group_size);
+    if (rc) return rc;
+    if (!aligned16(x)) return fail(W4A16_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+    w4a16_plan_t pl = plan ? *plan : w4a16_plan_t{};
+    if (pl.kernel == W4A16_KERNEL_AUTO) pl.kernel = (int32_t)auto_kernel(M, n_total, K);
+    if (pl.kernel == W4A16_KERNEL_PREFILL) {
+        // the prefill tiles fill the chip per matrix: one launch each, each with its own plan
+        // unless the caller forced one
+        const bool forced = plan && plan->kernel == W4A16_KERNEL_PREFILL;
+        for (int i = 0; i < n_mats; ++i) {                    // every plan is checked before any launch
+            w4a16_plan_t pi = forced ? *plan : w4a16_plan_t{};
+            rc = complete_plan(M, mats[i].N, K, group_size, &pi);
+            if (rc) return rc;
+        }
+        for (int i = 0; i < n_mats; ++i) {
+            rc = matmul_impl(x, mats[i].qweight, mats[i].scales, mats[i].zeros, mats[i].y, M, mats[i].N, K,
+                             group_size, layout, stream, forced ? plan : nullptr);
+            if (rc) return rc;
+        }
+        return ok();
+    }
+    rc = complete_plan(M, n_total, K, group_size, &pl);
+    if (rc) return rc;
+    return launch_skinny_mats(x, mats, n_mats, M, K, group_size, layout, stream, pl, false);
 }
 
 int w4a16_matmul_noalloc(const void* x, const int32_t* qweight, const void* scales, const void* zeros,

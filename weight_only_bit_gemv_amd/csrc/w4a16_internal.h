@@ -25,18 +25,29 @@ constexpr int kKStep = 32;           // K rows per MFMA step (4 packed rows)
 inline bool group_supported(int64_t g) { return g == 32 || g == 64 || g == 128 || g == 256; }
 inline int log2_exact(int64_t v) { int r = 0; while ((int64_t(1) << r) < v) ++r; return r; }
 
-struct SkinnyParams {
-    const uint16_t* x;        // fp16 [M, K]
+// One weight matrix of a skinny launch. A launch covers 1..kMaxGroupMats matrices that share
+// the activations x (and M, K, the group size, the layout and the plan); their column strips
+// are numbered one after the other: matrix i owns strips strip0 .. strip0 + ceil(N / cols) - 1.
+constexpr int kMaxGroupMats = 4;
+struct SkinnyMatrix {
     const uint32_t* qweight;  // int32 [K/8, N]
     const uint16_t* scales;   // fp16 [K/g, N]
     const uint16_t* zeros;    // fp16 [K/g, N]
     uint16_t* y;              // fp16 [M, N]
+    int N;
+    int strip0;               // first strip of this matrix
+};
+
+struct SkinnyParams {
+    const uint16_t* x;        // fp16 [M, K]
+    SkinnyMatrix mat[kMaxGroupMats];
+    int n_mats;               // matrices in this launch (1 for w4a16_matmul)
     float* ws;                // fp32 partials [row_blocks][n_strips][splits][16*row_tiles][cols]
     uint32_t* counters;       // arrival counters [row_blocks][n_strips], zero between calls
-    int M, N, K;
+    int M, K;
     int kc;                   // K-steps per wavefront
     int splits;               // work-groups along K per strip
-    int n_strips;             // ceil(N / cols)
+    int n_strips;             // strips of all matrices: sum of ceil(N_i / cols)
     int row_tiles;            // 16-row tiles per work-group (1..4)
     int row_blocks;           // ceil(M / (16 * row_tiles))
     int waves;                // wavefronts per work-group (4, 8 or 16), each on its own K range

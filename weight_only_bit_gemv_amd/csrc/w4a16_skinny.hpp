@@ -270,10 +270,18 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
     if (LW == 1 && b < ((p.n_strips * p.splits) & ~15)) b = (b & ~15) | ((b & 7) << 1) | ((b >> 3) & 1);
     const int strip = b % p.n_strips;
     const int split = b / p.n_strips;
+    // the matrix this strip belongs to (wave-uniform; a single matrix unless the launch
+    // groups several that share x)
+    int mi = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxGroupMats; ++j)
+        if (j < p.n_mats && strip >= p.mat[j].strip0) mi = j;
+    const SkinnyMatrix& mat = p.mat[mi];
+    const int N = mat.N;
     const int row0 = blockIdx.y * 16 * MT;
     const int rows = min(16 * MT, p.M - row0);          // valid output rows of this work-group
-    const int n = strip * CW + lc * LW;
-    const bool col_ok = n < p.N;
+    const int n = (strip - mat.strip0) * CW + lc * LW;
+    const bool col_ok = n < N;
     const int nl = col_ok ? n : 0;       // loads stay in bounds; results of such lanes are dropped
     const int KS = p.K / kKStep;
     const int chunk = split * W + wave;
@@ -285,17 +293,17 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
     // range.
     Streams<MT> st;
     {
-        const size_t w_rows = (size_t)(p.K / 8 - 4 * k0) * p.N * 4;
-        st.w = __builtin_amdgcn_make_buffer_rsrc((void*)(p.qweight + (size_t)4 * k0 * p.N), 0,
+        const size_t w_rows = (size_t)(p.K / 8 - 4 * k0) * N * 4;
+        st.w = __builtin_amdgcn_make_buffer_rsrc((void*)(mat.qweight + (size_t)4 * k0 * N), 0,
                                                  (int)min(w_rows, (size_t)0xffffffffu), kRsrcWord3);
         st.x = __builtin_amdgcn_make_buffer_rsrc((void*)(p.x + (size_t)row0 * p.K + (size_t)k0 * kKStep), 0,
                                                  (int)min(((size_t)(p.M - row0) * p.K - (size_t)k0 * kKStep) * 2, (size_t)0xffffffffu), kRsrcWord3);
-        const int sz_bytes = (p.K >> (p.gshift + 5)) * p.N * 2;
-        st.s = __builtin_amdgcn_make_buffer_rsrc((void*)p.scales, 0, sz_bytes, kRsrcWord3);
-        st.z = __builtin_amdgcn_make_buffer_rsrc((void*)p.zeros, 0, sz_bytes, kRsrcWord3);
+        const int sz_bytes = (p.K >> (p.gshift + 5)) * N * 2;
+        st.s = __builtin_amdgcn_make_buffer_rsrc((void*)mat.scales, 0, sz_bytes, kRsrcWord3);
+        st.z = __builtin_amdgcn_make_buffer_rsrc((void*)mat.zeros, 0, sz_bytes, kRsrcWord3);
     }
-    st.w_lane = (lg * p.N + nl) * 4;
-    st.w_step = 16 * p.N;
+    st.w_lane = (lg * N + nl) * 4;
+    st.w_step = 16 * N;
     // A-operand rows beyond M only feed output rows beyond M, which are never stored, so
     // their loads are clamped to row M-1 instead of being predicated (a predicated load
     // would put a branch between a segment's loads and their use, and the compiler then
@@ -304,7 +312,7 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
     for (int mt = 0; mt < MT; ++mt)
         st.x_lane[mt] = ((min(row0 + mt * 16 + lc, p.M - 1) - row0) * p.K + lg * 8) * 2;
     st.sz_lane = nl * 2;
-    st.sz_step = p.N * 2;
+    st.sz_step = N * 2;
     st.gshift = p.gshift;
     const UnpackConsts uc = unpack_consts();
 
@@ -386,7 +394,7 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int rl = mt * 16 + lg * 4 + r;
-                if (rl < rows) store_y<LW>(p.y + (size_t)(row0 + rl) * p.N + n, out[mt][r]);
+                if (rl < rows) store_y<LW>(mat.y + (size_t)(row0 + rl) * N + n, out[mt][r]);
             }
         return;
     }
@@ -452,7 +460,7 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int rl = mt * 16 + lg * 4 + r;
-                if (rl < rows) store_y<LW>(p.y + (size_t)(row0 + rl) * p.N + n, v[r]);
+                if (rl < rows) store_y<LW>(mat.y + (size_t)(row0 + rl) * N + n, v[r]);
             }
         }
     }
