@@ -20,12 +20,21 @@ Other workloads (same JSON keys, config.workload names them):
   prefill       M-crossover against torch fp16 matmul (hipBLASLt) for M = 1..2048 on
                 (8192,8192), (8192,28672), (28672,8192) and the decode shapes
 
-Printed: one JSON line. `value` is the algorithmic byte rate over the timed region
-(int4 weights + fp16 scales/zeros + fp16 x + fp16 y) / time, in GB/s. `roofline` relates
-the dominant kernel's average launch to the 8 TB/s HBM peak (MFMA peak for prefill);
-`cpu_baseline` times the oracle (NumPy, fp64) on the host cores on one decode sweep.
+Printed: one JSON line. `value` is the algorithmic byte rate (int4 weights + fp16
+scales/zeros + fp16 x + fp16 y) of one step over the median of up to 5 timed batches (the
+K steps split into batches of graph replays, each between HIP events; the minimum is
+reported too), in GB/s. `roofline` relates the average launch to the 8 TB/s HBM peak (MFMA
+peak for prefill), gives the fraction of the measured read ceiling (w4a16_read_probe at each
+call's byte count, same timing) and, from the committed kernel-trace summary of the same
+sources, the dominant kernel instance's own rate; `grouped` times q/k/v and gate/up as one
+grouped launch against one launch per matrix; `cpu_baseline` times the oracle (NumPy, fp64)
+on the host cores over passes of the decode sweep (about 10 s). --record FILE also writes
+the line with the command, the sources' hash and the machine.
 
 Profiling support:
+  --trace-pass             only the timed decode-sweep steps, for rocprofv3 --kernel-trace
+  --summarize-kernel-trace DIR...  per-call and per-instance kernel durations of such a run
+                           -> profiles/kernel_trace_skinny_decode_sweep.{json,md}
   --pmc-pass               a fixed copy calibration + a few eager sweep steps, for
                            rocprofv3 --pmc; prints no JSON (with --workload prefill:
                            eager prefill-kernel launches at M=2048, K=8192, N=28672)
@@ -65,6 +74,7 @@ PREFILL_SOURCES = sorted(os.path.relpath(f, ROOT) for f in
                          glob.glob(os.path.join(ROOT, "weight_only_bit_gemv_amd", "csrc", "w4a16_prefill*")) +
                          [os.path.join(ROOT, "weight_only_bit_gemv_amd", "csrc", "w4a16_device.hpp")])
 COPY_CAL_BYTES = 256 << 20     # calibration copy for the PMC byte counters
+KTRACE_FILE = os.path.join(ROOT, "profiles", "kernel_trace_skinny_decode_sweep.json")
 METRIC = "W4A16 weight-stream HBM GB/s (% of peak) and us/call at M=1..16"
 
 
@@ -246,37 +256,50 @@ def time_graph(torch, stream, body, reps, warm=2, busy_s=0.05, trials=3):
     return float(np.median(ts)), g
 
 
+def batch_sizes(steps, batches=5):
+    """Split `steps` into up to `batches` consecutive batches of near-equal size."""
+    n = max(1, min(batches, steps))
+    return [steps // n + (1 if i < steps % n else 0) for i in range(n)]
+
+
 def timed_steps(torch, runner, steps, warmup):
-    """Warm up eagerly (allocates this stream's split-K workspace), capture `steps` steps in
-    one graph, check replays against the eager outputs, time one replay. Returns seconds."""
+    """Warm up eagerly (allocates this stream's split-K workspace), capture the steps of each
+    batch size in a graph, check replays against the eager outputs, then time exactly `steps`
+    steps as up to 5 batches, each replay between HIP events on the launch stream. Returns
+    (total seconds, list of seconds per step of each batch)."""
     stream = runner.stream
     with torch.cuda.stream(stream):
         for _ in range(max(1, warmup)):
             runner.step()
     stream.synchronize()
     ref = [y.clone() for y in runner.y]
-
-    def body():
-        for _ in range(steps):
-            runner.step()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        body()
-    replay(torch, g, stream, max(0, warmup))
+    sizes = batch_sizes(steps)
+    graphs = {}
+    for n in sorted(set(sizes)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(n):
+                runner.step()
+        graphs[n] = g
+    for g in graphs.values():
+        replay(torch, g, stream, 1)
     stream.synchronize()
     _check_same(torch, runner, ref, "graph warm-up replay")
-    keep_busy(torch, stream, g, CLOCK_WARM_S)
+    keep_busy(torch, stream, graphs[sizes[0]], CLOCK_WARM_S)
     torch.cuda.synchronize()
-    e0, e1 = events(torch, stream)
+    marks = [events(torch, stream) for _ in sizes]
     with torch.cuda.stream(stream):
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
-    e1.synchronize()
+        for n, (e0, e1) in zip(sizes, marks):
+            e0.record(stream)
+            graphs[n].replay()
+            e1.record(stream)
+    marks[-1][1].synchronize()
     torch.cuda.synchronize()
-    _check_same(torch, runner, ref, "timed replay")
-    del g
-    return e0.elapsed_time(e1) / 1e3
+    _check_same(torch, runner, ref, "timed replays")
+    per_step = [e0.elapsed_time(e1) / 1e3 / n for n, (e0, e1) in zip(sizes, marks)]
+    total = sum(e0.elapsed_time(e1) / 1e3 for e0, e1 in marks)
+    del graphs
+    return total, per_step
 
 
 def _check_same(torch, runner, ref, what):
@@ -381,28 +404,30 @@ def dense_weights(torch, lib, runner, key):
     return [w16] + [w16.clone() for _ in range(copies - 1)]
 
 
-def cpu_baseline(runner, wid):
-    """The oracle as it stands (unpack + exact dequant + fp64 BLAS matmul) on one step."""
+def cpu_baseline(runner, wid, min_s=10.0, max_passes=40):
+    """The oracle as it stands (unpack + exact dequant + fp64 BLAS matmul) on whole passes over
+    the step's GEMMs, repeated until at least `min_s` seconds of CPU work (a bounded sample)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         blas_threads = None
-    total_bytes = 0
+    xs = {(M, K): synth.activations(M, K, wid=wid) for (M, K, N, key) in runner.items}
+    total_bytes, passes = 0, 0
     t0 = time.perf_counter()
-    for (M, K, N, key) in runner.items:
-        qw, s, z = runner.host[key]
-        x = synth.activations(M, K, wid=wid)
-        oracle.matmul(x, qw, s, z, runner.group, layout=runner.layout)
-        total_bytes += alg_bytes(M, K, N, runner.group)
+    while passes < max_passes and (passes == 0 or time.perf_counter() - t0 < min_s):
+        for (M, K, N, key) in runner.items:
+            qw, s, z = runner.host[key]
+            oracle.matmul(xs[(M, K)], qw, s, z, runner.group, layout=runner.layout)
+            total_bytes += alg_bytes(M, K, N, runner.group)
+        passes += 1
     dt = time.perf_counter() - t0
     return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": blas_threads,
             "kind": "oracle",
-            "sample": (f"one pass over the {len(runner.items)} GEMMs of one step (same shapes "
-                       f"and data), {dt:.1f} s; NumPy elementwise unpack/dequant on 1 thread, "
-                       f"fp64 BLAS matmul on {blas_threads} threads of "
-                       f"{len(os.sched_getaffinity(0))} available")}
+            "sample": (f"{passes} passes over the {len(runner.items)} GEMMs of one step (same shapes and "
+                       f"data), {dt:.1f} s; NumPy elementwise unpack/dequant on 1 thread, fp64 BLAS matmul "
+                       f"on {blas_threads} threads of {len(os.sched_getaffinity(0))} available")}
 
 
 def load_traffic():
@@ -459,6 +484,138 @@ def workload_items(name):
     raise SystemExit(f"unknown workload {name}")
 
 
+def read_ceiling(torch, lib, dev, stream, sizes):
+    """Seconds per plain read (w4a16_read_probe: 16-byte non-temporal loads, nothing else) of
+    each byte count in `sizes`, through windows rotated over 1 GiB and timed like the decode
+    calls (a graph of one read per window). The measured ceiling for a call that moves that
+    many bytes."""
+    so = lib.load()
+    buf = torch.empty(ROTATE_BYTES + (64 << 20), dtype=torch.uint8, device=dev)
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    out = {}
+    for b in sorted(set(sizes)):
+        n16 = -(-b // 16) * 16
+        stride = -(-n16 // 4096) * 4096
+        n = max(1, ROTATE_BYTES // stride)
+
+        def body():
+            for i in range(n):
+                rc = so.w4a16_read_probe(buf.data_ptr() + i * stride, n16, sink.data_ptr(), stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"w4a16_read_probe failed ({rc})")
+        sec, _ = time_graph(torch, stream, body, 5)
+        out[b] = sec / n
+    del buf
+    return out
+
+
+CHAIN_GROUPS = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+
+
+class GroupedChain:
+    """The chain_7b token with the projections that share an input launched together
+    (w4a16_matmul_grouped): per layer q/k/v in one launch, o, gate/up in one launch, down;
+    then lm_head: 129 launches instead of 225, on the same weights as `runner`."""
+
+    def __init__(self, torch, lib, runner):
+        B = lib._binding
+        self.torch, self.stream, self.so = torch, runner.stream, lib.load()
+        self.sptr = runner.stream.cuda_stream
+        self.layout_id, self.group = runner.layout_id, runner.group
+        self.calls, self.y, self.items = [], [], []     # one y and one item per matrix
+        self.step_bytes = runner.step_bytes
+        x = runner.x[(1, 4096, synth.WORKLOADS["decode_chain_7b"]["wid"])]
+        for layer in range(synth.CHAIN_7B_LAYERS):
+            for names in CHAIN_GROUPS:
+                keys = [(layer, nm) for nm in names]
+                arr = (B.w4a16_matrix_t * len(keys))()
+                K = None
+                for i, key in enumerate(keys):
+                    qw, s, z = runner.weights[key][0]
+                    K, N = qw.shape[0] * 8, qw.shape[1]
+                    y = torch.empty((1, N), dtype=torch.float16, device=runner.dev)
+                    self.y.append(y)
+                    self.items.append((1, K, N, key))
+                    arr[i] = B.w4a16_matrix_t(qw.data_ptr(), s.data_ptr(), z.data_ptr(), y.data_ptr(), N)
+                xk = x if K == 4096 else runner.x[(1, K, synth.WORKLOADS["decode_chain_7b"]["wid"])]
+                self.calls.append((xk, arr, len(keys), K))
+        lm = [i for i, it in enumerate(runner.items) if it[3] == ("lm_head",)][0]
+        self.lm = (runner, lm)
+        self.y.append(runner.y[lm])
+        self.items.append(runner.items[lm])
+
+    def step(self):
+        for xk, arr, n, K in self.calls:
+            rc = self.so.w4a16_matmul_grouped(xk.data_ptr(), arr, n, 1, K, self.group, self.layout_id, self.sptr, None)
+            if rc != 0:
+                raise RuntimeError(f"w4a16_matmul_grouped failed ({rc})")
+        self.lm[0].launch(self.lm[1])
+
+
+def grouped_decode(torch, lib, dev, stream, group=GROUP, layout="linear", ms=(1, 16)):
+    """The projections of the 7B-shaped layer that share an input, at M = 1 and 16: q/k/v
+    (3 x 4096 x 4096) and gate/up (2 x 4096 x 14336), as one grouped launch against one
+    launch per matrix, weights rotated over 1 GiB."""
+    B = lib._binding
+    so = lib.load()
+    lay = B._layout_id(layout)
+    wid = synth.WORKLOADS["decode_chain_7b"]["wid"]
+    shapes = dict((nm, (K, N)) for nm, K, N in synth.CHAIN_7B_LAYER)
+    out = []
+    for names in (("q", "k", "v"), ("gate", "up")):
+        one = []
+        for nm in names:
+            K, N = shapes[nm]
+            p = [nm0 for nm0, _, _ in synth.CHAIN_7B_LAYER].index(nm)
+            qw, s, z = lib.w4a16_pack(synth.weight(K, N, wid=wid, layer=p), group_size=group, layout=layout)
+            one.append([torch.from_numpy(a).to(dev) for a in (qw, s, z)])
+        per = sum(t.numel() * t.element_size() for m in one for t in m)
+        ring = [one] + [[[t.clone() for t in m] for m in one] for _ in range(max(1, -(-ROTATE_BYTES // per)) - 1)]
+        K = shapes[names[0]][0]
+        Ns = [shapes[nm][1] for nm in names]
+        for M in ms:
+            x = torch.from_numpy(synth.activations(M, K, wid=wid)).to(dev)
+            ys = [torch.empty((M, N), dtype=torch.float16, device=dev) for N in Ns]
+            arrs = []
+            for mats in ring:
+                arr = (B.w4a16_matrix_t * len(names))()
+                for i, ((q, s_, z_), y) in enumerate(zip(mats, ys)):
+                    arr[i] = B.w4a16_matrix_t(q.data_ptr(), s_.data_ptr(), z_.data_ptr(), y.data_ptr(), Ns[i])
+                arrs.append(arr)
+
+            def grouped():
+                for arr in arrs:
+                    if so.w4a16_matmul_grouped(x.data_ptr(), arr, len(names), M, K, group, lay, stream.cuda_stream, None):
+                        raise RuntimeError("w4a16_matmul_grouped failed")
+
+            def separate():
+                for mats in ring:
+                    for (q, s_, z_), y in zip(mats, ys):
+                        if so.w4a16_matmul_fmt(x.data_ptr(), q.data_ptr(), s_.data_ptr(), z_.data_ptr(), y.data_ptr(),
+                                               M, q.shape[1], K, group, lay, stream.cuda_stream, None):
+                            raise RuntimeError("w4a16_matmul_fmt failed")
+            tg = time_graph(torch, stream, grouped, 5)[0] / len(ring)
+            ts = time_graph(torch, stream, separate, 5)[0] / len(ring)
+            b = sum(alg_bytes(M, K, N, group) for N in Ns)
+            out.append({"matrices": "+".join(names), "M": M, "K": K, "N": Ns, "bytes": b,
+                        "grouped_us": round(tg * 1e6, 3), "grouped_GBps": round(b / tg / 1e9, 1),
+                        "grouped_frac_hbm": round(b / tg / 1e9 / HBM_PEAK_GBS, 4),
+                        "separate_launches_us": round(ts * 1e6, 3), "speedup": round(ts / tg, 3),
+                        "plan": lib.w4a16_plan(M, sum(Ns), K, group_size=group)})
+        del ring
+    return out
+
+
+def load_kernel_trace():
+    """Per-kernel durations from the committed kernel-trace summary of the decode sweep, if it
+    was taken on the current decode kernel sources and plans (else None)."""
+    try:
+        d = json.load(open(KTRACE_FILE))
+    except (OSError, ValueError):
+        return None
+    return d if d.get("kernel_source_sha") == decode_kernel_hash() else None
+
+
 def run_decode(args):
     import torch
     import weight_only_bit_gemv_amd as lib
@@ -467,7 +624,8 @@ def run_decode(args):
     torch.cuda.set_device(dev)
     stream = torch.cuda.Stream(device=dev)
     fam, items, desc, replicate = workload_items(args.workload)
-    rotate = 0 if args.workload == "chain_7b" else ROTATE_BYTES
+    chain = args.workload == "chain_7b"
+    rotate = 0 if chain else ROTATE_BYTES
     runner = Runner(torch, lib, dev, stream, fam, items, rotate, replicate, args.group_size,
                     args.symmetric, args.layout)
     if args.group_size != GROUP or args.symmetric or args.layout != "linear":
@@ -475,10 +633,14 @@ def run_decode(args):
                 f"; weight format: {'symmetric (zero 8)' if args.symmetric else 'asymmetric'}, "
                 f"group {args.group_size}, {args.layout} layout")
     launches = len(items)
-    steps = args.steps if args.workload != "chain_7b" else max(1, args.steps // 10)
-    elapsed = timed_steps(torch, runner, steps, args.warmup)
-    value = runner.step_bytes * steps / elapsed / 1e9
-    avg_launch_s = elapsed / (steps * launches)
+    steps = args.steps if not chain else max(1, args.steps // 10)
+    elapsed, per_step = timed_steps(torch, runner, steps, args.warmup)
+    t_med, t_min = float(np.median(per_step)), float(np.min(per_step))
+    value = runner.step_bytes / t_med / 1e9
+    avg_launch_s = t_med / launches
+    if args.trace_pass:
+        log(f"[trace] {steps} timed steps done")
+        return
 
     with torch.cuda.stream(stream):                 # eager rate, for reference
         e0, e1 = events(torch, stream)
@@ -489,8 +651,8 @@ def run_decode(args):
     e1.synchronize()
     eager_elapsed = e0.elapsed_time(e1) / 1e3
 
-    per = per_item_times(torch, lib, runner) if args.workload != "chain_7b" else []
-    if not args.no_dense and args.workload != "chain_7b":
+    per = per_item_times(torch, lib, runner) if not chain else []
+    if not args.no_dense and not chain:
         dw = {}
         for r in per:
             key = next(k for (M, K, N, k) in items if (K, N) == (r["K"], r["N"]))
@@ -503,37 +665,103 @@ def run_decode(args):
             r["speedup_vs_dense_fp16"] = round(d / (r["us"] / 1e6), 3)
         del dw
     copy_gbs = copy_bandwidth(torch, dev, stream)
+    ceil_s = {}
+    if not chain:
+        ceil_s = read_ceiling(torch, lib, dev, stream, [alg_bytes(M, K, N, args.group_size) for (M, K, N, _) in items])
+        for r in per:
+            b = alg_bytes(r["M"], r["K"], r["N"], args.group_size)
+            r["read_ceiling_us"] = round(ceil_s[b] * 1e6, 3)
+            r["frac_of_read_ceiling"] = round(ceil_s[b] / (r["us"] / 1e6), 4)
     achieved = runner.step_bytes / launches / avg_launch_s / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": (load_traffic() if args.workload == "decode_sweep" and args.group_size == GROUP
+                        and not args.symmetric and args.layout == "linear" else None),
+            "kernel": "skinny_kernel (decode weight stream, MFMA, split-K when K is deep)",
+            "achieved_is": ("algorithmic bytes per launch / (median step time / launches): whole-step rate, "
+                            "the gap between graph nodes included"),
+            "avg_launch_us": round(avg_launch_s * 1e6, 3)}
+    if ceil_s:
+        read_step = sum(ceil_s[alg_bytes(M, K, N, args.group_size)] for (M, K, N, _) in items)
+        roof["read_ceiling_GBps"] = round(runner.step_bytes / read_step / 1e9, 1)
+        roof["frac_of_read_ceiling"] = round(read_step / t_med, 4)
+    kt = load_kernel_trace() if (args.workload == "decode_sweep" and args.group_size == GROUP and
+                                 not args.symmetric and args.layout == "linear") else None
+    if kt:
+        dom = kt["dominant"]
+        roof["dominant_kernel"] = {
+            "name": dom["name"], "avg_ns": dom["avg_ns"], "alg_bytes_per_launch": dom["alg_bytes_per_launch"],
+            "GBps": dom["GBps"], "frac": dom["frac_hbm"], "share_of_kernel_time": dom["share"],
+            "source": os.path.relpath(KTRACE_FILE, ROOT),
+            "is": ("kernel-trace durations (rocprofv3) of the same sources and plans, no graph gap; the "
+                   "profiler lengthens kernels a little, so this is a lower bound of the unprofiled rate")}
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": steps, "warmup": args.warmup, "ms_per_step": round(elapsed / steps * 1e3, 4),
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(t_med * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": desc, "group_size": args.group_size, "symmetric": args.symmetric,
                    "layout": args.layout,
                    "launches_per_step": launches, "bytes_per_step": runner.step_bytes,
-                   "timing": "HIP graph of all steps, events on the launch stream",
-                   "weight_copies_rotated": {str(k): len(v) for k, v in runner.weights.items()
-                                             if args.workload != "chain_7b"}},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": (load_traffic() if args.workload == "decode_sweep" and args.group_size == GROUP
-                                 and not args.symmetric and args.layout == "linear" else None),
-                     "kernel": "skinny_kernel (decode weight stream, MFMA, split-K when K is deep)",
-                     "avg_launch_us": round(avg_launch_s * 1e6, 3)},
+                   "timing": (f"{len(per_step)} batches of HIP-graph replays ({'+'.join(map(str, batch_sizes(steps)))} "
+                              f"steps), events on the launch stream; value and ms_per_step from the median batch"),
+                   "weight_copies_rotated": {str(k): len(v) for k, v in runner.weights.items() if not chain}},
+        "roofline": roof,
+        "step_ms_median": round(t_med * 1e3, 4), "step_ms_min": round(t_min * 1e3, 4),
+        "value_at_min": round(runner.step_bytes / t_min / 1e9, 2),
+        "timed_total_ms": round(elapsed * 1e3, 4),
         "measured_copy_GBps": round(copy_gbs, 1),
         "frac_of_measured_copy": round(value / copy_gbs, 4),
         "eager_ms_per_step": round(eager_elapsed / steps * 1e3, 4),
         "per_shape": per,
     }
-    if args.workload == "chain_7b":
-        result["tokens_per_s"] = round(steps / elapsed, 2)
-        result["us_per_token"] = round(elapsed / steps * 1e6, 2)
+    if args.workload == "decode_sweep" and not args.no_grouped:
+        result["grouped"] = grouped_decode(torch, lib, dev, stream, args.group_size, args.layout)
+    if chain:
+        result["tokens_per_s"] = round(1.0 / t_med, 2)
+        result["us_per_token"] = round(t_med * 1e6, 2)
         result["ceiling_tokens_per_s_at_8TBps"] = round(HBM_PEAK_GBS * 1e9 / runner.step_bytes, 1)
         result["ceiling_tokens_per_s_at_measured_copy"] = round(copy_gbs * 1e9 / runner.step_bytes, 1)
+        gc = GroupedChain(torch, lib, runner)
+        g_elapsed, g_per = timed_steps(torch, gc, steps, args.warmup)
+        g_med = float(np.median(g_per))
+        result["grouped_chain"] = {"launches_per_token": len(gc.calls) + 1, "us_per_token": round(g_med * 1e6, 2),
+                                   "tokens_per_s": round(1.0 / g_med, 2),
+                                   "GBps": round(runner.step_bytes / g_med / 1e9, 1),
+                                   "frac_hbm": round(runner.step_bytes / g_med / 1e9 / HBM_PEAK_GBS, 4),
+                                   "groups": "per layer q+k+v, o, gate+up, down; then lm_head"}
     if not args.no_cpu and args.workload == "decode_sweep":
         result["cpu_baseline"] = cpu_baseline(runner, synth.WORKLOADS["decode_sweep"]["wid"])
+    emit(result, args)
+
+
+def emit(result, args):
+    """Print the JSON line; with --record, also write it with the command, the sources' hash
+    and the machine to a file."""
     print(json.dumps(result), flush=True)
+    if args.record:
+        import platform
+        import torch
+        rec = {"command": "python " + " ".join(sys.argv), "sources_sha": all_sources_hash(),
+               "host": platform.node(), "gpu": torch.cuda.get_device_name(0),
+               "date_utc": time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime()), "result": result}
+        os.makedirs(os.path.dirname(os.path.abspath(args.record)), exist_ok=True)
+        with open(args.record, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+
+
+def all_sources_hash():
+    """Hash of every source that decides a measured number: the kernels, the dispatcher, the
+    binding, synth.py and bench.py."""
+    files = sorted(glob.glob(os.path.join(ROOT, "weight_only_bit_gemv_amd", "csrc", "*")) +
+                   [os.path.join(ROOT, "weight_only_bit_gemv_amd", "_binding.py"), os.path.join(ROOT, "synth.py"),
+                    os.path.abspath(__file__), os.path.join(ROOT, "include", "w4a16.h")])
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def run_prefill(args):
@@ -620,7 +848,7 @@ def run_prefill(args):
                            "traffic": None, "kernel": PREFILL_KERNEL_NAMES.get(best["plan"]["tile"], "prefill"),
                            "shape": [best["M"], best["K"], best["N"]]},
               "rows": rows}
-    print(json.dumps(result), flush=True)
+    emit(result, args)
 
 
 PREFILL_PMC_SHAPE = (2048, 8192, 28672)      # M, K, N of the prefill counter pass
@@ -750,6 +978,89 @@ def summarize_pmc(dirs):
     print(json.dumps(summary, indent=1))
 
 
+def kernel_instance(plan, group=GROUP, nat=False):
+    """Name of the decode-kernel instance a skinny plan launches (its template arguments)."""
+    sg = min(plan["seg"], group // 32)
+    return (f"skinny_kernel<{plan['row_tiles']}, {plan['cols'] // 16}, {plan['seg']}, {sg}, {plan['waves']}, "
+            f"{'true' if nat else 'false'}>")
+
+
+def summarize_kernel_trace(dirs):
+    """Per-call and per-instance kernel durations of a `--trace-pass` run under rocprofv3
+    --kernel-trace: the decode sweep's skinny dispatches in launch order, dispatch j being
+    call j mod 15 of the step. Writes profiles/kernel_trace_skinny_decode_sweep.{json,md}."""
+    import csv
+    import weight_only_bit_gemv_amd as lib
+    rows = []
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+            for r in csv.DictReader(open(path)):
+                if "skinny_kernel" in r["Kernel_Name"]:
+                    rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+                                 r["Kernel_Name"]))
+    rows.sort()
+    items = workload_items("decode_sweep")[1]
+    L = len(items)
+    if not rows or len(rows) % L:
+        raise SystemExit(f"{len(rows)} skinny dispatches: not whole steps of {L}")
+    rows = rows[2 * L:]                                   # drop the first two (eager) steps
+    per_item = []
+    for i, (M, K, N, _) in enumerate(items):
+        durs = [r[1] for j, r in enumerate(rows) if j % L == i]
+        pl = lib.w4a16_plan(M, N, K)
+        b = alg_bytes(M, K, N)
+        avg = float(np.mean(durs))
+        per_item.append({"M": M, "K": K, "N": N, "kernel": kernel_instance(pl), "dispatches": len(durs),
+                         "avg_ns": round(avg, 1), "median_ns": float(np.median(durs)), "alg_bytes": b,
+                         "GBps": round(b / avg, 1), "frac_hbm": round(b / avg / HBM_PEAK_GBS, 4),
+                         "trace_name_sample": [r[2] for j, r in enumerate(rows) if j % L == i][0][:120]})
+    kern = {}
+    for it in per_item:
+        k = kern.setdefault(it["kernel"], {"calls_per_step": 0, "ns": 0.0, "bytes": 0})
+        k["calls_per_step"] += 1
+        k["ns"] += it["avg_ns"]
+        k["bytes"] += it["alg_bytes"]
+    total_ns = sum(k["ns"] for k in kern.values())
+    per_kernel = []
+    for name, k in kern.items():
+        avg = k["ns"] / k["calls_per_step"]
+        bpl = k["bytes"] / k["calls_per_step"]
+        per_kernel.append({"name": name, "calls_per_step": k["calls_per_step"], "avg_ns": round(avg, 1),
+                           "alg_bytes_per_launch": round(bpl), "GBps": round(bpl / avg, 1),
+                           "frac_hbm": round(bpl / avg / HBM_PEAK_GBS, 4), "share": round(k["ns"] / total_ns, 4)})
+    per_kernel.sort(key=lambda k: -k["share"])
+    step_bytes = sum(it["alg_bytes"] for it in per_item)
+    out = {"kernel_source_sha": decode_kernel_hash(),
+           "command": "rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
+                      "python -u bench.py --trace-pass --steps 20; python bench.py --summarize-kernel-trace <dir>",
+           "dispatches_used": len(rows), "per_call": per_item, "per_kernel": per_kernel, "dominant": per_kernel[0],
+           "kernel_only_step_us": round(total_ns / 1e3, 3),
+           "kernel_only_step_GBps": round(step_bytes / total_ns, 1)}
+    base = os.path.splitext(KTRACE_FILE)[0]
+    with open(KTRACE_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    lines = ["# skinny_kernel on the decode sweep: kernel-trace durations per call", "",
+             "Command (repository root, MI355X):", "", "```", out["command"], "```", "",
+             f"Sources: decode kernel + plans sha `{out['kernel_source_sha']}`; {len(rows)} dispatches after the two "
+             "eager warm-up steps (graph replays of the timed steps; no per-shape loops). Durations exclude "
+             "the gap between graph nodes.", "",
+             "| M | K | N | kernel | avg ns | GB/s | of 8 TB/s |", "|---|---|---|---|---|---|---|"]
+    for it in per_item:
+        lines.append(f"| {it['M']} | {it['K']} | {it['N']} | `{it['kernel']}` | {it['avg_ns']:.0f} | "
+                     f"{it['GBps']:.0f} | {it['frac_hbm']:.3f} |")
+    lines += ["", "| kernel | calls per step | avg ns | bytes per launch | GB/s | of 8 TB/s | share of kernel time |",
+              "|---|---|---|---|---|---|---|"]
+    for k in per_kernel:
+        lines.append(f"| `{k['name']}` | {k['calls_per_step']} | {k['avg_ns']:.0f} | {k['alg_bytes_per_launch']} | "
+                     f"{k['GBps']:.0f} | {k['frac_hbm']:.3f} | {k['share']:.3f} |")
+    lines += ["", f"Kernel time per step {out['kernel_only_step_us']} us: {out['kernel_only_step_GBps']} GB/s of "
+              "algorithmic bytes with the gaps between launches removed."]
+    with open(base + ".md", "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -765,6 +1076,11 @@ def main():
                     help="packing of the 4-bit codes in each int32 word")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense fp16 baseline")
+    ap.add_argument("--no-grouped", action="store_true", help="skip the grouped-projection timings")
+    ap.add_argument("--record", metavar="FILE", help="also write the JSON line with command, source hash and host")
+    ap.add_argument("--trace-pass", action="store_true",
+                    help="only the timed steps (for rocprofv3 --kernel-trace); prints no JSON")
+    ap.add_argument("--summarize-kernel-trace", nargs="+", metavar="DIR")
     ap.add_argument("--pmc-pass", action="store_true")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR")
     ap.add_argument("--summarize-prefill-pmc", nargs="+", metavar="DIR")
@@ -776,6 +1092,9 @@ def main():
         return 0
     if args.summarize_prefill_pmc:
         summarize_prefill_pmc(args.summarize_prefill_pmc, args.w4a8)
+        return 0
+    if args.summarize_kernel_trace:
+        summarize_kernel_trace(args.summarize_kernel_trace)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the W4A16 path is built and timed on a single "

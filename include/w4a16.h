@@ -362,6 +362,19 @@ int w4a8_matmul_ex(const uint8_t* xq, const float* sx, const int32_t* qweight, c
                    const void* zeros, void* y, int64_t M, int64_t N, int64_t K, int64_t group_size,
                    int layout, int splits, void* stream);
 
+/*
+ * w4a16_read_probe - measurement hook: a plain read of `bytes` bytes of `buf` with the
+ * decode kernel's load width (16 bytes per lane) and cache policy (non-temporal), and no
+ * other work. "Triton Kernel Matches bitsandbytes: Why Both Lose to Math", section "Roofline
+ * First: Calculate the Ceiling Before Writing Code", divides by the bandwidth measured on
+ * the machine itself; this is that measurement for the weight stream.
+ *   buf    device, 16-byte aligned; bytes a positive multiple of 16
+ *   sink   device uint32 [256], 4-byte aligned: written only in the unlikely case that the
+ *          XOR of a lane's 64 bytes equals 0x9E3779B9 (it keeps the loads alive)
+ * Asynchronous on `stream`. Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT, HIP.
+ */
+int w4a16_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
 /* w4a16_strerror - static description of an error code (never NULL). */
 const char* w4a16_strerror(int code);
 

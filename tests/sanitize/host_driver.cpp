@@ -43,6 +43,7 @@ int launch_dequant(const uint32_t*, const uint16_t*, const uint16_t*, uint8_t*, 
 int launch_w4a8_quantize(const uint16_t*, uint8_t*, float*, int, int, void*) { reached("launch_w4a8_quantize"); }
 int launch_w4a8(const W4A8Params&, void*) { reached("launch_w4a8"); }
 int scratch_workspace(void*, float**, uint32_t**) { reached("scratch_workspace"); }
+int launch_read_probe(const void*, int64_t, uint32_t*, void*) { reached("launch_read_probe"); }
 }  // namespace w4a16
 
 static int g_checks = 0;
@@ -219,6 +220,9 @@ static void device_call_errors() {
            W4A16_ERR_UNSUPPORTED, "w4a8 workspace offsets");
     expect(w4a8_matmul_ex(xq, sx, (const int32_t*)p[1], p[2], p[3], p[4], 4, 64, 256, 128, 0, 3, nullptr),
            W4A16_ERR_INVALID_ARG, "w4a8 splits > K/128");
+    expect(w4a16_read_probe(p[0], 100, (uint32_t*)p[1], nullptr), W4A16_ERR_INVALID_ARG, "read probe bytes%16");
+    expect(w4a16_read_probe(nullptr, 1024, (uint32_t*)p[1], nullptr), W4A16_ERR_INVALID_ARG, "read probe null");
+    expect(w4a16_read_probe(mis, 1024, (uint32_t*)p[1], nullptr), W4A16_ERR_ALIGNMENT, "read probe misaligned");
     for (int code = -7; code <= 1; ++code) {
         ++g_checks;
         if (!w4a16_strerror(code) || !*w4a16_strerror(code)) ++g_failed;

@@ -77,6 +77,7 @@ _SIGS = {
     "w4a8_matmul": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int, _P], ctypes.c_int),
     "w4a8_matmul_ex": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int, ctypes.c_int, _P],
                        ctypes.c_int),
+    "w4a16_read_probe": ([_P, _I64, _P, _P], ctypes.c_int),
     "w4a16_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "w4a16_last_error_detail": ([], ctypes.c_char_p),
     "w4a16_version": ([], ctypes.c_int),

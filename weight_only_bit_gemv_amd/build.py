@@ -22,7 +22,8 @@ ARCH = "gfx950"
 
 HIP_SOURCES = ["w4a16_skinny.hip", "w4a16_skinny_lw1.hip", "w4a16_skinny_lw2.hip", "w4a16_skinny_lw4.hip",
                "w4a16_prefill.hip", "w4a16_prefill_rb.hip", "w4a16_prefill_async.hip",
-               "w4a16_dequant.hip", "w4a8_prefill.hip", "w4a16_noalloc.hip"]
+               "w4a16_dequant.hip", "w4a8_prefill.hip", "w4a16_noalloc.hip",
+               "w4a16_readbw.hip"]
 # The packer must round every fp32 step on its own: no contraction, no fast-math.
 PACK_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math"]
 HIPCC_FLAGS = [

@@ -740,6 +740,18 @@ int w4a8_matmul(const uint8_t* xq, const float* sx, const int32_t* qweight, cons
     return w4a8_matmul_ex(xq, sx, qweight, scales, zeros, y, M, N, K, group_size, layout, 0, stream);
 }
 
+int w4a16_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+    if (!buf || !sink) return fail(W4A16_ERR_INVALID_ARG, "null pointer argument");
+    if (bytes < 16 || bytes % 16 != 0)
+        return fail(W4A16_ERR_INVALID_ARG, "bytes=%lld must be a positive multiple of 16", (long long)bytes);
+    if (bytes / (16 * 1024) >= INT32_MAX) return fail(W4A16_ERR_UNSUPPORTED, "buffer too large");
+    if (!aligned16(buf) || reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+        return fail(W4A16_ERR_ALIGNMENT, "buf must be 16-byte aligned, sink 4-byte aligned");
+    const int e = w4a16::launch_read_probe(buf, bytes, sink, stream);
+    if (e != (int)hipSuccess) return fail(W4A16_ERR_HIP, "read probe launch: %s", hipGetErrorString((hipError_t)e));
+    return ok();
+}
+
 const char* w4a16_strerror(int code) {
     switch (code) {
         case W4A16_OK: return "success";

@@ -40,8 +40,6 @@ struct SkinnyMatrix {
 
 struct SkinnyParams {
     const uint16_t* x;        // fp16 [M, K]
-    SkinnyMatrix mat[kMaxGroupMats];
-    int n_mats;               // matrices in this launch (1 for w4a16_matmul)
     float* ws;                // fp32 partials [row_blocks][n_strips][splits][16*row_tiles][cols]
     uint32_t* counters;       // arrival counters [row_blocks][n_strips], zero between calls
     int M, K;
@@ -55,6 +53,9 @@ struct SkinnyParams {
     int seg;                  // K-steps per software-pipeline segment (1, 2, 4, 8)
     int gshift;               // log2(K-steps per scale/zero group): group of K-step ks = ks >> gshift
     int layout;               // W4A16_LAYOUT_*
+    int n_mats;               // matrices in this launch (1 for w4a16_matmul)
+    // last, so that a single-matrix launch reads its arguments from one contiguous block
+    SkinnyMatrix mat[kMaxGroupMats];
 };
 
 // Workspace a skinny launch needs (bytes of partials, number of counters).
@@ -131,6 +132,9 @@ constexpr uint64_t kScratchPartialBytes = 64ull << 20;    // fp32 split-K partia
 // Device addresses of this device's counters and partials (the counters are cleared on the
 // device's first call, by a kernel on `stream`). Returns a hipError_t value.
 int scratch_workspace(void* stream, float** partials, uint32_t** counters);
+
+// ---- read probe (w4a16_readbw.hip) ----
+int launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
 
 // ---- dequant hook (w4a16_dequant.hip) ----
 int launch_dequant(const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,

@@ -250,8 +250,9 @@ __device__ __forceinline__ void partial_add(Row<LW>& r, __amdgpu_buffer_rsrc_t r
 // U = 8, K a multiple of 256, so every segment is exactly U K-steps inside whole groups and
 // the loop below needs no predicates. SG: min(U, K-steps per group). W: wavefronts per
 // work-group. NAT: the weights are packed in the interleaved layout (no activation permute).
+// GROUPED: the launch covers several matrices that share x (p.n_mats > 1).
 // Dynamic LDS: (W - 1) * rows * CW floats, rows = min(16 * MT, M - row0).
-template <int MT, int LW, int U, int SG, int W, bool NAT>
+template <int MT, int LW, int U, int SG, int W, bool NAT, bool GROUPED>
 __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
     static_assert(U == 1 || U == 2 || U == 4 || U == 8, "segment of 1, 2, 4 or 8 K-steps");
     constexpr int CW = 16 * LW;
@@ -272,11 +273,24 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
     const int split = b / p.n_strips;
     // the matrix this strip belongs to (wave-uniform; a single matrix unless the launch
     // groups several that share x)
-    int mi = 0;
+    // The matrix this strip belongs to. A single-matrix launch (GROUPED false) reads entry 0
+    // at constant offsets, in the same batch as the other arguments. A grouped launch reads
+    // the entries' first strips (one batch), picks the entry, then reads that entry: one
+    // more scalar round trip, where selecting among fully loaded entries compiled to a chain
+    // of dependent loads.
+    SkinnyMatrix mat;
+    if constexpr (GROUPED) {
+        int mi = 0;
 #pragma unroll
-    for (int j = 1; j < kMaxGroupMats; ++j)
-        if (j < p.n_mats && strip >= p.mat[j].strip0) mi = j;
-    const SkinnyMatrix& mat = p.mat[mi];
+        for (int j = 1; j < kMaxGroupMats; ++j) {
+            int s0 = p.mat[j].strip0;
+            asm volatile("" : "+s"(s0));
+            mi = (j < p.n_mats && strip >= s0) ? j : mi;
+        }
+        mat = p.mat[mi];
+    } else {
+        mat = p.mat[0];
+    }
     const int N = mat.N;
     const int row0 = blockIdx.y * 16 * MT;
     const int rows = min(16 * MT, p.M - row0);          // valid output rows of this work-group
@@ -473,10 +487,15 @@ hipError_t launch_one(const SkinnyParams& p, hipStream_t s) {
     const dim3 grid((unsigned)(p.n_strips * p.splits), (unsigned)p.row_blocks);
     const int rows = std::min(16 * MT, p.M);
     const size_t lds = (size_t)(W - 1) * rows * 16 * LW * sizeof(float);
-    if (p.layout == W4A16_LAYOUT_INTERLEAVED)
-        hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, true>), grid, dim3(64 * W), lds, s, p);
+    const bool nat = p.layout == W4A16_LAYOUT_INTERLEAVED, grouped = p.n_mats > 1;
+    if (nat && grouped)
+        hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, true, true>), grid, dim3(64 * W), lds, s, p);
+    else if (nat)
+        hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, true, false>), grid, dim3(64 * W), lds, s, p);
+    else if (grouped)
+        hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, false, true>), grid, dim3(64 * W), lds, s, p);
     else
-        hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, false>), grid, dim3(64 * W), lds, s, p);
+        hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, false, false>), grid, dim3(64 * W), lds, s, p);
     return hipGetLastError();
 }
 
