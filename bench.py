@@ -982,7 +982,7 @@ def kernel_instance(plan, group=GROUP, nat=False):
     """Name of the decode-kernel instance a skinny plan launches (its template arguments)."""
     sg = min(plan["seg"], group // 32)
     return (f"skinny_kernel<{plan['row_tiles']}, {plan['cols'] // 16}, {plan['seg']}, {sg}, {plan['waves']}, "
-            f"{'true' if nat else 'false'}>")
+            f"{'true' if nat else 'false'}, false>")
 
 
 def summarize_kernel_trace(dirs):
@@ -999,6 +999,14 @@ def summarize_kernel_trace(dirs):
                     rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
                                  r["Kernel_Name"]))
     rows.sort()
+    stats = []
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
+            for r in csv.DictReader(open(path)):
+                if "skinny_kernel" in r["Name"]:
+                    stats.append({"name": r["Name"], "calls": int(r["Calls"]), "avg_ns": round(float(r["AverageNs"]), 1),
+                                  "min_ns": int(float(r["MinNs"])), "max_ns": int(float(r["MaxNs"])),
+                                  "share": float(r["Percentage"])})
     items = workload_items("decode_sweep")[1]
     L = len(items)
     if not rows or len(rows) % L:
@@ -1034,6 +1042,7 @@ def summarize_kernel_trace(dirs):
            "command": "rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
                       "python -u bench.py --trace-pass --steps 20; python bench.py --summarize-kernel-trace <dir>",
            "dispatches_used": len(rows), "per_call": per_item, "per_kernel": per_kernel, "dominant": per_kernel[0],
+           "rocprof_kernel_stats": stats,
            "kernel_only_step_us": round(total_ns / 1e3, 3),
            "kernel_only_step_GBps": round(step_bytes / total_ns, 1)}
     base = os.path.splitext(KTRACE_FILE)[0]
@@ -1055,7 +1064,12 @@ def summarize_kernel_trace(dirs):
         lines.append(f"| `{k['name']}` | {k['calls_per_step']} | {k['avg_ns']:.0f} | {k['alg_bytes_per_launch']} | "
                      f"{k['GBps']:.0f} | {k['frac_hbm']:.3f} | {k['share']:.3f} |")
     lines += ["", f"Kernel time per step {out['kernel_only_step_us']} us: {out['kernel_only_step_GBps']} GB/s of "
-              "algorithmic bytes with the gaps between launches removed."]
+              "algorithmic bytes with the gaps between launches removed.", "",
+              "`run_kernel_stats.csv` of the same run (all dispatches, warm-up steps included):", "",
+              "| kernel | calls | average ns | min ns | max ns | share % |", "|---|---|---|---|---|---|"]
+    for k in stats:
+        lines.append(f"| `{k['name']}` | {k['calls']} | {k['avg_ns']:.0f} | {k['min_ns']} | {k['max_ns']} | "
+                     f"{k['share']:.2f} |")
     with open(base + ".md", "w") as f:
         f.write("\n".join(lines) + "\n")
     print(json.dumps(out, indent=1))
