@@ -1075,6 +1075,88 @@ def summarize_kernel_trace(dirs):
     print(json.dumps(out, indent=1))
 
 
+RECORD_KEEP_ROW = ("M", "K", "N", "w4a16_us", "w4a16_TFLOPs", "dense_fp16_us", "speedup_vs_dense",
+                   "dequant_then_dense_us", "w4a8_us", "w4a8_TFLOPs", "w4a8_with_quantize_us",
+                   "crossover_M_dense_faster_from")
+
+
+def summarize_records(paths):
+    """Trimmed copies of --record files in profiles/ (bench_<workload>.json) and one table of
+    the figures they hold (profiles/bench_records.md)."""
+    recs = []
+    for path in paths:
+        rec = json.load(open(path))
+        res = rec["result"]
+        wl = res["config"]["workload"].split(":")[0].split()[0]
+        if "rows" in res:                                   # prefill crossover
+            wl = "prefill"
+            rows = []
+            for r in res["rows"]:
+                t = {k: r[k] for k in RECORD_KEEP_ROW if k in r}
+                if "plan" in r:
+                    t["plan"] = f"k{r['plan']['kernel']}t{r['plan']['tile']}s{r['plan']['splits']}"
+                rows.append(t)
+            res = dict(res, rows=rows)
+        out = dict(rec, result=res)
+        with open(os.path.join(ROOT, "profiles", f"bench_{wl}.json"), "w") as f:
+            json.dump(out, f, separators=(",", ":"))
+            f.write("\n")
+        recs.append((wl, rec, res))
+    lines = ["# bench.py records (one MI355X)", "",
+             "Each `bench_<workload>.json` here is the record `python bench.py --workload <w> --record FILE` wrote on "
+             "the GPU box (command, hash of every measured source, host, date), trimmed by "
+             "`python bench.py --summarize-records FILE...`.", ""]
+    for wl, rec, res in recs:
+        lines += [f"## {wl}", "", f"`{rec['command']}`; sources `{rec['sources_sha']}`; {rec['gpu']} on host "
+                  f"`{rec['host']}`; {rec['date_utc']}.", ""]
+        if wl == "prefill":
+            lines += ["| K | N | M | W4A16 us | TFLOP/s | dense fp16 us | speedup | dequant+dense us | W4A8 us | plan |",
+                      "|---|---|---|---|---|---|---|---|---|---|"]
+            for r in res["rows"]:
+                if "crossover_M_dense_faster_from" in r:
+                    lines.append(f"| {r['K']} | {r['N']} | crossover: dense faster from M = "
+                                 f"{r['crossover_M_dense_faster_from']} | | | | | | | |")
+                elif r["M"] in (1, 16, 32, 64, 128, 256, 512, 1024, 2048):
+                    lines.append(f"| {r['K']} | {r['N']} | {r['M']} | {r['w4a16_us']} | {r['w4a16_TFLOPs']} | "
+                                 f"{r['dense_fp16_us']} | {r['speedup_vs_dense']} | {r['dequant_then_dense_us']} | "
+                                 f"{r.get('w4a8_us', '')} | {r.get('plan', '')} |")
+            lines.append("")
+            continue
+        roof = res["roofline"]
+        lines.append(f"value {res['value']} GB/s ({roof['frac']} of 8 TB/s), median step {res['ms_per_step']} ms, "
+                     f"min {res.get('step_ms_min')} ms; read ceiling {roof.get('read_ceiling_GBps')} GB/s "
+                     f"(fraction {roof.get('frac_of_read_ceiling')}); device copy {res['measured_copy_GBps']} GB/s.")
+        if "dominant_kernel" in roof:
+            dk = roof["dominant_kernel"]
+            lines.append(f"Dominant kernel `{dk['name']}`: {dk['avg_ns']} ns per launch on {dk['alg_bytes_per_launch']} B, "
+                         f"{dk['GBps']} GB/s, {dk['frac']} of 8 TB/s (kernel trace).")
+        if "tokens_per_s" in res:
+            gc = res["grouped_chain"]
+            lines.append(f"chain: {res['tokens_per_s']} tok/s (225 launches, {res['us_per_token']} us/token); grouped "
+                         f"{gc['tokens_per_s']} tok/s ({gc['launches_per_token']} launches, {gc['frac_hbm']} of 8 TB/s); "
+                         f"ceiling {res['ceiling_tokens_per_s_at_8TBps']} tok/s at 8 TB/s.")
+        if res.get("per_shape"):
+            lines += ["", "| M | K | N | us | GB/s | of 8 TB/s | read ceiling us | of read ceiling | dense fp16 us |",
+                      "|---|---|---|---|---|---|---|---|---|"]
+            for r in res["per_shape"]:
+                lines.append(f"| {r['M']} | {r['K']} | {r['N']} | {r['us']} | {r['GBps']} | {r['frac_hbm']} | "
+                             f"{r.get('read_ceiling_us', '')} | {r.get('frac_of_read_ceiling', '')} | "
+                             f"{r.get('dense_fp16_us', '')} |")
+        if res.get("grouped"):
+            lines += ["", "| grouped | M | us | GB/s | of 8 TB/s | one launch per matrix us | speedup |",
+                      "|---|---|---|---|---|---|---|"]
+            for g in res["grouped"]:
+                lines.append(f"| {g['matrices']} | {g['M']} | {g['grouped_us']} | {g['grouped_GBps']} | "
+                             f"{g['grouped_frac_hbm']} | {g['separate_launches_us']} | {g['speedup']} |")
+        if res.get("cpu_baseline"):
+            cb = res["cpu_baseline"]
+            lines.append(f"\nOracle on the host: {cb['value']} GB/s ({cb['sample']}).")
+        lines.append("")
+    with open(os.path.join(ROOT, "profiles", "bench_records.md"), "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -1095,6 +1177,7 @@ def main():
     ap.add_argument("--trace-pass", action="store_true",
                     help="only the timed steps (for rocprofv3 --kernel-trace); prints no JSON")
     ap.add_argument("--summarize-kernel-trace", nargs="+", metavar="DIR")
+    ap.add_argument("--summarize-records", nargs="+", metavar="FILE")
     ap.add_argument("--pmc-pass", action="store_true")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR")
     ap.add_argument("--summarize-prefill-pmc", nargs="+", metavar="DIR")
@@ -1109,6 +1192,9 @@ def main():
         return 0
     if args.summarize_kernel_trace:
         summarize_kernel_trace(args.summarize_kernel_trace)
+        return 0
+    if args.summarize_records:
+        summarize_records(args.summarize_records)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the W4A16 path is built and timed on a single "
