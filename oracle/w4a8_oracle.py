@@ -18,20 +18,22 @@ Readings taken where the pages are silent:
       fp32), scale sx = fl32(amax / 448) (1.0 when amax is 0), codes
       xq = E4M3(fl32(x / sx)), true fp32 division, round-to-nearest-even, saturating at
       +-448 (the format has no infinity).
-  R19 The weight operand of the 8-bit product is E4M3(q - z), round-to-nearest-even,
-      saturating: exact whenever |q - z| <= 16, i.e. for every group whose zero point lies
-      in [-1, 16] (every asymmetric group that contains 0, every symmetric group);
-      otherwise this rounding is part of the method.
-  R20 y[m, n] = sx[m] * sum_g s[g, n] * sum_{k in g} dec(xq[m, k]) * dec(wq[k, n]) with the
-      W4A16 grouping (one fp16 scale per group and column). Groups of 128 or 256 rows: one
-      8-bit matrix instruction spans 128 rows of K, and a scale must not change inside it.
-The matmul is defined in fp64 (each product of two E4M3 values and an fp16 scale is exact;
-only the sums round).
+  R19 The weight side is the exact dequantisation of [P1] "The design", (q - z) * s, with
+      q - z unrounded whatever the zero point: only the activations are 8-bit. (An
+      implementation may use the identity sum_k a_k (q_k - z) = sum_k a_k q_k - z sum_k a_k,
+      with the bare codes q, which E4M3 holds exactly, as the 8-bit operand.)
+  R20 y[m, n] = sx[m] * sum_g s[g, n] * sum_{k in g} dec(xq[m, k]) * (q[k, n] - z[g, n]) with
+      the W4A16 grouping (one fp16 scale per group and column). Groups of 128 or 256 rows:
+      one 8-bit matrix instruction spans 128 rows of K, and a scale must not change inside it.
+  R21 Block sums of the activation codes: S[b, m] = sum over the 128 K indices of block b of
+      dec(xq[m, k]), the per-row quantity the zero-point term of R19's identity needs.
+The matmul and the block sums are defined in fp64 (each product of an E4M3 value, an
+integer below 2^11 and an fp16 scale is exact; only the sums round).
 
 Pins (tests/oracle_pins_w4a8.py): the format's defining values, the round trip of every
 finite code, hand-worked ties and saturation, the quantiser's invariants, closed-form
-products, agreement with the W4A16 oracle on activations the format holds exactly, and a
-mutation suite (tests/test_oracle_mutants_w4a8.py).
+products (far zero points included), block sums, agreement with the W4A16 oracle on
+activations the format holds exactly, and a mutation suite (tests/test_oracle_mutants_w4a8.py).
 """
 import numpy as np
 
@@ -86,13 +88,30 @@ def quantize_activations(x):
     return e4m3_encode(scaled), sx
 
 
-def weight_operand(codes, zeros, group_size):
-    """R19: E4M3 codes of q - z [K, N] (q uint8 codes, zeros fp16 [K/g, N])."""
+BLOCK = 128               # R21: K rows per activation block sum (one 8-bit matrix instruction)
+
+
+def activation_block_sums(xq):
+    """R21: S[b, m] = sum_{k in block b} dec(xq[m, k]), fp64 [K/128, M] (block-major).
+
+    Exact: every finite E4M3 value is a multiple of 2^-9 of magnitude at most 448, so every
+    partial sum of 128 of them is a multiple of 2^-9 below 2^16, which fp64 holds exactly
+    in any summation order."""
+    xq = np.asarray(xq, dtype=np.uint8)
+    M, K = xq.shape
+    if K % BLOCK:
+        raise ValueError("K must be a multiple of 128")
+    a = e4m3_decode(xq)
+    return a.reshape(M, K // BLOCK, BLOCK).sum(axis=2).T
+
+
+def weight_values(codes, zeros, group_size):
+    """R19: the exact q - z [K, N] (q uint8 codes, zeros fp16 [K/g, N]), fp64."""
     codes = np.asarray(codes)
     K, N = codes.shape
     _check_group(K, group_size)
     z = np.repeat(np.asarray(zeros).astype(np.float64), group_size, axis=0)
-    return e4m3_encode(codes.astype(np.float64) - z)
+    return codes.astype(np.float64) - z
 
 
 def matmul_w4a8(xq, sx, qweight, scales, zeros, group_size=128, layout="linear"):
@@ -106,7 +125,7 @@ def matmul_w4a8(xq, sx, qweight, scales, zeros, group_size=128, layout="linear")
     if xq.shape[1] != K:
         raise ValueError("xq and qweight disagree on K")
     a = e4m3_decode(xq)                                     # [M, K]
-    w = e4m3_decode(weight_operand(codes, zeros, group_size))   # [K, N]
+    w = weight_values(codes, zeros, group_size)             # [K, N]
     s = np.asarray(scales).astype(np.float64)               # [K/g, N]
     y = np.zeros((xq.shape[0], N))
     for g in range(K // group_size):

@@ -88,17 +88,16 @@ def pin_activation_quantiser(o):
     assert np.all(err <= tol), err.max()
 
 
-def pin_weight_operand(o):
-    """q - z in E4M3: exact for a zero point of 8; with zero -5, q + 5 rounds 17 -> 16 and
-    19 -> 20 (ties to even), the rest exact."""
-    codes = np.tile(np.arange(16, dtype=np.uint8), 8)[:, None].repeat(2, axis=1)   # K=128, N=2
-    zeros = np.array([[8.0, -5.0]], dtype=np.float16)
-    w = o.e4m3_decode(o.weight_operand(codes, zeros, 128))
-    assert np.array_equal(w[:16, 0], np.arange(16) - 8.0)
-    expect = np.arange(16) + 5.0
-    expect[12] = 16.0
-    expect[14] = 20.0
-    assert np.array_equal(w[:16, 1], expect), w[:16, 1]
+def pin_weight_values(o):
+    """q - z exactly, whatever the zero point: zero 8 gives -8..7, zero -5 gives 5..20 (17 and
+    19 included: no 8-bit rounding of the weight side), zeros -1000 and 1024 give 1000..1015
+    and -1024..-1009."""
+    codes = np.tile(np.arange(16, dtype=np.uint8), 8)[:, None].repeat(4, axis=1)   # K=128, N=4
+    zeros = np.array([[8.0, -5.0, -1000.0, 1024.0]], dtype=np.float16)
+    w = o.weight_values(codes, zeros, 128)
+    q = np.arange(16.0)
+    assert np.array_equal(w[:16, 0], q - 8) and np.array_equal(w[:16, 1], q + 5), w[:16, :2]
+    assert np.array_equal(w[:16, 2], q + 1000) and np.array_equal(w[:16, 3], q - 1024), w[:16, 2:]
 
 
 def pin_w4a8_closed_form(o):
@@ -138,12 +137,15 @@ def _grid_activations(M, K, seed, log2_scale):
 
 
 def pin_w4a8_matches_w4a16_on_exact_activations(o):
-    """When every activation is held exactly (grid values, power-of-two row scale) and every
-    q - z is exact, W4A8 computes the same product as the W4A16 oracle."""
-    for g, shape, ls in [(128, (5, 512, 24), 0), (256, (3, 768, 16), -8), (128, (2, 256, 40), -3)]:
+    """When every activation is held exactly (grid values, power-of-two row scale), W4A8
+    computes the same product as the W4A16 oracle, for zero points near 8 and for one-signed
+    groups whose zero points lie far from it."""
+    for g, shape, ls, mean in [(128, (5, 512, 24), 0, 0.0), (256, (3, 768, 16), -8, 0.0), (128, (2, 256, 40), -3, 0.0),
+                               (128, (3, 384, 16), 0, 1.0), (256, (2, 512, 8), -2, -1.0)]:
         M, K, N = shape
-        qw, s, z = w4a16_oracle.quantize_pack(synth.weight(K, N, wid=5), g)
-        assert np.all(np.abs(z.astype(np.float64) - 7.5) <= 8.5)      # zeros in [-1, 16]
+        qw, s, z = w4a16_oracle.quantize_pack(synth.weight_custom(K, N, seed=5 + K, std=0.02, mean=mean), g)
+        if mean:
+            assert np.all(np.abs(z.astype(np.float64)) > 60)              # far from [-1, 16]
         x = _grid_activations(M, K, seed=K + g, log2_scale=ls)
         xq, sx = o.quantize_activations(x)
         assert np.array_equal(sx, np.full(M, 2.0 ** ls, np.float32))
@@ -166,27 +168,67 @@ def pin_w4a8_brute_force(o):
             terms = []
             for k in range(K):
                 g = k // 128
-                w = float(codes[k, n]) - float(z[g, n])          # |q - z| <= 16: exact in E4M3
-                assert abs(w) <= 16
+                w = float(codes[k, n]) - float(z[g, n])          # exact: no 8-bit rounding of q - z
                 terms.append(a[m, k] * w * float(s[g, n]))
             ref = math.fsum(terms) * float(sx[m])
             assert abs(y[m, n] - ref) <= 1e-12 * max(1.0, abs(ref)), (m, n, y[m, n], ref)
 
 
-def pin_w4a8_rounded_operand(o):
-    """A one-signed group (zero point -5): the product uses q - z rounded to E4M3, so the
-    code 12 (q - z = 17) contributes 16, 14 (19) contributes 20 and 13 (18) stays 18."""
-    codes = np.tile(np.arange(16, dtype=np.uint8), 8)[:, None]              # K=128, N=1
+def pin_w4a8_far_zero_exact(o):
+    """One-signed groups keep q - z exact in the product: zero -5 with codes 12, 14, 13 gives
+    17, 19, 18 (times the activation 448, row scale 1); zero 1000 with code 3 gives -997;
+    zero -1000 with code 15 gives 1015."""
+    codes = np.tile(np.arange(16, dtype=np.uint8), 8)[:, None].repeat(3, axis=1)   # K=128, N=3
     qw = w4a16_oracle.pack(codes)
-    s = np.array([[1.0]], dtype=np.float16)
-    z = np.array([[-5.0]], dtype=np.float16)
-    x = np.zeros((3, 128), dtype=np.float16)
-    x[0, 12] = x[1, 14] = x[2, 13] = 448                                    # row scale 1
+    s = np.array([[1.0, 0.5, 2.0 ** -10]], dtype=np.float16)
+    z = np.array([[-5.0, 1000.0, -1000.0]], dtype=np.float16)
+    x = np.zeros((4, 128), dtype=np.float16)
+    x[0, 12] = x[1, 14] = x[2, 13] = x[3, 3] = 448                        # row scale 1
+    x[3, 15] = -448
     xq, sx = o.quantize_activations(x)
+    assert np.array_equal(sx, np.ones(4, np.float32))
     y = o.matmul_w4a8(xq, sx, qw, s, z)
-    assert np.array_equal(y[:, 0], np.array([16.0, 20.0, 18.0]) * 448), y[:, 0]
+    assert np.array_equal(y[:3, 0], np.array([17.0, 19.0, 18.0]) * 448), y[:3, 0]
+    # row 3: 448 at q = 3 and -448 at q = 15
+    assert y[3, 1] == 0.5 * 448 * ((3 - 1000) - (15 - 1000)), y[3, 1]
+    assert y[3, 2] == 2.0 ** -10 * 448 * ((3 + 1000) - (15 + 1000)), y[3, 2]
+    assert y[0, 2] == 2.0 ** -10 * 448 * (12 + 1000), y[0, 2]
+
+
+def pin_block_sums(o):
+    """Per-(block, row) sums of the decoded codes: 128 x 448 gives 57344, alternating signs
+    give 0, a single code its value; on random codes the math.fsum of the decoded values;
+    and the identity sum_k a (q - z) = sum_k a q - z S that lets a kernel apply the zero
+    point to the sums."""
+    x = np.zeros((3, 256), dtype=np.float16)
+    x[0] = 448
+    x[1] = np.where(np.arange(256) % 2 == 0, 448, -448)
+    x[2, 130] = 448
+    x[2, 5] = 0.5 * 448
+    xq, sx = o.quantize_activations(x)
+    S = o.activation_block_sums(xq)
+    assert S.shape == (2, 3)
+    assert np.array_equal(S[:, 0], [57344.0, 57344.0]) and np.array_equal(S[:, 1], [0.0, 0.0])
+    assert np.array_equal(S[:, 2], [224.0, 448.0]), S[:, 2]
+    rng = np.random.default_rng(11)
+    codes = rng.integers(0, 256, size=(4, 384)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38                                  # no NaN codes
+    S = o.activation_block_sums(codes)
+    for b in range(3):
+        for m in range(4):
+            ref = math.fsum(float(o.e4m3_decode(np.array([c], np.uint8))[0]) for c in codes[m, b * 128:(b + 1) * 128])
+            assert S[b, m] == ref, (b, m, S[b, m], ref)
+    qw, s, z = w4a16_oracle.quantize_pack(synth.weight_custom(384, 5, seed=3, std=0.02, mean=1.0))
+    a = o.e4m3_decode(codes)
+    q = w4a16_oracle.unpack(qw).astype(np.float64)
+    for b in range(3):
+        rows = slice(128 * b, 128 * (b + 1))
+        lhs = a[:, rows] @ (q[rows] - z[b].astype(np.float64))
+        rhs = a[:, rows] @ q[rows] - np.outer(S[b], z[b].astype(np.float64))
+        assert np.allclose(lhs, rhs, rtol=0, atol=1e-9 * np.abs(lhs).max()), b
 
 
 ALL_PINS = [pin_e4m3_defining_values, pin_e4m3_roundtrip, pin_e4m3_rounding, pin_activation_quantiser,
-            pin_weight_operand, pin_w4a8_closed_form, pin_w4a8_rounded_operand, pin_w4a8_matches_w4a16_on_exact_activations,
+            pin_weight_values, pin_w4a8_closed_form, pin_w4a8_far_zero_exact, pin_block_sums,
+            pin_w4a8_matches_w4a16_on_exact_activations,
             pin_w4a8_brute_force]

@@ -36,13 +36,20 @@ MUTANTS = [
      "np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0))", "amax / np.float32(E4M3_MAX)"),
     ("row scale left out of the product",
      "return y * np.asarray(sx, dtype=np.float64)[:, None]", "return y"),
-    ("weight operand without the zero point",
-     "return e4m3_encode(codes.astype(np.float64) - z)", "return e4m3_encode(codes.astype(np.float64))"),
-    ("weight operand adds the zero point",
-     "return e4m3_encode(codes.astype(np.float64) - z)", "return e4m3_encode(codes.astype(np.float64) + z)"),
-    ("weight operand not rounded to E4M3 (q - z kept exact)",
-     "w = e4m3_decode(weight_operand(codes, zeros, group_size))",
-     "w = codes.astype(np.float64) - np.repeat(np.asarray(zeros).astype(np.float64), group_size, axis=0)"),
+    ("weight values without the zero point",
+     "return codes.astype(np.float64) - z", "return codes.astype(np.float64)"),
+    ("weight values add the zero point",
+     "return codes.astype(np.float64) - z", "return codes.astype(np.float64) + z"),
+    ("weight values rounded to E4M3 (8-bit weight operand q - z)",
+     "return codes.astype(np.float64) - z", "return e4m3_decode(e4m3_encode(codes.astype(np.float64) - z))"),
+    ("zero point clamped to the 4-bit code range",
+     "return codes.astype(np.float64) - z", "return codes.astype(np.float64) - np.clip(z, 0, 15)"),
+    ("block sums over 64 rows",
+     "BLOCK = 128               # R21", "BLOCK = 64                # R21"),
+    ("block sums of magnitudes",
+     "return a.reshape(M, K // BLOCK, BLOCK).sum(axis=2).T", "return np.abs(a).reshape(M, K // BLOCK, BLOCK).sum(axis=2).T"),
+    ("block sums row-major [M, K/128]",
+     "return a.reshape(M, K // BLOCK, BLOCK).sum(axis=2).T", "return a.reshape(M, K // BLOCK, BLOCK).sum(axis=2)"),
     ("first group's scale for every group",
      "y += (a[:, rows] @ w[rows, :]) * s[g][None, :]", "y += (a[:, rows] @ w[rows, :]) * s[0][None, :]"),
     ("last group dropped",
