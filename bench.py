@@ -183,19 +183,22 @@ class Runner:
         M, K, N, key = self.items[i]
         so = self.lib.load()
         if not hasattr(self, "xq"):
-            self.xq, self.sx = {}, {}
+            self.xq, self.sx, self.xsum = {}, {}, {}
         if quantize or i not in self.xq:
             if i not in self.xq:
                 self.xq[i] = self.torch.empty((M, K), dtype=self.torch.uint8, device=self.dev)
                 self.sx[i] = self.torch.empty((M,), dtype=self.torch.float32, device=self.dev)
+                self.xsum[i] = self.torch.empty((K // 128, self.lib.w4a8_sum_stride(M)), dtype=self.torch.float32,
+                                                device=self.dev)
             rc = so.w4a8_quantize_activations(self.xk[i].data_ptr(), self.xq[i].data_ptr(), self.sx[i].data_ptr(),
-                                              M, K, self.sptr)
+                                              self.xsum[i].data_ptr(), M, K, self.sptr)
             if rc != 0:
                 raise RuntimeError(f"w4a8_quantize_activations failed ({rc}) for M={M} K={K}")
         c = self.cursor[key]
         self.cursor[key] = (c + 1) % len(self.weights[key])
         qw, s, z = self.weights[key][c]
-        rc = so.w4a8_matmul(self.xq[i].data_ptr(), self.sx[i].data_ptr(), qw.data_ptr(), s.data_ptr(), z.data_ptr(),
+        rc = so.w4a8_matmul(self.xq[i].data_ptr(), self.sx[i].data_ptr(), self.xsum[i].data_ptr(), qw.data_ptr(),
+                            s.data_ptr(), z.data_ptr(),
                             self.y[i].data_ptr(), M, N, K, self.group, self.layout_id, self.sptr)
         if rc != 0:
             raise RuntimeError(f"w4a8_matmul failed ({rc}) for M={M} K={K} N={N}")

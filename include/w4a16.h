@@ -318,39 +318,47 @@ int w4a16_dequant_fmt(const int32_t* qweight, const void* scales, const void* ze
  * W4A8: 8-bit floating-point activations x the 4-bit weights above ("Beating FP16 with
  * 4-bit Weights", section "What's next": FP8 activations for a W4A8 variant; GemLite README:
  * FP8 x Wn, activations quantised dynamically with one scale per row). E4M3 is the OCP
- * 8-bit format: bias 7, subnormals, largest finite value 448, no infinities.
+ * 8-bit format: bias 7, subnormals, largest finite value 448, no infinities. Only the
+ * activations are 8-bit: the weights keep the exact (q - zero) * scale of "The design".
  *
  * w4a8_quantize_activations - per-row dynamic quantisation of x on the device:
  *   sx[m]    = amax_k |x[m, k]| / 448 (fp32 division; 1.0 for an all-zero row)
  *   xq[m, k] = E4M3(x[m, k] / sx[m])   (fp32 division, round to nearest even, saturating
  *                                       at +-448)
+ *   xsum[b * Ms + m] = sum of dec(xq[m, k]) over the 128 k of block b (fp32; Ms = M rounded
+ *                      up to a multiple of 4; entries m >= M are written 0): the per-row
+ *                      sums the product needs for its zero points
  *   x   device fp16 [M, K], 16-byte aligned;  xq device uint8 [M, K], 16-byte aligned;
- *   sx  device fp32 [M], 4-byte aligned;  K % 128 == 0.
+ *   sx  device fp32 [M], 4-byte aligned;  xsum device fp32 [K/128, Ms], 16-byte aligned;
+ *   K % 128 == 0.
  * Asynchronous on `stream`. NaN/Inf in x give unspecified codes. Errors: INVALID_ARG (null,
  * M or K < 1), UNSUPPORTED (K % 128, size), ALIGNMENT, HIP (launch failure).
  */
-int w4a8_quantize_activations(const void* x, uint8_t* xq, float* sx, int64_t M, int64_t K, void* stream);
+int w4a8_quantize_activations(const void* x, uint8_t* xq, float* sx, float* xsum, int64_t M, int64_t K,
+                              void* stream);
 
 /*
  * w4a8_matmul - y[m, n] = sx[m] * sum_g s[g, n] * sum_{k in group g} dec(xq[m, k]) *
- * dec(E4M3(q[k, n] - z[g, n])), fp32 accumulation on the 8-bit matrix cores, fp16 output
- * (round to nearest even), y fully overwritten.
- *   xq, sx     as written by w4a8_quantize_activations (or any E4M3 codes and fp32 scales)
+ * (q[k, n] - z[g, n]), q - z exact whatever the zero point, fp32 accumulation on the 8-bit
+ * matrix cores, fp16 output (round to nearest even), y fully overwritten. The 8-bit weight
+ * operand is q - zc with zc = z clamped to [-1, 16] (|q - zc| <= 16: exact in E4M3); a zero
+ * point outside that range adds its remainder -(z - zc) s[g, n] xsum per 128-row block in
+ * fp32 after the matrix products (so a far zero point costs extra work only in the
+ * wavefronts whose columns hold one).
+ *   xq, sx, xsum  as written by w4a8_quantize_activations (or any E4M3 codes, fp32 scales and
+ *              the matching block sums, same layout)
  *   qweight, scales, zeros, layout   the W4A16 weight format (w4a16_pack / w4a16_pack_ex)
  *   group_size 128 or 256 (one 8-bit matrix instruction spans 128 rows of K, and a group's
  *              scale must not change inside it)
  *   N % 8 == 0, K % 128 == 0; device pointers 16-byte aligned (sx 4-byte).
- * q - z is exact in E4M3 when |q - z| <= 16, i.e. for zero points in [-1, 16] (every
- * asymmetric group that contains 0, every symmetric group); otherwise it is rounded to E4M3
- * (nearest even, saturating at +-448) as part of the method.
  * Asynchronous on `stream`; deterministic (split-K partial sums are combined in a fixed
  * order). When the output tiles underfill the chip the K range is split over several
  * work-groups (w4a8_matmul_ex forces the count). Errors: INVALID_ARG, UNSUPPORTED (group
  * size, N % 8, K, size), ALIGNMENT, HIP (launch or workspace failure).
  */
-int w4a8_matmul(const uint8_t* xq, const float* sx, const int32_t* qweight, const void* scales,
-                const void* zeros, void* y, int64_t M, int64_t N, int64_t K, int64_t group_size,
-                int layout, void* stream);
+int w4a8_matmul(const uint8_t* xq, const float* sx, const float* xsum, const int32_t* qweight, const void* scales,
+                const void* zeros, void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, int layout,
+                void* stream);
 
 /* w4a8_matmul_ex - w4a8_matmul with the split-K count forced: `splits` work-groups along K
  * per output tile of 128 x 256 (64 or 32 rows when M is that small; 0: the library's
@@ -358,9 +366,9 @@ int w4a8_matmul(const uint8_t* xq, const float* sx, const int32_t* qweight, cons
  * (deterministic). With splits > 1 the call uses the split-K workspace of `stream` (see
  * w4a16_matmul on graph capture). Errors as w4a8_matmul, plus INVALID_ARG for splits out of
  * range. */
-int w4a8_matmul_ex(const uint8_t* xq, const float* sx, const int32_t* qweight, const void* scales,
-                   const void* zeros, void* y, int64_t M, int64_t N, int64_t K, int64_t group_size,
-                   int layout, int splits, void* stream);
+int w4a8_matmul_ex(const uint8_t* xq, const float* sx, const float* xsum, const int32_t* qweight,
+                   const void* scales, const void* zeros, void* y, int64_t M, int64_t N, int64_t K,
+                   int64_t group_size, int layout, int splits, void* stream);
 
 /*
  * w4a16_read_probe - measurement hook: a plain read of `bytes` bytes of `buf` with the

@@ -25,7 +25,7 @@ Readings taken where the pages are silent:
   R20 y[m, n] = sx[m] * sum_g s[g, n] * sum_{k in g} dec(xq[m, k]) * (q[k, n] - z[g, n]) with
       the W4A16 grouping (one fp16 scale per group and column). Groups of 128 or 256 rows:
       one 8-bit matrix instruction spans 128 rows of K, and a scale must not change inside it.
-  R21 Block sums of the activation codes: S[b, m] = sum over the 128 K indices of block b of
+  R22 Block sums of the activation codes: S[b, m] = sum over the 128 K indices of block b of
       dec(xq[m, k]), the per-row quantity the zero-point term of R19's identity needs.
 The matmul and the block sums are defined in fp64 (each product of an E4M3 value, an
 integer below 2^11 and an fp16 scale is exact; only the sums round).
@@ -88,11 +88,11 @@ def quantize_activations(x):
     return e4m3_encode(scaled), sx
 
 
-BLOCK = 128               # R21: K rows per activation block sum (one 8-bit matrix instruction)
+BLOCK = 128               # R22: K rows per activation block sum (one 8-bit matrix instruction)
 
 
 def activation_block_sums(xq):
-    """R21: S[b, m] = sum_{k in block b} dec(xq[m, k]), fp64 [K/128, M] (block-major).
+    """R22: S[b, m] = sum_{k in block b} dec(xq[m, k]), fp64 [K/128, M] (block-major).
 
     Exact: every finite E4M3 value is a multiple of 2^-9 of magnitude at most 448, so every
     partial sum of 128 of them is a multiple of 2^-9 below 2^16, which fp64 holds exactly

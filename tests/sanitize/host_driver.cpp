@@ -40,7 +40,9 @@ int launch_dequant(const uint32_t*, const uint16_t*, const uint16_t*, uint8_t*, 
                    void*) {
     reached("launch_dequant");
 }
-int launch_w4a8_quantize(const uint16_t*, uint8_t*, float*, int, int, void*) { reached("launch_w4a8_quantize"); }
+int launch_w4a8_quantize(const uint16_t*, uint8_t*, float*, float*, int, int, void*) {
+    reached("launch_w4a8_quantize");
+}
 int launch_w4a8(const W4A8Params&, void*) { reached("launch_w4a8"); }
 int scratch_workspace(void*, float**, uint32_t**) { reached("scratch_workspace"); }
 int launch_read_probe(const void*, int64_t, uint32_t*, void*) { reached("launch_read_probe"); }
@@ -201,24 +203,25 @@ static void device_call_errors() {
            W4A16_ERR_ALIGNMENT, "dequant misaligned codes");
     expect(w4a16_dequant_fmt((const int32_t*)p[1], p[2], p[3], codes, nullptr, 64, 128, 128, 4, nullptr),
            W4A16_ERR_INVALID_ARG, "dequant layout=4");
-    expect(w4a8_quantize_activations(p[0], (uint8_t*)p[1], (float*)p[2], 4, 200, nullptr), W4A16_ERR_UNSUPPORTED,
+    float* xs = (float*)p[3];
+    expect(w4a8_quantize_activations(p[0], (uint8_t*)p[1], (float*)p[2], xs, 4, 200, nullptr), W4A16_ERR_UNSUPPORTED,
            "w4a8 quantise K%128");
-    expect(w4a8_quantize_activations(p[0], (uint8_t*)p[1], reinterpret_cast<float*>(uintptr_t(0x100002)), 4, 256,
+    expect(w4a8_quantize_activations(p[0], (uint8_t*)p[1], reinterpret_cast<float*>(uintptr_t(0x100002)), xs, 4, 256,
                                      nullptr),
            W4A16_ERR_ALIGNMENT, "w4a8 quantise misaligned sx");
     const uint8_t* xq = (const uint8_t*)p[0];
     const float* sx = (const float*)p[5];
-    expect(w4a8_matmul(xq, sx, (const int32_t*)p[1], p[2], p[3], p[4], 4, 64, 256, 64, 0, nullptr),
+    expect(w4a8_matmul(xq, sx, xs, (const int32_t*)p[1], p[2], p[3], p[4], 4, 64, 256, 64, 0, nullptr),
            W4A16_ERR_UNSUPPORTED, "w4a8 g=64");
-    expect(w4a8_matmul(xq, sx, (const int32_t*)p[1], p[2], p[3], p[4], 4, 60, 256, 128, 0, nullptr),
+    expect(w4a8_matmul(xq, sx, xs, (const int32_t*)p[1], p[2], p[3], p[4], 4, 60, 256, 128, 0, nullptr),
            W4A16_ERR_UNSUPPORTED, "w4a8 N%8");
-    expect(w4a8_matmul_ex(xq, sx, (const int32_t*)p[1], p[2], p[3], p[4], 1, int64_t(1) << 25, 128, 128, 0, 0,
+    expect(w4a8_matmul_ex(xq, sx, xs, (const int32_t*)p[1], p[2], p[3], p[4], 1, int64_t(1) << 25, 128, 128, 0, 0,
                           nullptr),
            W4A16_ERR_UNSUPPORTED, "w4a8 weight offsets");
-    expect(w4a8_matmul_ex(xq, sx, (const int32_t*)p[1], p[2], p[3], p[4], 1, 8, int64_t(1) << 21, 128, 0, 16384,
+    expect(w4a8_matmul_ex(xq, sx, xs, (const int32_t*)p[1], p[2], p[3], p[4], 1, 8, int64_t(1) << 21, 128, 0, 16384,
                           nullptr),
            W4A16_ERR_UNSUPPORTED, "w4a8 workspace offsets");
-    expect(w4a8_matmul_ex(xq, sx, (const int32_t*)p[1], p[2], p[3], p[4], 4, 64, 256, 128, 0, 3, nullptr),
+    expect(w4a8_matmul_ex(xq, sx, xs, (const int32_t*)p[1], p[2], p[3], p[4], 4, 64, 256, 128, 0, 3, nullptr),
            W4A16_ERR_INVALID_ARG, "w4a8 splits > K/128");
     expect(w4a16_read_probe(p[0], 100, (uint32_t*)p[1], nullptr), W4A16_ERR_INVALID_ARG, "read probe bytes%16");
     expect(w4a16_read_probe(nullptr, 1024, (uint32_t*)p[1], nullptr), W4A16_ERR_INVALID_ARG, "read probe null");

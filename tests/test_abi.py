@@ -250,15 +250,18 @@ def test_prefill_split_plans():
 def test_w4a8_entry_points_reject_bad_arguments():
     so = B.load()
     q = so.w4a8_quantize_activations
-    assert q(None, P[1], P[2], 4, 256, None) == lib.W4A16_ERR_INVALID_ARG
-    assert q(P[0], P[1], P[2], 0, 256, None) == lib.W4A16_ERR_INVALID_ARG
-    assert q(P[0], P[1], P[2], 4, 200, None) == lib.W4A16_ERR_UNSUPPORTED
-    assert q(ctypes.c_void_p(A + 8), P[1], P[2], 4, 256, None) == lib.W4A16_ERR_ALIGNMENT
-    assert q(P[0], P[1], ctypes.c_void_p(A + 2), 4, 256, None) == lib.W4A16_ERR_ALIGNMENT
+    X = ctypes.c_void_p(A + 0x6000)                        # block sums
+    assert q(None, P[1], P[2], X, 4, 256, None) == lib.W4A16_ERR_INVALID_ARG
+    assert q(P[0], P[1], P[2], None, 4, 256, None) == lib.W4A16_ERR_INVALID_ARG
+    assert q(P[0], P[1], P[2], X, 0, 256, None) == lib.W4A16_ERR_INVALID_ARG
+    assert q(P[0], P[1], P[2], X, 4, 200, None) == lib.W4A16_ERR_UNSUPPORTED
+    assert q(ctypes.c_void_p(A + 8), P[1], P[2], X, 4, 256, None) == lib.W4A16_ERR_ALIGNMENT
+    assert q(P[0], P[1], ctypes.c_void_p(A + 2), X, 4, 256, None) == lib.W4A16_ERR_ALIGNMENT
+    assert q(P[0], P[1], P[2], ctypes.c_void_p(A + 0x6004), 4, 256, None) == lib.W4A16_ERR_ALIGNMENT
     m = so.w4a8_matmul
 
     def call(M=4, N=64, K=256, g=128, layout=0, ptrs=None):
-        pp = ptrs or [P[0], P[1], P[2], P[3], P[4], ctypes.c_void_p(A + 0x5000)]
+        pp = ptrs or [P[0], P[1], X, P[2], P[3], P[4], ctypes.c_void_p(A + 0x5000)]
         return m(*pp, M, N, K, g, layout, None)
     assert call(M=0) == lib.W4A16_ERR_INVALID_ARG
     assert call(layout=3) == lib.W4A16_ERR_INVALID_ARG
@@ -266,12 +269,16 @@ def test_w4a8_entry_points_reject_bad_arguments():
     assert call(g=32) == lib.W4A16_ERR_UNSUPPORTED
     assert call(N=60) == lib.W4A16_ERR_UNSUPPORTED                 # N % 8
     assert call(K=200) == lib.W4A16_ERR_UNSUPPORTED
-    bad = [P[0], P[1], P[2], P[3], ctypes.c_void_p(A + 0x4008), ctypes.c_void_p(A + 0x5000)]
+    bad = [P[0], P[1], X, P[2], P[3], ctypes.c_void_p(A + 0x4008), ctypes.c_void_p(A + 0x5000)]
     assert call(ptrs=bad) == lib.W4A16_ERR_ALIGNMENT
-    nul = [P[0], None, P[2], P[3], P[4], ctypes.c_void_p(A + 0x5000)]
+    bad = [P[0], P[1], ctypes.c_void_p(A + 0x6008), P[2], P[3], P[4], ctypes.c_void_p(A + 0x5000)]
+    assert call(ptrs=bad) == lib.W4A16_ERR_ALIGNMENT
+    nul = [P[0], None, X, P[2], P[3], P[4], ctypes.c_void_p(A + 0x5000)]
+    assert call(ptrs=nul) == lib.W4A16_ERR_INVALID_ARG
+    nul = [P[0], P[1], None, P[2], P[3], P[4], ctypes.c_void_p(A + 0x5000)]
     assert call(ptrs=nul) == lib.W4A16_ERR_INVALID_ARG
     ex = so.w4a8_matmul_ex
-    pp = [P[0], P[1], P[2], P[3], P[4], ctypes.c_void_p(A + 0x5000)]
+    pp = [P[0], P[1], X, P[2], P[3], P[4], ctypes.c_void_p(A + 0x5000)]
     assert ex(*pp, 4, 64, 256, 128, 0, -1, None) == lib.W4A16_ERR_INVALID_ARG
     assert ex(*pp, 4, 64, 256, 128, 0, 3, None) == lib.W4A16_ERR_INVALID_ARG      # > K / 128
 
@@ -300,7 +307,7 @@ def test_offsets_beyond_31_bits_are_rejected():
     partials of an output tile (128 KiB each, for W4A8 and the async W4A16 tile) with
     32-bit offsets: shapes or split counts past that are rejected before any HIP call."""
     so = B.load()
-    pp = [P[0], P[1], P[2], P[3], P[4], ctypes.c_void_p(A + 0x5000)]
+    pp = [P[0], P[1], ctypes.c_void_p(A + 0x6000), P[2], P[3], P[4], ctypes.c_void_p(A + 0x5000)]
     assert so.w4a8_matmul_ex(*pp, 1, 1 << 25, 128, 128, 0, 0, None) == lib.W4A16_ERR_UNSUPPORTED
     assert "32-bit" in B.load().w4a16_last_error_detail().decode()
     assert so.w4a8_matmul_ex(*pp, 1, 8, 1 << 21, 128, 0, 16384, None) == lib.W4A16_ERR_UNSUPPORTED

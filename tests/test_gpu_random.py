@@ -96,5 +96,8 @@ def test_random_w4a8(lib, case):
     qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=4000 + i, std=0.02), g, bool(i % 3 == 0), layout)
     x = synth.activations(M, K, wid=9)
     xq, sx = oracle.quantize_activations(x)
-    y = lib.w4a8_matmul(dev(xq), dev(sx), dev(qw), dev(s), dev(z), group_size=g, layout=layout, splits=splits)
+    S = oracle.activation_block_sums(xq)
+    xsum = np.zeros((S.shape[0], (M + 3) // 4 * 4), dtype=np.float32)
+    xsum[:, :M] = S
+    y = lib.w4a8_matmul(dev(xq), dev(sx), dev(xsum), dev(qw), dev(s), dev(z), group_size=g, layout=layout, splits=splits)
     check_y(y, oracle.matmul_w4a8(xq, sx, qw, s, z, g, layout), f"w4a8 {case}")

@@ -39,6 +39,15 @@ def check_y(y_gpu, y_ref, what=""):
     assert np.all(err <= bound), f"{what}: max err {err.max():.3e} at {worst}, y={y[worst]} ref={y_ref[worst]}"
 
 
+def block_sums(xq):
+    """The oracle's block sums of the decoded codes, in the library's layout: fp32
+    [K/128, M rounded up to 4], padding rows 0."""
+    S = oracle.activation_block_sums(xq)
+    out = np.zeros((S.shape[0], (xq.shape[0] + 3) // 4 * 4), dtype=np.float32)
+    out[:, :xq.shape[0]] = S
+    return out
+
+
 def _activations(M, K, kind, seed):
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((M, K))
@@ -62,13 +71,20 @@ QUANT_SHAPES = [(1, 128), (3, 4096), (17, 14336), (64, 2048), (130, 8192)]
 def test_quantize_activations_bit_exact(lib, M, K, kind):
     print(f"\n[w4a8 quantise] {kind} M={M} K={K}", flush=True)
     x = _activations(M, K, kind, seed=M + K)
-    xq, sx = lib.w4a8_quantize(dev(x))
+    xq, sx, xsum = lib.w4a8_quantize(dev(x))
     torch.cuda.synchronize()
     xq_ref, sx_ref = oracle.quantize_activations(x)
     assert np.array_equal(sx.cpu().numpy().view(np.uint32), sx_ref.view(np.uint32)), "row scales differ"
     got = xq.cpu().numpy()
     bad = np.argwhere(got != xq_ref)
     assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[0]}: {got[tuple(bad[0])]:#x} vs {xq_ref[tuple(bad[0])]:#x}"
+    # block sums: fp32 sums of 128 exact values, within 128 * 2^-24 * sum |dec| of the exact sum
+    S = oracle.activation_block_sums(xq_ref)
+    mag = oracle.activation_block_sums(xq_ref & 0x7F)
+    s_gpu = xsum.cpu().numpy()
+    assert s_gpu.shape == (K // 128, (M + 3) // 4 * 4)
+    assert np.all(np.abs(s_gpu[:, :M] - S) <= 128 * 2.0 ** -24 * mag), np.abs(s_gpu[:, :M] - S).max()
+    assert np.all(s_gpu[:, M:] == 0)
 
 
 MM_SHAPES = [(1, 128, 8), (3, 256, 104), (130, 384, 1416), (257, 1408, 264), (64, 768, 2056), (200, 128, 136),
@@ -82,7 +98,7 @@ def test_w4a8_matmul_matches_oracle(lib, M, K, N, layout):
     qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=900 + M, std=0.02), 128, False, layout)
     x = synth.activations(M, K, wid=9)
     xq, sx = oracle.quantize_activations(x)
-    y = lib.w4a8_matmul(dev(xq), dev(sx), dev(qw), dev(s), dev(z), layout=layout)
+    y = lib.w4a8_matmul(dev(xq), dev(sx), dev(block_sums(xq)), dev(qw), dev(s), dev(z), layout=layout)
     check_y(y, oracle.matmul_w4a8(xq, sx, qw, s, z, 128, layout), f"w4a8 {layout} M={M} K={K} N={N}")
 
 
@@ -93,13 +109,13 @@ def test_w4a8_formats(lib, M, K, N, g, sym):
     qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=950 + M, std=0.02), g, sym)
     x = synth.activations(M, K, wid=9)
     xq, sx = oracle.quantize_activations(x)
-    y = lib.w4a8_matmul(dev(xq), dev(sx), dev(qw), dev(s), dev(z), group_size=g)
+    y = lib.w4a8_matmul(dev(xq), dev(sx), dev(block_sums(xq)), dev(qw), dev(s), dev(z), group_size=g)
     check_y(y, oracle.matmul_w4a8(xq, sx, qw, s, z, g), f"w4a8 g={g} sym={sym}")
 
 
-def test_w4a8_zero_points_outside_the_exact_range(lib):
-    """Zero points where q - z is rounded (|q - z| > 16) or saturated (beyond +-448): the
-    clamp of the zero point and the conversion's rounding match the oracle's E4M3(q - z)."""
+def test_w4a8_zero_points_anywhere_in_the_domain(lib):
+    """Zero points anywhere in [-1024, 1024] (|q - z| up to 1039, far beyond what an 8-bit
+    weight operand holds): q - z stays exact, through the block sums."""
     K, N, M = 512, 64, 33
     rng = np.random.default_rng(4)
     codes = rng.integers(0, 16, size=(K, N)).astype(np.uint8)
@@ -109,8 +125,8 @@ def test_w4a8_zero_points_outside_the_exact_range(lib):
     qw = oracle.pack(codes)
     x = synth.activations(M, K, wid=9)
     xq, sx = oracle.quantize_activations(x)
-    y = lib.w4a8_matmul(dev(xq), dev(sx), dev(qw), dev(scales), dev(zeros))
-    check_y(y, oracle.matmul_w4a8(xq, sx, qw, scales, zeros), "w4a8 rounded operand")
+    y = lib.w4a8_matmul(dev(xq), dev(sx), dev(block_sums(xq)), dev(qw), dev(scales), dev(zeros))
+    check_y(y, oracle.matmul_w4a8(xq, sx, qw, scales, zeros), "w4a8 far zero points")
 
 
 def test_w4a8_end_to_end_and_repeatable(lib):
@@ -118,13 +134,13 @@ def test_w4a8_end_to_end_and_repeatable(lib):
     M, K, N = 300, 2048, 1032
     qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=77, std=0.02))
     x = _activations(M, K, "spiky", seed=5)
-    xq, sx = lib.w4a8_quantize(dev(x))
+    xq, sx, xsum = lib.w4a8_quantize(dev(x))
     args = [dev(qw), dev(s), dev(z)]
-    y = lib.w4a8_matmul(xq, sx, *args).clone()
+    y = lib.w4a8_matmul(xq, sx, xsum, *args).clone()
     xq_ref, sx_ref = oracle.quantize_activations(x)
     check_y(y, oracle.matmul_w4a8(xq_ref, sx_ref, qw, s, z), "w4a8 end to end")
     for _ in range(3):
-        y2 = lib.w4a8_matmul(xq, sx, *args)
+        y2 = lib.w4a8_matmul(xq, sx, xsum, *args)
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
@@ -140,8 +156,8 @@ def test_w4a8_prefill_shapes_sampled(lib, M, K, N):
     print(f"\n[w4a8 prefill] M={M} K={K} N={N}", flush=True)
     qw, s, z = oracle.quantize_pack(synth.weight(K, N, wid=wid))
     x = synth.activations(M, K, wid=wid)
-    xq, sx = lib.w4a8_quantize(dev(x))
-    y = lib.w4a8_matmul(xq, sx, dev(qw), dev(s), dev(z))
+    xq, sx, xsum = lib.w4a8_quantize(dev(x))
+    y = lib.w4a8_matmul(xq, sx, xsum, dev(qw), dev(s), dev(z))
     xq_ref, sx_ref = oracle.quantize_activations(x)
     cols = np.unique(np.concatenate([np.arange(0, N, max(1, N // 40)), [N - 1]]))
     y_ref = oracle.matmul_w4a8(xq_ref, sx_ref, qw[:, cols], s[:, cols], z[:, cols])
@@ -159,7 +175,7 @@ def test_w4a8_split_k(lib, M, K, N, splits, layout):
     qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=990 + M, std=0.02), 128, False, layout)
     x = synth.activations(M, K, wid=9)
     xq, sx = oracle.quantize_activations(x)
-    args = [dev(xq), dev(sx), dev(qw), dev(s), dev(z)]
+    args = [dev(xq), dev(sx), dev(block_sums(xq)), dev(qw), dev(s), dev(z)]
     y = lib.w4a8_matmul(*args, layout=layout, splits=splits).clone()
     check_y(y, oracle.matmul_w4a8(xq, sx, qw, s, z, 128, layout), f"w4a8 split-K S={splits}")
     for _ in range(2):                                   # same bits again: counters were reset
@@ -173,7 +189,7 @@ def test_w4a8_split_k_shares_counters_with_w4a16(lib):
     qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=3, std=0.02))
     x = synth.activations(M, K, wid=9)
     xq, sx = oracle.quantize_activations(x)
-    a8 = [dev(xq), dev(sx), dev(qw), dev(s), dev(z)]
+    a8 = [dev(xq), dev(sx), dev(block_sums(xq)), dev(qw), dev(s), dev(z)]
     a16 = [dev(x), dev(qw), dev(s), dev(z)]
     ref8 = oracle.matmul_w4a8(xq, sx, qw, s, z)
     ref16 = oracle.matmul(x, qw, s, z)
@@ -192,5 +208,5 @@ def test_w4a8_split_k_groups_of_256(lib, M, K, N, splits, layout):
     qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=1200 + M, std=0.02), 256, False, layout)
     x = synth.activations(M, K, wid=9)
     xq, sx = oracle.quantize_activations(x)
-    y = lib.w4a8_matmul(dev(xq), dev(sx), dev(qw), dev(s), dev(z), group_size=256, layout=layout, splits=splits)
+    y = lib.w4a8_matmul(dev(xq), dev(sx), dev(block_sums(xq)), dev(qw), dev(s), dev(z), group_size=256, layout=layout, splits=splits)
     check_y(y, oracle.matmul_w4a8(xq, sx, qw, s, z, 256, layout), f"w4a8 g=256 split-K S={splits}")

@@ -45,7 +45,7 @@ MUTANTS = [
     ("zero point clamped to the 4-bit code range",
      "return codes.astype(np.float64) - z", "return codes.astype(np.float64) - np.clip(z, 0, 15)"),
     ("block sums over 64 rows",
-     "BLOCK = 128               # R21", "BLOCK = 64                # R21"),
+     "BLOCK = 128               # R22", "BLOCK = 64                # R22"),
     ("block sums of magnitudes",
      "return a.reshape(M, K // BLOCK, BLOCK).sum(axis=2).T", "return np.abs(a).reshape(M, K // BLOCK, BLOCK).sum(axis=2).T"),
     ("block sums row-major [M, K/128]",

@@ -73,9 +73,9 @@ _SIGS = {
     "w4a16_plan": ([_I64, _I64, _I64, _I64, ctypes.POINTER(w4a16_plan_t)], ctypes.c_int),
     "w4a16_dequant": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "w4a16_dequant_fmt": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P], ctypes.c_int),
-    "w4a8_quantize_activations": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
-    "w4a8_matmul": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int, _P], ctypes.c_int),
-    "w4a8_matmul_ex": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int, ctypes.c_int, _P],
+    "w4a8_quantize_activations": ([_P, _P, _P, _P, _I64, _I64, _P], ctypes.c_int),
+    "w4a8_matmul": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int, _P], ctypes.c_int),
+    "w4a8_matmul_ex": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int, ctypes.c_int, _P],
                        ctypes.c_int),
     "w4a16_read_probe": ([_P, _I64, _P, _P], ctypes.c_int),
     "w4a16_strerror": ([ctypes.c_int], ctypes.c_char_p),
@@ -348,24 +348,33 @@ def w4a16_dequant(qweight, scales, zeros, codes=True, weights=True, group_size=G
 
 
 def w4a8_quantize(x, stream=None):
-    """Per-row E4M3 quantisation of fp16 activations on the device: returns (xq uint8
-    [M, K], sx float32 [M]) with x ~= dec(xq) * sx[:, None]."""
+    """Per-row E4M3 quantisation of fp16 activations on the device: returns (xq uint8 [M, K],
+    sx float32 [M], xsum float32 [K/128, Ms]) with x ~= dec(xq) * sx[:, None] and xsum the
+    per-128-column block sums of dec(xq) (Ms = M rounded up to 4, padding rows 0)."""
     import torch
     if x.dim() != 2:
         raise ValueError("x must be 2-D")
     M, K = x.shape
     xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     sx = torch.empty((M,), dtype=torch.float32, device=x.device)
+    xsum = torch.empty((K // 128, w4a8_sum_stride(M)), dtype=torch.float32, device=x.device)
     rc = load().w4a8_quantize_activations(_dev_ptr(x, "x", torch.float16), _dev_ptr(xq, "xq", torch.uint8),
-                                          _dev_ptr(sx, "sx", torch.float32), M, K, _stream_ptr(stream, x.device))
+                                          _dev_ptr(sx, "sx", torch.float32), _dev_ptr(xsum, "xsum", torch.float32),
+                                          M, K, _stream_ptr(stream, x.device))
     _check(rc, "w4a8_quantize_activations")
-    return xq, sx
+    return xq, sx, xsum
 
 
-def w4a8_matmul(xq, sx, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, layout="linear", stream=None,
+def w4a8_sum_stride(M):
+    """Row stride of the block sums: M rounded up to a multiple of 4."""
+    return (M + 3) // 4 * 4
+
+
+def w4a8_matmul(xq, sx, xsum, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, layout="linear", stream=None,
                 splits=0):
-    """y[M, N] = sx * (dec(xq) . dec(E4M3(q - z))) per group times its scales (W4A8);
-    `splits` forces the split-K count (0: the library's choice)."""
+    """y[M, N] = sx * sum_g s_g * (dec(xq) . (q - z)) per group (W4A8, q - z exact); xsum are
+    the block sums w4a8_quantize returns; `splits` forces the split-K count (0: the
+    library's choice)."""
     import torch
     if xq.dim() != 2 or qweight.dim() != 2 or sx.dim() != 1:
         raise ValueError("xq and qweight must be 2-D, sx 1-D")
@@ -373,6 +382,8 @@ def w4a8_matmul(xq, sx, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, l
     N = qweight.shape[1]
     if qweight.shape[0] * 8 != K or sx.shape[0] != M:
         raise ValueError("xq, sx and qweight disagree on M or K")
+    if tuple(xsum.shape) != (K // 128, w4a8_sum_stride(M)):
+        raise ValueError("xsum must be [K/128, M rounded up to 4]")
     if scales.shape != (K // group_size, N) or zeros.shape != (K // group_size, N):
         raise ValueError("scales/zeros must be [K/group_size, N]")
     if y is None:
@@ -380,6 +391,7 @@ def w4a8_matmul(xq, sx, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, l
     elif y.shape != (M, N):
         raise ValueError("y must be [M, N]")
     rc = load().w4a8_matmul_ex(_dev_ptr(xq, "xq", torch.uint8), _dev_ptr(sx, "sx", torch.float32),
+                               _dev_ptr(xsum, "xsum", torch.float32),
                                _dev_ptr(qweight, "qweight", torch.int32), _dev_ptr(scales, "scales", torch.float16),
                                _dev_ptr(zeros, "zeros", torch.float16), _dev_ptr(y, "y", torch.float16), M, N, K,
                                group_size, _layout_id(layout), splits, _stream_ptr(stream, xq.device))

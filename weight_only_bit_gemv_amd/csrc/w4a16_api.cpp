@@ -667,24 +667,26 @@ int w4a16_dequant(const int32_t* qweight, const void* scales, const void* zeros,
     return w4a16_dequant_fmt(qweight, scales, zeros, codes, w, N, K, group_size, W4A16_LAYOUT_LINEAR, stream);
 }
 
-int w4a8_quantize_activations(const void* x, uint8_t* xq, float* sx, int64_t M, int64_t K, void* stream) {
-    if (!x || !xq || !sx) return fail(W4A16_ERR_INVALID_ARG, "null pointer argument");
+int w4a8_quantize_activations(const void* x, uint8_t* xq, float* sx, float* xsum, int64_t M, int64_t K,
+                              void* stream) {
+    if (!x || !xq || !sx || !xsum) return fail(W4A16_ERR_INVALID_ARG, "null pointer argument");
     if (M < 1 || K < 1) return fail(W4A16_ERR_INVALID_ARG, "M, K must be >= 1 (got %lld, %lld)", (long long)M,
                                     (long long)K);
     if (K % 128 != 0) return fail(W4A16_ERR_UNSUPPORTED, "K=%lld is not a multiple of 128", (long long)K);
     if (M > 65535 * 1024ll || M * K > INT32_MAX) return fail(W4A16_ERR_UNSUPPORTED, "problem too large");
-    if (!aligned16(x) || !aligned16(xq) || reinterpret_cast<uintptr_t>(sx) % 4 != 0)
-        return fail(W4A16_ERR_ALIGNMENT, "x and xq must be 16-byte aligned, sx 4-byte aligned");
-    const int e = w4a16::launch_w4a8_quantize(static_cast<const uint16_t*>(x), xq, sx, (int)M, (int)K, stream);
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(xsum) || reinterpret_cast<uintptr_t>(sx) % 4 != 0)
+        return fail(W4A16_ERR_ALIGNMENT, "x, xq and xsum must be 16-byte aligned, sx 4-byte aligned");
+    const int e = w4a16::launch_w4a8_quantize(static_cast<const uint16_t*>(x), xq, sx, xsum, (int)M, (int)K, stream);
     if (e != (int)hipSuccess)
         return fail(W4A16_ERR_HIP, "activation quantiser launch: %s", hipGetErrorString((hipError_t)e));
     return ok();
 }
 
-int w4a8_matmul_ex(const uint8_t* xq, const float* sx, const int32_t* qweight, const void* scales, const void* zeros,
-                   void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, int layout, int splits,
-                   void* stream) {
-    if (!xq || !sx || !qweight || !scales || !zeros || !y) return fail(W4A16_ERR_INVALID_ARG, "null pointer argument");
+int w4a8_matmul_ex(const uint8_t* xq, const float* sx, const float* xsum, const int32_t* qweight, const void* scales,
+                   const void* zeros, void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, int layout,
+                   int splits, void* stream) {
+    if (!xq || !sx || !xsum || !qweight || !scales || !zeros || !y)
+        return fail(W4A16_ERR_INVALID_ARG, "null pointer argument");
     if (!w4a16::layout_supported(layout)) return fail(W4A16_ERR_INVALID_ARG, "unknown layout %d", layout);
     int rc = check_gpu_shape(M, N, K, group_size);
     if (rc) return rc;
@@ -695,12 +697,14 @@ int w4a8_matmul_ex(const uint8_t* xq, const float* sx, const int32_t* qweight, c
     if (64 * N > INT32_MAX)
         return fail(W4A16_ERR_UNSUPPORTED, "N=%lld exceeds the W4A8 kernel's 32-bit weight offsets", (long long)N);
     if (ceil_div(M, 128) > 65535) return fail(W4A16_ERR_UNSUPPORTED, "grid too large");
-    if (!aligned16(xq) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros) || !aligned16(y) ||
-        reinterpret_cast<uintptr_t>(sx) % 4 != 0)
+    if (!aligned16(xq) || !aligned16(xsum) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros) ||
+        !aligned16(y) || reinterpret_cast<uintptr_t>(sx) % 4 != 0)
         return fail(W4A16_ERR_ALIGNMENT, "device pointers must be 16-byte aligned (sx 4-byte)");
     w4a16::W4A8Params p{};
     p.xq = xq;
     p.sx = sx;
+    p.xsum = xsum;
+    p.Ms = (int)(ceil_div(M, 4) * 4);
     p.qweight = reinterpret_cast<const uint32_t*>(qweight);
     p.scales = static_cast<const uint16_t*>(scales);
     p.zeros = static_cast<const uint16_t*>(zeros);
@@ -735,9 +739,10 @@ int w4a8_matmul_ex(const uint8_t* xq, const float* sx, const int32_t* qweight, c
     return ok();
 }
 
-int w4a8_matmul(const uint8_t* xq, const float* sx, const int32_t* qweight, const void* scales, const void* zeros,
-                void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, int layout, void* stream) {
-    return w4a8_matmul_ex(xq, sx, qweight, scales, zeros, y, M, N, K, group_size, layout, 0, stream);
+int w4a8_matmul(const uint8_t* xq, const float* sx, const float* xsum, const int32_t* qweight, const void* scales,
+                const void* zeros, void* y, int64_t M, int64_t N, int64_t K, int64_t group_size, int layout,
+                void* stream) {
+    return w4a8_matmul_ex(xq, sx, xsum, qweight, scales, zeros, y, M, N, K, group_size, layout, 0, stream);
 }
 
 int w4a16_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {

@@ -107,6 +107,8 @@ int launch_prefill_async(const PrefillParams& p, void* stream);  // W4A16_TILE_A
 struct W4A8Params {
     const uint8_t* xq;        // E4M3 codes [M, K]
     const float* sx;          // fp32 row scales [M]
+    const float* xsum;        // fp32 block sums of the decoded codes [K/128, Ms]
+    int Ms;                   // row stride of xsum: M rounded up to a multiple of 4
     const uint32_t* qweight;  // int32 [K/8, N]
     const uint16_t* scales;   // fp16 [K/g, N]
     const uint16_t* zeros;    // fp16 [K/g, N]
@@ -123,7 +125,7 @@ struct W4A8Params {
     float* ws;
     uint32_t* counters;
 };
-int launch_w4a8_quantize(const uint16_t* x, uint8_t* xq, float* sx, int M, int K, void* stream);
+int launch_w4a8_quantize(const uint16_t* x, uint8_t* xq, float* sx, float* xsum, int M, int K, void* stream);
 int launch_w4a8(const W4A8Params& p, void* stream);   // returns a hipError_t value
 
 // ---- static scratch of w4a16_matmul_noalloc (w4a16_noalloc.hip) ----

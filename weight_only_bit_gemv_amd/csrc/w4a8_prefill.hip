@@ -4,16 +4,18 @@
 // README lists FP8 x Wn with activations quantised dynamically, one scale per row).
 //
 // Two kernels:
-//   quantize_rows_kernel  x fp16 [M, K] -> codes xq [M, K] (E4M3) and row scales sx [M]:
-//                         sx = amax / 448 (1 for a zero row), xq = E4M3(x / sx), nearest-
-//                         even, saturating (the hardware conversion rounds to nearest even;
-//                         values are clamped to +-448 first, as it returns NaN above 464).
-//   w4a8_kernel           y = sx * sum_g s_g * sum_{k in g} dec(xq) * dec(E4M3(q - z)).
+//   quantize_rows_kernel  x fp16 [M, K] -> codes xq [M, K] (E4M3), row scales sx [M] and
+//                         block sums xsum [K/128, Ms] (Ms = M rounded up to 4): sx = amax /
+//                         448 (1 for a zero row), xq = E4M3(x / sx), nearest-even,
+//                         saturating (the hardware conversion rounds to nearest even; values
+//                         are clamped to +-448 first, as it returns NaN above 464);
+//                         xsum[b, m] = sum of dec(xq[m, k]) over the 128 k of block b.
+//   w4a8_kernel           y = sx * sum_g s_g * sum_{k in g} dec(xq) * (q - z), q - z exact.
 //
 // The product kernel keeps the tiling of the async W4A16 tile (a work-group computes
 // BM x 256 of y, BM = 128, or 64 or 32 when M is that small, 4 wavefronts side by side
 // along N, each BM rows x 64 columns as BM/16 x 4 tiles of 16 x 16) and its direct
-// global-to-LDS loads, but a stage is one 128-row K group:
+// global-to-LDS loads, but a stage is one 128-row K block:
 // one v_mfma_f32_16x16x128_f8f6f4 per tile covers it. In that instruction lane (r, g)
 // (r = lane % 16, g = lane / 16) holds 32 bytes of row r of A and of column r of B, and
 // byte j of A pairs with byte j of B, so any assignment of K indices to (g, j) works if both
@@ -23,15 +25,21 @@
 // read four neighbouring chunks, which a bank-conflict probe showed conflict-free, while
 // chunks 2g and 2g + 1 conflict two ways), and the weight bytes come from packed rows
 // 2g, 2g + 1, 8 + 2g and 9 + 2g.
-// Each tile's product over the group comes out with a zero accumulator and is added to the
+// Each tile's product over the block comes out with a zero accumulator and is added to the
 // fp32 result times the group's scale of its column (four FMAs per instruction); the row
 // scale multiplies the result once at the end.
 //
-// Weight operand: the magic-number unpack of device.hpp gives q - z exactly in fp16, and
-// v_cvt_scalef32_pk_fp8_f16 (scale 1) rounds pairs of it to E4M3 (nearest even). q - z is
-// exact in E4M3 when |q - z| <= 16. The zero point is first clamped to [-448, 463]: that
-// keeps every |q - z| below 464 (the conversion's NaN threshold) and gives exactly the
-// saturated value for zero points beyond it.
+// Weight operand: E4M3(q - zc) with zc the zero point clamped to [-1, 16], so that
+// |q - zc| <= 16 and the operand is exact. The magic-number unpack of device.hpp gives
+// q - zc exactly in fp16, and v_cvt_scalef32_pk_fp8_f16 (scale 1) converts pairs of it.
+// A centred operand keeps the instruction's accumulation accurate: on rows with outlier
+// activations the 8-bit matrix unit rounds its sum to about 2^-13 of the largest products,
+// so an uncentred operand (the bare code q, exact in E4M3 as q * 2^-9) with the zero point
+// applied afterwards as -z * sum(a) measured 3 to 8 times the error of this one.
+// A zero point outside [-1, 16] (a one-signed group) leaves z - zc != 0: such work-groups
+// add the exact remainder -s (z - zc) S, S the block sums of the activations, after their
+// K loop, as a [rows x blocks] . [blocks x columns] contraction on v_mfma_f32_16x16x4_f32
+// (four blocks per instruction). Work-groups whose zero points all lie in [-1, 16] skip it.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -58,7 +66,8 @@ constexpr int kWaitVmcnt0 = 0 | (0x7 << 4) | (0xf << 8);
 constexpr int QT = 256;   // threads per row
 
 __global__ __launch_bounds__(QT) void quantize_rows_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ xq,
-                                                          float* __restrict__ sx, int K) {
+                                                          float* __restrict__ sx, float* __restrict__ xsum, int M,
+                                                          int K, int Ms) {
     const int m = blockIdx.x;
     const uint4* row = reinterpret_cast<const uint4*>(x + (size_t)m * K);   // 8 fp16 per uint4
     const int n8 = K / 8;
@@ -77,6 +86,8 @@ __global__ __launch_bounds__(QT) void quantize_rows_kernel(const uint16_t* __res
     const float s = amax > 0.f ? amax / kE4M3Max : 1.0f;
     if (threadIdx.x == 0) sx[m] = s;
     uint2* out = reinterpret_cast<uint2*>(xq + (size_t)m * K);              // 8 codes per uint2
+    // Thread t converts 8 codes per pass; the 16 threads of one 128-code block (K % 128 == 0,
+    // so a block's threads are all active together) sum their decoded codes, in a fixed order.
     for (int i = threadIdx.x; i < n8; i += QT) {
         const half8_t h = __builtin_bit_cast(half8_t, row[i]);
         float v[8];
@@ -88,7 +99,17 @@ __global__ __launch_bounds__(QT) void quantize_rows_kernel(const uint16_t* __res
         hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], hi, false);
         hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], hi, true);
         out[i] = make_uint2((uint32_t)lo, (uint32_t)hi);
+        float sum = ((__builtin_amdgcn_cvt_f32_fp8(lo, 0) + __builtin_amdgcn_cvt_f32_fp8(lo, 1)) +
+                     (__builtin_amdgcn_cvt_f32_fp8(lo, 2) + __builtin_amdgcn_cvt_f32_fp8(lo, 3))) +
+                    ((__builtin_amdgcn_cvt_f32_fp8(hi, 0) + __builtin_amdgcn_cvt_f32_fp8(hi, 1)) +
+                     (__builtin_amdgcn_cvt_f32_fp8(hi, 2) + __builtin_amdgcn_cvt_f32_fp8(hi, 3)));
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off, 16);
+        if ((threadIdx.x & 15) == 0) xsum[(size_t)(i >> 4) * Ms + m] = sum;
     }
+    if (m == M - 1)                                    // padding rows M .. Ms - 1 of every block
+        for (int j = threadIdx.x; j < (K / 128) * (Ms - M); j += QT)
+            xsum[(size_t)(j / (Ms - M)) * Ms + M + j % (Ms - M)] = 0.f;
 }
 
 // ---- product kernel ---------------------------------------------------------------------
@@ -217,6 +238,8 @@ __global__ __launch_bounds__(NT, 2) void w4a8_kernel(W4A8Params p) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[i][t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+    bool far_lane = false;   // a zero point of this lane's columns outside [-1, 16] so far
+
     auto compute = [&](const uint4* sl) {
         // the lane's four columns: scales and zero offsets of the group
         const uint4* szl = sl + kAChunks + kBChunks + wave * 8 + (lr >> 1);
@@ -233,7 +256,8 @@ __global__ __launch_bounds__(NT, 2) void w4a8_kernel(W4A8Params p) {
         int8v b[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const _Float16 zt = (_Float16)fminf(fmaxf((float)zc[t], -448.0f), 463.0f);
+            const _Float16 zt = (_Float16)fminf(fmaxf((float)zc[t], -1.0f), 16.0f);   // |q - zt| <= 16: exact
+            far_lane = far_lane || zt != zc[t];
             const ZeroOffsets zo = zero_offsets(zt);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -293,6 +317,39 @@ __global__ __launch_bounds__(NT, 2) void w4a8_kernel(W4A8Params p) {
     }
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");       // no load may outlive the work-group
 
+    // The remainder of the zero point beyond the clamp, for wavefronts that met one: the
+    // products used q - zc, so row tile i takes -s (z - zc) S[b, m] for every block b of the
+    // work-group's range (S: the activation block sums), just before it is stored. The lane
+    // holds rows 4 lg + r of the tile and its four columns. One tile at a time, so that only
+    // that tile's sums are carried through the loop over blocks.
+    const bool far_wave = __builtin_amdgcn_ballot_w64(far_lane) != 0;
+    auto correct_tile = [&](int i) __attribute__((always_inline)) {
+        // lane indices re-derived here, so that nothing of this block is computed before
+        // the main loop and held through it
+        int elg = lg, enw = nw;
+        asm volatile("" : "+v"(elg), "+v"(enw));
+        const int col = enw < p.N ? enw : 0;                 // nw % 4 == 0 and N % 8 == 0
+        // rows m0 + 16 i + 4 lg .. + 3; a quad at or past Ms (a multiple of 4, so past
+        // every stored row) reads the block's last four entries instead
+        const int row = min(m0 + 16 * i + 4 * elg, p.Ms - 4);
+        for (int kt = kbase; kt < kbase + KT; ++kt) {
+            const size_t grp = (size_t)((kt * KS) >> p.group_shift);
+            const uint2 sv = *reinterpret_cast<const uint2*>(p.scales + grp * p.N + col);
+            const uint2 zv = *reinterpret_cast<const uint2*>(p.zeros + grp * p.N + col);
+            const float4 sa = *reinterpret_cast<const float4*>(p.xsum + (size_t)kt * p.Ms + row);
+            const half2_t s01 = as_h2(sv.x), s23 = as_h2(sv.y), z01 = as_h2(zv.x), z23 = as_h2(zv.y);
+            const float sf[4] = {(float)s01[0], (float)s01[1], (float)s23[0], (float)s23[1]};
+            const float zf[4] = {(float)z01[0], (float)z01[1], (float)z23[0], (float)z23[1]};
+            const float sr[4] = {sa.x, sa.y, sa.z, sa.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float c = -(sf[t] * (zf[t] - fminf(fmaxf(zf[t], -1.0f), 16.0f)));   // exact
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(sr[r], c, acc[i][t][r]);
+            }
+        }
+    };
+
     // y rows 4 lg + r of row tile i, columns nw .. nw + 3, from fp32 sums v[t][r] times the
     // row scale
     auto store_rows = [&](int i, const floatx4 (&v)[4]) {
@@ -326,11 +383,13 @@ __global__ __launch_bounds__(NT, 2) void w4a8_kernel(W4A8Params p) {
         };
 #pragma unroll
         for (int i = 0; i < TI; ++i)
-            if (i < live_tiles)
+            if (i < live_tiles) {
+                if (far_wave) correct_tile(i);
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint4_vec, acc[i][t]), rs, off(split, i, t), 0,
                                                            kCpolSc1);
+            }
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);              // this wavefront's partial stores have completed
         __syncthreads();                                       // ... and every wavefront's
         if (tid == 0)
@@ -373,7 +432,10 @@ __global__ __launch_bounds__(NT, 2) void w4a8_kernel(W4A8Params p) {
 
     // epilogue: lane holds rows 4 lg + r of columns nw .. nw + 3 of each row tile
 #pragma unroll
-    for (int i = 0; i < TI; ++i) store_rows(i, acc[i]);
+    for (int i = 0; i < TI; ++i) {
+        if (far_wave && i < live_tiles) correct_tile(i);
+        store_rows(i, acc[i]);
+    }
 }
 
 template <bool NAT, int BM>
@@ -393,15 +455,17 @@ int launch_w4a8_t(const W4A8Params& p, hipStream_t s) {
 
 }  // namespace
 
-int launch_w4a8_quantize(const uint16_t* x, uint8_t* xq, float* sx, int M, int K, void* stream) {
+int launch_w4a8_quantize(const uint16_t* x, uint8_t* xq, float* sx, float* xsum, int M, int K, void* stream) {
+    const int Ms = (M + 3) / 4 * 4;
     hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)M), dim3(QT), 0, reinterpret_cast<hipStream_t>(stream),
-                       x, xq, sx, K);
+                       x, xq, sx, xsum, M, K, Ms);
     return (int)hipGetLastError();
 }
 
 int launch_w4a8(const W4A8Params& p, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (p.N % 8 != 0 || p.K % KS != 0 || (p.group_shift != 7 && p.group_shift != 8) || p.splits < 1 ||
+    if (p.N % 8 != 0 || p.K % KS != 0 || (p.group_shift != 7 && p.group_shift != 8) || p.splits < 1 || !p.xsum ||
+        p.Ms < p.M || p.Ms % 4 != 0 ||
         p.stages_per_split < 1 || (p.splits > 1 && (!p.ws || !p.counters)) || (p.bm != 32 && p.bm != 64 && p.bm != 128))
         return (int)hipErrorInvalidValue;
     const bool nat = p.layout == W4A16_LAYOUT_INTERLEAVED;
