@@ -27,7 +27,9 @@ reported too), in GB/s. `roofline` relates the average launch to the 8 TB/s HBM 
 peak for prefill), gives the fraction of the measured read ceiling (w4a16_read_probe at each
 call's byte count, same timing) and, from the committed kernel-trace summary of the same
 sources, the dominant kernel instance's own rate; `grouped` times q/k/v and gate/up as one
-grouped launch against one launch per matrix; `cpu_baseline` times the oracle (NumPy, fp64)
+grouped launch against one launch per matrix (decode_sweep), or the active experts' gate/up
+(one shared x) and down projections (each its own x) of mixture-of-experts layers
+(moe_expert); `cpu_baseline` times the oracle (NumPy, fp64)
 on the host cores over passes of the decode sweep (about 10 s). --record FILE also writes
 the line with the command, the sources' hash and the machine.
 
@@ -555,57 +557,87 @@ class GroupedChain:
         self.lm[0].launch(self.lm[1])
 
 
-def grouped_decode(torch, lib, dev, stream, group=GROUP, layout="linear", ms=(1, 16)):
-    """The projections of the 7B-shaped layer that share an input, at M = 1 and 16: q/k/v
-    (3 x 4096 x 4096) and gate/up (2 x 4096 x 14336), as one grouped launch against one
-    launch per matrix, weights rotated over 1 GiB."""
+def grouped_timing(torch, lib, dev, stream, label, mats, own_x, ms, wid, group=GROUP, layout="linear"):
+    """One grouped launch (w4a16_matmul_grouped) over the matrices `mats` = [(K, N, seed), ...]
+    (same K) against one launch per matrix, at each M in `ms`, weights rotated over 1 GiB.
+    own_x: every matrix reads its own activations (x_i) instead of one shared x."""
     B = lib._binding
     so = lib.load()
     lay = B._layout_id(layout)
+    K = mats[0][0]
+    Ns = [N for _, N, _ in mats]
+    one = []
+    for K_, N, seed in mats:
+        qw, s, z = lib.w4a16_pack(synth.weight(K_, N, wid=wid, layer=seed), group_size=group, layout=layout)
+        one.append([torch.from_numpy(a).to(dev) for a in (qw, s, z)])
+    per = sum(t.numel() * t.element_size() for m in one for t in m)
+    ring = [one] + [[[t.clone() for t in m] for m in one] for _ in range(max(1, -(-ROTATE_BYTES // per)) - 1)]
+    out = []
+    for M in ms:
+        x = torch.from_numpy(synth.activations(M, K, wid=wid)).to(dev)
+        xs = [torch.from_numpy(synth.activations(M, K, wid=wid + 1 + i)).to(dev) if own_x else x
+              for i in range(len(mats))]
+        ys = [torch.empty((M, N), dtype=torch.float16, device=dev) for N in Ns]
+        arrs = []
+        for ms_ in ring:
+            arr = (B.w4a16_matrix_t * len(mats))()
+            for i, ((q, s_, z_), y) in enumerate(zip(ms_, ys)):
+                arr[i] = B.w4a16_matrix_t(q.data_ptr(), s_.data_ptr(), z_.data_ptr(), y.data_ptr(), Ns[i],
+                                          xs[i].data_ptr() if own_x else None)
+            arrs.append(arr)
+
+        def grouped():
+            for arr in arrs:
+                if so.w4a16_matmul_grouped(x.data_ptr(), arr, len(mats), M, K, group, lay, stream.cuda_stream, None):
+                    raise RuntimeError("w4a16_matmul_grouped failed")
+
+        def separate():
+            for ms_ in ring:
+                for (q, s_, z_), y, xi in zip(ms_, ys, xs):
+                    if so.w4a16_matmul_fmt(xi.data_ptr(), q.data_ptr(), s_.data_ptr(), z_.data_ptr(), y.data_ptr(),
+                                           M, q.shape[1], K, group, lay, stream.cuda_stream, None):
+                        raise RuntimeError("w4a16_matmul_fmt failed")
+        tg = time_graph(torch, stream, grouped, 5)[0] / len(ring)
+        ts = time_graph(torch, stream, separate, 5)[0] / len(ring)
+        b = sum(alg_bytes(M, K, N, group) for N in Ns)
+        out.append({"matrices": label, "M": M, "K": K, "N": Ns, "own_x": own_x, "bytes": b,
+                    "grouped_us": round(tg * 1e6, 3), "grouped_GBps": round(b / tg / 1e9, 1),
+                    "grouped_frac_hbm": round(b / tg / 1e9 / HBM_PEAK_GBS, 4),
+                    "separate_launches_us": round(ts * 1e6, 3), "speedup": round(ts / tg, 3),
+                    "plan": lib.w4a16_plan(M, sum(Ns), K, group_size=group)})
+    del ring
+    return out
+
+
+def grouped_decode(torch, lib, dev, stream, group=GROUP, layout="linear", ms=(1, 16)):
+    """The projections of the 7B-shaped layer that share an input, at M = 1 and 16: q/k/v
+    (3 x 4096 x 4096) and gate/up (2 x 4096 x 14336), as one grouped launch against one
+    launch per matrix."""
     wid = synth.WORKLOADS["decode_chain_7b"]["wid"]
+    names = [nm for nm, _, _ in synth.CHAIN_7B_LAYER]
     shapes = dict((nm, (K, N)) for nm, K, N in synth.CHAIN_7B_LAYER)
     out = []
-    for names in (("q", "k", "v"), ("gate", "up")):
-        one = []
-        for nm in names:
-            K, N = shapes[nm]
-            p = [nm0 for nm0, _, _ in synth.CHAIN_7B_LAYER].index(nm)
-            qw, s, z = lib.w4a16_pack(synth.weight(K, N, wid=wid, layer=p), group_size=group, layout=layout)
-            one.append([torch.from_numpy(a).to(dev) for a in (qw, s, z)])
-        per = sum(t.numel() * t.element_size() for m in one for t in m)
-        ring = [one] + [[[t.clone() for t in m] for m in one] for _ in range(max(1, -(-ROTATE_BYTES // per)) - 1)]
-        K = shapes[names[0]][0]
-        Ns = [shapes[nm][1] for nm in names]
-        for M in ms:
-            x = torch.from_numpy(synth.activations(M, K, wid=wid)).to(dev)
-            ys = [torch.empty((M, N), dtype=torch.float16, device=dev) for N in Ns]
-            arrs = []
-            for mats in ring:
-                arr = (B.w4a16_matrix_t * len(names))()
-                for i, ((q, s_, z_), y) in enumerate(zip(mats, ys)):
-                    arr[i] = B.w4a16_matrix_t(q.data_ptr(), s_.data_ptr(), z_.data_ptr(), y.data_ptr(), Ns[i])
-                arrs.append(arr)
+    for group_names in (("q", "k", "v"), ("gate", "up")):
+        mats = [shapes[nm] + (names.index(nm),) for nm in group_names]
+        out += grouped_timing(torch, lib, dev, stream, "+".join(group_names), mats, False, ms, wid, group, layout)
+    return out
 
-            def grouped():
-                for arr in arrs:
-                    if so.w4a16_matmul_grouped(x.data_ptr(), arr, len(names), M, K, group, lay, stream.cuda_stream, None):
-                        raise RuntimeError("w4a16_matmul_grouped failed")
 
-            def separate():
-                for mats in ring:
-                    for (q, s_, z_), y in zip(mats, ys):
-                        if so.w4a16_matmul_fmt(x.data_ptr(), q.data_ptr(), s_.data_ptr(), z_.data_ptr(), y.data_ptr(),
-                                               M, q.shape[1], K, group, lay, stream.cuda_stream, None):
-                            raise RuntimeError("w4a16_matmul_fmt failed")
-            tg = time_graph(torch, stream, grouped, 5)[0] / len(ring)
-            ts = time_graph(torch, stream, separate, 5)[0] / len(ring)
-            b = sum(alg_bytes(M, K, N, group) for N in Ns)
-            out.append({"matrices": "+".join(names), "M": M, "K": K, "N": Ns, "bytes": b,
-                        "grouped_us": round(tg * 1e6, 3), "grouped_GBps": round(b / tg / 1e9, 1),
-                        "grouped_frac_hbm": round(b / tg / 1e9 / HBM_PEAK_GBS, 4),
-                        "separate_launches_us": round(ts * 1e6, 3), "speedup": round(ts / tg, 3),
-                        "plan": lib.w4a16_plan(M, sum(Ns), K, group_size=group)})
-        del ring
+def grouped_experts(torch, lib, dev, stream, group=GROUP, layout="linear"):
+    """Batch-1 decode of mixture-of-experts layers built from the expert shapes: the gate and
+    up projections of the active experts read the token (one shared x), and each expert's
+    down projection reads its own input. E active experts of hidden 2048 and expert width F:
+    2E matrices 2048 x F with one x, then E matrices F x 2048 with their own x, each set as
+    one grouped launch against one launch per matrix."""
+    wid = synth.WORKLOADS["moe_expert"]["wid"]
+    out = []
+    for E, F in ((4, 1408), (8, 768)):
+        up = [(2048, F, 100 + e) for e in range(2 * E)]
+        down = [(F, 2048, 200 + e) for e in range(E)]
+        out += grouped_timing(torch, lib, dev, stream, f"{E} experts gate+up ({2 * E} x 2048x{F})", up, False, (1,),
+                              wid, group, layout)
+        out += grouped_timing(torch, lib, dev, stream, f"{E} experts down ({E} x {F}x2048, own x)", down, True, (1,),
+                              wid, group, layout)
     return out
 
 
@@ -720,6 +752,8 @@ def run_decode(args):
     }
     if args.workload == "decode_sweep" and not args.no_grouped:
         result["grouped"] = grouped_decode(torch, lib, dev, stream, args.group_size, args.layout)
+    if args.workload == "moe_expert" and not args.no_grouped:
+        result["grouped"] = grouped_experts(torch, lib, dev, stream, args.group_size, args.layout)
     if chain:
         result["tokens_per_s"] = round(1.0 / t_med, 2)
         result["us_per_token"] = round(t_med * 1e6, 2)

@@ -176,11 +176,15 @@ static void device_call_errors() {
            W4A16_ERR_UNSUPPORTED, "noalloc plan beyond the static scratch");
     expect(w4a16_matmul_noalloc(p[0], nullptr, p[2], p[3], p[4], 1, 64, 128, 128, 0, nullptr, nullptr),
            W4A16_ERR_INVALID_ARG, "noalloc null qweight");
-    w4a16_matrix_t gm[5];
-    for (int i = 0; i < 5; ++i)
-        gm[i] = w4a16_matrix_t{(const int32_t*)p[1], p[2], p[3], p[4], 64};
-    expect(w4a16_matmul_grouped(p[0], gm, 5, 1, 4096, 128, 0, nullptr, nullptr), W4A16_ERR_INVALID_ARG,
-           "grouped 5 matrices");
+    w4a16_matrix_t gm[17];
+    for (int i = 0; i < 17; ++i)
+        gm[i] = w4a16_matrix_t{(const int32_t*)p[1], p[2], p[3], p[4], 64, nullptr};
+    expect(w4a16_matmul_grouped(p[0], gm, 17, 1, 4096, 128, 0, nullptr, nullptr), W4A16_ERR_INVALID_ARG,
+           "grouped 17 matrices");
+    gm[1].x = mis;
+    expect(w4a16_matmul_grouped(p[0], gm, 3, 1, 4096, 128, 0, nullptr, nullptr), W4A16_ERR_ALIGNMENT,
+           "grouped misaligned own x");
+    gm[1].x = p[0];
     expect(w4a16_matmul_grouped(p[0], gm, 0, 1, 4096, 128, 0, nullptr, nullptr), W4A16_ERR_INVALID_ARG,
            "grouped 0 matrices");
     gm[2].N = 62;

@@ -360,7 +360,8 @@ def test_grouped_rejects_bad_arguments():
     def call(arr, n=None, M=1, K=4096, g=128, layout=0, x=P[0], plan=None):
         return so.w4a16_matmul_grouped(x, arr, len(arr) if n is None else n, M, K, g, layout, None, plan)
     assert call(mats(64), n=0) == lib.W4A16_ERR_INVALID_ARG
-    assert call(mats(64, 64, 64, 64, 64)) == lib.W4A16_ERR_INVALID_ARG            # at most 4
+    assert call(mats(*[64] * 17)) == lib.W4A16_ERR_INVALID_ARG                      # at most 16
+    assert call(mats(64, 64, bad=(1, "x", A + 0x4008))) == lib.W4A16_ERR_ALIGNMENT  # a matrix's own x
     assert call(mats(64, 64), x=None) == lib.W4A16_ERR_INVALID_ARG
     assert call(mats(64, 64, bad=(1, "zeros", None))) == lib.W4A16_ERR_INVALID_ARG
     assert call(mats(64, 62)) == lib.W4A16_ERR_UNSUPPORTED                         # N % 4

@@ -1,4 +1,5 @@
-"""GPU parity of w4a16_matmul_grouped: several weight matrices that share x in one launch.
+"""GPU parity of w4a16_matmul_grouped: several weight matrices in one launch, sharing x or each
+with its own.
 
 Each y_i must equal, bit for bit, a w4a16_matmul_fmt call on its own matrix under the plan
 the grouped call used (same kernel, strip width, waves, K range per wavefront, splits), and
@@ -102,3 +103,44 @@ def test_grouped_repeated_calls_bitwise(lib):
         torch.cuda.synchronize()
         for a, b in zip(first, ys):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# mixture-of-experts layers at decode: the gate and up projections of the active experts read
+# one token (shared x); each expert's down projection reads its own input
+MOE_CASES = [
+    # (name, M, K, N, experts, own x per matrix (True / False / "mixed"), group, layout, forced plan)
+    ("moe-gate-up-16", 1, 2048, 768, 16, False, 128, "linear", None),
+    ("moe-down-8-own-x", 1, 768, 2048, 8, True, 128, "linear", None),
+    ("moe-down-4-own-x-M4", 4, 1408, 2048, 4, True, 64, "interleaved", None),
+    ("moe-mixed-split", 3, 2048, 1408, 6, "mixed", 128, "linear", dict(kernel=1, cols=16, kc=8, waves=4)),
+    ("own-x-row-blocks", 80, 1024, 264, 3, True, 128, "linear", None),
+    ("own-x-prefill", 200, 1024, 264, 3, True, 128, "linear", None),
+]
+
+
+@pytest.mark.parametrize("name,M,K,N,E,own,g,layout,plan", MOE_CASES, ids=[c[0] for c in MOE_CASES])
+def test_grouped_experts_with_their_own_inputs(lib, name, M, K, N, E, own, g, layout, plan):
+    """Up to 16 matrices in one call, each with the call's x or its own: every y_i equals, bit
+    for bit, a single call on (x_i, W_i) under the plan the grouped call used (decode kernel),
+    and meets the oracle's bar against x_i."""
+    mats = _inputs(name, K, [N] * E, g, layout)
+    xs = [synth.activations(M, K, wid=20 + i) for i in range(E)]
+    x0 = synth.activations(M, K, wid=12)
+    use_own = [own is True or (own == "mixed" and i % 2 == 1) for i in range(E)]
+    pl = lib.w4a16_plan(M, N * E, K, group_size=g, **(plan or {}))
+    print(f"\n[grouped-own-x] {name} M={M} K={K} N={N} x{E} own={own} plan={pl}", flush=True)
+    dx0 = dev(x0)
+    dxs = [dev(x) for x in xs]
+    dmats = [(dev(q), dev(s), dev(z)) + ((dxs[i],) if use_own[i] else ()) for i, (q, s, z) in enumerate(mats)]
+    ys = lib.w4a16_matmul_grouped(dx0, dmats, group_size=g, plan=plan, layout=layout)
+    torch.cuda.synchronize()
+    for i, ((q, s, z), y) in enumerate(zip(mats, ys)):
+        xi, dxi = (xs[i], dxs[i]) if use_own[i] else (x0, dx0)
+        if pl["kernel"] == 1:
+            single = lib.w4a16_matmul(dxi, *dmats[i][:3], group_size=g, layout=layout,
+                                      plan={k: v for k, v in pl.items() if k != "tile"})
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), single.view(torch.int16)), (name, i)
+        y_ref = oracle.matmul(xi, q, s, z, g, layout=layout)
+        err = np.abs(y.cpu().numpy().astype(np.float64) - y_ref)
+        assert np.all(err <= 1e-2 + 5e-3 * np.abs(y_ref)), (name, i, err.max())

@@ -50,7 +50,10 @@ class w4a16_plan_t(ctypes.Structure):
 
 class w4a16_matrix_t(ctypes.Structure):
     _fields_ = [("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p),
-                ("y", ctypes.c_void_p), ("N", ctypes.c_int64)]
+                ("y", ctypes.c_void_p), ("N", ctypes.c_int64), ("x", ctypes.c_void_p)]
+
+
+MAX_GROUP_MATS = 16
 
 
 _lib = None
@@ -258,19 +261,22 @@ def w4a16_matmul(x, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, strea
 
 
 def w4a16_matmul_grouped(x, weights, ys=None, group_size=GROUP_SIZE, stream=None, plan=None, layout="linear"):
-    """y_i = x . dequant(W_i) for the matrices in `weights` (a list of (qweight, scales, zeros),
-    1..4 of them) in one call of w4a16_matmul_grouped; returns the list of y_i (allocated when
-    `ys` is None)."""
+    """y_i = x_i . dequant(W_i) for the matrices in `weights` (a list of (qweight, scales, zeros)
+    or (qweight, scales, zeros, x_i), 1..16 of them; x_i defaults to x) in one call of
+    w4a16_matmul_grouped; returns the list of y_i (allocated when `ys` is None)."""
     import torch
     if x.dim() != 2:
         raise ValueError("x must be 2-D")
     M, K = x.shape
-    if not 1 <= len(weights) <= 4:
-        raise ValueError("1..4 weight matrices")
+    if not 1 <= len(weights) <= MAX_GROUP_MATS:
+        raise ValueError(f"1..{MAX_GROUP_MATS} weight matrices")
+    weights = [tuple(w) if len(w) == 4 else tuple(w) + (None,) for w in weights]
     if ys is None:
-        ys = [torch.empty((M, qw.shape[1]), dtype=torch.float16, device=x.device) for qw, _, _ in weights]
+        ys = [torch.empty((M, w[0].shape[1]), dtype=torch.float16, device=x.device) for w in weights]
     arr = (w4a16_matrix_t * len(weights))()
-    for i, ((qw, s, z), y) in enumerate(zip(weights, ys)):
+    for i, ((qw, s, z, xi), y) in enumerate(zip(weights, ys)):
+        if xi is not None and xi.shape != (M, K):
+            raise ValueError(f"matrix {i}: its x must be [M, K] = [{M}, {K}]")
         N = qw.shape[1]
         if qw.dim() != 2 or qw.shape[0] * 8 != K:
             raise ValueError(f"matrix {i}: qweight must be [K/8, N] with K={K}")
@@ -279,7 +285,8 @@ def w4a16_matmul_grouped(x, weights, ys=None, group_size=GROUP_SIZE, stream=None
         if y.shape != (M, N):
             raise ValueError(f"matrix {i}: y must be [M, N]")
         arr[i] = w4a16_matrix_t(_dev_ptr(qw, "qweight", torch.int32), _dev_ptr(s, "scales", torch.float16),
-                                _dev_ptr(z, "zeros", torch.float16), _dev_ptr(y, "y", torch.float16), N)
+                                _dev_ptr(z, "zeros", torch.float16), _dev_ptr(y, "y", torch.float16), N,
+                                None if xi is None else _dev_ptr(xi, "x", torch.float16))
     pl = ctypes.byref(_make_plan(plan)) if plan is not None else None
     rc = load().w4a16_matmul_grouped(_dev_ptr(x, "x", torch.float16), arr, len(weights), M, K, group_size,
                                      _layout_id(layout), _stream_ptr(stream, x.device), pl)

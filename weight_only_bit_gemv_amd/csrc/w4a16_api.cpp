@@ -435,9 +435,9 @@ int call_workspace(bool noalloc, void* stream, uint64_t bytes, uint64_t n_counte
     return W4A16_OK;
 }
 
-// One launch of the decode kernel over 1..kMaxGroupMats matrices that share x (validated,
-// plan completed for M, the summed N and K): their column strips are numbered one after the
-// other, so each work-group finds its matrix from its strip.
+// One launch of the decode kernel over 1..kMaxGroupMats matrices (validated, plan completed
+// for M, the summed N and K): their column strips are numbered one after the other, so each
+// work-group finds its matrix from its strip. A matrix whose x is null reads the call's x.
 int launch_skinny_mats(const void* x, const w4a16_matrix_t* mats, int n_mats, int64_t M, int64_t K,
                        int64_t group_size, int layout, void* stream, const w4a16_plan_t& pl, bool noalloc) {
     w4a16::SkinnyParams p{};
@@ -446,6 +446,7 @@ int launch_skinny_mats(const void* x, const w4a16_matrix_t* mats, int n_mats, in
     int64_t strips = 0;
     for (int i = 0; i < w4a16::kMaxGroupMats; ++i) {
         const w4a16_matrix_t& m = mats[std::min(i, n_mats - 1)];       // unused entries repeat the last
+        p.mat[i].x = static_cast<const uint16_t*>(m.x ? m.x : x);
         p.mat[i].qweight = reinterpret_cast<const uint32_t*>(m.qweight);
         p.mat[i].scales = static_cast<const uint16_t*>(m.scales);
         p.mat[i].zeros = static_cast<const uint16_t*>(m.zeros);
@@ -520,7 +521,7 @@ int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const
         return ok();
     }
 
-    const w4a16_matrix_t one{qweight, scales, zeros, y, N};
+    const w4a16_matrix_t one{qweight, scales, zeros, y, N, nullptr};
     return launch_skinny_mats(x, &one, 1, M, K, group_size, layout, stream, pl, noalloc);
 }
 
@@ -594,7 +595,8 @@ int w4a16_matmul_grouped(const void* x, const w4a16_matrix_t* mats, int n_mats, 
             return fail(W4A16_ERR_INVALID_ARG, "null pointer in matrix %d", i);
         int rc = check_gpu_shape(M, m.N, K, group_size);
         if (rc) return rc;
-        if (!aligned16(m.qweight) || !aligned16(m.scales) || !aligned16(m.zeros) || !aligned16(m.y))
+        if (!aligned16(m.qweight) || !aligned16(m.scales) || !aligned16(m.zeros) || !aligned16(m.y) ||
+            !aligned16(m.x))
             return fail(W4A16_ERR_ALIGNMENT, "device pointers of matrix %d must be 16-byte aligned", i);
         n_total += m.N;
     }
@@ -613,8 +615,8 @@ int w4a16_matmul_grouped(const void* x, const w4a16_matrix_t* mats, int n_mats, 
             if (rc) return rc;
         }
         for (int i = 0; i < n_mats; ++i) {
-            rc = matmul_impl(x, mats[i].qweight, mats[i].scales, mats[i].zeros, mats[i].y, M, mats[i].N, K,
-                             group_size, layout, stream, forced ? plan : nullptr);
+            rc = matmul_impl(mats[i].x ? mats[i].x : x, mats[i].qweight, mats[i].scales, mats[i].zeros, mats[i].y,
+                             M, mats[i].N, K, group_size, layout, stream, forced ? plan : nullptr);
             if (rc) return rc;
         }
         return ok();

@@ -26,10 +26,12 @@ inline bool group_supported(int64_t g) { return g == 32 || g == 64 || g == 128 |
 inline int log2_exact(int64_t v) { int r = 0; while ((int64_t(1) << r) < v) ++r; return r; }
 
 // One weight matrix of a skinny launch. A launch covers 1..kMaxGroupMats matrices that share
-// the activations x (and M, K, the group size, the layout and the plan); their column strips
-// are numbered one after the other: matrix i owns strips strip0 .. strip0 + ceil(N / cols) - 1.
-constexpr int kMaxGroupMats = 4;
+// M, K, the group size, the layout and the plan (each with its own activations x, which may
+// be the same buffer); their column strips are numbered one after the other: matrix i owns
+// strips strip0 .. strip0 + ceil(N / cols) - 1.
+constexpr int kMaxGroupMats = 16;
 struct SkinnyMatrix {
+    const uint16_t* x;        // fp16 [M, K]
     const uint32_t* qweight;  // int32 [K/8, N]
     const uint16_t* scales;   // fp16 [K/g, N]
     const uint16_t* zeros;    // fp16 [K/g, N]
@@ -38,8 +40,9 @@ struct SkinnyMatrix {
     int strip0;               // first strip of this matrix
 };
 
-struct SkinnyParams {
-    const uint16_t* x;        // fp16 [M, K]
+// The scalar arguments of a skinny launch.
+struct SkinnyHeader {
+    const uint16_t* x;        // fp16 [M, K] of a single-matrix launch (a grouped one reads mat[i].x)
     float* ws;                // fp32 partials [row_blocks][n_strips][splits][16*row_tiles][cols]
     uint32_t* counters;       // arrival counters [row_blocks][n_strips], zero between calls
     int M, K;
@@ -54,9 +57,16 @@ struct SkinnyParams {
     int gshift;               // log2(K-steps per scale/zero group): group of K-step ks = ks >> gshift
     int layout;               // W4A16_LAYOUT_*
     int n_mats;               // matrices in this launch (1 for w4a16_matmul)
-    // last, so that a single-matrix launch reads its arguments from one contiguous block
-    SkinnyMatrix mat[kMaxGroupMats];
 };
+
+// Kernel arguments with NM matrix slots: a single-matrix launch passes one slot (its
+// arguments stay one small contiguous block: a 16-slot table made every launch of the
+// 4096 x 4096 GEMV 0.15 us slower), a grouped launch the whole table.
+template <int NM>
+struct SkinnyArgs : SkinnyHeader {
+    SkinnyMatrix mat[NM];
+};
+typedef SkinnyArgs<kMaxGroupMats> SkinnyParams;   // as the host fills them
 
 // Workspace a skinny launch needs (bytes of partials, number of counters).
 inline void skinny_workspace(const SkinnyParams& p, uint64_t* ws_bytes, uint64_t* n_counters) {

@@ -250,10 +250,10 @@ __device__ __forceinline__ void partial_add(Row<LW>& r, __amdgpu_buffer_rsrc_t r
 // U = 8, K a multiple of 256, so every segment is exactly U K-steps inside whole groups and
 // the loop below needs no predicates. SG: min(U, K-steps per group). W: wavefronts per
 // work-group. NAT: the weights are packed in the interleaved layout (no activation permute).
-// GROUPED: the launch covers several matrices that share x (p.n_mats > 1).
+// GROUPED: the launch covers several matrices (p.n_mats > 1).
 // Dynamic LDS: (W - 1) * rows * CW floats, rows = min(16 * MT, M - row0).
 template <int MT, int LW, int U, int SG, int W, bool NAT, bool GROUPED>
-__global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
+__global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyArgs<GROUPED ? kMaxGroupMats : 1> p) {
     static_assert(U == 1 || U == 2 || U == 4 || U == 8, "segment of 1, 2, 4 or 8 K-steps");
     constexpr int CW = 16 * LW;
     extern __shared__ float red[];                  // [W - 1][rows][CW]
@@ -271,13 +271,11 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
     if (LW == 1 && b < ((p.n_strips * p.splits) & ~15)) b = (b & ~15) | ((b & 7) << 1) | ((b >> 3) & 1);
     const int strip = b % p.n_strips;
     const int split = b / p.n_strips;
-    // the matrix this strip belongs to (wave-uniform; a single matrix unless the launch
-    // groups several that share x)
-    // The matrix this strip belongs to. A single-matrix launch (GROUPED false) reads entry 0
-    // at constant offsets, in the same batch as the other arguments. A grouped launch reads
-    // the entries' first strips (one batch), picks the entry, then reads that entry: one
-    // more scalar round trip, where selecting among fully loaded entries compiled to a chain
-    // of dependent loads.
+    // The matrix this strip belongs to (wave-uniform). A single-matrix launch (GROUPED false)
+    // has one entry, read at constant offsets in the same batch as the other arguments. A
+    // grouped launch reads the entries' first strips (one batch), picks the entry, then reads
+    // that entry: one more scalar round trip, where selecting among fully loaded entries
+    // compiled to a chain of dependent loads.
     SkinnyMatrix mat;
     if constexpr (GROUPED) {
         int mi = 0;
@@ -310,7 +308,8 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
         const size_t w_rows = (size_t)(p.K / 8 - 4 * k0) * N * 4;
         st.w = __builtin_amdgcn_make_buffer_rsrc((void*)(mat.qweight + (size_t)4 * k0 * N), 0,
                                                  (int)min(w_rows, (size_t)0xffffffffu), kRsrcWord3);
-        st.x = __builtin_amdgcn_make_buffer_rsrc((void*)(p.x + (size_t)row0 * p.K + (size_t)k0 * kKStep), 0,
+        const uint16_t* x = GROUPED ? mat.x : p.x;
+        st.x = __builtin_amdgcn_make_buffer_rsrc((void*)(x + (size_t)row0 * p.K + (size_t)k0 * kKStep), 0,
                                                  (int)min(((size_t)(p.M - row0) * p.K - (size_t)k0 * kKStep) * 2, (size_t)0xffffffffu), kRsrcWord3);
         const int sz_bytes = (p.K >> (p.gshift + 5)) * N * 2;
         st.s = __builtin_amdgcn_make_buffer_rsrc((void*)mat.scales, 0, sz_bytes, kRsrcWord3);
@@ -488,14 +487,17 @@ hipError_t launch_one(const SkinnyParams& p, hipStream_t s) {
     const int rows = std::min(16 * MT, p.M);
     const size_t lds = (size_t)(W - 1) * rows * 16 * LW * sizeof(float);
     const bool nat = p.layout == W4A16_LAYOUT_INTERLEAVED, grouped = p.n_mats > 1;
+    SkinnyArgs<1> one;
+    static_cast<SkinnyHeader&>(one) = p;
+    one.mat[0] = p.mat[0];
     if (nat && grouped)
         hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, true, true>), grid, dim3(64 * W), lds, s, p);
     else if (nat)
-        hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, true, false>), grid, dim3(64 * W), lds, s, p);
+        hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, true, false>), grid, dim3(64 * W), lds, s, one);
     else if (grouped)
         hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, false, true>), grid, dim3(64 * W), lds, s, p);
     else
-        hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, false, false>), grid, dim3(64 * W), lds, s, p);
+        hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, false, false>), grid, dim3(64 * W), lds, s, one);
     return hipGetLastError();
 }
 
