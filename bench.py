@@ -1019,7 +1019,7 @@ def kernel_instance(plan, group=GROUP, nat=False):
     """Name of the decode-kernel instance a skinny plan launches (its template arguments)."""
     sg = min(plan["seg"], group // 32)
     return (f"skinny_kernel<{plan['row_tiles']}, {plan['cols'] // 16}, {plan['seg']}, {sg}, {plan['waves']}, "
-            f"{'true' if nat else 'false'}, false>")
+            f"{'true' if nat else 'false'}, 1>")
 
 
 def summarize_kernel_trace(dirs):

@@ -452,7 +452,7 @@ int launch_skinny_mats(const void* x, const w4a16_matrix_t* mats, int n_mats, in
         p.mat[i].zeros = static_cast<const uint16_t*>(m.zeros);
         p.mat[i].y = static_cast<uint16_t*>(m.y);
         p.mat[i].N = (int)m.N;
-        p.mat[i].strip0 = (int)strips;
+        p.mat[i].strip0 = p.strip0[i] = (int)strips;
         if (i < n_mats) strips += ceil_div(m.N, pl.cols);
     }
     p.M = (int)M;

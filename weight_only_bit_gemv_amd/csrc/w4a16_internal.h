@@ -59,12 +59,24 @@ struct SkinnyHeader {
     int n_mats;               // matrices in this launch (1 for w4a16_matmul)
 };
 
-// Kernel arguments with NM matrix slots: a single-matrix launch passes one slot (its
-// arguments stay one small contiguous block: a 16-slot table made every launch of the
-// 4096 x 4096 GEMV 0.15 us slower), a grouped launch the whole table.
-template <int NM>
+// Kernel arguments, by launch kind GM (each kind is its own kernel instance; sharing one
+// argument block between them measured slower per launch):
+//   GM = 1               a single matrix: one small contiguous block, x in the header (a
+//                        16-entry table made every 4096 x 4096 GEMV 0.15 us slower);
+//   GM = kSharedXMats    up to 4 matrices that share the header's x (q/k/v, gate/up);
+//   GM = kMaxGroupMats   up to 16 matrices, each with its own x (mixture-of-experts layers):
+//                        the entries' first strips side by side, then the table. Against
+//                        the 4-entry kind this costs 0.2 us (x from the entry) + 0.3 us (16
+//                        entries) per launch on q/k/v.
+constexpr int kSharedXMats = 4;
+template <int GM>
 struct SkinnyArgs : SkinnyHeader {
-    SkinnyMatrix mat[NM];
+    SkinnyMatrix mat[GM];
+};
+template <>
+struct SkinnyArgs<kMaxGroupMats> : SkinnyHeader {
+    int strip0[kMaxGroupMats];   // mat[i].strip0
+    SkinnyMatrix mat[kMaxGroupMats];
 };
 typedef SkinnyArgs<kMaxGroupMats> SkinnyParams;   // as the host fills them
 

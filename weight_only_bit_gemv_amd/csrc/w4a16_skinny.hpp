@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "w4a16_device.hpp"
 #include "w4a16_internal.h"
@@ -250,10 +251,11 @@ __device__ __forceinline__ void partial_add(Row<LW>& r, __amdgpu_buffer_rsrc_t r
 // U = 8, K a multiple of 256, so every segment is exactly U K-steps inside whole groups and
 // the loop below needs no predicates. SG: min(U, K-steps per group). W: wavefronts per
 // work-group. NAT: the weights are packed in the interleaved layout (no activation permute).
-// GROUPED: the launch covers several matrices (p.n_mats > 1).
+// GM: the launch kind (SkinnyArgs): 1 matrix, up to kSharedXMats sharing x, or up to
+// kMaxGroupMats each with its own x.
 // Dynamic LDS: (W - 1) * rows * CW floats, rows = min(16 * MT, M - row0).
-template <int MT, int LW, int U, int SG, int W, bool NAT, bool GROUPED>
-__global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyArgs<GROUPED ? kMaxGroupMats : 1> p) {
+template <int MT, int LW, int U, int SG, int W, bool NAT, int GM>
+__global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyArgs<GM> p) {
     static_assert(U == 1 || U == 2 || U == 4 || U == 8, "segment of 1, 2, 4 or 8 K-steps");
     constexpr int CW = 16 * LW;
     extern __shared__ float red[];                  // [W - 1][rows][CW]
@@ -271,23 +273,34 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyArgs<GROUPED ? kMa
     if (LW == 1 && b < ((p.n_strips * p.splits) & ~15)) b = (b & ~15) | ((b & 7) << 1) | ((b >> 3) & 1);
     const int strip = b % p.n_strips;
     const int split = b / p.n_strips;
-    // The matrix this strip belongs to (wave-uniform). A single-matrix launch (GROUPED false)
-    // has one entry, read at constant offsets in the same batch as the other arguments. A
-    // grouped launch reads the entries' first strips (one batch), picks the entry, then reads
-    // that entry: one more scalar round trip, where selecting among fully loaded entries
-    // compiled to a chain of dependent loads.
+    // The matrix this strip belongs to (wave-uniform), and its activations. A single-matrix
+    // launch has one entry, read at constant offsets in the same batch as the other
+    // arguments. A grouped launch reads the entries' first strips (one batch), picks the
+    // entry, then reads that entry: one more scalar round trip, where selecting among fully
+    // loaded entries compiled to a chain of dependent loads.
     SkinnyMatrix mat;
-    if constexpr (GROUPED) {
+    const uint16_t* x;
+    if constexpr (GM == kSharedXMats) {
         int mi = 0;
 #pragma unroll
-        for (int j = 1; j < kMaxGroupMats; ++j) {
+        for (int j = 1; j < GM; ++j) {
             int s0 = p.mat[j].strip0;
             asm volatile("" : "+s"(s0));
             mi = (j < p.n_mats && strip >= s0) ? j : mi;
         }
         mat = p.mat[mi];
+        x = p.x;
+    } else if constexpr (GM == kMaxGroupMats) {
+        // the starts increase with the entry, so the entry is the number of later entries
+        // (below n_mats) whose start the strip has reached
+        int mi = 0;
+#pragma unroll
+        for (int j = 1; j < GM; ++j) mi += (j < p.n_mats && strip >= p.strip0[j]) ? 1 : 0;
+        mat = p.mat[mi];
+        x = mat.x;
     } else {
         mat = p.mat[0];
+        x = p.x;
     }
     const int N = mat.N;
     const int row0 = blockIdx.y * 16 * MT;
@@ -308,7 +321,6 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyArgs<GROUPED ? kMa
         const size_t w_rows = (size_t)(p.K / 8 - 4 * k0) * N * 4;
         st.w = __builtin_amdgcn_make_buffer_rsrc((void*)(mat.qweight + (size_t)4 * k0 * N), 0,
                                                  (int)min(w_rows, (size_t)0xffffffffu), kRsrcWord3);
-        const uint16_t* x = GROUPED ? mat.x : p.x;
         st.x = __builtin_amdgcn_make_buffer_rsrc((void*)(x + (size_t)row0 * p.K + (size_t)k0 * kKStep), 0,
                                                  (int)min(((size_t)(p.M - row0) * p.K - (size_t)k0 * kKStep) * 2, (size_t)0xffffffffu), kRsrcWord3);
         const int sz_bytes = (p.K >> (p.gshift + 5)) * N * 2;
@@ -486,18 +498,27 @@ hipError_t launch_one(const SkinnyParams& p, hipStream_t s) {
     const dim3 grid((unsigned)(p.n_strips * p.splits), (unsigned)p.row_blocks);
     const int rows = std::min(16 * MT, p.M);
     const size_t lds = (size_t)(W - 1) * rows * 16 * LW * sizeof(float);
-    const bool nat = p.layout == W4A16_LAYOUT_INTERLEAVED, grouped = p.n_mats > 1;
-    SkinnyArgs<1> one;
-    static_cast<SkinnyHeader&>(one) = p;
-    one.mat[0] = p.mat[0];
-    if (nat && grouped)
-        hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, true, true>), grid, dim3(64 * W), lds, s, p);
-    else if (nat)
-        hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, true, false>), grid, dim3(64 * W), lds, s, one);
-    else if (grouped)
-        hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, false, true>), grid, dim3(64 * W), lds, s, p);
-    else
-        hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, false, false>), grid, dim3(64 * W), lds, s, one);
+    const bool nat = p.layout == W4A16_LAYOUT_INTERLEAVED;
+    // the launch kind: one matrix; up to kSharedXMats sharing the header's x; or the table
+    // with each matrix's own x
+    bool shared_x = p.n_mats <= kSharedXMats;
+    for (int i = 0; i < p.n_mats; ++i) shared_x = shared_x && p.mat[i].x == p.x;
+    if (p.n_mats == 1) {
+        SkinnyArgs<1> a;
+        static_cast<SkinnyHeader&>(a) = p;
+        a.mat[0] = p.mat[0];
+        if (nat) hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, true, 1>), grid, dim3(64 * W), lds, s, a);
+        else hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, false, 1>), grid, dim3(64 * W), lds, s, a);
+    } else if (shared_x) {
+        SkinnyArgs<kSharedXMats> a;
+        static_cast<SkinnyHeader&>(a) = p;
+        for (int i = 0; i < kSharedXMats; ++i) a.mat[i] = p.mat[i];
+        if (nat) hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, true, kSharedXMats>), grid, dim3(64 * W), lds, s, a);
+        else hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, false, kSharedXMats>), grid, dim3(64 * W), lds, s, a);
+    } else {
+        if (nat) hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, true, kMaxGroupMats>), grid, dim3(64 * W), lds, s, p);
+        else hipLaunchKernelGGL((skinny_kernel<MT, LW, U, SG, W, false, kMaxGroupMats>), grid, dim3(64 * W), lds, s, p);
+    }
     return hipGetLastError();
 }
 
