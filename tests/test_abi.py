@@ -303,9 +303,10 @@ def test_missing_library_fails_loudly(monkeypatch):
 
 
 def test_offsets_beyond_31_bits_are_rejected():
-    """The W4A8 kernel addresses 16 packed rows of weights (64 N bytes) and the split
-    partials of an output tile (128 KiB each, for W4A8 and the async W4A16 tile) with
-    32-bit offsets: shapes or split counts past that are rejected before any HIP call."""
+    """The W4A8 kernel addresses 16 packed rows of weights (64 N bytes), the async W4A16 tile
+    8 packed rows and 128 activation rows of a stage, and both the split partials of an
+    output tile (128 KiB each) with 32-bit offsets: shapes or split counts past that are
+    rejected before any HIP call."""
     so = B.load()
     pp = [P[0], P[1], ctypes.c_void_p(A + 0x6000), P[2], P[3], P[4], ctypes.c_void_p(A + 0x5000)]
     assert so.w4a8_matmul_ex(*pp, 1, 1 << 25, 128, 128, 0, 0, None) == lib.W4A16_ERR_UNSUPPORTED
@@ -315,6 +316,14 @@ def test_offsets_beyond_31_bits_are_rejected():
         lib.w4a16_plan(1, 8, 1 << 21, kernel=2, tile=3, splits=16384)
     assert e.value.code == lib.W4A16_ERR_UNSUPPORTED
     assert lib.w4a16_plan(1, 8, 1 << 21, kernel=2, tile=3, splits=16383)["splits"] <= 16383
+    # the async tile's loads: 32 N bytes of weights and 128 K 2 bytes of activations per stage
+    for M, N, K in [(8, (1 << 26) + 8, 128), (128, 8, 1 << 23)]:
+        with pytest.raises(lib.W4A16Error) as e:
+            lib.w4a16_plan(M, N, K, kernel=2, tile=3)
+        assert e.value.code == lib.W4A16_ERR_UNSUPPORTED
+        assert "load offsets" in B.load().w4a16_last_error_detail().decode()
+    assert lib.w4a16_plan(8, (1 << 26) - 8, 128, kernel=2, tile=3)["tile"] == 3
+    assert lib.w4a16_plan(128, 8, (1 << 23) - 128, kernel=2, tile=3)["tile"] == 3
 
 
 def test_binding_dequant_checks_scale_shapes():

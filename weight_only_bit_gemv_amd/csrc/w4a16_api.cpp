@@ -293,6 +293,11 @@ int complete_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, w4a16_pla
             return fail(W4A16_ERR_INVALID_ARG, "splits=%d leaves fewer than 2 stages of 64 K rows per split",
                         pl->splits);
         if (pl->tile == W4A16_TILE_ASYNC) {
+            // its loads address a stage with 32-bit byte offsets: up to 32 N (weights) and
+            // 128 K 2 (activations)
+            if ((int64_t)32 * N > INT32_MAX || (int64_t)128 * K * 2 > INT32_MAX)
+                return fail(W4A16_ERR_UNSUPPORTED, "N=%lld or K=%lld exceeds the async tile's 32-bit load offsets",
+                            (long long)N, (long long)K);
             if (pl->splits == 0) pl->splits = (int32_t)auto_prefill_splits(M, N, K);
             // the kernel addresses a tile's split partials (128 KiB each) with 32-bit offsets
             if ((int64_t)pl->splits * w4a16::kPrefillTileFloats * 4 > INT32_MAX)

@@ -91,20 +91,23 @@ __device__ __forceinline__ void stage_barrier() {
 // one chunk of 16 consecutive rows hit 16 different 16-byte bank groups.
 __device__ __forceinline__ int a_slot(int row, int ch) { return row * 8 + (ch ^ ((row >> 1) & 7)); }
 
-// 16 bytes per lane from global memory to LDS (wave-uniform LDS base in M0; the one wait
-// state between the M0 write and the LDS-DMA load is the s_nop).
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds_addr) : "memory");
+// 16 bytes per lane from global memory to LDS: source = wave-uniform base (scalar
+// registers) + the lane's 32-bit byte offset, destination = the wave-uniform LDS base in M0
+// (the one wait state between the M0 write and the LDS-DMA load is the s_nop). A stage moves
+// only the scalar base, so the loop carries no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_addr)
+                 : "memory");
 }
 
 // The same for the lanes in `lanes` only. EXEC is switched inside the one asm statement,
 // so the compiler sees straight-line code (a branch here would split the loop into blocks
 // across which it moves the dequantisation away from the MFMAs it should overlap).
-__device__ __forceinline__ void dma16_lanes(const void* gptr, uint32_t lds_addr, uint64_t lanes) {
+__device__ __forceinline__ void dma16_lanes(uint32_t voff, const void* sbase, uint32_t lds_addr, uint64_t lanes) {
     uint64_t saved;
-    asm volatile("s_mov_b64 %0, exec\n\ts_mov_b64 exec, %3\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-                 "global_load_lds_dwordx4 %1, off\n\ts_mov_b64 exec, %0"
-                 : "=&s"(saved) : "v"(gptr), "s"(lds_addr), "s"(lanes) : "memory");
+    asm volatile("s_mov_b64 %0, exec\n\ts_mov_b64 exec, %4\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, %2\n\ts_mov_b64 exec, %0"
+                 : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(lds_addr), "s"(lanes) : "memory");
 }
 
 // Half H of the fp16 (q - z) * s of one word, in natural K order: H = 0 dequantises the
@@ -154,38 +157,44 @@ __global__ __launch_bounds__(NT, 2) void prefill_async_kernel(PrefillParams p) {
     const int KT = min(p.stages_per_split, p.K / 64 - kbase);
     const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
-    // Per-lane sources of stage 0; stage kt adds a uniform offset. Instruction i of a
-    // wavefront fills chunks (4 i + wave) * 64 + lane of its region.
-    const uint16_t* a_src[NA];
+    // Per-lane byte offsets of the loads from the stage's wave-uniform bases (activations:
+    // row m0 of x at the stage's first K; weights: its first packed row; scales/zeros: its
+    // group's row). Instruction i of a wavefront fills chunks (4 i + wave) * 64 + lane of its
+    // region. The dispatcher keeps BM K 2 and 32 N below 2^31.
+    uint32_t a_off[NA];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
         const int c = (4 * i + wave) * 64 + lane;
         const int row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);   // inverse of a_slot
-        a_src[i] = p.x + (size_t)min(m0 + row, p.M - 1) * p.K + ch * 8;   // rows >= M: not stored
+        a_off[i] = (uint32_t)(((min(m0 + row, p.M - 1) - m0) * p.K + ch * 8) * 2);   // rows >= M: not stored
     }
-    const uint32_t* b_src[2];
+    uint32_t b_off[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int c = (4 * i + wave) * 64 + lane;
         const int col = n0 + 4 * (c & 63);
-        b_src[i] = p.qweight + (size_t)(c >> 6) * p.N + (col < p.N ? col : 0);   // columns >= N: not stored
+        b_off[i] = (uint32_t)(((c >> 6) * p.N + (col < p.N ? col : 0)) * 4);   // columns >= N: not stored
     }
     // scales/zeros: lane < kSzLanes loads chunk wave * kSzLanes + lane = group * 64 +
-    // (zeros ? 32 : 0) + 8-column chunk; N % 8 == 0, so a chunk never straddles the row end
+    // (zeros ? 32 : 0) + 8-column chunk; N % 8 == 0, so a chunk never straddles the row end.
+    // Group and array are uniform per wavefront.
     const int csz = wave * S::kSzLanes + lane;
-    const int sz_group = csz >> 6;                           // uniform per wavefront
+    const int sz_group = (wave * S::kSzLanes) >> 6;
     const int sz_col = n0 + (csz & 31) * 8;
-    const uint16_t* sz_src = ((csz >> 5) & 1 ? p.zeros : p.scales) + (sz_col < p.N ? sz_col : 0);
+    const uint32_t sz_off = (uint32_t)((sz_col < p.N ? sz_col : 0) * 2);
+    const uint16_t* sz_base = ((wave * S::kSzLanes) >> 5) & 1 ? p.zeros : p.scales;
+    const uint16_t* x_base = p.x + (size_t)m0 * p.K;
 
     auto issue = [&](int kt, int slot) {
         const uint32_t sb = lds_base + (uint32_t)(slot * S::kChunks) * 16u;
+        const uint16_t* xa = x_base + (size_t)kt * 64;
+        const uint32_t* wb = p.qweight + (size_t)kt * 8 * p.N;
 #pragma unroll
-        for (int i = 0; i < NA; ++i) dma16(a_src[i] + (size_t)kt * 64, sb + (uint32_t)((4 * i + wave) * 64) * 16u);
+        for (int i = 0; i < NA; ++i) dma16(a_off[i], xa, sb + (uint32_t)((4 * i + wave) * 64) * 16u);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            dma16(b_src[i] + (size_t)kt * 8 * p.N, sb + (uint32_t)(kAChunks + (4 * i + wave) * 64) * 16u);
+        for (int i = 0; i < 2; ++i) dma16(b_off[i], wb, sb + (uint32_t)(kAChunks + (4 * i + wave) * 64) * 16u);
         const size_t grp = G32 ? (size_t)(2 * kt + sz_group) : (size_t)((kt * 64) >> p.group_shift);
-        dma16_lanes(sz_src + grp * p.N, sb + (uint32_t)(kAChunks + kBChunks + wave * S::kSzLanes) * 16u,
+        dma16_lanes(sz_off, sz_base + grp * p.N, sb + (uint32_t)(kAChunks + kBChunks + wave * S::kSzLanes) * 16u,
                     (uint64_t(1) << S::kSzLanes) - 1);
     };
 
@@ -384,7 +393,8 @@ int launch_async(const PrefillParams& p, hipStream_t s) {
 int launch_prefill_async(const PrefillParams& p, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (p.N % 8 != 0 || p.splits < 1 || p.stages_per_split < 1 || (p.splits > 1 && (!p.ws || !p.counters)) ||
-        (p.bm != 32 && p.bm != 64 && p.bm != 128))
+        (p.bm != 32 && p.bm != 64 && p.bm != 128) || (int64_t)32 * p.N > INT32_MAX ||
+        (int64_t)p.bm * p.K * 2 > INT32_MAX)
         return (int)hipErrorInvalidValue;
     const bool g32 = p.group_shift == 5, nat = p.layout == W4A16_LAYOUT_INTERLEAVED;
 #define W4A16_ASYNC_BM(BM_)                                                                       \
