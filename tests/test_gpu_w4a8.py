@@ -113,20 +113,35 @@ def test_w4a8_formats(lib, M, K, N, g, sym):
     check_y(y, oracle.matmul_w4a8(xq, sx, qw, s, z, g), f"w4a8 g={g} sym={sym}")
 
 
-def test_w4a8_zero_points_anywhere_in_the_domain(lib):
+FAR_ZERO_CASES = [
+    # (M, K, N, forced splits (0: the library's), layout, group): every row-tile size (32, 64,
+    # 128 rows), M not a multiple of 4 (padded block sums), ragged N and split-K
+    (33, 512, 64, 0, "linear", 128),
+    (7, 1024, 136, 1, "linear", 128),
+    (150, 1024, 264, 4, "interleaved", 256),
+    (130, 512, 520, 1, "linear", 128),
+    (1, 2048, 72, 8, "interleaved", 128),
+]
+
+
+@pytest.mark.parametrize("M,K,N,splits,layout,g", FAR_ZERO_CASES)
+def test_w4a8_zero_points_anywhere_in_the_domain(lib, M, K, N, splits, layout, g):
     """Zero points anywhere in [-1024, 1024] (|q - z| up to 1039, far beyond what an 8-bit
-    weight operand holds): q - z stays exact, through the block sums."""
-    K, N, M = 512, 64, 33
-    rng = np.random.default_rng(4)
+    weight operand holds) next to ordinary ones: q - z stays exact, through the block sums,
+    with and without split-K."""
+    print(f"\n[w4a8 far zeros] M={M} K={K} N={N} splits={splits} {layout} g={g}", flush=True)
+    rng = np.random.default_rng((4, M, K, N))
     codes = rng.integers(0, 16, size=(K, N)).astype(np.uint8)
     zeros = rng.choice([-700.0, -449.0, -448.0, -300.0, -17.0, -5.0, -1.0, 8.0, 16.0, 17.0, 30.0, 463.0, 464.0,
-                        600.0, 1024.0], size=(K // 128, N)).astype(np.float16)
-    scales = (rng.random((K // 128, N)) * 2e-4 + 1e-5).astype(np.float16)
-    qw = oracle.pack(codes)
+                        600.0, 1024.0], size=(K // g, N)).astype(np.float16)
+    zeros[:, ::3] = 7.0                                     # whole wavefronts with no far zero point
+    scales = (rng.random((K // g, N)) * 2e-4 + 1e-5).astype(np.float16)
+    qw = oracle.pack(codes, layout=layout)
     x = synth.activations(M, K, wid=9)
     xq, sx = oracle.quantize_activations(x)
-    y = lib.w4a8_matmul(dev(xq), dev(sx), dev(block_sums(xq)), dev(qw), dev(scales), dev(zeros))
-    check_y(y, oracle.matmul_w4a8(xq, sx, qw, scales, zeros), "w4a8 far zero points")
+    y = lib.w4a8_matmul(dev(xq), dev(sx), dev(block_sums(xq)), dev(qw), dev(scales), dev(zeros), group_size=g,
+                        layout=layout, splits=splits)
+    check_y(y, oracle.matmul_w4a8(xq, sx, qw, scales, zeros, g, layout), "w4a8 far zero points")
 
 
 def test_w4a8_end_to_end_and_repeatable(lib):
