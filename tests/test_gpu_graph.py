@@ -1,4 +1,4 @@
-"""HIP graph capture of w4a16_matmul (needs an MI355X).
+"""HIP graph capture of w4a16_matmul, grouped launches and the W4A8 pair (needs an MI355X).
 
 A captured call is replayed several times, with eager calls of other shapes on the same
 stream between the replays (they take and release the same split-K arrival counters, and
@@ -108,3 +108,82 @@ def test_split_k_capture_without_workspace_fails_cleanly(lib):
     del g
     torch.cuda.synchronize()
     assert hip.hipStreamDestroy(handle) == 0
+
+
+def _replay_against_eager(g, outs, refs, between):
+    """Replay g four times, `between()` (eager calls on the capture stream) after each, and
+    check every output against the eager result bit for bit."""
+    for rep in range(4):
+        for y in outs:
+            y.fill_(7.0)                                         # a kernel, not a memset
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (y, r) in enumerate(zip(outs, refs)):
+            assert torch.equal(y.view(torch.int16), r.view(torch.int16)), f"replay {rep} output {i}"
+        between(rep)
+
+
+@pytest.mark.parametrize("own_x,plan", [(False, None), (True, dict(kernel=1, cols=16, kc=8, waves=4)),
+                                       (True, None)], ids=["shared-x", "own-x-split", "own-x"])
+def test_grouped_graph_replays_match_eager(lib, own_x, plan):
+    """A grouped launch (q/k/v-like with one x, or experts with their own) captured and
+    replayed, with a single-matrix split-K call and a grouped call of the other kind on the
+    stream between the replays."""
+    M, K, Ns = 2, 2048, ([1408] * 6 if own_x else [2048, 512, 512])
+    mats = [oracle.quantize_pack(synth.weight_custom(K, N, seed=90 + i, std=0.02)) for i, N in enumerate(Ns)]
+    xs = [dev(synth.activations(M, K, wid=30 + i)) for i in range(len(Ns))]
+    dmats = [(dev(q), dev(s), dev(z)) + ((xs[i],) if own_x else ()) for i, (q, s, z) in enumerate(mats)]
+    print(f"\n[graph grouped] own_x={own_x} N={Ns} plan={lib.w4a16_plan(M, sum(Ns), K, **(plan or {}))}",
+          flush=True)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        refs = [y.clone() for y in lib.w4a16_matmul_grouped(xs[0], dmats, plan=plan)]
+    st.synchronize()
+    outs = [torch.zeros_like(r) for r in refs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        lib.w4a16_matmul_grouped(xs[0], dmats, ys=outs, plan=plan)
+    other = _problem(4, 14336, 4096, seed=5)[4]
+    other_group = [d[:3] for d in dmats[:2]] if own_x else [d + (xs[1],) for d in dmats[:2]]
+
+    def between(rep):
+        with torch.cuda.stream(st):
+            if rep % 2 == 0:
+                lib.w4a16_matmul(*other)                             # decode split-K (4 splits)
+            else:
+                lib.w4a16_matmul_grouped(xs[0], other_group)
+        st.synchronize()
+    _replay_against_eager(g, outs, refs, between)
+
+
+def test_w4a8_graph_replays_match_eager(lib):
+    """The activation quantiser and a split-K W4A8 product captured together and replayed,
+    with other W4A8 calls on the stream between the replays."""
+    M, K, N = 100, 2048, 264
+    qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=44, std=0.02))
+    w = [dev(qw), dev(s), dev(z)]
+    x = dev(synth.activations(M, K, wid=8))
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        xq, sx, xsum = lib.w4a8_quantize(x)
+        ref = lib.w4a8_matmul(xq, sx, xsum, *w, splits=4).clone()
+    st.synchronize()
+    y = torch.zeros_like(ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        a, b, c = lib.w4a8_quantize(x)
+        lib.w4a8_matmul(a, b, c, *w, y=y, splits=4)
+    qw2, s2, z2 = oracle.quantize_pack(synth.weight_custom(4096, 1032, seed=45, std=0.02))
+    w2 = [dev(qw2), dev(s2), dev(z2)]
+    x2 = dev(synth.activations(7, 4096, wid=8))
+
+    def between(rep):
+        with torch.cuda.stream(st):
+            q3, s3, c3 = lib.w4a8_quantize(x2)
+            lib.w4a8_matmul(q3, s3, c3, *w2, splits=8 if rep % 2 else 1)
+        st.synchronize()
+    _replay_against_eager(g, [y], [ref], between)
+    # the captured quantiser's outputs too
+    assert torch.equal(a, xq) and torch.equal(b.view(torch.int32), sx.view(torch.int32))
+    assert torch.equal(c.view(torch.int32), xsum.view(torch.int32))

@@ -64,3 +64,36 @@ def test_noalloc_matches_allocating_entry_point(lib, name, calls):
         lib.w4a16_matmul_noalloc(*args, y2, plan=plan, layout=layout)
         torch.cuda.synchronize()
         assert torch.equal(y2.view(torch.int16), y.view(torch.int16)), name
+
+
+def test_noalloc_under_graph_capture(lib):
+    """The callers it is for: a split-K call captured in a HIP graph (the first call on the
+    device, which takes the scratch address and clears its counters, happens eagerly before)
+    and replayed four times, with eager no-alloc calls of other shapes (sharing the scratch)
+    on the stream between the replays; every replay gives the eager call's bits."""
+    M, K, N = 4, 14336, 4096
+    qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=66, std=0.02))
+    args = [dev(synth.activations(M, K, wid=11)), dev(qw), dev(s), dev(z)]
+    assert lib.w4a16_plan(M, N, K)["splits"] > 1
+    q2, s2, z2 = oracle.quantize_pack(synth.weight_custom(4096, 1032, seed=67, std=0.02))
+    other = [dev(synth.activations(130, 4096, wid=11)), dev(q2), dev(s2), dev(z2)]
+    print(f"\n[noalloc graph] M={M} K={K} N={N} plan={lib.w4a16_plan(M, N, K)}", flush=True)
+    st = torch.cuda.Stream()
+    ref = torch.empty((M, N), dtype=torch.float16, device=DEV)
+    y_other = torch.empty((130, 1032), dtype=torch.float16, device=DEV)
+    with torch.cuda.stream(st):
+        lib.w4a16_matmul_noalloc(*args, ref)
+    st.synchronize()
+    y = torch.zeros_like(ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        lib.w4a16_matmul_noalloc(*args, y)
+    for rep in range(4):
+        y.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
+        with torch.cuda.stream(st):
+            lib.w4a16_matmul_noalloc(*other, y_other, plan=dict(kernel=2, tile=3, splits=2 + rep))
+        st.synchronize()
