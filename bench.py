@@ -23,10 +23,13 @@ Other workloads (same JSON keys, config.workload names them):
 Printed: one JSON line. `value` is the algorithmic byte rate (int4 weights + fp16
 scales/zeros + fp16 x + fp16 y) of one step over the median of up to 5 timed batches (the
 K steps split into batches of graph replays, each between HIP events; the minimum is
-reported too), in GB/s. `roofline` relates the average launch to the 8 TB/s HBM peak (MFMA
-peak for prefill), gives the fraction of the measured read ceiling (w4a16_read_probe at each
-call's byte count, same timing) and, from the committed kernel-trace summary of the same
-sources, the dominant kernel instance's own rate; `grouped` times q/k/v and gate/up as one
+reported too), in GB/s. `roofline` is the dominant kernel's line (the decode-kernel instance
+with the most time per step): algorithmic bytes per launch over its average launch time,
+each of its calls graph-timed with HIP events on the launch stream, against the 8 TB/s HBM
+peak (MFMA peak for prefill), its fraction of the measured read ceiling (w4a16_read_probe
+at each call's byte count, same timing), its HBM traffic per launch from the committed
+counter summary, and, from the committed kernel-trace summary of the same sources, its
+kernel-only rate; `roofline.step` gives the same for the whole step (all kernels); `grouped` times q/k/v and gate/up as one
 grouped launch against one launch per matrix (decode_sweep), or the active experts' gate/up
 (one shared x) and down projections (each its own x) of mixture-of-experts layers
 (moe_expert); `cpu_baseline` times the oracle (NumPy, fp64)
@@ -435,15 +438,18 @@ def cpu_baseline(runner, wid, min_s=10.0, max_passes=40):
                        f"on {blas_threads} threads of {len(os.sched_getaffinity(0))} available")}
 
 
-def load_traffic():
-    """Measured HBM bytes per launch from the committed PMC summary, if it was taken on the
-    current kernel source (else None)."""
+def load_traffic(kernel=None):
+    """Measured HBM bytes per launch from the committed PMC summary (of one decode-kernel
+    instance, or the mean over the sweep's launches), if it was taken on the current kernel
+    sources and plans (else None)."""
     try:
         d = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     if d.get("kernel_source_sha") != decode_kernel_hash():
         return None
+    if kernel is not None:
+        return d.get("per_kernel", {}).get(kernel, {}).get("traffic_bytes_per_launch")
     return d.get("traffic_bytes_per_launch")
 
 
@@ -708,18 +714,54 @@ def run_decode(args):
             r["read_ceiling_us"] = round(ceil_s[b] * 1e6, 3)
             r["frac_of_read_ceiling"] = round(ceil_s[b] / (r["us"] / 1e6), 4)
     achieved = runner.step_bytes / launches / avg_launch_s / 1e9
-    roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": (load_traffic() if args.workload == "decode_sweep" and args.group_size == GROUP
-                        and not args.symmetric and args.layout == "linear" else None),
-            "kernel": "skinny_kernel (decode weight stream, MFMA, split-K when K is deep)",
-            "achieved_is": ("algorithmic bytes per launch / (median step time / launches): whole-step rate, "
-                            "the gap between graph nodes included"),
-            "avg_launch_us": round(avg_launch_s * 1e6, 3)}
+    measured_plans = args.workload == "decode_sweep" and args.group_size == GROUP and not args.symmetric \
+        and args.layout == "linear"
+    # the dominant kernel: the decode-kernel instance with the most time per step, from the
+    # per-shape graph-timed calls (HIP events on the launch stream; every shape appears once
+    # per step)
+    inst = {}
+    for r in per:
+        if r["plan"]["kernel"] != lib.W4A16_KERNEL_SKINNY:
+            continue
+        name = kernel_instance(r["plan"], args.group_size, args.layout == "interleaved")
+        g = inst.setdefault(name, {"calls": 0, "us": 0.0, "bytes": 0})
+        g["calls"] += 1
+        g["us"] += r["us"]
+        g["bytes"] += alg_bytes(r["M"], r["K"], r["N"], args.group_size)
+    if inst:
+        dom_name, dom = max(inst.items(), key=lambda kv: kv[1]["us"])
+        dom_gbs = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(dom_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                "traffic": load_traffic(dom_name) if measured_plans else None,
+                "kernel": dom_name,
+                "achieved_is": (f"the dominant kernel ({dom['calls']} of {launches} calls per step, "
+                                f"{round(dom['us'] / sum(g['us'] for g in inst.values()), 3)} of the calls' time): "
+                                "algorithmic bytes per launch / its average launch time, each call graph-timed "
+                                "with HIP events on the launch stream (the gap between graph nodes included)"),
+                "avg_launch_us": round(dom["us"] / dom["calls"], 3),
+                "alg_bytes_per_launch": round(dom["bytes"] / dom["calls"]),
+                "step": {"achieved": round(achieved, 2), "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "avg_launch_us": round(avg_launch_s * 1e6, 3),
+                         "traffic": load_traffic() if measured_plans else None,
+                         "is": "algorithmic bytes per launch / (median step time / launches), all kernels"}}
+    else:
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "skinny_kernel (decode weight stream, MFMA, split-K when K is deep)",
+                "achieved_is": ("algorithmic bytes per launch / (median step time / launches): whole-step rate, "
+                                "the gap between graph nodes included"),
+                "avg_launch_us": round(avg_launch_s * 1e6, 3)}
     if ceil_s:
         read_step = sum(ceil_s[alg_bytes(M, K, N, args.group_size)] for (M, K, N, _) in items)
-        roof["read_ceiling_GBps"] = round(runner.step_bytes / read_step / 1e9, 1)
-        roof["frac_of_read_ceiling"] = round(read_step / t_med, 4)
+        step = roof.get("step", roof)
+        step["read_ceiling_GBps"] = round(runner.step_bytes / read_step / 1e9, 1)
+        step["frac_of_read_ceiling"] = round(read_step / t_med, 4)
+        if inst:   # the dominant kernel's calls against plain reads of the same byte counts
+            rows = [r for r in per if r["plan"]["kernel"] == lib.W4A16_KERNEL_SKINNY and
+                    kernel_instance(r["plan"], args.group_size, args.layout == "interleaved") == roof["kernel"]]
+            roof["frac_of_read_ceiling"] = round(sum(r["read_ceiling_us"] for r in rows) /
+                                                 sum(r["us"] for r in rows), 4)
     kt = load_kernel_trace() if (args.workload == "decode_sweep" and args.group_size == GROUP and
                                  not args.symmetric and args.layout == "linear") else None
     if kt:
@@ -1002,11 +1044,28 @@ def summarize_pmc(dirs):
     launches = len(SWEEP_M) * len(SWEEP_KN)
     alg = sum(alg_bytes(M, K, N) for (K, N) in SWEEP_KN for M in SWEEP_M) / launches
     traffic = out["FETCH_SIZE"]["kernel_bytes_mean"] + out["WRITE_SIZE"]["kernel_bytes_mean"]
+    # per decode-kernel instance: the mean per dispatch over its own calls (every sweep call
+    # is launched equally often), against the mean algorithmic bytes of those calls
+    import weight_only_bit_gemv_amd as lib
+    per_kernel = {}
+    for (K, N) in SWEEP_KN:
+        for M in SWEEP_M:
+            inst = kernel_instance(lib.w4a16_plan(M, N, K))
+            per_kernel.setdefault(inst, {"alg": []})["alg"].append(alg_bytes(M, K, N))
+    for inst, d in per_kernel.items():
+        t = 0.0
+        for name in ("FETCH_SIZE", "WRITE_SIZE"):
+            ks = [v for _, k, v in vals[name] if inst in k]
+            t += float(np.mean(ks)) * 1024 * out[name]["scale"]
+        a = float(np.mean(d.pop("alg")))
+        d.update({"traffic_bytes_per_launch": round(t), "algorithmic_bytes_per_launch": round(a),
+                  "traffic_over_algorithmic": round(t / a, 4)})
     summary = {"kernel_source_sha": decode_kernel_hash(),
                "workload": "decode_sweep (15 shapes), mean over dispatches",
                "traffic_bytes_per_launch": round(traffic),
                "algorithmic_bytes_per_launch": round(alg),
                "traffic_over_algorithmic": round(traffic / alg, 4),
+               "per_kernel": per_kernel,
                "counters": out}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
@@ -1160,9 +1219,15 @@ def summarize_records(paths):
             lines.append("")
             continue
         roof = res["roofline"]
-        lines.append(f"value {res['value']} GB/s ({roof['frac']} of 8 TB/s), median step {res['ms_per_step']} ms, "
-                     f"min {res.get('step_ms_min')} ms; read ceiling {roof.get('read_ceiling_GBps')} GB/s "
-                     f"(fraction {roof.get('frac_of_read_ceiling')}); device copy {res['measured_copy_GBps']} GB/s.")
+        step = roof.get("step", roof)
+        lines.append(f"value {res['value']} GB/s ({step['frac']} of 8 TB/s), median step {res['ms_per_step']} ms, "
+                     f"min {res.get('step_ms_min')} ms; read ceiling {step.get('read_ceiling_GBps')} GB/s "
+                     f"(fraction {step.get('frac_of_read_ceiling')}); device copy {res['measured_copy_GBps']} GB/s.")
+        if "step" in roof:
+            lines.append(f"Roofline line (dominant kernel `{roof['kernel']}`, graph-timed calls): "
+                         f"{roof['achieved']} GB/s = {roof['frac']} of 8 TB/s, {roof['avg_launch_us']} us per launch "
+                         f"on {roof['alg_bytes_per_launch']} B; {roof.get('frac_of_read_ceiling')} of the read ceiling; "
+                         f"HBM traffic {roof.get('traffic')} B per launch (counters).")
         if "dominant_kernel" in roof:
             dk = roof["dominant_kernel"]
             lines.append(f"Dominant kernel `{dk['name']}`: {dk['avg_ns']} ns per launch on {dk['alg_bytes_per_launch']} B, "
