@@ -60,7 +60,9 @@ int check_gpu_shape(int64_t M, int64_t N, int64_t K, int64_t group_size) {
 // shape and cache the winner: "Things I got wrong along the way" on the Triton W4A16 page):
 // kTuned holds, for the projection shapes of the decode, MoE-expert and prefill workloads,
 // the fastest plan of a sweep of cols x waves x kc x seg on MI355X (graph-timed launches
-// after a clock warm-up, weights rotated over 600 MB), per M bucket: an entry covers M up to m_max and above the
+// after a clock warm-up, weights rotated over 600 MB), per M bucket (the decode-sweep and
+// MoE shapes re-swept on the current kernel, 180-243 plans each; entries marked re-swept
+// won an alternating A/B against the earlier plan): an entry covers M up to m_max and above the
 // previous entry's m_max. Other shapes take the rule the table follows for most shapes:
 // 64-column strips for wide or deep matrices, 16 otherwise (32 past M = 32); 4 wavefronts;
 // each wavefront streams 32 K-steps (fewer when K is short, so that one work-group covers
@@ -72,22 +74,22 @@ struct TunedPlan {
 
 const TunedPlan kTuned[] = {
     //  K       N      m_max cols waves kc seg      time of the plan in the sweep
-    {  768,   2048,  1, 16,  8,  4, 4},   // 2.84 us
+    {  768,   2048,  1, 16,  4,  8, 4},   // 2.93 us (re-swept: 2.98 us before)
     {  768,   2048,  4, 16,  4,  8, 4},   // 3.11 us
     {  768,   2048, 16, 16,  4,  8, 4},   // 3.41 us
     { 1408,   2048,  1, 16, 16,  4, 4},   // 3.32 us
     { 1408,   2048,  4, 16,  8,  8, 4},   // 3.74 us
-    { 1408,   2048, 16, 16,  4, 16, 4},   // 4.16 us
+    { 1408,   2048, 16, 16,  4, 12, 4},   // 4.20 us (re-swept: 4.32 us before)
     { 2048,    768,  1, 16,  8,  8, 4},   // 3.08 us
-    { 2048,    768,  4, 16,  4, 16, 4},   // 3.55 us
-    { 2048,    768, 16, 16,  4, 16, 4},   // 4.39 us
+    { 2048,    768,  4, 16,  8,  8, 4},   // 3.94 us (re-swept: 4.09 us before)
+    { 2048,    768, 16, 16,  4, 24, 8},   // 4.80 us (re-swept: 4.90 us before)
     { 2048,   1408,  1, 16,  8,  8, 4},   // 3.41 us
-    { 2048,   1408,  4, 16,  8,  8, 4},   // 3.95 us
-    { 2048,   1408, 16, 16,  4, 16, 4},   // 4.78 us
+    { 2048,   1408,  4, 16,  4, 16, 8},   // 3.92 us (re-swept: 4.07 us before)
+    { 2048,   1408, 16, 16,  4, 24, 8},   // 4.88 us (re-swept: 4.93 us before)
     { 4096,   4096,  1, 16, 16,  8, 4},   // 4.88 us
     { 4096,   4096,  2, 16, 16,  8, 4},   // 5.18 us
     { 4096,   4096,  4, 16,  8, 16, 4},   // 5.72 us
-    { 4096,   4096,  8, 16,  8, 16, 4},   // 6.19 us
+    { 4096,   4096,  8, 16,  4, 32, 4},   // 6.00 us (re-swept: 6.13 us before)
     { 4096,   4096, 16, 16,  4, 32, 4},   // 7.22 us
     { 4096,   4096, 32, 64,  4,  8, 2},   // 9.71 us (4 splits)
     { 4096,   4096, 64, 32,  4, 48, 4},   // 11.79 us
