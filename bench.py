@@ -13,6 +13,7 @@ eager run.
 
 Other workloads (same JSON keys, config.workload names them):
   gemv_4096     one M=1, 4096 x 4096 GEMV
+  gemv_lm_head  one M=1, 4096 x 128256 GEMV (the 7B-shaped chain's lm_head, 279 MB)
   moe_expert    M in {1,4,16} on (2048,1408), (1408,2048), (2048,768), (768,2048)
   chain_7b      batch-1 decode weight stream of a 32-layer 7B-shaped model + lm_head:
                 225 GEMVs per token in one graph (one layer's weights packed once and
@@ -467,6 +468,11 @@ def workload_items(name):
     if name == "gemv_4096":
         fam = {(4096, 4096): (4096, 4096, 0, 0)}
         return fam, [(1, 4096, 4096, (4096, 4096))], "gemv_4096: M=1, K=N=4096, group 128", None
+    if name == "gemv_lm_head":
+        _, K, N = synth.CHAIN_7B_LM_HEAD
+        fam = {(K, N): (K, N, synth.WORKLOADS["decode_chain_7b"]["wid"], 100)}
+        return fam, [(1, K, N, (K, N))], ("gemv_lm_head: M=1, K=4096, N=128256 (the lm_head of the 7B-shaped "
+                                          "chain, 279 MB per call), group 128"), None
     if name == "moe_expert":
         wid = synth.WORKLOADS[name]["wid"]
         kns = [(2048, 1408), (1408, 2048), (2048, 768), (768, 2048)]
@@ -1265,7 +1271,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_sweep",
-                    choices=["decode_sweep", "gemv_4096", "moe_expert", "chain_7b", "prefill"])
+                    choices=["decode_sweep", "gemv_4096", "gemv_lm_head", "moe_expert", "chain_7b", "prefill"])
     ap.add_argument("--group-size", type=int, default=GROUP, choices=[32, 64, 128, 256],
                     help="K rows per scale/zero group (decode workloads)")
     ap.add_argument("--symmetric", action="store_true",
