@@ -2,7 +2,8 @@
 
     python -m weight_only_bit_gemv_amd.build        (or __graft_entry__.build())
 
-Output: weight_only_bit_gemv_amd/lib/libw4a16.so. Objects go to weight_only_bit_gemv_amd/_build/.
+Output: weight_only_bit_gemv_amd/lib/libw4a16.so (and lib/w4a16_capi_driver, a test program
+that calls the library through its C ABI only). Objects go to weight_only_bit_gemv_amd/_build/.
 """
 import os
 import shutil
@@ -17,6 +18,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libw4a16.so")
+# a test program that drives the library through the C ABI alone (tests/test_gpu_capi.py)
+CAPI_DRIVER_SRC = os.path.join(ROOT, "tests", "capi", "capi_driver.cpp")
+CAPI_DRIVER = os.path.join(LIBDIR, "w4a16_capi_driver")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
@@ -78,6 +82,11 @@ def build(verbose=False):
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs +
          ["-lpthread"])
     os.replace(tmp, LIB)
+    if os.path.exists(CAPI_DRIVER_SRC):
+        tmp = CAPI_DRIVER + ".tmp"
+        _run([hipcc, "-O2", "-std=c++17", "-I", INCLUDE, CAPI_DRIVER_SRC, "-o", tmp, "-L", LIBDIR, "-lw4a16",
+              "-Wl,-rpath,$ORIGIN"])
+        os.replace(tmp, CAPI_DRIVER)
     return LIB
 
 
