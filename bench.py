@@ -569,10 +569,11 @@ class GroupedChain:
         self.lm[0].launch(self.lm[1])
 
 
-def grouped_timing(torch, lib, dev, stream, label, mats, own_x, ms, wid, group=GROUP, layout="linear"):
+def grouped_timing(torch, lib, dev, stream, label, mats, own_x, ms, wid, group=GROUP, layout="linear", rows=None):
     """One grouped launch (w4a16_matmul_grouped) over the matrices `mats` = [(K, N, seed), ...]
     (same K) against one launch per matrix, at each M in `ms`, weights rotated over 1 GiB.
-    own_x: every matrix reads its own activations (x_i) instead of one shared x."""
+    own_x: every matrix reads its own activations (x_i) instead of one shared x. rows: each
+    matrix's own row count M_i (then ms is (max rows,), and x_i has M_i rows)."""
     B = lib._binding
     so = lib.load()
     lay = B._layout_id(layout)
@@ -586,16 +587,17 @@ def grouped_timing(torch, lib, dev, stream, label, mats, own_x, ms, wid, group=G
     ring = [one] + [[[t.clone() for t in m] for m in one] for _ in range(max(1, -(-ROTATE_BYTES // per)) - 1)]
     out = []
     for M in ms:
+        Ms = rows or [M] * len(mats)
         x = torch.from_numpy(synth.activations(M, K, wid=wid)).to(dev)
-        xs = [torch.from_numpy(synth.activations(M, K, wid=wid + 1 + i)).to(dev) if own_x else x
+        xs = [torch.from_numpy(synth.activations(Ms[i], K, wid=wid + 1 + i)).to(dev) if own_x else x
               for i in range(len(mats))]
-        ys = [torch.empty((M, N), dtype=torch.float16, device=dev) for N in Ns]
+        ys = [torch.empty((m, N), dtype=torch.float16, device=dev) for m, N in zip(Ms, Ns)]
         arrs = []
         for ms_ in ring:
             arr = (B.w4a16_matrix_t * len(mats))()
             for i, ((q, s_, z_), y) in enumerate(zip(ms_, ys)):
                 arr[i] = B.w4a16_matrix_t(q.data_ptr(), s_.data_ptr(), z_.data_ptr(), y.data_ptr(), Ns[i],
-                                          xs[i].data_ptr() if own_x else None)
+                                          xs[i].data_ptr() if own_x else None, Ms[i])
             arrs.append(arr)
 
         def grouped():
@@ -605,14 +607,14 @@ def grouped_timing(torch, lib, dev, stream, label, mats, own_x, ms, wid, group=G
 
         def separate():
             for ms_ in ring:
-                for (q, s_, z_), y, xi in zip(ms_, ys, xs):
+                for (q, s_, z_), y, xi, m in zip(ms_, ys, xs, Ms):
                     if so.w4a16_matmul_fmt(xi.data_ptr(), q.data_ptr(), s_.data_ptr(), z_.data_ptr(), y.data_ptr(),
-                                           M, q.shape[1], K, group, lay, stream.cuda_stream, None):
+                                           m, q.shape[1], K, group, lay, stream.cuda_stream, None):
                         raise RuntimeError("w4a16_matmul_fmt failed")
         tg = time_graph(torch, stream, grouped, 5)[0] / len(ring)
         ts = time_graph(torch, stream, separate, 5)[0] / len(ring)
-        b = sum(alg_bytes(M, K, N, group) for N in Ns)
-        out.append({"matrices": label, "M": M, "K": K, "N": Ns, "own_x": own_x, "bytes": b,
+        b = sum(alg_bytes(m, K, N, group) for m, N in zip(Ms, Ns))
+        out.append({"matrices": label, "M": M if rows is None else Ms, "K": K, "N": Ns, "own_x": own_x, "bytes": b,
                     "grouped_us": round(tg * 1e6, 3), "grouped_GBps": round(b / tg / 1e9, 1),
                     "grouped_frac_hbm": round(b / tg / 1e9 / HBM_PEAK_GBS, 4),
                     "separate_launches_us": round(ts * 1e6, 3), "speedup": round(ts / tg, 3),
@@ -650,6 +652,16 @@ def grouped_experts(torch, lib, dev, stream, group=GROUP, layout="linear"):
                               wid, group, layout)
         out += grouped_timing(torch, lib, dev, stream, f"{E} experts down ({E} x {F}x2048, own x)", down, True, (1,),
                               wid, group, layout)
+    # a batch of 16 tokens, each routed to 2 of 8 experts (seeded): the down projections of
+    # the experts, each over its own tokens (M_e rows), in one launch
+    rng = np.random.default_rng((7, 16, 8))
+    picks = np.array([rng.choice(8, size=2, replace=False) for _ in range(16)])
+    counts = [int(c) for c in np.bincount(picks.ravel(), minlength=8)]
+    active = [e for e in range(8) if counts[e] > 0]
+    down = [(1408, 2048, 300 + e) for e in active]
+    out += grouped_timing(torch, lib, dev, stream, f"16 tokens top-2 of 8 experts, down ({len(active)} x 1408x2048, "
+                          f"tokens per expert {[counts[e] for e in active]})", down, True,
+                          (max(counts),), wid, group, layout, rows=[counts[e] for e in active])
     return out
 
 

@@ -223,23 +223,25 @@ int w4a16_matmul_fmt(const void* x, const int32_t* qweight, const void* scales,
 
 /*
  * w4a16_matrix_t - one weight matrix of a grouped product (w4a16_matmul_grouped): device
- * pointers in the layouts above, N its output columns (N >= 4, N % 4 == 0), and the
- * activations it multiplies: x NULL for the call's x, or its own fp16 [M, K] (16-byte
- * aligned), as for the experts of a mixture-of-experts layer, whose down projections each
- * read their own input.
+ * pointers in the layouts above, N its output columns (N >= 4, N % 4 == 0), the activations
+ * it multiplies (x NULL for the call's x, or its own fp16 [M_i, K], 16-byte aligned) and
+ * their row count M_i (0 for the call's M; otherwise 1..M): the experts of a
+ * mixture-of-experts layer, whose down projections each read their own input, and which at
+ * a batch of several tokens each see their own number of tokens.
  */
 typedef struct w4a16_matrix {
     const int32_t* qweight;   /* int32 [K/8, N] */
     const void* scales;       /* fp16 [K/g, N]  */
     const void* zeros;        /* fp16 [K/g, N]  */
-    void* y;                  /* fp16 [M, N], fully overwritten */
+    void* y;                  /* fp16 [M_i, N], fully overwritten */
     int64_t N;
-    const void* x;            /* fp16 [M, K], or NULL: the call's x */
+    const void* x;            /* fp16 [M_i, K], or NULL: the call's x (its first M_i rows) */
+    int64_t M;                /* M_i, or 0: the call's M */
 } w4a16_matrix_t;
 
 /*
  * w4a16_matmul_grouped - y_i = x_i . dequant(W_i) for 1..16 weight matrices with the same
- * M, K, group size and layout, in one launch of the decode kernel: the projections that read
+ * K, group size and layout and M_i <= M rows each, in one launch of the decode kernel: the projections that read
  * one input, such as the query, key and value projections of an attention layer or the gate
  * and up projections of an FFN or of the active experts of a mixture-of-experts layer (x_i
  * = x), and the experts' down projections (each its own x_i). "Beating FP16 with 4-bit
@@ -248,17 +250,18 @@ typedef struct w4a16_matrix {
  * launch overhead among the costs of a decode step: one launch over the matrices' combined
  * columns pays the per-launch cost once and gives the chip more work-groups.
  *   x        device fp16 [M, K], 16-byte aligned: the activations of every matrix whose x is
- *            NULL (non-NULL even when every matrix has its own)
+ *            NULL (non-NULL even when every matrix has its own); M the largest M_i (the
+ *            plan is made for it)
  *   mats     host array of n_mats w4a16_matrix_t (read during the call only)
  *   n_mats   1..16
  *   plan     NULL or a forced plan. The plan is chosen (or completed) for M, the summed N and
  *            K; when it selects the decode kernel (W4A16_KERNEL_SKINNY) one launch covers
  *            every matrix with that plan, and each y_i is bitwise equal to
- *            w4a16_matmul_fmt(x_i, W_i, ...) under the same plan. When it selects the prefill
+ *            w4a16_matmul_fmt(x_i, W_i, M_i, ...) under the same plan. When it selects the prefill
  *            kernel, each matrix is launched on its own (with the forced plan, or with the
  *            dispatcher's plan for its shape), as the prefill tiles fill the chip per matrix.
  * Asynchronous on `stream`; split-K uses the stream's workspace as w4a16_matmul does.
- * Errors: INVALID_ARG (null pointers, n_mats, layout, plan), UNSUPPORTED (a matrix's shape,
+ * Errors: INVALID_ARG (null pointers, n_mats, layout, plan, M_i outside 0..M), UNSUPPORTED (a matrix's shape,
  * or the summed N, outside what w4a16_matmul accepts), ALIGNMENT, HIP; all found before any
  * launch except HIP errors of a later matrix when the prefill kernel is launched per matrix.
  */

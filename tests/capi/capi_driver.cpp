@@ -132,7 +132,7 @@ int main(int argc, char** argv) {
     check(w4a16_matmul(dx, dqw, ds, dz, dy, M, N, K, G, st), "w4a16_matmul");
     check(w4a16_matmul_noalloc(dx, dqw, ds, dz, dy_na, M, N, K, G, W4A16_LAYOUT_LINEAR, st, nullptr),
           "w4a16_matmul_noalloc");
-    const w4a16_matrix_t mats[2] = {{dqw, ds, dz, dy_g0, N, nullptr}, {dqw, ds, dz, dy_g1, N, dxneg}};
+    const w4a16_matrix_t mats[2] = {{dqw, ds, dz, dy_g0, N, nullptr, 0}, {dqw, ds, dz, dy_g1, N, dxneg, 0}};
     check(w4a16_matmul_grouped(dx, mats, 2, M, K, G, W4A16_LAYOUT_LINEAR, st, nullptr), "w4a16_matmul_grouped");
 
     // an argument error is reported before anything is enqueued

@@ -178,13 +178,17 @@ static void device_call_errors() {
            W4A16_ERR_INVALID_ARG, "noalloc null qweight");
     w4a16_matrix_t gm[17];
     for (int i = 0; i < 17; ++i)
-        gm[i] = w4a16_matrix_t{(const int32_t*)p[1], p[2], p[3], p[4], 64, nullptr};
+        gm[i] = w4a16_matrix_t{(const int32_t*)p[1], p[2], p[3], p[4], 64, nullptr, 0};
     expect(w4a16_matmul_grouped(p[0], gm, 17, 1, 4096, 128, 0, nullptr, nullptr), W4A16_ERR_INVALID_ARG,
            "grouped 17 matrices");
     gm[1].x = mis;
     expect(w4a16_matmul_grouped(p[0], gm, 3, 1, 4096, 128, 0, nullptr, nullptr), W4A16_ERR_ALIGNMENT,
            "grouped misaligned own x");
     gm[1].x = p[0];
+    gm[2].M = 2;                                        // more rows than the call's M = 1
+    expect(w4a16_matmul_grouped(p[0], gm, 3, 1, 4096, 128, 0, nullptr, nullptr), W4A16_ERR_INVALID_ARG,
+           "grouped M_i > M");
+    gm[2].M = 0;
     expect(w4a16_matmul_grouped(p[0], gm, 0, 1, 4096, 128, 0, nullptr, nullptr), W4A16_ERR_INVALID_ARG,
            "grouped 0 matrices");
     gm[2].N = 62;

@@ -371,6 +371,8 @@ def test_grouped_rejects_bad_arguments():
     assert call(mats(64), n=0) == lib.W4A16_ERR_INVALID_ARG
     assert call(mats(*[64] * 17)) == lib.W4A16_ERR_INVALID_ARG                      # at most 16
     assert call(mats(64, 64, bad=(1, "x", A + 0x4008))) == lib.W4A16_ERR_ALIGNMENT  # a matrix's own x
+    assert call(mats(64, 64, bad=(1, "M", 2))) == lib.W4A16_ERR_INVALID_ARG         # M_i > M
+    assert call(mats(64, 64, bad=(1, "M", -1))) == lib.W4A16_ERR_INVALID_ARG
     assert call(mats(64, 64), x=None) == lib.W4A16_ERR_INVALID_ARG
     assert call(mats(64, 64, bad=(1, "zeros", None))) == lib.W4A16_ERR_INVALID_ARG
     assert call(mats(64, 62)) == lib.W4A16_ERR_UNSUPPORTED                         # N % 4

@@ -144,3 +144,41 @@ def test_grouped_experts_with_their_own_inputs(lib, name, M, K, N, E, own, g, la
         y_ref = oracle.matmul(xi, q, s, z, g, layout=layout)
         err = np.abs(y.cpu().numpy().astype(np.float64) - y_ref)
         assert np.all(err <= 1e-2 + 5e-3 * np.abs(y_ref)), (name, i, err.max())
+
+
+# experts that each see their own number of tokens (a batch routed over the active experts)
+ROW_CASES = [
+    # (name, K, N, rows per matrix, group, layout, forced plan)
+    ("tokens-16-over-8", 2048, 1408, [3, 1, 5, 2, 16, 1, 4, 2], 128, "linear", None),
+    ("rows-split", 4096, 520, [40, 7, 17, 1, 33], 64, "interleaved", dict(kernel=1, cols=16, kc=8, waves=4)),
+    ("rows-two-row-tiles", 1024, 264, [64, 20, 1, 47], 128, "linear", dict(kernel=1, cols=32, kc=8, waves=4,
+                                                                            row_tiles=2)),
+    ("rows-prefill", 1024, 264, [200, 64, 130], 128, "linear", None),
+]
+
+
+@pytest.mark.parametrize("name,K,N,rows,g,layout,plan", ROW_CASES, ids=[c[0] for c in ROW_CASES])
+def test_grouped_matrices_with_their_own_row_counts(lib, name, K, N, rows, g, layout, plan):
+    """Each matrix with its own x of M_i <= M rows (M = the largest): y_i has M_i rows, equal
+    bit for bit to a single call on (x_i, W_i) under the grouped call's plan (decode kernel)
+    and within the oracle's bar."""
+    M = max(rows)
+    mats = _inputs(name, K, [N] * len(rows), g, layout)
+    xs = [synth.activations(m, K, wid=40 + i) for i, m in enumerate(rows)]
+    big = [i for i, m in enumerate(rows) if m == M][0]
+    pl = lib.w4a16_plan(M, N * len(rows), K, group_size=g, **(plan or {}))
+    print(f"\n[grouped-rows] {name} rows={rows} K={K} N={N} plan={pl}", flush=True)
+    dxs = [dev(x) for x in xs]
+    dmats = [(dev(q), dev(s), dev(z), dxs[i]) for i, (q, s, z) in enumerate(mats)]
+    ys = lib.w4a16_matmul_grouped(dxs[big], dmats, group_size=g, plan=plan, layout=layout)
+    torch.cuda.synchronize()
+    for i, ((q, s, z), y) in enumerate(zip(mats, ys)):
+        assert tuple(y.shape) == (rows[i], N)
+        if pl["kernel"] == 1:
+            single = lib.w4a16_matmul(dxs[i], *dmats[i][:3], group_size=g, layout=layout,
+                                      plan={k: v for k, v in pl.items() if k != "tile"})
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), single.view(torch.int16)), (name, i)
+        y_ref = oracle.matmul(xs[i], q, s, z, g, layout=layout)
+        err = np.abs(y.cpu().numpy().astype(np.float64) - y_ref)
+        assert np.all(err <= 1e-2 + 5e-3 * np.abs(y_ref)), (name, i, err.max())

@@ -50,7 +50,7 @@ class w4a16_plan_t(ctypes.Structure):
 
 class w4a16_matrix_t(ctypes.Structure):
     _fields_ = [("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p),
-                ("y", ctypes.c_void_p), ("N", ctypes.c_int64), ("x", ctypes.c_void_p)]
+                ("y", ctypes.c_void_p), ("N", ctypes.c_int64), ("x", ctypes.c_void_p), ("M", ctypes.c_int64)]
 
 
 MAX_GROUP_MATS = 16
@@ -262,8 +262,9 @@ def w4a16_matmul(x, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, strea
 
 def w4a16_matmul_grouped(x, weights, ys=None, group_size=GROUP_SIZE, stream=None, plan=None, layout="linear"):
     """y_i = x_i . dequant(W_i) for the matrices in `weights` (a list of (qweight, scales, zeros)
-    or (qweight, scales, zeros, x_i), 1..16 of them; x_i defaults to x) in one call of
-    w4a16_matmul_grouped; returns the list of y_i (allocated when `ys` is None)."""
+    or (qweight, scales, zeros, x_i), 1..16 of them; x_i defaults to x; an x_i of M_i <= M rows
+    gives y_i of M_i rows) in one call of w4a16_matmul_grouped; returns the list of y_i
+    (allocated when `ys` is None)."""
     import torch
     if x.dim() != 2:
         raise ValueError("x must be 2-D")
@@ -271,22 +272,23 @@ def w4a16_matmul_grouped(x, weights, ys=None, group_size=GROUP_SIZE, stream=None
     if not 1 <= len(weights) <= MAX_GROUP_MATS:
         raise ValueError(f"1..{MAX_GROUP_MATS} weight matrices")
     weights = [tuple(w) if len(w) == 4 else tuple(w) + (None,) for w in weights]
+    rows = [M if w[3] is None else w[3].shape[0] for w in weights]
     if ys is None:
-        ys = [torch.empty((M, w[0].shape[1]), dtype=torch.float16, device=x.device) for w in weights]
+        ys = [torch.empty((m, w[0].shape[1]), dtype=torch.float16, device=x.device) for m, w in zip(rows, weights)]
     arr = (w4a16_matrix_t * len(weights))()
-    for i, ((qw, s, z, xi), y) in enumerate(zip(weights, ys)):
-        if xi is not None and xi.shape != (M, K):
-            raise ValueError(f"matrix {i}: its x must be [M, K] = [{M}, {K}]")
+    for i, ((qw, s, z, xi), y, Mi) in enumerate(zip(weights, ys, rows)):
+        if xi is not None and (xi.dim() != 2 or xi.shape[1] != K or not 1 <= Mi <= M):
+            raise ValueError(f"matrix {i}: its x must be [M_i, K] with 1 <= M_i <= M = {M}, K = {K}")
         N = qw.shape[1]
         if qw.dim() != 2 or qw.shape[0] * 8 != K:
             raise ValueError(f"matrix {i}: qweight must be [K/8, N] with K={K}")
         if scales_shape_bad(s, z, K, N, group_size):
             raise ValueError(f"matrix {i}: scales/zeros must be [K/group_size, N]")
-        if y.shape != (M, N):
-            raise ValueError(f"matrix {i}: y must be [M, N]")
+        if y.shape != (Mi, N):
+            raise ValueError(f"matrix {i}: y must be [M_i, N]")
         arr[i] = w4a16_matrix_t(_dev_ptr(qw, "qweight", torch.int32), _dev_ptr(s, "scales", torch.float16),
                                 _dev_ptr(z, "zeros", torch.float16), _dev_ptr(y, "y", torch.float16), N,
-                                None if xi is None else _dev_ptr(xi, "x", torch.float16))
+                                None if xi is None else _dev_ptr(xi, "x", torch.float16), Mi)
     pl = ctypes.byref(_make_plan(plan)) if plan is not None else None
     rc = load().w4a16_matmul_grouped(_dev_ptr(x, "x", torch.float16), arr, len(weights), M, K, group_size,
                                      _layout_id(layout), _stream_ptr(stream, x.device), pl)

@@ -454,6 +454,7 @@ int launch_skinny_mats(const void* x, const w4a16_matrix_t* mats, int n_mats, in
     for (int i = 0; i < w4a16::kMaxGroupMats; ++i) {
         const w4a16_matrix_t& m = mats[std::min(i, n_mats - 1)];       // unused entries repeat the last
         p.mat[i].x = static_cast<const uint16_t*>(m.x ? m.x : x);
+        p.rows[i] = (int)(m.M ? m.M : M);
         p.mat[i].qweight = reinterpret_cast<const uint32_t*>(m.qweight);
         p.mat[i].scales = static_cast<const uint16_t*>(m.scales);
         p.mat[i].zeros = static_cast<const uint16_t*>(m.zeros);
@@ -528,7 +529,7 @@ int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const
         return ok();
     }
 
-    const w4a16_matrix_t one{qweight, scales, zeros, y, N, nullptr};
+    const w4a16_matrix_t one{qweight, scales, zeros, y, N, nullptr, 0};
     return launch_skinny_mats(x, &one, 1, M, K, group_size, layout, stream, pl, noalloc);
 }
 
@@ -605,6 +606,9 @@ int w4a16_matmul_grouped(const void* x, const w4a16_matrix_t* mats, int n_mats, 
         if (!aligned16(m.qweight) || !aligned16(m.scales) || !aligned16(m.zeros) || !aligned16(m.y) ||
             !aligned16(m.x))
             return fail(W4A16_ERR_ALIGNMENT, "device pointers of matrix %d must be 16-byte aligned", i);
+        if (m.M < 0 || m.M > M)
+            return fail(W4A16_ERR_INVALID_ARG, "matrix %d: M=%lld must lie in 0..M (%lld; 0: M)", i, (long long)m.M,
+                        (long long)M);
         n_total += m.N;
     }
     int rc = check_gpu_shape(M, n_total, K, group_size);
@@ -623,7 +627,8 @@ int w4a16_matmul_grouped(const void* x, const w4a16_matrix_t* mats, int n_mats, 
         }
         for (int i = 0; i < n_mats; ++i) {
             rc = matmul_impl(mats[i].x ? mats[i].x : x, mats[i].qweight, mats[i].scales, mats[i].zeros, mats[i].y,
-                             M, mats[i].N, K, group_size, layout, stream, forced ? plan : nullptr);
+                             mats[i].M ? mats[i].M : M, mats[i].N, K, group_size, layout, stream,
+                             forced ? plan : nullptr);
             if (rc) return rc;
         }
         return ok();

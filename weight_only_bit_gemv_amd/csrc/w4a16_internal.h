@@ -64,7 +64,8 @@ struct SkinnyHeader {
 //   GM = 1               a single matrix: one small contiguous block, x in the header (a
 //                        16-entry table made every 4096 x 4096 GEMV 0.15 us slower);
 //   GM = kSharedXMats    up to 4 matrices that share the header's x (q/k/v, gate/up);
-//   GM = kMaxGroupMats   up to 16 matrices, each with its own x (mixture-of-experts layers):
+//   GM = kMaxGroupMats   up to 16 matrices, each with its own x and row count (mixture-of-experts
+//                        layers):
 //                        the entries' first strips side by side, then the table. Against
 //                        the 4-entry kind this costs 0.2 us (x from the entry) + 0.3 us (16
 //                        entries) per launch on q/k/v.
@@ -76,6 +77,7 @@ struct SkinnyArgs : SkinnyHeader {
 template <>
 struct SkinnyArgs<kMaxGroupMats> : SkinnyHeader {
     int strip0[kMaxGroupMats];   // mat[i].strip0
+    int rows[kMaxGroupMats];     // rows of matrix i's x and y (<= M; the grid covers M)
     SkinnyMatrix mat[kMaxGroupMats];
 };
 typedef SkinnyArgs<kMaxGroupMats> SkinnyParams;   // as the host fills them

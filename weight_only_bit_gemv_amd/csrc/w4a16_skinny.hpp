@@ -280,6 +280,7 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyArgs<GM> p) {
     // loaded entries compiled to a chain of dependent loads.
     SkinnyMatrix mat;
     const uint16_t* x;
+    int mrows = p.M;                     // rows of this matrix's x and y
     if constexpr (GM == kSharedXMats) {
         int mi = 0;
 #pragma unroll
@@ -298,13 +299,18 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyArgs<GM> p) {
         for (int j = 1; j < GM; ++j) mi += (j < p.n_mats && strip >= p.strip0[j]) ? 1 : 0;
         mat = p.mat[mi];
         x = mat.x;
+        mrows = p.rows[mi];
     } else {
         mat = p.mat[0];
         x = p.x;
     }
     const int N = mat.N;
     const int row0 = blockIdx.y * 16 * MT;
-    const int rows = min(16 * MT, p.M - row0);          // valid output rows of this work-group
+    const int rows = min(16 * MT, mrows - row0);        // valid output rows of this work-group
+    // a matrix with fewer rows than the launch has none in this block: nothing to load or
+    // store (every work-group of the block and strip returns here, so its split-K counter
+    // is never taken)
+    if (GM == kMaxGroupMats && rows <= 0) return;
     const int n = (strip - mat.strip0) * CW + lc * LW;
     const bool col_ok = n < N;
     const int nl = col_ok ? n : 0;       // loads stay in bounds; results of such lanes are dropped
@@ -322,7 +328,7 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyArgs<GM> p) {
         st.w = __builtin_amdgcn_make_buffer_rsrc((void*)(mat.qweight + (size_t)4 * k0 * N), 0,
                                                  (int)min(w_rows, (size_t)0xffffffffu), kRsrcWord3);
         st.x = __builtin_amdgcn_make_buffer_rsrc((void*)(x + (size_t)row0 * p.K + (size_t)k0 * kKStep), 0,
-                                                 (int)min(((size_t)(p.M - row0) * p.K - (size_t)k0 * kKStep) * 2, (size_t)0xffffffffu), kRsrcWord3);
+                                                 (int)min(((size_t)(mrows - row0) * p.K - (size_t)k0 * kKStep) * 2, (size_t)0xffffffffu), kRsrcWord3);
         const int sz_bytes = (p.K >> (p.gshift + 5)) * N * 2;
         st.s = __builtin_amdgcn_make_buffer_rsrc((void*)mat.scales, 0, sz_bytes, kRsrcWord3);
         st.z = __builtin_amdgcn_make_buffer_rsrc((void*)mat.zeros, 0, sz_bytes, kRsrcWord3);
@@ -335,7 +341,7 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyArgs<GM> p) {
     // waits for every outstanding load at the branch's end).
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-        st.x_lane[mt] = ((min(row0 + mt * 16 + lc, p.M - 1) - row0) * p.K + lg * 8) * 2;
+        st.x_lane[mt] = ((min(row0 + mt * 16 + lc, mrows - 1) - row0) * p.K + lg * 8) * 2;
     st.sz_lane = nl * 2;
     st.sz_step = N * 2;
     st.gshift = p.gshift;
@@ -499,11 +505,11 @@ hipError_t launch_one(const SkinnyParams& p, hipStream_t s) {
     const int rows = std::min(16 * MT, p.M);
     const size_t lds = (size_t)(W - 1) * rows * 16 * LW * sizeof(float);
     const bool nat = p.layout == W4A16_LAYOUT_INTERLEAVED;
-    // the launch kind: one matrix; up to kSharedXMats sharing the header's x; or the table
-    // with each matrix's own x
+    // the launch kind: one matrix; up to kSharedXMats sharing the header's x (and M); or the
+    // table with each matrix's own x and row count
     bool shared_x = p.n_mats <= kSharedXMats;
-    for (int i = 0; i < p.n_mats; ++i) shared_x = shared_x && p.mat[i].x == p.x;
-    if (p.n_mats == 1) {
+    for (int i = 0; i < p.n_mats; ++i) shared_x = shared_x && p.mat[i].x == p.x && p.rows[i] == p.M;
+    if (p.n_mats == 1 && shared_x) {
         SkinnyArgs<1> a;
         static_cast<SkinnyHeader&>(a) = p;
         a.mat[0] = p.mat[0];
