@@ -117,7 +117,9 @@ def test_dequant_rejects_bad_arguments():
 
 PLAN_SHAPES = [(m, k, n) for m in (1, 2, 4, 8, 16, 17, 23, 24, 33, 48, 49, 63, 64, 65, 96, 97, 128, 129, 512, 2048)
                for (k, n) in [(4096, 4096), (4096, 14336), (14336, 4096), (2048, 1408), (8192, 28672),
-                              (768, 2048), (4096, 128256), (128, 4), (384, 100), (4096, 28676)]]
+                              (768, 2048), (4096, 128256), (128, 4), (384, 100), (4096, 28676),
+                              (4096, 1024), (5120, 5120), (13824, 5120), (3584, 18944), (7168, 1024),
+                              (2560, 10240), (3072, 3072), (896, 4864)]]
 
 
 @pytest.mark.parametrize("M,K,N", PLAN_SHAPES)

@@ -182,6 +182,31 @@ def test_chain_lm_head_sampled(lib):
     check_y(y[:, torch.from_numpy(cols).to(DEV)], y_ref, "lm_head")
 
 
+# Projection shapes of other common decoder configurations, each with a plan of its own in
+# the dispatcher's table (narrow key/value projections; 11008-, 13824- and 18944-wide
+# feed-forward layers; their transposes): full-size launches with the plan the dispatcher
+# picks for one M of each of its buckets (1, 2..4, 5..16; ragged M pads the MFMA rows),
+# checked on sampled columns. Two shapes outside the table exercise the rule for the others.
+DECODER_KN = [(4096, 512), (4096, 1024), (5120, 1024), (8192, 1024), (16384, 1024), (2048, 512),
+              (2048, 2048), (4096, 2048), (8192, 2048), (1024, 4096), (6144, 4096), (8192, 4096),
+              (11008, 4096), (4096, 6144), (4096, 8192), (2048, 8192), (5120, 5120), (13824, 5120),
+              (18944, 3584), (4096, 11008), (5120, 13824), (3584, 18944),
+              (7168, 1024), (2560, 10240)]
+DECODER_SHAPES = [(m, k, n) for (k, n) in DECODER_KN for m in (1, 3, 11)]
+
+
+@pytest.mark.parametrize("M,K,N", DECODER_SHAPES, ids=[f"M{m}-K{k}-N{n}" for m, k, n in DECODER_SHAPES])
+def test_matmul_decoder_shapes_sampled(lib, M, K, N):
+    wid = synth.WORKLOADS["decode_chain_7b"]["wid"]
+    print(f"\n[matmul] decoder M={M} K={K} N={N} plan={lib.w4a16_plan(M, N, K)}", flush=True)
+    qw, s, z = quantised(K, N, wid)
+    x = synth.activations(M, K, wid=wid)
+    y = run(lib, x, qw, s, z)
+    cols = _sample_cols(N)
+    y_ref = oracle.matmul(x, qw[:, cols], s[:, cols], z[:, cols])
+    check_y(y[:, torch.from_numpy(cols).to(DEV)], y_ref, f"decoder M={M} K={K} N={N}")
+
+
 # ---------------------------------------------------------------------------------------
 # ragged edges, every plan, determinism, streams, overwrite
 

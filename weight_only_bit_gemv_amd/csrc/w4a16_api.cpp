@@ -62,11 +62,23 @@ int check_gpu_shape(int64_t M, int64_t N, int64_t K, int64_t group_size) {
 // the fastest plan of a sweep of cols x waves x kc x seg on MI355X (graph-timed launches
 // after a clock warm-up, weights rotated over 600 MB), per M bucket (the decode-sweep and
 // MoE shapes re-swept on the current kernel, 180-243 plans each; entries marked re-swept
-// won an alternating A/B against the earlier plan): an entry covers M up to m_max and above the
-// previous entry's m_max. Other shapes take the rule the table follows for most shapes:
-// 64-column strips for wide or deep matrices, 16 otherwise (32 past M = 32); 4 wavefronts;
-// each wavefront streams 32 K-steps (fewer when K is short, so that one work-group covers
-// K), and longer K is split over work-groups.
+// won an alternating A/B against the earlier plan), and for the projections of 34 other
+// decoder shapes (K and N from 512 to 18944: narrow key/value projections, 4864- to
+// 18944-wide feed-forward layers and their transposes; 72 plans each at 4-step segments, the
+// earlier rule's plan timed beside them): an entry covers M up to m_max and above the
+// previous entry's m_max. Other shapes take a rule fitted to those sweeps, for M <= 16 (on
+// those 34 shapes its plans are on average 3 % (K <= 4096) and 9 % (deeper K) slower than
+// each shape's best, against 8 % and 25 % for the rule before it; fitted on half of the
+// shapes, it is 2-5 % and 9-12 % slower on the other half):
+//  * K <= 4096: one work-group covers K, at M = 1 with 16 wavefronts (K = 4096), 8 (K = 2048
+//    to 4095) or 4 (shorter K), at larger M with 4; strips of 16 columns up to N = 4096, 32
+//    up to 8192, 64 beyond;
+//  * deeper K: 12 K-steps per wavefront and 8 wavefronts at M = 1, 16 K-steps and 4
+//    wavefronts above, K split over work-groups; strips of 16 columns up to N = 1024, 32 up
+//    to 4096, 64 beyond.
+// Past M = 16, where no sweep of the rule was made, the earlier rule stays: 64-column strips
+// for wide or deep matrices, 16 otherwise (32 past M = 32), 4 wavefronts, 32 K-steps per
+// wavefront (fewer when K is short, so that one work-group covers K).
 struct TunedPlan {
     int32_t K, N, m_max;
     int8_t cols, waves, kc, seg;
@@ -77,15 +89,57 @@ const TunedPlan kTuned[] = {
     {  768,   2048,  1, 16,  4,  8, 4},   // 2.93 us (re-swept: 2.98 us before)
     {  768,   2048,  4, 16,  4,  8, 4},   // 3.11 us
     {  768,   2048, 16, 16,  4,  8, 4},   // 3.41 us
+    {  896,   4864,  1, 32,  4,  8, 4},   // 3.47 us (earlier rule for other shapes: 3.48 us)
+    {  896,   4864,  4, 32,  4,  8, 4},   // 3.72 us (earlier rule for other shapes: 3.72 us)
+    {  896,   4864, 16, 32,  4,  8, 4},   // 3.94 us (earlier rule for other shapes: 3.94 us)
+    { 1024,   4096,  1, 16,  4,  8, 4},   // 3.07 us (earlier rule for other shapes: 3.08 us)
+    { 1024,   4096,  4, 16,  4,  8, 4},   // 3.40 us (earlier rule for other shapes: 3.40 us)
+    { 1024,   4096, 16, 16,  4,  8, 4},   // 3.85 us (earlier rule for other shapes: 3.86 us)
     { 1408,   2048,  1, 16, 16,  4, 4},   // 3.32 us
     { 1408,   2048,  4, 16,  8,  8, 4},   // 3.74 us
     { 1408,   2048, 16, 16,  4, 12, 4},   // 4.20 us (re-swept: 4.32 us before)
+    { 1536,   8960,  1, 64,  4, 12, 4},   // 4.63 us (earlier rule for other shapes: 4.63 us)
+    { 1536,   8960,  4, 64,  4, 12, 4},   // 5.09 us (earlier rule for other shapes: 5.14 us)
+    { 1536,   8960, 16, 64,  4, 12, 4},   // 5.47 us (earlier rule for other shapes: 5.48 us)
+    { 2048,    512,  1, 16,  8,  8, 4},   // 3.47 us (earlier rule for other shapes: 3.74 us)
+    { 2048,    512,  4, 16,  8,  8, 4},   // 3.91 us (earlier rule for other shapes: 4.04 us)
+    { 2048,    512, 16, 16,  4, 16, 4},   // 4.76 us (earlier rule for other shapes: 4.76 us)
     { 2048,    768,  1, 16,  8,  8, 4},   // 3.08 us
     { 2048,    768,  4, 16,  8,  8, 4},   // 3.94 us (re-swept: 4.09 us before)
     { 2048,    768, 16, 16,  4, 24, 8},   // 4.80 us (re-swept: 4.90 us before)
     { 2048,   1408,  1, 16,  8,  8, 4},   // 3.41 us
     { 2048,   1408,  4, 16,  4, 16, 8},   // 3.92 us (re-swept: 4.07 us before)
     { 2048,   1408, 16, 16,  4, 24, 8},   // 4.88 us (re-swept: 4.93 us before)
+    { 2048,   2048,  1, 16,  8,  8, 4},   // 3.57 us (earlier rule for other shapes: 3.86 us)
+    { 2048,   2048,  4, 16,  8,  8, 4},   // 4.07 us (earlier rule for other shapes: 4.19 us)
+    { 2048,   2048, 16, 16,  4, 16, 4},   // 4.88 us (earlier rule for other shapes: 4.88 us)
+    { 2048,   8192,  1, 32, 16,  4, 4},   // 4.58 us (earlier rule for other shapes: 5.37 us)
+    { 2048,   8192,  4, 32,  8,  8, 4},   // 5.02 us (earlier rule for other shapes: 5.76 us)
+    { 2048,   8192, 16, 32,  8,  8, 4},   // 5.62 us (earlier rule for other shapes: 6.21 us)
+    { 2560,  10240,  1, 64,  4, 20, 4},   // 6.10 us (earlier rule for other shapes: 6.10 us)
+    { 2560,  10240,  4, 64,  4, 20, 4},   // 6.45 us (earlier rule for other shapes: 6.45 us)
+    { 2560,  10240, 16, 64,  4, 20, 4},   // 7.46 us (earlier rule for other shapes: 7.46 us)
+    { 3072,   3072,  1, 16, 16,  8, 4},   // 4.23 us (earlier rule for other shapes: 5.47 us)
+    { 3072,   3072,  4, 16,  8, 12, 4},   // 4.79 us (earlier rule for other shapes: 5.74 us)
+    { 3072,   3072, 16, 16,  4, 24, 4},   // 6.03 us (earlier rule for other shapes: 6.56 us)
+    { 3072,   8192,  1, 32,  8, 12, 4},   // 5.51 us (earlier rule for other shapes: 5.81 us)
+    { 3072,   8192,  4, 32,  8, 12, 4},   // 5.98 us (earlier rule for other shapes: 6.04 us)
+    { 3072,   8192, 16, 32,  4, 24, 4},   // 6.82 us (earlier rule for other shapes: 6.82 us)
+    { 3584,  18944,  1, 64,  4,  8, 4},   // 11.13 us (earlier rule for other shapes: 11.74 us)
+    { 3584,  18944,  4, 64,  4,  8, 4},   // 11.54 us (earlier rule for other shapes: 12.34 us)
+    { 3584,  18944, 16, 64,  4,  8, 4},   // 13.27 us (earlier rule for other shapes: 14.85 us)
+    { 4096,    512,  1, 16, 16,  8, 4},   // 4.49 us (earlier rule for other shapes: 5.23 us)
+    { 4096,    512,  4, 16,  4,  8, 4},   // 5.03 us (earlier rule for other shapes: 5.54 us)
+    { 4096,    512, 16, 16,  4,  8, 4},   // 5.57 us (earlier rule for other shapes: 6.88 us)
+    { 4096,   1024,  1, 16, 16,  8, 4},   // 4.57 us (earlier rule for other shapes: 5.28 us)
+    { 4096,   1024,  4, 16,  8, 16, 4},   // 5.35 us (earlier rule for other shapes: 5.57 us)
+    { 4096,   1024, 16, 32,  4,  8, 4},   // 6.00 us (earlier rule for other shapes: 6.90 us)
+    { 4096,   2048,  1, 16, 16,  8, 4},   // 4.71 us (earlier rule for other shapes: 5.42 us)
+    { 4096,   2048,  4, 16,  8, 16, 4},   // 5.43 us (earlier rule for other shapes: 5.73 us)
+    { 4096,   2048, 16, 32,  4, 12, 4},   // 6.54 us (earlier rule for other shapes: 6.97 us)
+    { 4096,   3072,  1, 16, 16,  8, 4},   // 4.78 us (earlier rule for other shapes: 6.40 us)
+    { 4096,   3072,  4, 16,  8, 16, 4},   // 5.53 us (earlier rule for other shapes: 6.63 us)
+    { 4096,   3072, 16, 32,  4,  8, 4},   // 6.98 us (earlier rule for other shapes: 7.74 us)
     { 4096,   4096,  1, 16, 16,  8, 4},   // 4.88 us
     { 4096,   4096,  2, 16, 16,  8, 4},   // 5.18 us
     { 4096,   4096,  4, 16,  8, 16, 4},   // 5.72 us
@@ -93,6 +147,15 @@ const TunedPlan kTuned[] = {
     { 4096,   4096, 16, 16,  4, 32, 4},   // 7.22 us
     { 4096,   4096, 32, 64,  4,  8, 2},   // 9.71 us (4 splits)
     { 4096,   4096, 64, 32,  4, 48, 4},   // 11.79 us
+    { 4096,   6144,  1, 32, 16,  8, 4},   // 6.23 us (earlier rule for other shapes: 7.36 us)
+    { 4096,   6144,  4, 32,  4, 32, 4},   // 6.88 us (earlier rule for other shapes: 8.25 us)
+    { 4096,   6144, 16, 32,  4, 32, 4},   // 8.13 us (earlier rule for other shapes: 11.59 us)
+    { 4096,   8192,  1, 32, 16,  8, 4},   // 6.43 us (earlier rule for other shapes: 7.71 us)
+    { 4096,   8192,  4, 32,  4, 32, 4},   // 6.93 us (earlier rule for other shapes: 8.04 us)
+    { 4096,   8192, 16, 32,  4, 32, 4},   // 8.03 us (earlier rule for other shapes: 9.01 us)
+    { 4096,  11008,  1, 64, 16,  8, 4},   // 7.82 us (earlier rule for other shapes: 8.02 us)
+    { 4096,  11008,  4, 64,  4, 32, 4},   // 8.38 us (earlier rule for other shapes: 8.40 us)
+    { 4096,  11008, 16, 64,  4, 32, 4},   // 9.76 us (earlier rule for other shapes: 9.76 us)
     { 4096,  12288,  1, 64, 16,  8, 4},   // 8.28 us (q, k, v of 4096 x 4096 in one grouped launch)
     { 4096,  14336,  1, 64,  4, 32, 4},   // 9.01 us
     { 4096,  14336,  2, 64,  4, 32, 4},   // 9.13 us
@@ -102,6 +165,36 @@ const TunedPlan kTuned[] = {
     { 4096,  14336, 32, 64,  4, 32, 4},   // 14.79 us
     { 4096,  14336, 64, 64,  4, 48, 4},   // 23.98 us
     { 4096, 128256,  1, 64,  8, 28, 4},   // 47.1 us (re-swept: 47.6 us before)
+    { 4864,    896,  1, 16,  8,  8, 4},   // 5.19 us (earlier rule for other shapes: 5.51 us)
+    { 4864,    896,  4, 16,  8,  8, 4},   // 5.69 us (earlier rule for other shapes: 5.83 us)
+    { 4864,    896, 16, 16,  4, 12, 4},   // 6.21 us (earlier rule for other shapes: 6.51 us)
+    { 5120,   1024,  1, 16,  8,  8, 4},   // 5.17 us (earlier rule for other shapes: 6.75 us)
+    { 5120,   1024,  4, 16,  8,  8, 4},   // 5.62 us (earlier rule for other shapes: 7.04 us)
+    { 5120,   1024, 16, 16,  4, 12, 4},   // 6.32 us (earlier rule for other shapes: 8.48 us)
+    { 5120,   5120,  1, 32, 16, 12, 4},   // 7.34 us (earlier rule for other shapes: 9.56 us)
+    { 5120,   5120,  4, 32,  4, 12, 4},   // 7.82 us (earlier rule for other shapes: 10.45 us)
+    { 5120,   5120, 16, 64,  4, 16, 4},   // 8.36 us (earlier rule for other shapes: 14.99 us)
+    { 5120,  13824,  1, 64,  8, 24, 4},   // 10.53 us (earlier rule for other shapes: 12.27 us)
+    { 5120,  13824,  4, 64,  4, 48, 4},   // 10.74 us (earlier rule for other shapes: 12.71 us)
+    { 5120,  13824, 16, 64,  4, 48, 4},   // 11.82 us (earlier rule for other shapes: 15.14 us)
+    { 6144,   4096,  1, 16, 16, 12, 4},   // 6.23 us (earlier rule for other shapes: 7.86 us)
+    { 6144,   4096,  4, 16,  8, 24, 4},   // 7.17 us (earlier rule for other shapes: 8.53 us)
+    { 6144,   4096, 16, 64,  4, 12, 4},   // 8.22 us (earlier rule for other shapes: 11.22 us)
+    { 7168,   1024,  1, 16,  8,  8, 4},   // 5.49 us (earlier rule for other shapes: 6.00 us)
+    { 7168,   1024,  4, 16,  8,  8, 4},   // 5.82 us (earlier rule for other shapes: 6.15 us)
+    { 7168,   1024, 16, 16,  4, 16, 4},   // 6.79 us (earlier rule for other shapes: 6.79 us)
+    { 8192,   1024,  1, 16,  8,  8, 4},   // 5.76 us (earlier rule for other shapes: 8.87 us)
+    { 8192,   1024,  4, 16,  8,  8, 4},   // 6.19 us (earlier rule for other shapes: 9.32 us)
+    { 8192,   1024, 16, 16,  4, 16, 4},   // 7.07 us (earlier rule for other shapes: 10.10 us)
+    { 8192,   2048,  1, 16,  8,  8, 4},   // 6.27 us (earlier rule for other shapes: 9.04 us)
+    { 8192,   2048,  4, 16,  8,  8, 4},   // 6.79 us (earlier rule for other shapes: 9.46 us)
+    { 8192,   2048, 16, 32,  8,  8, 4},   // 7.99 us (earlier rule for other shapes: 10.27 us)
+    { 8192,   3072,  1, 16, 16, 16, 4},   // 7.18 us (earlier rule for other shapes: 7.77 us)
+    { 8192,   3072,  4, 64,  4, 16, 4},   // 8.06 us (earlier rule for other shapes: 8.21 us)
+    { 8192,   3072, 16, 64,  4, 16, 4},   // 8.35 us (earlier rule for other shapes: 9.51 us)
+    { 8192,   4096,  1, 16, 16, 16, 4},   // 7.45 us (earlier rule for other shapes: 9.27 us)
+    { 8192,   4096,  4, 32,  8,  8, 4},   // 8.46 us (earlier rule for other shapes: 9.79 us)
+    { 8192,   4096, 16, 64,  4, 16, 4},   // 8.90 us (earlier rule for other shapes: 10.65 us)
     { 8192,   8192,  1, 32, 16, 16, 4},   // 10.61 us
     { 8192,   8192, 16, 32,  4, 64, 4},   // 13.64 us
     { 8192,   8192, 32, 64,  4, 32, 4},   // 20.16 us
@@ -110,6 +203,21 @@ const TunedPlan kTuned[] = {
     { 8192,  28672, 16, 64,  4, 64, 4},   // 33.76 us
     { 8192,  28672, 32, 64,  4, 64, 4},   // 48.56 us
     { 8192,  28672, 64, 64,  4, 64, 4},   // 80.77 us
+    { 8960,   1536,  1, 16, 16,  8, 4},   // 6.40 us (earlier rule for other shapes: 6.97 us)
+    { 8960,   1536,  4, 16,  8,  8, 4},   // 7.12 us (earlier rule for other shapes: 7.36 us)
+    { 8960,   1536, 16, 32,  4, 16, 4},   // 7.90 us (earlier rule for other shapes: 8.88 us)
+    {10240,   2560,  1, 32,  8, 12, 4},   // 7.73 us (earlier rule for other shapes: 8.33 us)
+    {10240,   2560,  4, 32,  8, 12, 4},   // 8.25 us (earlier rule for other shapes: 8.71 us)
+    {10240,   2560, 16, 64,  4, 16, 4},   // 9.34 us (earlier rule for other shapes: 10.66 us)
+    {11008,   4096,  1, 64,  4, 24, 4},   // 9.11 us (earlier rule for other shapes: 9.75 us)
+    {11008,   4096,  4, 64,  4, 24, 4},   // 9.59 us (earlier rule for other shapes: 10.16 us)
+    {11008,   4096, 16, 64,  4, 24, 4},   // 10.03 us (earlier rule for other shapes: 10.99 us)
+    {12288,   4096,  1, 64,  4, 24, 4},   // 9.48 us (earlier rule for other shapes: 10.20 us)
+    {12288,   4096,  4, 64,  4, 24, 4},   // 9.89 us (earlier rule for other shapes: 10.66 us)
+    {12288,   4096, 16, 64,  4, 24, 4},   // 10.38 us (earlier rule for other shapes: 12.86 us)
+    {13824,   5120,  1, 64,  4, 12, 4},   // 12.10 us (earlier rule for other shapes: 12.59 us)
+    {13824,   5120,  4, 64,  4, 48, 4},   // 12.51 us (earlier rule for other shapes: 13.26 us)
+    {13824,   5120, 16, 64,  4, 12, 4},   // 14.26 us (earlier rule for other shapes: 15.39 us)
     {14336,   4096,  1, 64,  4, 28, 4},   // 10.56 us (4 splits of 112 K-steps)
     {14336,   4096,  2, 64,  4, 28, 4},   // 10.72 us
     {14336,   4096,  4, 64,  4, 28, 4},   // 11.04 us
@@ -117,6 +225,12 @@ const TunedPlan kTuned[] = {
     {14336,   4096, 16, 64,  4, 28, 4},   // 11.65 us
     {14336,   4096, 32, 64,  4, 28, 4},   // 16.54 us
     {14336,   4096, 64, 64,  4, 28, 4},   // 26.29 us
+    {16384,   1024,  1, 16, 16,  8, 4},   // 6.68 us (earlier rule for other shapes: 9.29 us)
+    {16384,   1024,  4, 16,  8, 16, 4},   // 7.23 us (earlier rule for other shapes: 9.67 us)
+    {16384,   1024, 16, 32,  4, 16, 4},   // 8.49 us (earlier rule for other shapes: 10.44 us)
+    {18944,   3584,  1, 64, 16, 12, 4},   // 12.11 us (earlier rule for other shapes: 14.37 us)
+    {18944,   3584,  4, 64,  4, 48, 4},   // 12.86 us (earlier rule for other shapes: 14.97 us)
+    {18944,   3584, 16, 64,  4, 16, 4},   // 14.49 us (earlier rule for other shapes: 17.27 us)
     {28672,   8192,  1, 64,  8, 56, 4},   // 23.5 us (re-swept: 25.6 us before; 2 even splits of 448 K-steps)
     {28672,   8192, 16, 64,  8, 56, 4},   // 29.4 us at M = 16 (re-swept: 31.6 us before)
     {28672,   8192, 32, 64,  8, 64, 4},   // 53.76 us
@@ -163,10 +277,26 @@ int64_t roundup4(int64_t v) { return ceil_div(v, 4) * 4; }
 void default_skinny_plan(int64_t M, int64_t N, int64_t K, int64_t group_steps, w4a16_plan_t* pl) {
     const TunedPlan* t = tuned_plan(M, N, K);
     const int64_t KS = K / w4a16::kKStep;
-    if (pl->cols == 0) pl->cols = t ? t->cols : (N >= 8192 || K >= 8192) ? 64 : (M > 32 ? 32 : 16);
-    if (pl->waves == 0) pl->waves = t ? t->waves : 4;
-    if (pl->kc == 0)
-        pl->kc = t ? t->kc : (int32_t)(KS <= 4 * 32 ? std::max<int64_t>(4, roundup4(ceil_div(KS, pl->waves))) : 32);
+    if (t) {
+        if (pl->cols == 0) pl->cols = t->cols;
+        if (pl->waves == 0) pl->waves = t->waves;
+        if (pl->kc == 0) pl->kc = t->kc;
+    } else if (M <= 16 && KS <= 4 * 32) {
+        // one work-group covers K; at M = 1 with about 8 K-steps per wavefront (short chains)
+        if (pl->cols == 0) pl->cols = N <= 4096 ? 16 : N <= 8192 ? 32 : 64;
+        if (pl->waves == 0) pl->waves = M > 1 ? 4 : KS >= 128 ? 16 : KS >= 64 ? 8 : 4;
+        if (pl->kc == 0) pl->kc = (int32_t)std::max<int64_t>(4, roundup4(ceil_div(KS, pl->waves)));
+    } else if (M <= 16) {
+        // K is split over work-groups
+        if (pl->cols == 0) pl->cols = N <= 1024 ? 16 : N <= 4096 ? 32 : 64;
+        if (pl->waves == 0) pl->waves = M <= 1 ? 8 : 4;
+        if (pl->kc == 0) pl->kc = M <= 1 ? 12 : 16;
+    } else {
+        if (pl->cols == 0) pl->cols = (N >= 8192 || K >= 8192) ? 64 : (M > 32 ? 32 : 16);
+        if (pl->waves == 0) pl->waves = 4;
+        if (pl->kc == 0)
+            pl->kc = (int32_t)(KS <= 4 * 32 ? std::max<int64_t>(4, roundup4(ceil_div(KS, pl->waves))) : 32);
+    }
     if (pl->seg == 0) {
         int32_t seg = t ? t->seg : 4;
         // 8-step segments are built for 128-row groups only
