@@ -300,6 +300,46 @@ int w4a16_matmul_noalloc(const void* x, const int32_t* qweight, const void* scal
 int w4a16_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, w4a16_plan_t* plan);
 
 /*
+ * w4a16_autotune - measure the plans of one shape on the device and keep the fastest for
+ * later calls: the per-shape tuning, with the winner cached, that "Beating FP16 with 4-bit
+ * Weights", section "Things I got wrong along the way", asks for (the best block sizes and
+ * split factor differ between projections of one model).
+ *   x, qweight, scales, zeros, y, M, N, K, group_size, layout  as for w4a16_matmul_fmt
+ *   stream   the caller's stream: the call first waits for the work enqueued on it
+ *   best     NULL, or receives the chosen plan (complete)
+ *   seconds  NULL, or receives its measured time per call
+ * The candidates are the dispatcher's plan, every built decode-kernel plan (M <= 128) and
+ * the prefill tiles with each split count (M >= 17). Each is timed on a stream of the
+ * library's own as a HIP graph of calls that rotate over copies of the weights (512 MiB in
+ * all, 2 to 512 copies: allocated by the call and freed before it returns), so that every
+ * call reads its weights from HBM; the five fastest are timed again and the fastest is kept,
+ * the dispatcher's own plan unless another is more than 1 % faster. From then on, in this
+ * process, calls of that (M, N, K, group_size) that leave the plan to the dispatcher take it:
+ * w4a16_matmul, w4a16_matmul_ex/_fmt/_noalloc with a NULL or all-zero plan,
+ * w4a16_matmul_grouped (for its summed N) and w4a16_plan. (w4a16_matmul_noalloc returns
+ * UNSUPPORTED if the plan's split-K needs more than its static scratch.)
+ * Synchronous; allocates device memory; not allowed while `stream` is being captured. On
+ * return y holds the product, computed with the chosen plan.
+ * Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT (all before any HIP call), HIP.
+ */
+int w4a16_autotune(const void* x, const int32_t* qweight, const void* scales, const void* zeros, void* y,
+                   int64_t M, int64_t N, int64_t K, int64_t group_size, int layout, void* stream,
+                   w4a16_plan_t* best, double* seconds);
+
+/*
+ * w4a16_set_plan - make `plan` the plan of (M, N, K, group_size) for later calls that leave
+ * the plan to the dispatcher, as w4a16_autotune does with the plan it measures: for instance
+ * to restore, at start-up, plans that an earlier process measured. The plan is completed and
+ * validated as w4a16_plan does with a forced plan. NULL removes the shape's entry. Host only;
+ * no HIP call. Errors: INVALID_ARG (a plan that names no kernel, or one not usable for the
+ * shape), UNSUPPORTED.
+ */
+int w4a16_set_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, const w4a16_plan_t* plan);
+
+/* w4a16_clear_plans - forget every plan set by w4a16_autotune or w4a16_set_plan. Host only. */
+int w4a16_clear_plans(void);
+
+/*
  * w4a16_dequant - the GPU's unpack/dequant, exposed for bit-exact checks: the unpack and the
  * (q - zero) * scale dequantisation of "Beating FP16 with 4-bit Weights", section "The
  * design", that the product kernels perform in registers.

@@ -31,6 +31,23 @@ hipError_t hipMalloc(void**, size_t) { reached("hipMalloc"); }
 hipError_t hipFree(void*) { reached("hipFree"); }
 hipError_t hipMemsetAsync(void*, int, size_t, hipStream_t) { reached("hipMemsetAsync"); }
 hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus*) { reached("hipStreamIsCapturing"); }
+hipError_t hipStreamSynchronize(hipStream_t) { reached("hipStreamSynchronize"); }
+hipError_t hipStreamCreateWithFlags(hipStream_t*, unsigned int) { reached("hipStreamCreateWithFlags"); }
+hipError_t hipStreamDestroy(hipStream_t) { reached("hipStreamDestroy"); }
+hipError_t hipStreamBeginCapture(hipStream_t, hipStreamCaptureMode) { reached("hipStreamBeginCapture"); }
+hipError_t hipStreamEndCapture(hipStream_t, hipGraph_t*) { reached("hipStreamEndCapture"); }
+hipError_t hipGraphInstantiate(hipGraphExec_t*, hipGraph_t, hipGraphNode_t*, char*, size_t) {
+    reached("hipGraphInstantiate");
+}
+hipError_t hipGraphLaunch(hipGraphExec_t, hipStream_t) { reached("hipGraphLaunch"); }
+hipError_t hipGraphExecDestroy(hipGraphExec_t) { reached("hipGraphExecDestroy"); }
+hipError_t hipGraphDestroy(hipGraph_t) { reached("hipGraphDestroy"); }
+hipError_t hipEventCreate(hipEvent_t*) { reached("hipEventCreate"); }
+hipError_t hipEventRecord(hipEvent_t, hipStream_t) { reached("hipEventRecord"); }
+hipError_t hipEventSynchronize(hipEvent_t) { reached("hipEventSynchronize"); }
+hipError_t hipEventElapsedTime(float*, hipEvent_t, hipEvent_t) { reached("hipEventElapsedTime"); }
+hipError_t hipEventDestroy(hipEvent_t) { reached("hipEventDestroy"); }
+hipError_t hipMemcpyAsync(void*, const void*, size_t, hipMemcpyKind, hipStream_t) { reached("hipMemcpyAsync"); }
 }
 
 namespace w4a16 {
@@ -234,6 +251,29 @@ static void device_call_errors() {
     expect(w4a16_read_probe(p[0], 100, (uint32_t*)p[1], nullptr), W4A16_ERR_INVALID_ARG, "read probe bytes%16");
     expect(w4a16_read_probe(nullptr, 1024, (uint32_t*)p[1], nullptr), W4A16_ERR_INVALID_ARG, "read probe null");
     expect(w4a16_read_probe(mis, 1024, (uint32_t*)p[1], nullptr), W4A16_ERR_ALIGNMENT, "read probe misaligned");
+    expect(w4a16_autotune(nullptr, (const int32_t*)p[1], p[2], p[3], p[4], 1, 64, 128, 128, 0, nullptr, nullptr,
+                          nullptr),
+           W4A16_ERR_INVALID_ARG, "autotune null x");
+    expect(w4a16_autotune(p[0], (const int32_t*)p[1], p[2], p[3], mis, 1, 64, 128, 128, 0, nullptr, nullptr, nullptr),
+           W4A16_ERR_ALIGNMENT, "autotune misaligned y");
+    expect(w4a16_autotune(p[0], (const int32_t*)p[1], p[2], p[3], p[4], 1, 66, 128, 128, 0, nullptr, nullptr, nullptr),
+           W4A16_ERR_UNSUPPORTED, "autotune N%4");
+    {
+        w4a16_plan_t none{}, bad{}, good{};
+        bad.kernel = W4A16_KERNEL_SKINNY;
+        bad.cols = 48;
+        good.kernel = W4A16_KERNEL_SKINNY;
+        good.cols = 32;
+        good.waves = 8;
+        expect(w4a16_set_plan(1, 4096, 4096, 128, &none), W4A16_ERR_INVALID_ARG, "set_plan names no kernel");
+        expect(w4a16_set_plan(1, 4096, 4096, 128, &bad), W4A16_ERR_INVALID_ARG, "set_plan cols 48");
+        expect(w4a16_set_plan(1, 4096, 4096, 128, &good), W4A16_OK, "set_plan");
+        w4a16_plan_t got{};
+        expect(w4a16_plan(1, 4096, 4096, 128, &got), W4A16_OK, "plan after set_plan");
+        expect(got.cols == 32 && got.waves == 8, 1, "plan is the one set");
+        expect(w4a16_set_plan(1, 4096, 4096, 128, nullptr), W4A16_OK, "set_plan remove");
+        expect(w4a16_clear_plans(), W4A16_OK, "clear_plans");
+    }
     for (int code = -7; code <= 1; ++code) {
         ++g_checks;
         if (!w4a16_strerror(code) || !*w4a16_strerror(code)) ++g_failed;

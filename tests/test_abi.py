@@ -385,3 +385,61 @@ def test_grouped_rejects_bad_arguments():
     bad_plan = B.w4a16_plan_t(kernel=1, cols=24)
     assert call(mats(64, 64), plan=ctypes.byref(bad_plan)) == lib.W4A16_ERR_INVALID_ARG
     assert so.w4a16_matmul_grouped(P[0], None, 1, 1, 4096, 128, 0, None, None) == lib.W4A16_ERR_INVALID_ARG
+
+
+# ---- plans set at run time (w4a16_set_plan / w4a16_autotune), host side ----
+
+def test_set_plan_takes_precedence_until_removed():
+    M, N, K = 1, 4096, 4096
+    default = lib.w4a16_plan(M, N, K)
+    forced = dict(kernel=lib.W4A16_KERNEL_SKINNY, cols=64, waves=8, kc=8, seg=4)
+    try:
+        lib.w4a16_set_plan(M, N, K, forced)
+        got = lib.w4a16_plan(M, N, K)
+        assert got == lib.w4a16_plan(M, N, K, **forced)          # stored complete
+        assert got != default
+        assert lib.w4a16_plan(M, N, K, group_size=64) == lib.w4a16_plan(M, N, K, group_size=64)
+        assert lib.w4a16_plan(2, N, K) == lib.w4a16_plan(2, N, K)  # other shapes untouched
+        # a forced plan still wins over the stored one
+        assert lib.w4a16_plan(M, N, K, kernel=1, cols=16, waves=4, kc=32)["cols"] == 16
+        lib.w4a16_set_plan(M, N, K, None)
+        assert lib.w4a16_plan(M, N, K) == default
+        lib.w4a16_set_plan(M, N, K, forced)
+        lib.w4a16_clear_plans()
+        assert lib.w4a16_plan(M, N, K) == default
+    finally:
+        lib.w4a16_clear_plans()
+
+
+def test_set_plan_rejects_unusable_plans():
+    so = B.load()
+    try:
+        for kw, code in [(dict(), lib.W4A16_ERR_INVALID_ARG), (dict(kernel=1, cols=48), lib.W4A16_ERR_INVALID_ARG),
+                         (dict(kernel=1, kc=6), lib.W4A16_ERR_INVALID_ARG), (dict(kernel=9), lib.W4A16_ERR_INVALID_ARG)]:
+            pl = B.w4a16_plan_t(**kw)
+            assert so.w4a16_set_plan(1, 4096, 4096, 128, ctypes.byref(pl)) == code, kw
+            assert so.w4a16_last_error_detail().decode()
+        pl = B.w4a16_plan_t(kernel=1)
+        assert so.w4a16_set_plan(1, 66, 4096, 128, ctypes.byref(pl)) == lib.W4A16_ERR_UNSUPPORTED
+        assert so.w4a16_set_plan(0, 64, 4096, 128, ctypes.byref(pl)) == lib.W4A16_ERR_INVALID_ARG
+        assert lib.w4a16_plan(1, 4096, 4096) == lib.w4a16_plan(1, 4096, 4096)
+    finally:
+        lib.w4a16_clear_plans()
+
+
+def test_autotune_rejects_bad_arguments_before_any_hip_call():
+    so = B.load()
+
+    def tune(ptrs, M=1, N=64, K=128, g=128, layout=0):
+        return so.w4a16_autotune(ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], M, N, K, g, layout, None, None, None)
+    for i in range(5):
+        ptrs = list(P)
+        ptrs[i] = None
+        assert tune(ptrs) == lib.W4A16_ERR_INVALID_ARG
+        ptrs = list(P)
+        ptrs[i] = ctypes.c_void_p(A + 8)
+        assert tune(ptrs) == lib.W4A16_ERR_ALIGNMENT
+    assert tune(P, layout=5) == lib.W4A16_ERR_INVALID_ARG
+    assert tune(P, N=66) == lib.W4A16_ERR_UNSUPPORTED
+    assert tune(P, M=0) == lib.W4A16_ERR_INVALID_ARG
+    assert tune(P, g=96) == lib.W4A16_ERR_UNSUPPORTED

@@ -81,6 +81,10 @@ _SIGS = {
     "w4a8_matmul_ex": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int, ctypes.c_int, _P],
                        ctypes.c_int),
     "w4a16_read_probe": ([_P, _I64, _P, _P], ctypes.c_int),
+    "w4a16_autotune": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int, _P,
+                        ctypes.POINTER(w4a16_plan_t), ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
+    "w4a16_set_plan": ([_I64, _I64, _I64, _I64, ctypes.POINTER(w4a16_plan_t)], ctypes.c_int),
+    "w4a16_clear_plans": ([], ctypes.c_int),
     "w4a16_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "w4a16_last_error_detail": ([], ctypes.c_char_p),
     "w4a16_version": ([], ctypes.c_int),
@@ -258,6 +262,45 @@ def w4a16_matmul(x, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, strea
         rc = load().w4a16_matmul_fmt(*args[:-1], lay, args[-1], pl)
         _check(rc, "w4a16_matmul_fmt")
     return y
+
+
+def w4a16_autotune(x, qweight, scales, zeros, y=None, group_size=GROUP_SIZE, stream=None, layout="linear"):
+    """Time the plans of this shape on the device (w4a16_autotune) and keep the fastest for
+    later calls of (M, N, K, group_size) in this process. Synchronous. Returns (plan dict,
+    seconds per call); y (allocated when None) holds the product afterwards."""
+    import torch
+    if x.dim() != 2 or qweight.dim() != 2:
+        raise ValueError("x and qweight must be 2-D")
+    M, K = x.shape
+    N = qweight.shape[1]
+    if qweight.shape[0] * 8 != K:
+        raise ValueError(f"qweight rows {qweight.shape[0]} do not match K={K}")
+    if scales_shape_bad(scales, zeros, K, N, group_size):
+        raise ValueError("scales/zeros must be [K/group_size, N]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    elif y.shape != (M, N):
+        raise ValueError("y must be [M, N]")
+    pl = w4a16_plan_t()
+    sec = ctypes.c_double(0.0)
+    rc = load().w4a16_autotune(_dev_ptr(x, "x", torch.float16), _dev_ptr(qweight, "qweight", torch.int32),
+                               _dev_ptr(scales, "scales", torch.float16), _dev_ptr(zeros, "zeros", torch.float16),
+                               _dev_ptr(y, "y", torch.float16), M, N, K, group_size, _layout_id(layout),
+                               _stream_ptr(stream, x.device), ctypes.byref(pl), ctypes.byref(sec))
+    _check(rc, "w4a16_autotune")
+    return pl.as_dict(), sec.value
+
+
+def w4a16_set_plan(M, N, K, plan, group_size=GROUP_SIZE):
+    """Make `plan` (a dict as w4a16_plan returns, or None to remove) the plan that later calls
+    of (M, N, K, group_size) take when they leave the plan to the dispatcher."""
+    pl = ctypes.byref(_make_plan(plan)) if plan is not None else None
+    _check(load().w4a16_set_plan(M, N, K, group_size, pl), "w4a16_set_plan")
+
+
+def w4a16_clear_plans():
+    """Forget every plan set by w4a16_autotune or w4a16_set_plan."""
+    _check(load().w4a16_clear_plans(), "w4a16_clear_plans")
 
 
 def w4a16_matmul_grouped(x, weights, ys=None, group_size=GROUP_SIZE, stream=None, plan=None, layout="linear"):

@@ -406,7 +406,38 @@ int64_t auto_kernel(int64_t M, int64_t N, int64_t K) {
     return (tiles >= kPrefillMinTiles || M > kSkinnyMaxM) ? W4A16_KERNEL_PREFILL : W4A16_KERNEL_SKINNY;
 }
 
-int complete_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, w4a16_plan_t* pl) {
+// Plans measured on the device at run time (w4a16_autotune) or installed by the caller
+// (w4a16_set_plan), per (M, N, K, group size): they take precedence over kTuned and the rule
+// for calls that leave the plan to the dispatcher.
+struct ShapeKey {
+    int64_t M, N, K, g;
+    bool operator<(const ShapeKey& o) const {
+        return M != o.M ? M < o.M : N != o.N ? N < o.N : K != o.K ? K < o.K : g < o.g;
+    }
+};
+std::mutex g_tuned_mu;
+std::map<ShapeKey, w4a16_plan_t> g_tuned;
+
+bool plan_is_auto(const w4a16_plan_t& p) {
+    return !p.kernel && !p.kc && !p.splits && !p.row_tiles && !p.tile && !p.waves && !p.cols && !p.seg;
+}
+
+bool plan_equal(const w4a16_plan_t& a, const w4a16_plan_t& b) {
+    return a.kernel == b.kernel && a.kc == b.kc && a.splits == b.splits && a.row_tiles == b.row_tiles &&
+           a.tile == b.tile && a.waves == b.waves && a.cols == b.cols && a.seg == b.seg;
+}
+
+bool lookup_tuned(int64_t M, int64_t N, int64_t K, int64_t g, w4a16_plan_t* out) {
+    std::lock_guard<std::mutex> lock(g_tuned_mu);
+    auto it = g_tuned.find(ShapeKey{M, N, K, g});
+    if (it == g_tuned.end()) return false;
+    *out = it->second;
+    return true;
+}
+
+int complete_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, w4a16_plan_t* pl, bool use_tuned = true) {
+    // a plan measured or installed for this shape (stored complete and validated)
+    if (use_tuned && plan_is_auto(*pl) && lookup_tuned(M, N, K, group_size, pl)) return W4A16_OK;
     const int64_t group_steps = group_size / w4a16::kKStep;
     if (pl->kernel == W4A16_KERNEL_AUTO) pl->kernel = (int32_t)auto_kernel(M, N, K);
     if (pl->kernel == W4A16_KERNEL_PREFILL) {
@@ -663,6 +694,257 @@ int matmul_impl(const void* x, const int32_t* qweight, const void* scales, const
     return launch_skinny_mats(x, &one, 1, M, K, group_size, layout, stream, pl, noalloc);
 }
 
+// ---- autotuning (w4a16_autotune) ------------------------------------------------------
+
+// Weights are rotated over copies totalling this much memory (at least two, at most
+// kTuneMaxCopies), so that each timed call reads its weights from HBM as in a model, where
+// the layers' weights far exceed the 256 MB Infinity Cache.
+constexpr uint64_t kTuneRotateBytes = 512ull << 20;
+constexpr int kTuneMaxCopies = 512;
+constexpr int kTuneFinalists = 5;
+
+// Frees the workspace of a stream the library created and has synchronised (no enqueued
+// launch or captured graph refers to it any more).
+void release_workspace(void* stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return;
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    auto it = g_ws.find({dev, stream});
+    if (it == g_ws.end()) return;
+    (void)hipFree(it->second.partials);
+    (void)hipFree(it->second.counters);
+    g_ws.erase(it);
+}
+
+// Split-K workspace of one call under a completed plan (what matmul_impl requests).
+void plan_workspace(int64_t M, int64_t N, int64_t K, const w4a16_plan_t& pl, uint64_t* bytes, uint64_t* counters) {
+    *bytes = 0;
+    *counters = 0;
+    if (pl.kernel == W4A16_KERNEL_PREFILL) {
+        if (pl.tile == W4A16_TILE_ASYNC && pl.splits > 1) {
+            const int64_t tiles = ceil_div(M, async_rows(M)) * ceil_div(N, 256);
+            *bytes = (uint64_t)tiles * pl.splits * w4a16::kPrefillTileFloats * 4;
+            *counters = (uint64_t)tiles;
+        }
+        return;
+    }
+    w4a16::SkinnyParams p{};
+    p.splits = pl.splits;
+    p.row_tiles = pl.row_tiles;
+    p.row_blocks = (int)ceil_div(M, 16 * (int64_t)pl.row_tiles);
+    p.n_strips = (int)ceil_div(N, pl.cols);
+    p.lw = pl.cols / 16;
+    (void)K;
+    w4a16::skinny_workspace(p, bytes, counters);
+}
+
+// The plans w4a16_autotune times: the dispatcher's own (tuned or not), every built decode-kernel
+// plan when M <= 128, and the prefill tiles (each split count the async tile settles on) when
+// M >= 17.
+std::vector<w4a16_plan_t> tune_candidates(int64_t M, int64_t N, int64_t K, int64_t g) {
+    std::vector<w4a16_plan_t> out;
+    auto add = [&](w4a16_plan_t p, bool use_tuned) {
+        if (complete_plan(M, N, K, g, &p, use_tuned) != W4A16_OK) return;
+        for (const w4a16_plan_t& q : out)
+            if (plan_equal(q, p)) return;
+        out.push_back(p);
+    };
+    add(w4a16_plan_t{}, false);
+    add(w4a16_plan_t{}, true);
+    if (M <= 128)
+        for (int cols : {16, 32, 64})
+            for (int waves : {4, 8, 16})
+                for (int kc : {4, 8, 12, 16, 20, 24, 28, 32, 40, 48, 56, 64})
+                    for (int seg : {2, 4, 8}) {
+                        w4a16_plan_t p{};
+                        p.kernel = W4A16_KERNEL_SKINNY;
+                        p.cols = cols;
+                        p.waves = waves;
+                        p.kc = kc;
+                        p.seg = seg;
+                        add(p, false);
+                    }
+    if (M >= 17) {
+        if (N % 8 == 0) {
+            for (int splits : {1, 2, 3, 4, 6, 8, 12, 16}) {
+                w4a16_plan_t p{};
+                p.kernel = W4A16_KERNEL_PREFILL;
+                p.tile = W4A16_TILE_ASYNC;
+                p.splits = splits;
+                add(p, false);
+            }
+        } else {
+            for (int tile : {W4A16_TILE_LDS, W4A16_TILE_REGISTER_B}) {
+                w4a16_plan_t p{};
+                p.kernel = W4A16_KERNEL_PREFILL;
+                p.tile = tile;
+                add(p, false);
+            }
+        }
+    }
+    return out;
+}
+
+struct TuneCtx {
+    const void* x;
+    void* y;
+    int64_t M, N, K, g;
+    int layout;
+    hipStream_t s;
+    std::vector<const int32_t*> qw;   // rotation copies; the first is the caller's
+    std::vector<const void*> sc, zr;
+};
+
+// Seconds per call of `pl`: a HIP graph of one call per rotation copy, captured on the tuning
+// stream, replayed once to warm up and then `reps` times between two events, best of
+// `trials`. Negative when the plan cannot be captured or run.
+double time_plan(const TuneCtx& c, const w4a16_plan_t& pl, int reps, int trials) {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    if (hipStreamBeginCapture(c.s, hipStreamCaptureModeThreadLocal) != hipSuccess) return -1.0;
+    int rc = W4A16_OK;
+    for (size_t i = 0; i < c.qw.size() && rc == W4A16_OK; ++i)
+        rc = matmul_impl(c.x, c.qw[i], c.sc[i], c.zr[i], c.y, c.M, c.N, c.K, c.g, c.layout, c.s, &pl);
+    const hipError_t ec = hipStreamEndCapture(c.s, &graph);
+    if (rc != W4A16_OK || ec != hipSuccess || !graph) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return -1.0;
+    }
+    if (hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess) {
+        (void)hipGraphDestroy(graph);
+        return -1.0;
+    }
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    double best = -1.0;
+    bool good = hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess &&
+                hipGraphLaunch(exec, c.s) == hipSuccess;
+    for (int t = 0; good && t < trials; ++t) {
+        good = hipEventRecord(e0, c.s) == hipSuccess;
+        for (int r = 0; good && r < reps; ++r) good = hipGraphLaunch(exec, c.s) == hipSuccess;
+        float ms = 0.f;
+        good = good && hipEventRecord(e1, c.s) == hipSuccess && hipEventSynchronize(e1) == hipSuccess &&
+               hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+        const double sec = ms * 1e-3 / ((double)reps * (double)c.qw.size());
+        if (good && (best < 0.0 || sec < best)) best = sec;
+    }
+    (void)hipStreamSynchronize(c.s);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(graph);
+    return good ? best : -1.0;
+}
+
+int autotune_impl(const void* x, const int32_t* qweight, const void* scales, const void* zeros, void* y,
+                  int64_t M, int64_t N, int64_t K, int64_t g, int layout, void* stream, w4a16_plan_t* best_out,
+                  double* best_sec) {
+    if (!x || !qweight || !scales || !zeros || !y) return fail(W4A16_ERR_INVALID_ARG, "null pointer argument");
+    if (!w4a16::layout_supported(layout)) return fail(W4A16_ERR_INVALID_ARG, "unknown layout %d", layout);
+    int rc = check_gpu_shape(M, N, K, g);
+    if (rc) return rc;
+    if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros) || !aligned16(y))
+        return fail(W4A16_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+    hipStream_t cs = reinterpret_cast<hipStream_t>(stream);
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(cs, &cap) == hipSuccess && cap != hipStreamCaptureStatusNone)
+        return fail(W4A16_ERR_INVALID_ARG, "w4a16_autotune cannot run under stream capture");
+    const std::vector<w4a16_plan_t> cands = tune_candidates(M, N, K, g);
+    if (cands.empty()) return fail(W4A16_ERR_UNSUPPORTED, "no plan runs this shape");
+    uint64_t ws_bytes = 0, ws_counters = 0;
+    for (const w4a16_plan_t& p : cands) {
+        uint64_t b = 0, c = 0;
+        plan_workspace(M, N, K, p, &b, &c);
+        ws_bytes = std::max(ws_bytes, b);
+        ws_counters = std::max(ws_counters, c);
+    }
+
+    hipError_t e = hipStreamSynchronize(cs);                 // the caller's inputs are ready
+    if (e != hipSuccess) return fail(W4A16_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+    TuneCtx c{x, y, M, N, K, g, layout, nullptr, {}, {}, {}};
+    e = hipStreamCreateWithFlags(&c.s, hipStreamNonBlocking);
+    if (e != hipSuccess) return fail(W4A16_ERR_HIP, "hipStreamCreate: %s", hipGetErrorString(e));
+    const uint64_t qb = (uint64_t)(K / 8) * N * 4, sb = (uint64_t)(K / g) * N * 2;
+    const uint64_t qa = (qb + 255) & ~255ull, sa = (sb + 255) & ~255ull, per = qa + 2 * sa;
+    const int copies = (int)std::min<uint64_t>(kTuneMaxCopies, std::max<uint64_t>(2, (kTuneRotateBytes + per - 1) / per));
+    char* rot = nullptr;
+    double t_best = -1.0;
+    w4a16_plan_t p_best{};
+    rc = W4A16_OK;
+    e = hipMalloc(reinterpret_cast<void**>(&rot), per * (copies - 1));
+    if (e != hipSuccess) rc = fail(W4A16_ERR_HIP, "hipMalloc of %d weight copies: %s", copies - 1, hipGetErrorString(e));
+    c.qw.push_back(qweight);
+    c.sc.push_back(scales);
+    c.zr.push_back(zeros);
+    for (int i = 0; rc == W4A16_OK && i < copies - 1; ++i) {
+        char* b = rot + per * i;
+        if (hipMemcpyAsync(b, qweight, qb, hipMemcpyDeviceToDevice, c.s) != hipSuccess ||
+            hipMemcpyAsync(b + qa, scales, sb, hipMemcpyDeviceToDevice, c.s) != hipSuccess ||
+            hipMemcpyAsync(b + qa + sa, zeros, sb, hipMemcpyDeviceToDevice, c.s) != hipSuccess)
+            rc = fail(W4A16_ERR_HIP, "copying the weights for rotation failed");
+        c.qw.push_back(reinterpret_cast<const int32_t*>(b));
+        c.sc.push_back(b + qa);
+        c.zr.push_back(b + qa + sa);
+    }
+    // the largest workspace any candidate needs, allocated once before any capture
+    if (rc == W4A16_OK && ws_bytes) {
+        Workspace w;
+        rc = get_workspace(c.s, ws_bytes, ws_counters, &w);
+    }
+    if (rc == W4A16_OK && hipStreamSynchronize(c.s) != hipSuccess) rc = fail(W4A16_ERR_HIP, "tuning stream failed");
+    if (rc == W4A16_OK) {
+        // clock warm-up: about 0.1 s of the dispatcher's plan
+        const double t0 = time_plan(c, cands[0], 1, 1);
+        if (t0 > 0.0)
+            (void)time_plan(c, cands[0], (int)std::min(200.0, std::max(1.0, 0.1 / (t0 * copies))), 1);
+        std::vector<std::pair<double, size_t>> screen;
+        for (size_t i = 0; i < cands.size(); ++i) {
+            const double t = time_plan(c, cands[i], 2, 2);
+            if (t > 0.0) screen.emplace_back(t, i);
+        }
+        std::sort(screen.begin(), screen.end());
+        // finalists (and the dispatcher's plan) timed again, interleaved, best of both rounds
+        std::vector<size_t> fin;
+        for (size_t i = 0; i < screen.size() && (int)fin.size() < kTuneFinalists; ++i) fin.push_back(screen[i].second);
+        if (std::find(fin.begin(), fin.end(), (size_t)0) == fin.end() && !screen.empty()) fin.push_back(0);
+        std::vector<double> tf(fin.size(), -1.0);
+        for (int round = 0; round < 2; ++round)
+            for (size_t j = 0; j < fin.size(); ++j) {
+                const double t = time_plan(c, cands[fin[j]], 3, 3);
+                if (t > 0.0 && (tf[j] < 0.0 || t < tf[j])) tf[j] = t;
+            }
+        double t_default = -1.0;
+        for (size_t j = 0; j < fin.size(); ++j) {
+            if (fin[j] == 0) t_default = tf[j];
+            if (tf[j] > 0.0 && (t_best < 0.0 || tf[j] < t_best)) {
+                t_best = tf[j];
+                p_best = cands[fin[j]];
+            }
+        }
+        // the dispatcher's plan unless another is more than 1 % faster (timing noise)
+        if (t_default > 0.0 && t_default <= 1.01 * t_best) {
+            t_best = t_default;
+            p_best = cands[0];
+        }
+        if (t_best < 0.0) rc = fail(W4A16_ERR_HIP, "no plan could be timed");
+    }
+    if (rc == W4A16_OK) {                                   // y = the product, with the winner
+        rc = matmul_impl(x, qweight, scales, zeros, y, M, N, K, g, layout, c.s, &p_best);
+        if (rc == W4A16_OK && hipStreamSynchronize(c.s) != hipSuccess) rc = fail(W4A16_ERR_HIP, "tuning stream failed");
+    }
+    (void)hipStreamSynchronize(c.s);
+    if (rot) (void)hipFree(rot);
+    release_workspace(c.s);
+    (void)hipStreamDestroy(c.s);
+    if (rc) return rc;
+    {
+        std::lock_guard<std::mutex> lock(g_tuned_mu);
+        g_tuned[ShapeKey{M, N, K, g}] = p_best;
+    }
+    if (best_out) *best_out = p_best;
+    if (best_sec) *best_sec = t_best;
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -745,6 +1027,7 @@ int w4a16_matmul_grouped(const void* x, const w4a16_matrix_t* mats, int n_mats, 
     if (rc) return rc;
     if (!aligned16(x)) return fail(W4A16_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
     w4a16_plan_t pl = plan ? *plan : w4a16_plan_t{};
+    if (plan_is_auto(pl)) (void)lookup_tuned(M, n_total, K, group_size, &pl);
     if (pl.kernel == W4A16_KERNEL_AUTO) pl.kernel = (int32_t)auto_kernel(M, n_total, K);
     if (pl.kernel == W4A16_KERNEL_PREFILL) {
         // the prefill tiles fill the chip per matrix: one launch each, each with its own plan
@@ -898,6 +1181,35 @@ int w4a16_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* strea
         return fail(W4A16_ERR_ALIGNMENT, "buf must be 16-byte aligned, sink 4-byte aligned");
     const int e = w4a16::launch_read_probe(buf, bytes, sink, stream);
     if (e != (int)hipSuccess) return fail(W4A16_ERR_HIP, "read probe launch: %s", hipGetErrorString((hipError_t)e));
+    return ok();
+}
+
+int w4a16_autotune(const void* x, const int32_t* qweight, const void* scales, const void* zeros, void* y,
+                   int64_t M, int64_t N, int64_t K, int64_t group_size, int layout, void* stream,
+                   w4a16_plan_t* best, double* seconds) {
+    return autotune_impl(x, qweight, scales, zeros, y, M, N, K, group_size, layout, stream, best, seconds);
+}
+
+int w4a16_set_plan(int64_t M, int64_t N, int64_t K, int64_t group_size, const w4a16_plan_t* plan) {
+    int rc = check_gpu_shape(M, N, K, group_size);
+    if (rc) return rc;
+    if (!plan) {
+        std::lock_guard<std::mutex> lock(g_tuned_mu);
+        g_tuned.erase(ShapeKey{M, N, K, group_size});
+        return ok();
+    }
+    w4a16_plan_t pl = *plan;
+    if (plan_is_auto(pl)) return fail(W4A16_ERR_INVALID_ARG, "the plan names no kernel");
+    rc = complete_plan(M, N, K, group_size, &pl, false);
+    if (rc) return rc;
+    std::lock_guard<std::mutex> lock(g_tuned_mu);
+    g_tuned[ShapeKey{M, N, K, group_size}] = pl;
+    return ok();
+}
+
+int w4a16_clear_plans(void) {
+    std::lock_guard<std::mutex> lock(g_tuned_mu);
+    g_tuned.clear();
     return ok();
 }
 
