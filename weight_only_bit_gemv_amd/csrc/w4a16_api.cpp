@@ -65,14 +65,15 @@ int check_gpu_shape(int64_t M, int64_t N, int64_t K, int64_t group_size) {
 // won an alternating A/B against the earlier plan), and for the projections of 34 other
 // decoder shapes (K and N from 512 to 18944: narrow key/value projections, 4864- to
 // 18944-wide feed-forward layers and their transposes; 72 plans each at 4-step segments, the
-// earlier rule's plan timed beside them): an entry covers M up to m_max and above the
+// earlier rule's plan timed beside them) and the summed N of the grouped launches of the
+// benchmarks (gate+up of 4096 x 14336, experts' gate+up and down): an entry covers M up to m_max and above the
 // previous entry's m_max. Other shapes take a rule fitted to those sweeps, for M <= 16 (on
 // those 34 shapes its plans are on average 3 % (K <= 4096) and 9 % (deeper K) slower than
 // each shape's best, against 8 % and 25 % for the rule before it; fitted on half of the
 // shapes, it is 2-5 % and 9-12 % slower on the other half):
 //  * K <= 4096: one work-group covers K, at M = 1 with 16 wavefronts (K = 4096), 8 (K = 2048
-//    to 4095) or 4 (shorter K), at larger M with 4; strips of 16 columns up to N = 4096, 32
-//    up to 8192, 64 beyond;
+//    to 4095) or 4 (shorter K), at larger M or N >= 16384 (256 or more 64-column strips) with
+//    4; strips of 16 columns up to N = 4096, 32 up to 8192, 64 beyond;
 //  * deeper K: 12 K-steps per wavefront and 8 wavefronts at M = 1, 16 K-steps and 4
 //    wavefronts above, K split over work-groups; strips of 16 columns up to N = 1024, 32 up
 //    to 4096, 64 beyond.
@@ -89,6 +90,9 @@ const TunedPlan kTuned[] = {
     {  768,   2048,  1, 16,  4,  8, 4},   // 2.93 us (re-swept: 2.98 us before)
     {  768,   2048,  4, 16,  4,  8, 4},   // 3.11 us
     {  768,   2048, 16, 16,  4,  8, 4},   // 3.41 us
+    {  768,  16384,  1, 32,  8,  4, 4},   // 4.19 us (summed N of a grouped launch)
+    {  768,  16384,  4, 32,  4,  8, 4},   // 4.43 us (summed N of a grouped launch)
+    {  768,  16384, 16, 64,  4,  8, 4},   // 4.70 us (summed N of a grouped launch)
     {  896,   4864,  1, 32,  4,  8, 4},   // 3.47 us (earlier rule for other shapes: 3.48 us)
     {  896,   4864,  4, 32,  4,  8, 4},   // 3.72 us (earlier rule for other shapes: 3.72 us)
     {  896,   4864, 16, 32,  4,  8, 4},   // 3.94 us (earlier rule for other shapes: 3.94 us)
@@ -98,6 +102,12 @@ const TunedPlan kTuned[] = {
     { 1408,   2048,  1, 16, 16,  4, 4},   // 3.32 us
     { 1408,   2048,  4, 16,  8,  8, 4},   // 3.74 us
     { 1408,   2048, 16, 16,  4, 12, 4},   // 4.20 us (re-swept: 4.32 us before)
+    { 1408,   8192,  1, 32,  4, 12, 4},   // 4.09 us (summed N of a grouped launch)
+    { 1408,   8192,  4, 32,  4, 12, 4},   // 4.39 us (summed N of a grouped launch)
+    { 1408,   8192, 16, 32,  4, 12, 4},   // 4.72 us (summed N of a grouped launch)
+    { 1408,  16384,  1, 64,  4, 12, 4},   // 5.07 us (summed N of a grouped launch)
+    { 1408,  16384,  4, 64,  4, 12, 4},   // 5.47 us (summed N of a grouped launch)
+    { 1408,  16384, 16, 64,  4, 12, 4},   // 5.67 us (summed N of a grouped launch)
     { 1536,   8960,  1, 64,  4, 12, 4},   // 4.63 us (earlier rule for other shapes: 4.63 us)
     { 1536,   8960,  4, 64,  4, 12, 4},   // 5.09 us (earlier rule for other shapes: 5.14 us)
     { 1536,   8960, 16, 64,  4, 12, 4},   // 5.47 us (earlier rule for other shapes: 5.48 us)
@@ -116,6 +126,12 @@ const TunedPlan kTuned[] = {
     { 2048,   8192,  1, 32, 16,  4, 4},   // 4.58 us (earlier rule for other shapes: 5.37 us)
     { 2048,   8192,  4, 32,  8,  8, 4},   // 5.02 us (earlier rule for other shapes: 5.76 us)
     { 2048,   8192, 16, 32,  8,  8, 4},   // 5.62 us (earlier rule for other shapes: 6.21 us)
+    { 2048,  11264,  1, 64,  8,  8, 4},   // 5.44 us (summed N of a grouped launch)
+    { 2048,  11264,  4, 64,  4, 16, 4},   // 5.91 us (summed N of a grouped launch)
+    { 2048,  11264, 16, 64,  4, 16, 4},   // 6.48 us (summed N of a grouped launch)
+    { 2048,  12288,  1, 64,  8,  8, 4},   // 5.61 us (summed N of a grouped launch)
+    { 2048,  12288,  4, 64,  4, 16, 4},   // 6.06 us (summed N of a grouped launch)
+    { 2048,  12288, 16, 64,  4, 16, 4},   // 6.80 us (summed N of a grouped launch)
     { 2560,  10240,  1, 64,  4, 20, 4},   // 6.10 us (earlier rule for other shapes: 6.10 us)
     { 2560,  10240,  4, 64,  4, 20, 4},   // 6.45 us (earlier rule for other shapes: 6.45 us)
     { 2560,  10240, 16, 64,  4, 20, 4},   // 7.46 us (earlier rule for other shapes: 7.46 us)
@@ -157,6 +173,8 @@ const TunedPlan kTuned[] = {
     { 4096,  11008,  4, 64,  4, 32, 4},   // 8.38 us (earlier rule for other shapes: 8.40 us)
     { 4096,  11008, 16, 64,  4, 32, 4},   // 9.76 us (earlier rule for other shapes: 9.76 us)
     { 4096,  12288,  1, 64, 16,  8, 4},   // 8.28 us (q, k, v of 4096 x 4096 in one grouped launch)
+    { 4096,  12288,  4, 64,  4, 32, 4},   // 8.60 us (summed N of a grouped launch)
+    { 4096,  12288, 16, 64,  4, 32, 4},   // 10.20 us (summed N of a grouped launch)
     { 4096,  14336,  1, 64,  4, 32, 4},   // 9.01 us
     { 4096,  14336,  2, 64,  4, 32, 4},   // 9.13 us
     { 4096,  14336,  4, 64,  4, 32, 4},   // 9.30 us
@@ -164,6 +182,9 @@ const TunedPlan kTuned[] = {
     { 4096,  14336, 16, 64,  4, 32, 4},   // 10.35 us
     { 4096,  14336, 32, 64,  4, 32, 4},   // 14.79 us
     { 4096,  14336, 64, 64,  4, 48, 4},   // 23.98 us
+    { 4096,  28672,  1, 64,  4, 32, 4},   // 14.44 us (summed N of a grouped launch)
+    { 4096,  28672,  4, 64,  4, 32, 4},   // 15.23 us (summed N of a grouped launch)
+    { 4096,  28672, 16, 64,  4, 32, 4},   // 18.40 us (summed N of a grouped launch)
     { 4096, 128256,  1, 64,  8, 28, 4},   // 47.1 us (re-swept: 47.6 us before)
     { 4864,    896,  1, 16,  8,  8, 4},   // 5.19 us (earlier rule for other shapes: 5.51 us)
     { 4864,    896,  4, 16,  8,  8, 4},   // 5.69 us (earlier rule for other shapes: 5.83 us)
@@ -284,7 +305,7 @@ void default_skinny_plan(int64_t M, int64_t N, int64_t K, int64_t group_steps, w
     } else if (M <= 16 && KS <= 4 * 32) {
         // one work-group covers K; at M = 1 with about 8 K-steps per wavefront (short chains)
         if (pl->cols == 0) pl->cols = N <= 4096 ? 16 : N <= 8192 ? 32 : 64;
-        if (pl->waves == 0) pl->waves = M > 1 ? 4 : KS >= 128 ? 16 : KS >= 64 ? 8 : 4;
+        if (pl->waves == 0) pl->waves = M > 1 || N >= 16384 ? 4 : KS >= 128 ? 16 : KS >= 64 ? 8 : 4;
         if (pl->kc == 0) pl->kc = (int32_t)std::max<int64_t>(4, roundup4(ceil_div(KS, pl->waves)));
     } else if (M <= 16) {
         // K is split over work-groups
