@@ -15,6 +15,8 @@ Other workloads (same JSON keys, config.workload names them):
   gemv_4096     one M=1, 4096 x 4096 GEMV
   gemv_lm_head  one M=1, 4096 x 128256 GEMV (the 7B-shaped chain's lm_head, 279 MB)
   moe_expert    M in {1,4,16} on (2048,1408), (1408,2048), (2048,768), (768,2048)
+  shard_8       M in {1,4,16} on one GPU's column share (N / 8) of the 7B-shaped projections
+                and lm_head: (4096,512), (4096,1792), (14336,512), (4096,16032)
   chain_7b      batch-1 decode weight stream of a 32-layer 7B-shaped model + lm_head:
                 225 GEMVs per token in one graph (one layer's weights packed once and
                 copied into 32 distinct device buffers); also reports tokens/s
@@ -68,6 +70,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak (8 TB/s)
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA peak
 GROUP = 128
 SWEEP_KN = [(4096, 14336), (14336, 4096), (4096, 4096)]
+# one GPU's column share (N / 8) of the 7B-shaped projections and lm_head: tensor parallelism
+# over 8 GPUs without any exchange inside the product
+SHARD8_KN = [(4096, 512), (4096, 1792), (14336, 512), (4096, 16032)]
 SWEEP_M = [1, 2, 4, 8, 16]
 ROTATE_BYTES = 1 << 30         # >= 4x the 256 MB Infinity Cache per shape family
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_skinny_decode_sweep.json")
@@ -479,6 +484,14 @@ def workload_items(name):
         fam = {(K, N): (K, N, wid, 0) for (K, N) in kns}
         items = [(M, K, N, (K, N)) for (K, N) in kns for M in (1, 4, 16)]
         return fam, items, "moe_expert: M in {1,4,16} x (2048,1408),(1408,2048),(2048,768),(768,2048)", None
+    if name == "shard_8":
+        wid = synth.WORKLOADS["decode_sweep"]["wid"]
+        fam = {(K, N): (K, N, wid, 8) for (K, N) in SHARD8_KN}
+        items = [(M, K, N, (K, N)) for (K, N) in SHARD8_KN for M in (1, 4, 16)]
+        desc = ("shard_8: one GPU's share of the 7B-shaped decode projections split by output columns "
+                "over 8 GPUs: (K,N) in {(4096,512) q/k/v/o, (4096,1792) gate/up, (14336,512) down, "
+                "(4096,16032) lm_head}, M in {1,4,16}, group 128")
+        return fam, items, desc, None
     if name == "chain_7b":
         wid = synth.WORKLOADS["decode_chain_7b"]["wid"]
         fam, items, replicate = {}, [], {}
@@ -1283,7 +1296,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_sweep",
-                    choices=["decode_sweep", "gemv_4096", "gemv_lm_head", "moe_expert", "chain_7b", "prefill"])
+                    choices=["decode_sweep", "gemv_4096", "gemv_lm_head", "moe_expert", "shard_8", "chain_7b",
+                             "prefill"])
     ap.add_argument("--group-size", type=int, default=GROUP, choices=[32, 64, 128, 256],
                     help="K rows per scale/zero group (decode workloads)")
     ap.add_argument("--symmetric", action="store_true",

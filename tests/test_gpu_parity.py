@@ -184,13 +184,15 @@ def test_chain_lm_head_sampled(lib):
 
 # Projection shapes of other common decoder configurations, each with a plan of its own in
 # the dispatcher's table (narrow key/value projections; 11008-, 13824- and 18944-wide
-# feed-forward layers; their transposes): full-size launches with the plan the dispatcher
+# feed-forward layers; their transposes; one GPU's column share of the 7B-shaped
+# projections over 8 GPUs): full-size launches with the plan the dispatcher
 # picks for one M of each of its buckets (1, 2..4, 5..16; ragged M pads the MFMA rows),
 # checked on sampled columns. Two shapes outside the table exercise the rule for the others.
 DECODER_KN = [(4096, 512), (4096, 1024), (5120, 1024), (8192, 1024), (16384, 1024), (2048, 512),
               (2048, 2048), (4096, 2048), (8192, 2048), (1024, 4096), (6144, 4096), (8192, 4096),
               (11008, 4096), (4096, 6144), (4096, 8192), (2048, 8192), (5120, 5120), (13824, 5120),
               (18944, 3584), (4096, 11008), (5120, 13824), (3584, 18944),
+              (4096, 1792), (14336, 512), (4096, 16032),
               (7168, 1024), (2560, 10240)]
 DECODER_SHAPES = [(m, k, n) for (k, n) in DECODER_KN for m in (1, 3, 11)]
 

@@ -66,7 +66,8 @@ int check_gpu_shape(int64_t M, int64_t N, int64_t K, int64_t group_size) {
 // decoder shapes (K and N from 512 to 18944: narrow key/value projections, 4864- to
 // 18944-wide feed-forward layers and their transposes; 72 plans each at 4-step segments, the
 // earlier rule's plan timed beside them) and the summed N of the grouped launches of the
-// benchmarks (gate+up of 4096 x 14336, experts' gate+up and down): an entry covers M up to m_max and above the
+// benchmarks (gate+up of 4096 x 14336, experts' gate+up and down) and one GPU's share of
+// the decode shapes split by columns over 8 GPUs: an entry covers M up to m_max and above the
 // previous entry's m_max. Other shapes take a rule fitted to those sweeps, for M <= 16 (on
 // those 34 shapes its plans are on average 3 % (K <= 4096) and 9 % (deeper K) slower than
 // each shape's best, against 8 % and 25 % for the rule before it; fitted on half of the
@@ -150,6 +151,9 @@ const TunedPlan kTuned[] = {
     { 4096,   1024,  1, 16, 16,  8, 4},   // 4.57 us (earlier rule for other shapes: 5.28 us)
     { 4096,   1024,  4, 16,  8, 16, 4},   // 5.35 us (earlier rule for other shapes: 5.57 us)
     { 4096,   1024, 16, 32,  4,  8, 4},   // 6.00 us (earlier rule for other shapes: 6.90 us)
+    { 4096,   1792,  1, 16, 16,  8, 4},   // 4.65 us (one GPU's column share of 8)
+    { 4096,   1792,  4, 16,  8, 16, 4},   // 5.43 us (one GPU's column share of 8)
+    { 4096,   1792, 16, 32,  4,  8, 4},   // 6.33 us (one GPU's column share of 8)
     { 4096,   2048,  1, 16, 16,  8, 4},   // 4.71 us (earlier rule for other shapes: 5.42 us)
     { 4096,   2048,  4, 16,  8, 16, 4},   // 5.43 us (earlier rule for other shapes: 5.73 us)
     { 4096,   2048, 16, 32,  4, 12, 4},   // 6.54 us (earlier rule for other shapes: 6.97 us)
@@ -182,6 +186,9 @@ const TunedPlan kTuned[] = {
     { 4096,  14336, 16, 64,  4, 32, 4},   // 10.35 us
     { 4096,  14336, 32, 64,  4, 32, 4},   // 14.79 us
     { 4096,  14336, 64, 64,  4, 48, 4},   // 23.98 us
+    { 4096,  16032,  1, 64,  8, 32, 4},   // 8.88 us (one GPU's column share of 8)
+    { 4096,  16032,  4, 64,  4, 32, 4},   // 9.05 us (one GPU's column share of 8)
+    { 4096,  16032, 16, 64,  4, 32, 4},   // 9.99 us (one GPU's column share of 8)
     { 4096,  28672,  1, 64,  4, 32, 4},   // 14.44 us (summed N of a grouped launch)
     { 4096,  28672,  4, 64,  4, 32, 4},   // 15.23 us (summed N of a grouped launch)
     { 4096,  28672, 16, 64,  4, 32, 4},   // 18.40 us (summed N of a grouped launch)
@@ -239,6 +246,9 @@ const TunedPlan kTuned[] = {
     {13824,   5120,  1, 64,  4, 12, 4},   // 12.10 us (earlier rule for other shapes: 12.59 us)
     {13824,   5120,  4, 64,  4, 48, 4},   // 12.51 us (earlier rule for other shapes: 13.26 us)
     {13824,   5120, 16, 64,  4, 12, 4},   // 14.26 us (earlier rule for other shapes: 15.39 us)
+    {14336,    512,  1, 16, 16,  8, 4},   // 6.07 us (one GPU's column share of 8)
+    {14336,    512,  4, 16,  8,  8, 4},   // 6.64 us (one GPU's column share of 8)
+    {14336,    512, 16, 16,  4, 16, 4},   // 7.47 us (one GPU's column share of 8)
     {14336,   4096,  1, 64,  4, 28, 4},   // 10.56 us (4 splits of 112 K-steps)
     {14336,   4096,  2, 64,  4, 28, 4},   // 10.72 us
     {14336,   4096,  4, 64,  4, 28, 4},   // 11.04 us
