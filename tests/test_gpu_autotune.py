@@ -94,3 +94,24 @@ def test_set_plan_is_taken_by_every_entry_point(lib):
             assert torch.equal(y, forced), what
     finally:
         lib.w4a16_clear_plans()
+
+
+def test_autotune_other_formats(lib):
+    """The interleaved layout and 64-row groups: the tuned plan is kept per (M, N, K, group
+    size) and the results stay at the bar."""
+    M, K, N = 2, 2048, 1536
+    wid = synth.WORKLOADS["decode_chain_7b"]["wid"]
+    W = synth.weight(K, N, wid=wid, layer=9)
+    try:
+        for layout, g in (("interleaved", 128), ("linear", 64)):
+            qw, s, z = oracle.quantize_pack(W, g, layout=layout)
+            x = synth.activations(M, K, wid=wid)
+            d = [dev(a) for a in (x, qw, s, z)]
+            plan, sec = lib.w4a16_autotune(*d, group_size=g, layout=layout)
+            print(f"\n[autotune] {layout} g={g}: {plan} at {sec * 1e6:.2f} us", flush=True)
+            assert lib.w4a16_plan(M, N, K, group_size=g) == plan
+            y = lib.w4a16_matmul(*d, group_size=g, layout=layout)
+            torch.cuda.synchronize()
+            check_y(y, oracle.matmul(x, qw, s, z, g, layout=layout), f"{layout} g={g}")
+    finally:
+        lib.w4a16_clear_plans()
