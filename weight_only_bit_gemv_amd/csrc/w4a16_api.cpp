@@ -748,7 +748,7 @@ void release_workspace(void* stream) {
 }
 
 // Split-K workspace of one call under a completed plan (what matmul_impl requests).
-void plan_workspace(int64_t M, int64_t N, int64_t K, const w4a16_plan_t& pl, uint64_t* bytes, uint64_t* counters) {
+void plan_workspace(int64_t M, int64_t N, const w4a16_plan_t& pl, uint64_t* bytes, uint64_t* counters) {
     *bytes = 0;
     *counters = 0;
     if (pl.kernel == W4A16_KERNEL_PREFILL) {
@@ -765,7 +765,6 @@ void plan_workspace(int64_t M, int64_t N, int64_t K, const w4a16_plan_t& pl, uin
     p.row_blocks = (int)ceil_div(M, 16 * (int64_t)pl.row_tiles);
     p.n_strips = (int)ceil_div(N, pl.cols);
     p.lw = pl.cols / 16;
-    (void)K;
     w4a16::skinny_workspace(p, bytes, counters);
 }
 
@@ -884,7 +883,7 @@ int autotune_impl(const void* x, const int32_t* qweight, const void* scales, con
     uint64_t ws_bytes = 0, ws_counters = 0;
     for (const w4a16_plan_t& p : cands) {
         uint64_t b = 0, c = 0;
-        plan_workspace(M, N, K, p, &b, &c);
+        plan_workspace(M, N, p, &b, &c);
         ws_bytes = std::max(ws_bytes, b);
         ws_counters = std::max(ws_counters, c);
     }
