@@ -187,3 +187,34 @@ def test_w4a8_graph_replays_match_eager(lib):
     # the captured quantiser's outputs too
     assert torch.equal(a, xq) and torch.equal(b.view(torch.int32), sx.view(torch.int32))
     assert torch.equal(c.view(torch.int32), xsum.view(torch.int32))
+
+
+def test_set_plan_is_captured(lib):
+    """A plan installed with w4a16_set_plan (here one with split-K) is what a captured call of
+    that shape takes: every replay gives the bits of the same plan forced in an eager call."""
+    M, K, N = 3, 4096, 2048
+    plan = lib.w4a16_plan(M, N, K, kernel=lib.W4A16_KERNEL_SKINNY, cols=64, waves=4, kc=8)
+    assert plan["splits"] > 1
+    x, qw, s, z, args = _problem(M, K, N, seed=77)
+    st = torch.cuda.Stream()
+    try:
+        lib.w4a16_set_plan(M, N, K, plan)
+        y_ref = torch.empty((M, N), dtype=torch.float16, device=DEV)
+        with torch.cuda.stream(st):
+            lib.w4a16_matmul(*args, y=y_ref, plan=plan)       # eager, forced; sizes the workspace
+        st.synchronize()
+        y_g = torch.zeros_like(y_ref)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            lib.w4a16_matmul(*args, y=y_g)                     # the dispatcher's (installed) plan
+        for rep in range(3):
+            y_g.fill_(7.0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y_g.view(torch.int16), y_ref.view(torch.int16)), f"replay {rep}"
+    finally:
+        lib.w4a16_clear_plans()
+    y = y_ref.cpu().numpy().astype(np.float64)
+    ref = oracle.matmul(x, qw, s, z)
+    assert np.all(np.abs(y - ref) <= 1e-2 + 5e-3 * np.abs(ref))
