@@ -71,6 +71,37 @@ def test_random_w4a16(lib, case):
     check_y(y, oracle.matmul(x, qw, s, z, g, layout=layout), f"w4a16 {case}")
 
 
+def _deep_cases(count=16, seed=2026):
+    """Decode-sized M with K up to 16384 and N up to 6144, on the dispatcher's plan: the
+    shapes outside its table that take the split-K branch of its rule (K > 4096)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        g = int(rng.choice([64, 128, 256]))
+        K = 256 * int(rng.integers(17, 65))
+        N = 4 * int(rng.integers(1, 1537))
+        M = int(rng.integers(1, 17))
+        layout = str(rng.choice(["linear", "interleaved"]))
+        cases.append((i, M, K, N, g, layout))
+    return cases
+
+
+DEEP_CASES = _deep_cases()
+
+
+@pytest.mark.parametrize("case", DEEP_CASES, ids=[f"c{c[0]}-M{c[1]}-K{c[2]}-N{c[3]}-g{c[4]}-{c[5][:3]}" for c in DEEP_CASES])
+def test_random_deep_k_dispatcher_plan(lib, case):
+    i, M, K, N, g, layout = case
+    print(f"\n[random deep] {case} plan={lib.w4a16_plan(M, N, K, group_size=g)}", flush=True)
+    qw, s, z = oracle.quantize_pack(synth.weight_custom(K, N, seed=5000 + i, std=0.02), g, bool(i % 3 == 0), layout)
+    x = synth.activations(M, K, wid=9)
+    y = lib.w4a16_matmul(dev(x), dev(qw), dev(s), dev(z), group_size=g, layout=layout)
+    rng = np.random.default_rng((6, i))
+    cols = np.unique(np.concatenate([rng.choice(N, size=min(N, 96), replace=False), [0, N - 1]]))
+    ref = oracle.matmul(x, qw[:, cols], s[:, cols], z[:, cols], g, layout=layout)
+    check_y(y[:, torch.from_numpy(cols).to(DEV)], ref, f"deep {case}")
+
+
 def _w4a8_cases(count=24, seed=2025):
     rng = np.random.default_rng(seed)
     cases = []
