@@ -291,6 +291,9 @@ int w4a16_matmul_noalloc(const void* x, const int32_t* qweight, const void* scal
 /*
  * w4a16_plan - the plan w4a16_matmul would use for (M, N, K, group_size), or the completed
  * version of a forced plan when `plan->kernel` is non-zero on entry. Host only; no HIP call.
+ * The dispatcher takes, in this order: a plan set for the shape by w4a16_autotune or
+ * w4a16_set_plan; the library's table of plans measured on MI355X for common decoder
+ * projection shapes (per bucket of M); otherwise a rule fitted to those measurements.
  * The choice is per shape, from measurements, as "Beating FP16 with 4-bit Weights", section
  * "Things I got wrong along the way", asks (autotune per shape; the best split factor is not
  * the same for every projection), and as "Triton Kernel Matches bitsandbytes: Why Both Lose to
