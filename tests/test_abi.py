@@ -120,6 +120,15 @@ PLAN_SHAPES = [(m, k, n) for m in (1, 2, 4, 8, 16, 17, 23, 24, 33, 48, 49, 63, 6
                               (768, 2048), (4096, 128256), (128, 4), (384, 100), (4096, 28676),
                               (4096, 1024), (5120, 5120), (13824, 5120), (3584, 18944), (7168, 1024),
                               (2560, 10240), (3072, 3072), (896, 4864)]]
+# every (K, N) of the dispatcher's plan table beyond the shapes above, at the M of each bucket
+# and around its edges
+TABLE_KN = [(4096, 512), (5120, 1024), (8192, 1024), (16384, 1024), (2048, 512), (2048, 2048), (4096, 2048),
+            (8192, 2048), (1024, 4096), (6144, 4096), (8192, 4096), (11008, 4096), (4096, 6144), (4096, 8192),
+            (2048, 8192), (18944, 3584), (4096, 11008), (5120, 13824), (10240, 2560), (4864, 896),
+            (1536, 8960), (8960, 1536), (3072, 8192), (8192, 3072), (4096, 3072), (12288, 4096), (4096, 28672),
+            (4096, 12288), (2048, 11264), (2048, 12288), (1408, 8192), (768, 16384), (1408, 16384),
+            (4096, 1792), (14336, 512), (4096, 16032), (8192, 8192), (8192, 28672), (28672, 8192)]
+PLAN_SHAPES += [(m, k, n) for m in (1, 2, 4, 5, 16, 17) for (k, n) in TABLE_KN]
 
 
 @pytest.mark.parametrize("M,K,N", PLAN_SHAPES)
